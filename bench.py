@@ -1,0 +1,270 @@
+"""Benchmark of the FP8 linear-layer hot path on one MI355X.
+
+One step = the whole path over the four Llama-3.1-8B decoder linears at the
+training batch of M = 8192 tokens (8 sequences x 1024):
+  for each of QKV (4096->6144), O (4096->4096), gate+up (4096->28672), down (14336->4096):
+    128x128 re-quantization of the BF16 master weight (+ transposed codes),
+    1x128 quantization of X, forward GEMM with the fused 1x128 quantization of Y,
+    1x128 quantization of dY, dgrad GEMM, 128x1 quantization of dY (transposed),
+    128x1 re-quantization of X from its FP8 codes (transposed), wgrad GEMM.
+Inputs are seeded synthetic tensors resident in HBM before timing starts.
+`value` = GEMM FLOPs of the step (3 x 2*M*N*K per linear) / step time.
+
+Prints ONE JSON line.  --gpus above 1 is refused: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+METRIC = "FP8 linear fwd+bwd TFLOP/s (% FP8 MFMA peak) + quantizer GB/s, Llama-8B shapes"
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense OCP-FP8 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+LAYERS = [("qkv", 6144, 4096), ("o", 4096, 4096), ("gate_up", 28672, 4096), ("down", 4096, 14336)]
+M_TOKENS = 8192
+COUNTERS = os.path.join(ROOT, "profiles", "gemm_counters.json")
+GEMM_SRC = os.path.join(ROOT, "fp8_blockwise_quantized_amd", "csrc", "gemm.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run 1 GiB device copies first (HBM counter calibration)")
+    ap.add_argument("--events", type=int, default=1, help="per-kernel HIP events in the timed loop")
+    return ap.parse_args()
+
+
+def q_bytes_1x128(M, K):      # BF16 in, E4M3 + FP32 scale per 128 out
+    return M * K * 2 + M * K + M * K // 128 * 4
+
+
+def q_bytes_w(N, K, transposed=True):
+    return N * K * 2 + N * K * (2 if transposed else 1) + N * K // 16384 * 4
+
+
+def q_bytes_128x1_bf16(M, K):
+    return M * K * 2 + M * K + M * K // 128 * 4
+
+
+def q_bytes_128x1_fp8(M, K):  # E4M3 + 1x128 scales in, E4M3 + 128x1 scales out
+    return M * K + M * K // 128 * 4 + M * K + M * K // 128 * 4
+
+
+class Layer:
+    def __init__(self, J, torch, name, N, K, M, seed):
+        from fp8_blockwise_quantized_amd import inputs
+        self.name, self.N, self.K, self.M = name, N, K, M
+        dev = "cuda"
+        bf = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(dev)
+        self.x = bf(inputs.activations_with_outliers(M, K, seed=seed))
+        self.w = bf(inputs.normal_bf16((N, K), 0.02, seed=seed, tensor_id=inputs.ID_W))
+        self.dy = bf(inputs.normal_bf16((M, N), 1e-3, seed=seed, tensor_id=inputs.ID_DY))
+        u8, f32 = torch.uint8, torch.float32
+        e = lambda shape, dt: torch.empty(shape, dtype=dt, device=dev)
+        Mp = -(-M // 128) * 128
+        self.wq, self.ws, self.wqT = e((N, K), u8), e((N // 128, K // 128), f32), e((K, N), u8)
+        self.xq, self.xs = e((M, K), u8), e((K // 128, M), f32)
+        self.y, self.yq, self.ys = e((M, N), torch.bfloat16), e((M, N), u8), e((N // 128, M), f32)
+        self.dyq, self.dys = e((M, N), u8), e((N // 128, M), f32)
+        self.dx = e((M, K), torch.bfloat16)
+        self.dyqT, self.dysT = e((N, Mp), u8), e((Mp // 128, N), f32)
+        self.xqT, self.xsT = e((K, Mp), u8), e((Mp // 128, K), f32)
+        self.dw = e((N, K), f32)
+        self.flops = 2.0 * M * N * K
+
+    def ops(self, J):
+        """(kernel kind, algorithmic work, unit, callable) in path order."""
+        M, N, K = self.M, self.N, self.K
+        return [
+            ("quant_w128x128", q_bytes_w(N, K), "B",
+             lambda: J.jet_quant_weight_128x128(self.w, q=self.wq, s=self.ws, qT=self.wqT)),
+            ("quant_1x128", q_bytes_1x128(M, K), "B",
+             lambda: J.jet_quant_act_1x128(self.x, q=self.xq, s=self.xs)),
+            ("gemm_fwd", self.flops, "F",
+             lambda: J.jet_fp8_linear_fwd(self.xq, self.xs, self.wq, self.ws, y=self.y,
+                                          fuse_quant=True, yq=self.yq, ys=self.ys)),
+            ("quant_1x128", q_bytes_1x128(M, N), "B",
+             lambda: J.jet_quant_act_1x128(self.dy, q=self.dyq, s=self.dys)),
+            ("gemm_dgrad", self.flops, "F",
+             lambda: J.jet_fp8_linear_dgrad(self.dyq, self.dys, self.wqT, self.ws, dx=self.dx)),
+            ("quant_128x1_T_bf16", q_bytes_128x1_bf16(M, N), "B",
+             lambda: J.jet_quant_act_128x1_T(self.dy, qT=self.dyqT, sT=self.dysT)),
+            ("quant_128x1_T_fp8", q_bytes_128x1_fp8(M, K), "B",
+             lambda: J.jet_quant_act_128x1_T(self.xq, src_s=self.xs, qT=self.xqT, sT=self.xsT)),
+            ("gemm_wgrad", self.flops, "F",
+             lambda: J.jet_fp8_linear_wgrad(self.dyqT, self.dysT, self.xqT, self.xsT, M, dw=self.dw)),
+        ]
+
+
+def copy_probe(torch):
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+
+
+def cpu_baseline():
+    """The oracle (untuned) on a bounded sample of the workload: the QKV
+    linear (4096 -> 6144) with its full weight and 512 of the 8192 tokens,
+    through every step of the path; scaled to TFLOP/s of the sample's GEMMs."""
+    from oracle import jet_oracle as O
+    from fp8_blockwise_quantized_amd import inputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    Ms, N, K = 512, 6144, 4096
+    x = inputs.activations_with_outliers(Ms, K, seed=0)
+    w = inputs.normal_bf16((N, K), 0.02, seed=0, tensor_id=inputs.ID_W)
+    dy = inputs.normal_bf16((Ms, N), 1e-3, seed=0, tensor_id=inputs.ID_DY)
+    t0 = time.perf_counter()
+    wq, ws = O.quant_128x128(w)
+    xq, xs = O.quant_1x128(x)
+    y = O.bf16_rne(O.fl32(O.gemm_fwd(xq, xs, wq, ws)))
+    O.quant_1x128(y)
+    dyq, dys = O.quant_1x128(dy)
+    O.gemm_dgrad(dyq, dys, wq, ws)
+    dyqT, dysT = O.quant_128x1_T(dy)
+    xqT, xsT = O.requant_128x1_T_from_1x128(xq, xs)
+    O.gemm_wgrad(dyqT, dysT, xqT, xsT, Ms)
+    dt = time.perf_counter() - t0
+    flops = 3 * 2.0 * Ms * N * K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"QKV linear 4096->6144, full weight, {Ms} of {M_TOKENS} tokens, all path steps "
+                      f"(weight/act quantizers, fwd+fused quant, dgrad, 128x1 quantizers, wgrad); "
+                      f"host cpu_count={os.cpu_count()}"}
+
+
+def counters_for(kernel: str):
+    """HBM traffic per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None if absent or taken on a different gemm.hip."""
+    try:
+        c = json.load(open(COUNTERS))
+    except (OSError, ValueError):
+        return None
+    sha = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
+    if c.get("gemm_source_sha256") != sha:
+        return None
+    k = c.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: this build runs on exactly one GPU "
+              f"(the path shards by tokens; see DESIGN.md for the multi-GPU design).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    from fp8_blockwise_quantized_amd import jetfp8 as J
+
+    if args.copy_probe:
+        copy_probe(torch)
+    layers = [Layer(J, torch, n, N, K, M_TOKENS, seed=0) for (n, N, K) in LAYERS]
+    plan = [(l.name, kind, work, unit, fn) for l in layers for (kind, work, unit, fn) in l.ops(J)]
+    torch.cuda.synchronize()
+
+    def step(evs=None):
+        for i, (_, _, _, _, fn) in enumerate(plan):
+            if evs is not None:
+                evs[i][0].record()
+            fn()
+            if evs is not None:
+                evs[i][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    E = torch.cuda.Event
+    per = [[[E(enable_timing=True), E(enable_timing=True)] for _ in plan] for _ in range(args.steps)]
+    t_start, t_end = E(enable_timing=True), E(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for s in range(args.steps):
+        step(per[s] if args.events else None)
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+
+    # per-kernel-kind aggregates over the timed region
+    agg = {}
+    for s in range(args.steps):
+        for i, (lname, kind, work, unit, _) in enumerate(plan):
+            if not args.events:
+                continue
+            ms = per[s][i][0].elapsed_time(per[s][i][1])
+            a = agg.setdefault(kind, {"ms": 0.0, "work": 0.0, "launches": 0, "unit": unit})
+            a["ms"] += ms
+            a["work"] += work
+            a["launches"] += 1
+    flops_step = sum(3 * l.flops for l in layers)
+    value = flops_step / (ms_step * 1e-3) / 1e12
+
+    kernels = {}
+    for kind, a in agg.items():
+        sec = a["ms"] * 1e-3
+        rate = a["work"] / sec
+        d = {"avg_us": round(a["ms"] / a["launches"] * 1e3, 2), "launches_per_step": a["launches"] // args.steps,
+             "share_of_step": round(a["ms"] / args.steps / ms_step, 4)}
+        if a["unit"] == "F":
+            d.update(tflops=round(rate / 1e12, 1), frac_fp8_peak=round(rate / 1e12 / PEAK_FP8_TFLOPS, 4))
+        else:
+            d.update(gbs=round(rate / 1e9, 1), frac_hbm_peak=round(rate / 1e9 / PEAK_HBM_GBS, 4))
+        kernels[kind] = d
+
+    gemm_kinds = [k for k in agg if agg[k]["unit"] == "F"]
+    roofline = None
+    if gemm_kinds:
+        dom = max(gemm_kinds, key=lambda k: agg[k]["ms"])
+        a = agg[dom]
+        achieved = a["work"] / a["launches"] / (a["ms"] / a["launches"] * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+                    "traffic": counters_for(dom),
+                    "flops_per_launch": a["work"] / a["launches"]}
+
+    quant_bytes = sum(agg[k]["work"] for k in agg if agg[k]["unit"] == "B") / args.steps
+    quant_ms = sum(agg[k]["ms"] for k in agg if agg[k]["unit"] == "B") / args.steps
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "e4m3",
+        "data": "synthetic",
+        "config": {"workload": "Llama-3.1-8B decoder linears (QKV 4096->6144, O 4096->4096, "
+                               "gate+up 4096->28672, down 14336->4096), training batch M=8192 tokens, "
+                               "fwd + dgrad + wgrad with every quantizer and the BF16-master weight "
+                               "re-quantization per step",
+                   "M": M_TOKENS, "parallelism": "none (1 GPU)"},
+        "frac_fp8_peak_step": round(value / PEAK_FP8_TFLOPS, 4),
+        "quantizer_gbs_step": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1) if quant_ms else None,
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,204 @@
+// C ABI of the FP8 linear-layer library (declarations and contracts in
+// include/jetfp8.h).  This file validates arguments, maps each entry point
+// onto a kernel launch and reports errors; it holds no arithmetic.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/jetfp8.h"
+#include "jet_launch.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return JET_OK;
+  return fail(JET_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+constexpr int64_t kG = 128;
+constexpr int64_t kMaxDim = int64_t(1) << 30;   // GEMM tile indices are 32-bit
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int jet_abi_version(void) { return JET_ABI_VERSION; }
+
+const char* jet_status_string(int status) {
+  switch (status) {
+    case JET_OK: return "JET_OK";
+    case JET_ERR_NULL: return "JET_ERR_NULL";
+    case JET_ERR_SHAPE: return "JET_ERR_SHAPE";
+    case JET_ERR_ALIGN: return "JET_ERR_ALIGN";
+    case JET_ERR_DTYPE: return "JET_ERR_DTYPE";
+    case JET_ERR_WORKSPACE: return "JET_ERR_WORKSPACE";
+    case JET_ERR_HIP: return "JET_ERR_HIP";
+    default: return "JET_ERR_UNKNOWN";
+  }
+}
+
+const char* jet_last_error(void) { return g_last_error; }
+
+int jet_quant_act_1x128(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,
+                        float* s, void* stream) {
+  g_last_error[0] = 0;
+  if (M < 0 || K < 0 || K % kG || M > kMaxDim || K > kMaxDim)
+    return fail(JET_ERR_SHAPE, "quant_act_1x128: need M >= 0 and K a multiple of 128 (M=%lld K=%lld)",
+                (long long)M, (long long)K);
+  if (M == 0 || K == 0) return JET_OK;
+  if (!x || !q || !s) return fail(JET_ERR_NULL, "quant_act_1x128: null pointer");
+  if (ldx < K || ldq < K) return fail(JET_ERR_SHAPE, "quant_act_1x128: leading dimension < K");
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4) || ldx % 8 || ldq % 16)
+    return fail(JET_ERR_ALIGN, "quant_act_1x128: x, q need 16-byte alignment, ldx %% 8, ldq %% 16");
+  return hip_status(jet::launch_quant_1x128(static_cast<const uint16_t*>(x), M, K, ldx, q, ldq, s,
+                                            as_stream(stream)),
+                    "quant_act_1x128");
+}
+
+int jet_quant_act_128x1_T(const void* src, int src_dtype, const float* src_s, int64_t M, int64_t K,
+                          int64_t ldsrc, uint8_t* qT, int64_t ldqT, float* sT, void* stream) {
+  g_last_error[0] = 0;
+  if (src_dtype != JET_BF16 && src_dtype != JET_E4M3)
+    return fail(JET_ERR_DTYPE, "quant_act_128x1_T: src_dtype must be JET_BF16 or JET_E4M3");
+  if (M < 0 || K < 0 || K % kG || M > kMaxDim || K > kMaxDim)
+    return fail(JET_ERR_SHAPE, "quant_act_128x1_T: need M >= 0 and K a multiple of 128");
+  if (M == 0 || K == 0) return JET_OK;
+  const bool fp8 = src_dtype == JET_E4M3;
+  if (!src || !qT || !sT || (fp8 && !src_s))
+    return fail(JET_ERR_NULL, "quant_act_128x1_T: null pointer");
+  const int64_t Mp = (M + kG - 1) / kG * kG;
+  if (ldsrc < K || ldqT < Mp)
+    return fail(JET_ERR_SHAPE, "quant_act_128x1_T: ldsrc < K or ldqT < ceil(M/128)*128");
+  const int64_t ld_bytes = fp8 ? ldsrc : 2 * ldsrc;
+  if (!aligned(src, 16) || !aligned(qT, 16) || !aligned(sT, 16) || ld_bytes % 16 || ldqT % 16 ||
+      (fp8 && !aligned(src_s, 4)))
+    return fail(JET_ERR_ALIGN, "quant_act_128x1_T: src, qT, sT need 16-byte alignment; row strides 16 bytes");
+  return hip_status(jet::launch_quant_128x1_T(src, fp8, src_s, M, K, ldsrc, qT, ldqT, sT,
+                                              as_stream(stream)),
+                    "quant_act_128x1_T");
+}
+
+int jet_quant_weight_128x128(const void* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q, float* s,
+                             uint8_t* qT, void* stream) {
+  g_last_error[0] = 0;
+  if (N < 0 || K < 0 || N % kG || K % kG || N > kMaxDim || K > kMaxDim)
+    return fail(JET_ERR_SHAPE, "quant_weight_128x128: N and K must be multiples of 128");
+  if (N == 0 || K == 0) return JET_OK;
+  if (!w || !q || !s) return fail(JET_ERR_NULL, "quant_weight_128x128: null pointer");
+  if (ldw < K) return fail(JET_ERR_SHAPE, "quant_weight_128x128: ldw < K");
+  if (!aligned(w, 16) || !aligned(q, 16) || !aligned(s, 4) || ldw % 8 || (qT && !aligned(qT, 16)))
+    return fail(JET_ERR_ALIGN, "quant_weight_128x128: w, q, qT need 16-byte alignment, ldw %% 8");
+  return hip_status(jet::launch_quant_128x128(static_cast<const uint16_t*>(w), N, K, ldw, q, s, qT,
+                                              as_stream(stream)),
+                    "quant_weight_128x128");
+}
+
+size_t jet_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {
+  (void)op; (void)M; (void)N; (void)K;
+  return 0;
+}
+
+static int check_gemm_common(const char* name, int64_t M, int64_t N, int64_t K, int op,
+                             size_t ws_bytes, const void* workspace) {
+  if (M < 0 || N < 0 || K < 0 || N % kG || K % kG || M > kMaxDim || N > kMaxDim || K > kMaxDim)
+    return fail(JET_ERR_SHAPE, "%s: need M >= 0, N and K multiples of 128 (M=%lld N=%lld K=%lld)",
+                name, (long long)M, (long long)N, (long long)K);
+  const size_t need = jet_workspace_bytes(op, M, N, K);
+  if (ws_bytes < need || (need && !workspace))
+    return fail(JET_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", name, need);
+  return JET_OK;
+}
+
+int jet_fp8_linear_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
+                       int64_t M, int64_t N, int64_t K, void* y, int y_dtype, uint8_t* yq, float* ys,
+                       void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  if (int st = check_gemm_common("fp8_linear_fwd", M, N, K, JET_OP_FWD, ws_bytes, workspace)) return st;
+  if (y_dtype != JET_BF16 && y_dtype != JET_F32)
+    return fail(JET_ERR_DTYPE, "fp8_linear_fwd: y_dtype must be JET_BF16 or JET_F32");
+  const bool fuse = yq || ys;
+  if (fuse && (!yq || !ys)) return fail(JET_ERR_NULL, "fp8_linear_fwd: yq and ys go together");
+  if (fuse && y_dtype != JET_BF16)
+    return fail(JET_ERR_DTYPE, "fp8_linear_fwd: the fused 1x128 output needs y_dtype JET_BF16");
+  if (M == 0 || N == 0) return JET_OK;
+  if (!xq || !xs || !wq || !ws || !y) return fail(JET_ERR_NULL, "fp8_linear_fwd: null pointer");
+  if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(y, 16) || !aligned(xs, 4) || !aligned(ws, 4) ||
+      (fuse && (!aligned(yq, 16) || !aligned(ys, 4))))
+    return fail(JET_ERR_ALIGN, "fp8_linear_fwd: operands and outputs need 16-byte alignment");
+  jet::GemmArgs a{};
+  a.A = xq; a.lda = K;
+  a.B = wq; a.ldb = K;
+  a.sA = xs; a.sA_ld = M;
+  a.sB = ws; a.sB_o = K / kG; a.sB_c = 1;
+  a.C = y; a.ldc = N; a.Cq = yq; a.Cs = ys;
+  a.M = (int)M; a.N = (int)N; a.Kc = (int)K;
+  return hip_status(jet::launch_gemm(a, jet::kRowBlock, y_dtype == JET_BF16 ? jet::kOutBf16 : jet::kOutF32,
+                                     false, fuse, as_stream(stream)),
+                    "fp8_linear_fwd");
+}
+
+int jet_fp8_linear_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* wqT, const float* ws,
+                         int64_t M, int64_t N, int64_t K, void* dx, int dx_dtype, void* workspace,
+                         size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  if (int st = check_gemm_common("fp8_linear_dgrad", M, N, K, JET_OP_DGRAD, ws_bytes, workspace)) return st;
+  if (dx_dtype != JET_BF16 && dx_dtype != JET_F32)
+    return fail(JET_ERR_DTYPE, "fp8_linear_dgrad: dx_dtype must be JET_BF16 or JET_F32");
+  if (M == 0 || K == 0) return JET_OK;
+  if (!dyq || !dys || !wqT || !ws || !dx) return fail(JET_ERR_NULL, "fp8_linear_dgrad: null pointer");
+  if (!aligned(dyq, 16) || !aligned(wqT, 16) || !aligned(dx, 16) || !aligned(dys, 4) || !aligned(ws, 4))
+    return fail(JET_ERR_ALIGN, "fp8_linear_dgrad: operands and output need 16-byte alignment");
+  jet::GemmArgs a{};
+  a.A = dyq; a.lda = N;
+  a.B = wqT; a.ldb = N;
+  a.sA = dys; a.sA_ld = M;
+  a.sB = ws; a.sB_o = 1; a.sB_c = K / kG;
+  a.C = dx; a.ldc = K;
+  a.M = (int)M; a.N = (int)K; a.Kc = (int)N;
+  return hip_status(jet::launch_gemm(a, jet::kRowBlock, dx_dtype == JET_BF16 ? jet::kOutBf16 : jet::kOutF32,
+                                     false, false, as_stream(stream)),
+                    "fp8_linear_dgrad");
+}
+
+int jet_fp8_linear_wgrad(const uint8_t* dyqT, const float* dysT, const uint8_t* xqT, const float* xsT,
+                         int64_t M, int64_t N, int64_t K, void* dw, int dw_dtype, int accumulate,
+                         void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  if (int st = check_gemm_common("fp8_linear_wgrad", M, N, K, JET_OP_WGRAD, ws_bytes, workspace)) return st;
+  if (dw_dtype != JET_F32 && dw_dtype != JET_BF16)
+    return fail(JET_ERR_DTYPE, "fp8_linear_wgrad: dw_dtype must be JET_F32 or JET_BF16");
+  if (accumulate && dw_dtype != JET_F32)
+    return fail(JET_ERR_DTYPE, "fp8_linear_wgrad: accumulate needs dw_dtype JET_F32");
+  if (N == 0 || K == 0) return JET_OK;
+  if (!dw) return fail(JET_ERR_NULL, "fp8_linear_wgrad: null pointer");
+  if (M > 0 && (!dyqT || !dysT || !xqT || !xsT)) return fail(JET_ERR_NULL, "fp8_linear_wgrad: null pointer");
+  const int64_t Mp = (M + kG - 1) / kG * kG;
+  if (!aligned(dw, 16) || (M > 0 && (!aligned(dyqT, 16) || !aligned(xqT, 16) || !aligned(dysT, 4) ||
+                                     !aligned(xsT, 4))))
+    return fail(JET_ERR_ALIGN, "fp8_linear_wgrad: operands and output need 16-byte alignment");
+  jet::GemmArgs a{};
+  a.A = dyqT; a.lda = Mp;
+  a.B = xqT; a.ldb = Mp;
+  a.sA = dysT; a.sA_ld = N;
+  a.sB = xsT; a.sB_o = 1; a.sB_c = K;
+  a.C = dw; a.ldc = K;
+  a.M = (int)N; a.N = (int)K; a.Kc = (int)Mp;
+  return hip_status(jet::launch_gemm(a, jet::kRowCol, dw_dtype == JET_BF16 ? jet::kOutBf16 : jet::kOutF32,
+                                     accumulate != 0, false, as_stream(stream)),
+                    "fp8_linear_wgrad");
+}
+
+}  // extern "C"

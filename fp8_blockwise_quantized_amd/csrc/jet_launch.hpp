@@ -1,0 +1,36 @@
+// Internal launch interface between the C ABI (abi.hip) and the kernels.
+// Arguments are validated by the caller; these functions only launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace jet {
+
+enum { kRowBlock = 0, kRowCol = 1 };   // scale modes of the GEMM
+enum { kOutBf16 = 0, kOutF32 = 1 };    // GEMM output element types
+
+// C[M, N] (+)= sum_kb scale * A[M, Kc-slab] . B[N, Kc-slab]^T ; see gemm.hip.
+struct GemmArgs {
+  const uint8_t* A;      // [M, Kc] E4M3, row stride lda bytes
+  const uint8_t* B;      // [N, Kc] E4M3, row stride ldb bytes
+  const float* sA;       // row scales: sA[kb * sA_ld + m]
+  const float* sB;       // ROWBLOCK: sB[(n/128) * sB_o + kb * sB_c]; ROWCOL: sB[kb * sB_c + n]
+  void* C;               // [M, N] output, row stride ldc elements
+  uint8_t* Cq;           // fused 1x128 quantization of a BF16 C (or null)
+  float* Cs;             //   and its scales [N/128, M]
+  int64_t lda, ldb, sA_ld, sB_o, sB_c, ldc;
+  int M, N, Kc;
+};
+
+hipError_t launch_quant_1x128(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                              int64_t ldq, float* s, hipStream_t st);
+hipError_t launch_quant_128x128(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
+                                float* s, uint8_t* qT, hipStream_t st);
+hipError_t launch_quant_128x1_T(const void* src, bool fp8src, const float* src_s, int64_t M,
+                                int64_t K, int64_t ldsrc, uint8_t* qT, int64_t ldqT, float* sT,
+                                hipStream_t st);
+hipError_t launch_gemm(const GemmArgs& a, int mode, int out, bool accum, bool fuseq,
+                       hipStream_t st);
+
+}  // namespace jet

@@ -1,0 +1,243 @@
+// E4M3 group quantizers for gfx950 (bandwidth-bound; no MFMA).
+//
+//  * 1x128 groups along the row (activations, output gradients): gist.science
+//    explainer "Jet-RL ...", section "Quantisierungsschema"; nmedialink table
+//    in section "为什么FP8适配线性层？" ([1,128], FP32 scale).
+//  * 128x128 blocks (weights, re-quantized from the BF16 master on every weight
+//    sync): same sources ([128,128]); 66260.cn FP8-RL item, weight-sync paragraph.
+//  * 128x1 groups along the token axis, written transposed, for the weight
+//    gradient: explainer "Quantisierungsschema" (128x1 for WGrad); 163.com
+//    write-up section 五 (1x128 activations re-quantized as 128x1).
+//
+// Every kernel reads each input byte once from HBM with 16-byte loads, keeps the
+// group in registers, reduces the group maximum with integer/DPP operations
+// inside one wavefront (plus one LDS exchange for the 128x128 block), and
+// writes codes with 8-byte stores.
+#include "jet_device.hpp"
+#include "jet_launch.hpp"
+
+namespace jet {
+
+// ---------------------------------------------------------------------------
+// 1x128.  One 16-lane DPP row handles one group of 128 BF16 values (256 bytes,
+// 16 bytes per lane); a 256-thread block handles 16 rows of one column group
+// per pass and PASSES passes, all loads issued before any compute.
+// ---------------------------------------------------------------------------
+template <int PASSES>
+__global__ __launch_bounds__(256) void k_quant_1x128(const uint16_t* __restrict__ x, int64_t M,
+                                                     int64_t ldx, uint8_t* __restrict__ q,
+                                                     int64_t ldq, float* __restrict__ s) {
+  const int lane16 = threadIdx.x & 15;
+  const int64_t j = blockIdx.y;
+  const int64_t mrow = (int64_t)blockIdx.x * (16 * PASSES) + (threadIdx.x >> 4);
+  uint4 v[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int64_t m = mrow + 16 * p;
+    v[p] = make_uint4(0u, 0u, 0u, 0u);
+    if (m < M) v[p] = *reinterpret_cast<const uint4*>(x + m * ldx + j * kGroup + lane16 * 8);
+  }
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int64_t m = mrow + 16 * p;
+    uint32_t am = max_abs_bf16x2(0u, v[p].x);
+    am = max_abs_bf16x2(am, v[p].y);
+    am = max_abs_bf16x2(am, v[p].z);
+    am = max_abs_bf16x2(am, v[p].w);
+    am = row16_max_u16x2(am);
+    const ScalePair sp = scale_pair(fold_bf16x2(am));
+    const uint32_t c0 = e4m3x4(bf16_lo(v[p].x) * sp.r, bf16_hi(v[p].x) * sp.r,
+                               bf16_lo(v[p].y) * sp.r, bf16_hi(v[p].y) * sp.r);
+    const uint32_t c1 = e4m3x4(bf16_lo(v[p].z) * sp.r, bf16_hi(v[p].z) * sp.r,
+                               bf16_lo(v[p].w) * sp.r, bf16_hi(v[p].w) * sp.r);
+    if (m < M) {
+      *reinterpret_cast<uint2*>(q + m * ldq + j * kGroup + lane16 * 8) = make_uint2(c0, c1);
+      if (lane16 == 0) s[j * M + m] = sp.s;
+    }
+  }
+}
+
+hipError_t launch_quant_1x128(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                              int64_t ldq, float* s, hipStream_t st) {
+  if (M == 0) return hipSuccess;
+  constexpr int kPasses = 4;
+  dim3 grid((unsigned)((M + 16 * kPasses - 1) / (16 * kPasses)), (unsigned)(K / kGroup));
+  hipLaunchKernelGGL(k_quant_1x128<kPasses>, grid, dim3(256), 0, st, x, M, ldx, q, ldq, s);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// 128x128.  One 256-thread block per block of the weight; thread t owns rows
+// 8*(t/16)..+7 and columns 8*(t%16)..+7, i.e. an 8x8 tile held in registers.
+// The block maximum: packed-u16 max over the tile, DPP over the 16 lanes of a
+// row, then one LDS exchange between the 16 DPP rows of the block.  Row-major
+// codes are packed along the tile's rows, transposed codes along its columns.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_quant_128x128(const uint16_t* __restrict__ w, int64_t N,
+                                                       int64_t K, int64_t ldw,
+                                                       uint8_t* __restrict__ q,
+                                                       float* __restrict__ s,
+                                                       uint8_t* __restrict__ qT) {
+  __shared__ uint32_t red[16];
+  const int c = threadIdx.x & 15;
+  const int ri = threadIdx.x >> 4;
+  const int64_t kb = blockIdx.x, nb = blockIdx.y;
+  const int64_t n0 = nb * kGroup + 8 * ri;
+  const int64_t k0 = kb * kGroup + 8 * c;
+  uint4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = *reinterpret_cast<const uint4*>(w + (n0 + i) * ldw + k0);
+  uint32_t am = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    am = max_abs_bf16x2(am, v[i].x);
+    am = max_abs_bf16x2(am, v[i].y);
+    am = max_abs_bf16x2(am, v[i].z);
+    am = max_abs_bf16x2(am, v[i].w);
+  }
+  am = row16_max_u16x2(am);
+  if (c == 0) red[ri] = am;
+  __syncthreads();
+  am = red[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) am = max_abs_bf16x2(am, red[i]);
+  const ScalePair sp = scale_pair(fold_bf16x2(am));
+  if (threadIdx.x == 0) s[nb * (K / kGroup) + kb] = sp.s;
+
+  float f[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    f[i][0] = bf16_lo(v[i].x) * sp.r; f[i][1] = bf16_hi(v[i].x) * sp.r;
+    f[i][2] = bf16_lo(v[i].y) * sp.r; f[i][3] = bf16_hi(v[i].y) * sp.r;
+    f[i][4] = bf16_lo(v[i].z) * sp.r; f[i][5] = bf16_hi(v[i].z) * sp.r;
+    f[i][6] = bf16_lo(v[i].w) * sp.r; f[i][7] = bf16_hi(v[i].w) * sp.r;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t lo = e4m3x4(f[i][0], f[i][1], f[i][2], f[i][3]);
+    const uint32_t hi = e4m3x4(f[i][4], f[i][5], f[i][6], f[i][7]);
+    *reinterpret_cast<uint2*>(q + (n0 + i) * K + k0) = make_uint2(lo, hi);
+  }
+  if (qT != nullptr) {
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const uint32_t lo = e4m3x4(f[0][jj], f[1][jj], f[2][jj], f[3][jj]);
+      const uint32_t hi = e4m3x4(f[4][jj], f[5][jj], f[6][jj], f[7][jj]);
+      *reinterpret_cast<uint2*>(qT + (k0 + jj) * N + n0) = make_uint2(lo, hi);
+    }
+  }
+}
+
+hipError_t launch_quant_128x128(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
+                                float* s, uint8_t* qT, hipStream_t st) {
+  if (N == 0 || K == 0) return hipSuccess;
+  dim3 grid((unsigned)(K / kGroup), (unsigned)(N / kGroup));
+  hipLaunchKernelGGL(k_quant_128x128, grid, dim3(256), 0, st, w, N, K, ldw, q, s, qT);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// 128x1, transposed.  A block handles one 128-row group g and 16*CW columns;
+// thread t owns rows 8*(t%16)..+7 of the group and columns CW*(t/16)..+CW-1
+// (16 source bytes per row).  The 16 lanes of a DPP row share the columns and
+// cover all 128 rows, so each column's maximum is a DPP-row reduction.  Codes
+// of column k for the thread's 8 rows are packed into one 8-byte store at
+// qT[k][128g + 8*(t%16)], so a wavefront store writes 128 contiguous bytes of
+// four qT rows.  Rows past M are zeros: they do not change a column maximum
+// and they encode to 0x00 in the padding columns.
+//
+// FP8SRC: the source is the 1x128-quantized activation (codes + [K/128, M]
+// scales); the value re-quantized is fl32(E4M3value(code) * scale).
+// ---------------------------------------------------------------------------
+template <bool FP8SRC>
+__global__ __launch_bounds__(256) void k_quant_128x1_T(const void* __restrict__ src,
+                                                       const float* __restrict__ src_s,
+                                                       int64_t M, int64_t K, int64_t ldsrc,
+                                                       uint8_t* __restrict__ qT, int64_t ldqT,
+                                                       float* __restrict__ sT) {
+  constexpr int CW = FP8SRC ? 16 : 8;
+  const int ri = threadIdx.x & 15;
+  const int c = threadIdx.x >> 4;
+  const int64_t g = blockIdx.y;
+  const int64_t col0 = (int64_t)blockIdx.x * (16 * CW) + (int64_t)c * CW;
+  const bool colok = col0 < K;
+  const int64_t m0 = g * kGroup + 8 * ri;
+
+  float f[8][CW];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t m = m0 + i;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (colok && m < M) {
+      if (FP8SRC)
+        v = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(src) + m * ldsrc + col0);
+      else
+        v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + m * ldsrc + col0);
+    }
+    if constexpr (FP8SRC) {
+      float sc = 0.0f;
+      if (colok && m < M) sc = src_s[(col0 / kGroup) * M + m];
+      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        f[i][4 * d + 0] = e4m3_at<0>(wv[d]) * sc;
+        f[i][4 * d + 1] = e4m3_at<1>(wv[d]) * sc;
+        f[i][4 * d + 2] = e4m3_at<2>(wv[d]) * sc;
+        f[i][4 * d + 3] = e4m3_at<3>(wv[d]) * sc;
+      }
+    } else {
+      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        f[i][2 * d + 0] = bf16_lo(wv[d]);
+        f[i][2 * d + 1] = bf16_hi(wv[d]);
+      }
+    }
+  }
+
+  float rr[CW];
+  float ss[CW];
+#pragma unroll
+  for (int jj = 0; jj < CW; ++jj) {
+    float a = fabsf(f[0][jj]);
+#pragma unroll
+    for (int i = 1; i < 8; ++i) a = fmaxf(a, fabsf(f[i][jj]));
+    a = row16_max_f32(a);
+    const ScalePair sp = scale_pair(a);
+    rr[jj] = sp.r;
+    ss[jj] = sp.s;
+  }
+  if (!colok) return;
+  if (ri == 0) {
+#pragma unroll
+    for (int jj = 0; jj < CW; jj += 4)
+      *reinterpret_cast<float4*>(sT + g * K + col0 + jj) =
+          make_float4(ss[jj], ss[jj + 1], ss[jj + 2], ss[jj + 3]);
+  }
+#pragma unroll
+  for (int jj = 0; jj < CW; ++jj) {
+    const float r = rr[jj];
+    const uint32_t lo = e4m3x4(f[0][jj] * r, f[1][jj] * r, f[2][jj] * r, f[3][jj] * r);
+    const uint32_t hi = e4m3x4(f[4][jj] * r, f[5][jj] * r, f[6][jj] * r, f[7][jj] * r);
+    *reinterpret_cast<uint2*>(qT + (col0 + jj) * ldqT + m0) = make_uint2(lo, hi);
+  }
+}
+
+hipError_t launch_quant_128x1_T(const void* src, bool fp8src, const float* src_s, int64_t M,
+                                int64_t K, int64_t ldsrc, uint8_t* qT, int64_t ldqT, float* sT,
+                                hipStream_t st) {
+  if (M == 0 || K == 0) return hipSuccess;
+  const unsigned groups = (unsigned)((M + kGroup - 1) / kGroup);
+  if (fp8src) {
+    dim3 grid((unsigned)((K + 255) / 256), groups);
+    hipLaunchKernelGGL(k_quant_128x1_T<true>, grid, dim3(256), 0, st, src, src_s, M, K, ldsrc,
+                       qT, ldqT, sT);
+  } else {
+    dim3 grid((unsigned)(K / kGroup), groups);
+    hipLaunchKernelGGL(k_quant_128x1_T<false>, grid, dim3(256), 0, st, src, src_s, M, K, ldsrc,
+                       qT, ldqT, sT);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace jet

@@ -1,0 +1,228 @@
+"""Python binding of libjetfp8.so: argument marshalling only.
+
+Each function has the name of the C entry point it calls (include/jetfp8.h)
+and takes torch tensors: torch provides device memory and the current HIP
+stream, nothing else.  Every step of the computation runs in the library's
+HIP kernels; if the library is missing, importing this module fails.
+
+E4M3 codes are held in torch.uint8 tensors (torch.float8_e4m3fn tensors are
+accepted and viewed as bytes).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libjetfp8.so")
+
+JET_OK, JET_ERR_NULL, JET_ERR_SHAPE, JET_ERR_ALIGN, JET_ERR_DTYPE, JET_ERR_WORKSPACE, JET_ERR_HIP = range(7)
+JET_BF16, JET_F32, JET_E4M3 = 1, 2, 3
+JET_OP_FWD, JET_OP_DGRAD, JET_OP_WGRAD = 0, 1, 2
+
+_p, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+
+# name -> argtypes, in header order
+SIGNATURES = {
+    "jet_abi_version": [],
+    "jet_status_string": [_i32],
+    "jet_last_error": [],
+    "jet_quant_act_1x128": [_p, _i64, _i64, _i64, _p, _i64, _p, _p],
+    "jet_quant_act_128x1_T": [_p, _i32, _p, _i64, _i64, _i64, _p, _i64, _p, _p],
+    "jet_quant_weight_128x128": [_p, _i64, _i64, _i64, _p, _p, _p, _p],
+    "jet_fp8_linear_fwd": [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _p, _p, _p, _sz, _p],
+    "jet_fp8_linear_dgrad": [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _p, _sz, _p],
+    "jet_fp8_linear_wgrad": [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _i32, _p, _sz, _p],
+    "jet_workspace_bytes": [_i32, _i64, _i64, _i64],
+}
+_RESTYPES = {"jet_status_string": ctypes.c_char_p, "jet_last_error": ctypes.c_char_p,
+             "jet_workspace_bytes": _sz}
+
+
+class JetError(RuntimeError):
+    def __init__(self, name: str, status: int, detail: str):
+        super().__init__(f"{name} failed: {_status_name(status)}: {detail}")
+        self.status = status
+
+
+def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m fp8_blockwise_quantized_amd._build`")
+    lib = ctypes.CDLL(path)
+    for name, args in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = _RESTYPES.get(name, ctypes.c_int)
+    return lib
+
+
+_lib = load_library()
+
+
+def _status_name(status: int) -> str:
+    return _lib.jet_status_string(status).decode()
+
+
+def _check(name: str, status: int) -> None:
+    if status != JET_OK:
+        raise JetError(name, status, _lib.jet_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _codes(t):
+    if t is None:
+        return None
+    if t.dtype == torch.float8_e4m3fn:
+        t = t.view(torch.uint8)
+    if t.dtype != torch.uint8:
+        raise TypeError("E4M3 codes must be uint8 or float8_e4m3fn tensors")
+    return t
+
+
+def _rowmajor(t, name):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D tensor with a contiguous last dimension")
+    return t
+
+
+def _empty(shape, dtype, like):
+    return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+# ---------------------------------------------------------------------------
+def jet_abi_version() -> int:
+    return _lib.jet_abi_version()
+
+
+def jet_status_string(status: int) -> str:
+    return _status_name(status)
+
+
+def jet_last_error() -> str:
+    return _lib.jet_last_error().decode()
+
+
+def jet_workspace_bytes(op: int, M: int, N: int, K: int) -> int:
+    return int(_lib.jet_workspace_bytes(op, M, N, K))
+
+
+def jet_quant_act_1x128(x, q=None, s=None, stream=None):
+    """x BF16 [M, K] -> (q uint8 [M, K], s float32 [K/128, M])."""
+    _rowmajor(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    M, K = x.shape
+    q = _codes(q) if q is not None else _empty((M, K), torch.uint8, x)
+    s = s if s is not None else _empty((K // 128, M), torch.float32, x)
+    _rowmajor(q, "q")
+    _check("jet_quant_act_1x128", _lib.jet_quant_act_1x128(
+        _ptr(x), M, K, x.stride(0), _ptr(q), q.stride(0), _ptr(s), _stream(stream)))
+    return q, s
+
+
+def jet_quant_act_128x1_T(src, src_s=None, qT=None, sT=None, stream=None):
+    """128x1 groups along rows, written transposed.
+
+    src BF16 [M, K] (src_s None), or E4M3 codes [M, K] with 1x128 scales
+    src_s [K/128, M].  Returns (qT uint8 [K, Mp], sT float32 [Mp/128, K]),
+    Mp = ceil(M/128)*128.
+    """
+    _rowmajor(src, "src")
+    M, K = src.shape
+    if src_s is None:
+        if src.dtype != torch.bfloat16:
+            raise TypeError("src must be bfloat16 when src_s is None")
+        dt = JET_BF16
+    else:
+        src = _codes(src)
+        dt = JET_E4M3
+    Mp = -(-M // 128) * 128
+    qT = _codes(qT) if qT is not None else _empty((K, Mp), torch.uint8, src)
+    sT = sT if sT is not None else _empty((Mp // 128, K), torch.float32, src)
+    _rowmajor(qT, "qT")
+    _check("jet_quant_act_128x1_T", _lib.jet_quant_act_128x1_T(
+        _ptr(src), dt, _ptr(src_s), M, K, src.stride(0), _ptr(qT), qT.stride(0), _ptr(sT),
+        _stream(stream)))
+    return qT, sT
+
+
+def jet_quant_weight_128x128(w, q=None, s=None, qT=None, transposed=True, stream=None):
+    """w BF16 [N, K] -> (q uint8 [N, K], s float32 [N/128, K/128], qT uint8 [K, N] or None)."""
+    _rowmajor(w, "w")
+    if w.dtype != torch.bfloat16:
+        raise TypeError("w must be bfloat16")
+    N, K = w.shape
+    q = _codes(q) if q is not None else _empty((N, K), torch.uint8, w)
+    s = s if s is not None else _empty((N // 128, K // 128), torch.float32, w)
+    if transposed and qT is None:
+        qT = _empty((K, N), torch.uint8, w)
+    qT = _codes(qT)
+    _check("jet_quant_weight_128x128", _lib.jet_quant_weight_128x128(
+        _ptr(w), N, K, w.stride(0), _ptr(q), _ptr(s), _ptr(qT), _stream(stream)))
+    return q, s, qT
+
+
+def _dtype_code(dt):
+    return {torch.bfloat16: JET_BF16, torch.float32: JET_F32}[dt]
+
+
+def jet_fp8_linear_fwd(xq, xs, wq, ws, y=None, out_dtype=torch.bfloat16, fuse_quant=False,
+                       yq=None, ys=None, workspace=None, stream=None):
+    """Y = deq(xq) . deq(wq)^T.  Returns y, or (y, yq, ys) with fuse_quant."""
+    xq, wq = _codes(xq), _codes(wq)
+    M, K = xq.shape
+    N = wq.shape[0]
+    y = y if y is not None else _empty((M, N), out_dtype, xq)
+    if fuse_quant:
+        yq = _codes(yq) if yq is not None else _empty((M, N), torch.uint8, xq)
+        ys = ys if ys is not None else _empty((N // 128, M), torch.float32, xq)
+    need = jet_workspace_bytes(JET_OP_FWD, M, N, K)
+    if workspace is None and need:
+        workspace = _empty((need,), torch.uint8, xq)
+    _check("jet_fp8_linear_fwd", _lib.jet_fp8_linear_fwd(
+        _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), M, N, K, _ptr(y), _dtype_code(y.dtype),
+        _ptr(yq), _ptr(ys), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+        _stream(stream)))
+    return (y, yq, ys) if fuse_quant else y
+
+
+def jet_fp8_linear_dgrad(dyq, dys, wqT, ws, dx=None, out_dtype=torch.bfloat16, workspace=None,
+                         stream=None):
+    """dX = deq(dyq) . deq(W); wqT is the transposed weight codes [K, N]."""
+    dyq, wqT = _codes(dyq), _codes(wqT)
+    M, N = dyq.shape
+    K = wqT.shape[0]
+    dx = dx if dx is not None else _empty((M, K), out_dtype, dyq)
+    need = jet_workspace_bytes(JET_OP_DGRAD, M, N, K)
+    if workspace is None and need:
+        workspace = _empty((need,), torch.uint8, dyq)
+    _check("jet_fp8_linear_dgrad", _lib.jet_fp8_linear_dgrad(
+        _ptr(dyq), _ptr(dys), _ptr(wqT), _ptr(ws), M, N, K, _ptr(dx), _dtype_code(dx.dtype),
+        _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream)))
+    return dx
+
+
+def jet_fp8_linear_wgrad(dyqT, dysT, xqT, xsT, M, dw=None, out_dtype=torch.float32,
+                         accumulate=False, workspace=None, stream=None):
+    """dW (+)= deq(dyqT) . deq(xqT)^T over the M tokens (operands [N, Mp], [K, Mp])."""
+    dyqT, xqT = _codes(dyqT), _codes(xqT)
+    N, K = dyqT.shape[0], xqT.shape[0]
+    dw = dw if dw is not None else _empty((N, K), out_dtype, dyqT)
+    need = jet_workspace_bytes(JET_OP_WGRAD, M, N, K)
+    if workspace is None and need:
+        workspace = _empty((need,), torch.uint8, dyqT)
+    _check("jet_fp8_linear_wgrad", _lib.jet_fp8_linear_wgrad(
+        _ptr(dyqT), _ptr(dysT), _ptr(xqT), _ptr(xsT), M, N, K, _ptr(dw), _dtype_code(dw.dtype),
+        1 if accumulate else 0, _ptr(workspace), 0 if workspace is None else workspace.numel(),
+        _stream(stream)))
+    return dw

@@ -1,0 +1,186 @@
+/*
+ * jetfp8.h -- C ABI of the MI355X (gfx950) unified-precision FP8 linear layer.
+ *
+ * The method (Jet-RL, "Jet-RL: Enabling On-Policy FP8 Reinforcement Learning
+ * with Unified Training and Rollout Precision Flow", gist.science explainer,
+ * section "Quantisierungsschema"; and the quantization table of
+ * "NVIDIA强化学习加速实操：10分钟提升2倍训练效率", section
+ * "为什么FP8适配线性层？") runs every linear layer in FP8 E4M3 with FP32
+ * scales: activations and output gradients in 1x128 groups, weights in
+ * 128x128 blocks, and a 128x1 grouping for the weight gradient.  The same
+ * quantizers and forward GEMM serve rollout and training.
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers on the current HIP device, owned by the
+ *    caller.  The library never allocates, frees or retains device memory and
+ *    keeps no pointer after a call returns.  `stream` is a hipStream_t
+ *    (NULL = the null stream).
+ *  - Every call only enqueues work on `stream` and returns; it never
+ *    synchronizes.  Device faults surface at the caller's next sync.
+ *  - Arguments are validated before anything is launched.  On failure a
+ *    non-zero jet_status is returned, nothing is launched and no output is
+ *    touched; jet_last_error() gives a thread-local description.
+ *  - E4M3 is the OCP 8-bit format E4M3 (bias 7, subnormals, max +-448, no
+ *    infinities).  Encoding rounds to nearest (ties to even) and saturates at
+ *    +-448; the sign of zero is kept.
+ *  - Scale of a group with maximum magnitude amax:
+ *        amax_c = max(amax, 2^-96),  s = fl32(amax_c / 448),
+ *        code   = E4M3(fl32(x * fl32(448 / amax_c))).
+ *    s is the stored (dequantisation) scale: value ~= E4M3value(code) * s.
+ *  - Inputs must be finite.  Outputs must not alias inputs.
+ *  - BF16 is bfloat16 (raw 16-bit storage); outputs rounded to BF16 use
+ *    round-to-nearest-even from the FP32 accumulator.
+ *  - Identical inputs give bit-identical outputs (no atomics in reductions).
+ *  - The library keeps no global mutable state other than the thread-local
+ *    error string; calls from several host threads are safe.
+ */
+#ifndef JETFP8_H
+#define JETFP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define JET_ABI_VERSION 1
+
+typedef enum {
+  JET_OK = 0,
+  JET_ERR_NULL = 1,      /* a required pointer is NULL                          */
+  JET_ERR_SHAPE = 2,     /* a size is negative, or not a multiple of 128 where  */
+                         /* required, or a leading dimension is too small       */
+  JET_ERR_ALIGN = 3,     /* a pointer or leading dimension breaks alignment     */
+  JET_ERR_DTYPE = 4,     /* unsupported dtype code                              */
+  JET_ERR_WORKSPACE = 5, /* workspace smaller than jet_workspace_bytes()        */
+  JET_ERR_HIP = 6        /* a HIP launch or query failed (see jet_last_error)   */
+} jet_status;
+
+typedef enum { JET_BF16 = 1, JET_F32 = 2, JET_E4M3 = 3 } jet_dtype;
+
+typedef enum { JET_OP_FWD = 0, JET_OP_DGRAD = 1, JET_OP_WGRAD = 2 } jet_op;
+
+/* ABI version of the loaded library (JET_ABI_VERSION). */
+int jet_abi_version(void);
+/* Static name of a jet_status code. */
+const char* jet_status_string(int status);
+/* Thread-local text of the last failure on this host thread ("" if none). */
+const char* jet_last_error(void);
+
+/*
+ * 1x128 group quantization of an activation or output gradient.
+ * Gist.science explainer, "Quantisierungsschema" (activations 1x128);
+ * nmedialink table (input activations and output gradients, [1,128], FP32).
+ *
+ *   x  : BF16 [M, K], row stride ldx elements (ldx >= K, ldx % 8 == 0)
+ *   q  : E4M3 [M, K], row stride ldq bytes   (ldq >= K, ldq % 16 == 0)
+ *   s  : FP32 [K/128, M]; the scale of row m, columns 128j..128j+127 is s[j*M+m]
+ *   M >= 0, K % 128 == 0.  x 16-byte aligned, q 16-byte aligned, s 4-byte aligned.
+ */
+int jet_quant_act_1x128(const void* x, int64_t M, int64_t K, int64_t ldx,
+                        uint8_t* q, int64_t ldq, float* s, void* stream);
+
+/*
+ * 128x1 group quantization along the row (token) axis, written transposed, for
+ * the weight-gradient GEMM.  Explainer "Quantisierungsschema" (128x1 for WGrad);
+ * 163.com write-up section 五 (1x128 activations re-quantized as 128x1).
+ *
+ *   src_dtype == JET_BF16: src is BF16 [M, K] (row stride ldsrc elements), src_s NULL.
+ *   src_dtype == JET_E4M3: src is the E4M3 [M, K] output of jet_quant_act_1x128
+ *       (row stride ldsrc bytes) and src_s its scales [K/128, M]; the values
+ *       re-quantized are fl32(E4M3value(code) * scale).
+ *   qT : E4M3 [K, Mp] with Mp = ceil(M/128)*128, row stride ldqT bytes
+ *        (ldqT >= Mp, ldqT % 16 == 0); columns M..Mp-1 receive zero codes.
+ *   sT : FP32 [ceil(M/128), K]; scale of rows 128g..min(128g+127, M-1) of
+ *        column k is sT[g*K + k].  A partial last group uses its valid rows only.
+ *   M >= 0, K % 128 == 0.  ldsrc % 16 bytes, src and qT 16-byte aligned.
+ */
+int jet_quant_act_128x1_T(const void* src, int src_dtype, const float* src_s,
+                          int64_t M, int64_t K, int64_t ldsrc,
+                          uint8_t* qT, int64_t ldqT, float* sT, void* stream);
+
+/*
+ * 128x128 block quantization of a BF16 master weight (run on every weight
+ * sync).  Explainer "Quantisierungsschema" (weights 128x128) and "Kernarchitektur"
+ * (BF16 master weights); 66260.cn FP8-RL item (block-wise re-conversion of the
+ * updated parameters at each weight synchronisation).
+ *
+ *   w  : BF16 [N, K], row stride ldw elements (ldw >= K, ldw % 8 == 0)
+ *   q  : E4M3 [N, K], dense (row stride K)
+ *   s  : FP32 [N/128, K/128], block (i, j) at s[i*(K/128)+j]
+ *   qT : optional E4M3 [K, N], dense (row stride N): the same codes transposed,
+ *        used as the B operand of jet_fp8_linear_dgrad.  NULL = not written.
+ *   N % 128 == 0, K % 128 == 0.
+ */
+int jet_quant_weight_128x128(const void* w, int64_t N, int64_t K, int64_t ldw,
+                             uint8_t* q, float* s, uint8_t* qT, void* stream);
+
+/*
+ * Forward GEMM  Y[m,n] = sum_k Xhat[m,k] * What[n,k]  with Xhat = E4M3(xq)*xs
+ * (1x128) and What = E4M3(wq)*ws (128x128); FP32 accumulation, the FP32
+ * scales applied at every 128-wide K step.  163.com section 五 (1x128 input
+ * times 128x128 weight); explainer "Quantisierungsschema".
+ *
+ *   xq : E4M3 [M, K] dense; xs : FP32 [K/128, M]
+ *   wq : E4M3 [N, K] dense; ws : FP32 [N/128, K/128]
+ *   y  : [M, N] dense, y_dtype JET_BF16 or JET_F32
+ *   yq, ys : optional fused epilogue (both NULL or both set, y_dtype must be
+ *        JET_BF16): yq E4M3 [M, N] dense and ys FP32 [N/128, M] receive
+ *        jet_quant_act_1x128 of the BF16 Y -- the next layer's FP8 input
+ *        (163.com section 五: quantization fused with the preceding operator).
+ *   workspace : device scratch of at least jet_workspace_bytes(JET_OP_FWD, M, N, K)
+ *        bytes (may be NULL when that is 0).
+ *   M >= 0, N % 128 == 0, K % 128 == 0, all pointers 16-byte aligned.
+ */
+int jet_fp8_linear_fwd(const uint8_t* xq, const float* xs,
+                       const uint8_t* wq, const float* ws,
+                       int64_t M, int64_t N, int64_t K,
+                       void* y, int y_dtype, uint8_t* yq, float* ys,
+                       void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Data-gradient GEMM  dX[m,k] = sum_n dYhat[m,n] * What[n,k].
+ * Explainer "Quantisierungsschema" (DGrad in FP8; BF16 gradients between
+ * operators); nmedialink table (output gradients 1x128).
+ *
+ *   dyq : E4M3 [M, N] dense (jet_quant_act_1x128 of dY); dys : FP32 [N/128, M]
+ *   wqT : E4M3 [K, N] dense -- the transposed codes written by
+ *         jet_quant_weight_128x128 (its qT output); ws : FP32 [N/128, K/128]
+ *         (the same block scales as the forward).
+ *   dx  : [M, K] dense, dx_dtype JET_BF16 or JET_F32
+ *   M >= 0, N % 128 == 0, K % 128 == 0, all pointers 16-byte aligned.
+ */
+int jet_fp8_linear_dgrad(const uint8_t* dyq, const float* dys,
+                         const uint8_t* wqT, const float* ws,
+                         int64_t M, int64_t N, int64_t K,
+                         void* dx, int dx_dtype,
+                         void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Weight-gradient GEMM  dW[n,k] (+)= sum_m dYhat[m,n] * Xhat[m,k]  with both
+ * operands grouped 128x1 along the M tokens (a per-row times per-column FP32
+ * scale at every 128-token step).  Explainer "Quantisierungsschema" (WGrad in
+ * FP8 with 1x128/128x1 groupings).
+ *
+ *   dyqT : E4M3 [N, Mp] dense, Mp = ceil(M/128)*128; dysT : FP32 [Mp/128, N]
+ *   xqT  : E4M3 [K, Mp] dense;                         xsT  : FP32 [Mp/128, K]
+ *          (both as written by jet_quant_act_128x1_T; padding columns hold zeros)
+ *   dw   : [N, K] dense, dw_dtype JET_F32 or JET_BF16; accumulate != 0 adds
+ *          to the existing contents (JET_F32 only).
+ *   M >= 0, N % 128 == 0, K % 128 == 0, all pointers 16-byte aligned.
+ */
+int jet_fp8_linear_wgrad(const uint8_t* dyqT, const float* dysT,
+                         const uint8_t* xqT, const float* xsT,
+                         int64_t M, int64_t N, int64_t K,
+                         void* dw, int dw_dtype, int accumulate,
+                         void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes the GEMM `op` (jet_op) needs at this shape (0 = none). */
+size_t jet_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JETFP8_H */

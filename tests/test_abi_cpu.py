@@ -1,0 +1,91 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/jetfp8.h declares, and rejects bad arguments with the
+documented status before anything is launched.  No call here reaches a
+kernel launch: every argument set fails validation or has an empty shape."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "jetfp8.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(jet_[a-z0-9_]+[A-Za-z0-9_]*)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def J():
+    from fp8_blockwise_quantized_amd import jetfp8
+    return jetfp8
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["jet_quant_act_1x128", "jet_quant_act_128x1_T", "jet_quant_weight_128x128",
+              "jet_fp8_linear_fwd", "jet_fp8_linear_dgrad", "jet_fp8_linear_wgrad"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(J):
+    lib = ctypes.CDLL(J._LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", J._LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (jet_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_binding_covers_header(J):
+    assert set(J.SIGNATURES) == set(declared_functions())
+
+
+def test_version_and_status_strings(J):
+    assert J.jet_abi_version() == 1
+    assert J.jet_status_string(J.JET_ERR_SHAPE) == "JET_ERR_SHAPE"
+    assert J.jet_status_string(99) == "JET_ERR_UNKNOWN"
+
+
+P16 = ctypes.c_void_p(4096)       # fake, 16-byte aligned; never dereferenced
+P17 = ctypes.c_void_p(4097)       # misaligned
+
+
+def test_quantizer_validation(J):
+    L = J._lib
+    assert L.jet_quant_act_1x128(P16, 4, 100, 128, P16, 128, P16, None) == J.JET_ERR_SHAPE
+    assert L.jet_quant_act_1x128(P16, -1, 128, 128, P16, 128, P16, None) == J.JET_ERR_SHAPE
+    assert L.jet_quant_act_1x128(None, 4, 128, 128, P16, 128, P16, None) == J.JET_ERR_NULL
+    assert L.jet_quant_act_1x128(P16, 4, 128, 64, P16, 128, P16, None) == J.JET_ERR_SHAPE
+    assert L.jet_quant_act_1x128(P17, 4, 128, 128, P16, 128, P16, None) == J.JET_ERR_ALIGN
+    assert L.jet_quant_act_1x128(P16, 4, 128, 132, P16, 128, P16, None) == J.JET_ERR_ALIGN
+    assert "ldx" in J.jet_last_error()
+    assert L.jet_quant_act_1x128(None, 0, 128, 128, None, 128, None, None) == J.JET_OK   # empty: no-op
+    assert L.jet_quant_act_128x1_T(P16, 7, None, 4, 128, 128, P16, 128, P16, None) == J.JET_ERR_DTYPE
+    assert L.jet_quant_act_128x1_T(P16, J.JET_E4M3, None, 4, 128, 128, P16, 128, P16, None) == J.JET_ERR_NULL
+    assert L.jet_quant_act_128x1_T(P16, J.JET_BF16, None, 200, 128, 128, P16, 200, P16, None) == J.JET_ERR_SHAPE
+    assert L.jet_quant_weight_128x128(P16, 100, 128, 128, P16, P16, None, None) == J.JET_ERR_SHAPE
+    assert L.jet_quant_weight_128x128(P16, 128, 128, 128, P16, P16, P17, None) == J.JET_ERR_ALIGN
+
+
+def test_gemm_validation(J):
+    L = J._lib
+    a = [P16, P16, P16, P16]
+    assert L.jet_fp8_linear_fwd(*a, 64, 100, 128, P16, J.JET_BF16, None, None, None, 0, None) == J.JET_ERR_SHAPE
+    assert L.jet_fp8_linear_fwd(*a, 64, 128, 128, P16, 9, None, None, None, 0, None) == J.JET_ERR_DTYPE
+    assert L.jet_fp8_linear_fwd(*a, 64, 128, 128, P16, J.JET_BF16, P16, None, None, 0, None) == J.JET_ERR_NULL
+    assert L.jet_fp8_linear_fwd(*a, 64, 128, 128, P16, J.JET_F32, P16, P16, None, 0, None) == J.JET_ERR_DTYPE
+    assert L.jet_fp8_linear_fwd(P16, P16, None, P16, 64, 128, 128, P16, J.JET_BF16, None, None, None, 0,
+                                None) == J.JET_ERR_NULL
+    assert L.jet_fp8_linear_fwd(P17, P16, P16, P16, 64, 128, 128, P16, J.JET_BF16, None, None, None, 0,
+                                None) == J.JET_ERR_ALIGN
+    assert L.jet_fp8_linear_dgrad(*a, 64, 128, 96, P16, J.JET_BF16, None, 0, None) == J.JET_ERR_SHAPE
+    assert L.jet_fp8_linear_wgrad(*a, 64, 128, 128, P16, J.JET_BF16, 1, None, 0, None) == J.JET_ERR_DTYPE
+    assert L.jet_fp8_linear_wgrad(*a, 64, 128, 128, None, J.JET_F32, 0, None, 0, None) == J.JET_ERR_NULL
+    assert L.jet_fp8_linear_fwd(None, None, None, None, 0, 128, 128, None, J.JET_BF16, None, None, None, 0,
+                                None) == J.JET_OK
+    assert J.jet_workspace_bytes(J.JET_OP_FWD, 64, 4096, 4096) >= 0

@@ -1,0 +1,254 @@
+"""GPU parity of the three block-scaled FP8 GEMMs (forward, dgrad, wgrad) and
+the fused 1x128 epilogue against the oracle.
+
+Rules (gpu_helpers): FP32 outputs within 2^-11 * sum|a*b| per element (the
+measured sub-block precision of the FP8 MFMA, with margin) and 1e-4 relative
+Frobenius of the float64 product of the dequantized operands; BF16 outputs
+within one BF16 ulp plus that allowance and 1e-3 relative Frobenius of
+bf16_rne(fl32(reference)); the integer special case and the fused
+quantization are bit-exact.  Operands are always quantized on the GPU
+and first checked bit-exact against the oracle's quantizers, so both sides
+multiply the same codes and scales.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import jet_oracle as O
+from fp8_blockwise_quantized_amd import inputs
+from tests.gpu_helpers import (assert_bits_equal, check_bf16_output, check_f32_output, dev_bf16,
+                               host, oracle_absprod)
+
+pytestmark = pytest.mark.gpu
+
+
+def quantize_all(J, x, w, dy):
+    """GPU quantization of one linear layer's tensors, checked against the oracle."""
+    xd, wd, dyd = dev_bf16(x), dev_bf16(w), dev_bf16(dy)
+    xq, xs = J.jet_quant_act_1x128(xd)
+    wq, ws, wqT = J.jet_quant_weight_128x128(wd)
+    dyq, dys = J.jet_quant_act_1x128(dyd)
+    dyqT, dysT = J.jet_quant_act_128x1_T(dyd)
+    xqT, xsT = J.jet_quant_act_128x1_T(xq, src_s=xs)
+    torch.cuda.synchronize()
+    ref = {}
+    ref["xq"], ref["xs"] = O.quant_1x128(x)
+    ref["wq"], ref["ws"] = O.quant_128x128(w)
+    ref["dyq"], ref["dys"] = O.quant_1x128(dy)
+    ref["dyqT"], ref["dysT"] = O.quant_128x1_T(dy)
+    ref["xqT"], ref["xsT"] = O.requant_128x1_T_from_1x128(ref["xq"], ref["xs"])
+    dev = dict(xq=xq, xs=xs, wq=wq, ws=ws, wqT=wqT, dyq=dyq, dys=dys, dyqT=dyqT, dysT=dysT,
+               xqT=xqT, xsT=xsT)
+    for k in ref:
+        assert_bits_equal(host(dev[k]), ref[k], k)
+    assert_bits_equal(host(wqT), ref["wq"].T, "wqT")
+    return dev, ref
+
+
+def layer_inputs(M, N, K, seed):
+    x = inputs.activations_with_outliers(M, K, seed=seed)
+    w = inputs.normal_bf16((N, K), 0.02, seed=seed, tensor_id=inputs.ID_W)
+    dy = inputs.normal_bf16((M, N), 1e-3, seed=seed, tensor_id=inputs.ID_DY)
+    return x, w, dy
+
+
+def run_and_check(J, M, N, K, seed, out_f32=True):
+    x, w, dy = layer_inputs(M, N, K, seed)
+    d, r = quantize_all(J, x, w, dy)
+    a_x = O.dequant_1x128(r["xq"], r["xs"])
+    b_w = O.dequant_128x128(r["wq"], r["ws"])
+    a_dy = O.dequant_1x128(r["dyq"], r["dys"])
+    a_dyT = O.dequant_128x1_T(r["dyqT"], r["dysT"], M)
+    a_xT = O.dequant_128x1_T(r["xqT"], r["xsT"], M)
+    # forward
+    y_ref = a_x @ b_w.T
+    y_abs = oracle_absprod(a_x, b_w)
+    y16, yq, ys = J.jet_fp8_linear_fwd(d["xq"], d["xs"], d["wq"], d["ws"], fuse_quant=True)
+    dx16 = J.jet_fp8_linear_dgrad(d["dyq"], d["dys"], d["wqT"], d["ws"])
+    dw32 = J.jet_fp8_linear_wgrad(d["dyqT"], d["dysT"], d["xqT"], d["xsT"], M)
+    torch.cuda.synchronize()
+    tag = f"M={M} N={N} K={K}"
+    check_bf16_output(host(y16), y_ref, y_abs, f"fwd bf16 {tag}")
+    # fused epilogue: bit-exact 1x128 quantization of the GPU's own BF16 Y
+    qo, so = O.quant_1x128(host(y16))
+    assert_bits_equal(host(yq), qo, f"fused codes {tag}")
+    assert_bits_equal(host(ys), so, f"fused scales {tag}")
+    dx_ref = a_dy @ b_w
+    check_bf16_output(host(dx16), dx_ref, oracle_absprod(a_dy, b_w.T), f"dgrad bf16 {tag}")
+    dw_ref = a_dyT @ a_xT.T
+    check_f32_output(host(dw32), dw_ref, oracle_absprod(a_dyT, a_xT), f"wgrad f32 {tag}")
+    if out_f32:
+        y32 = J.jet_fp8_linear_fwd(d["xq"], d["xs"], d["wq"], d["ws"], out_dtype=torch.float32)
+        dx32 = J.jet_fp8_linear_dgrad(d["dyq"], d["dys"], d["wqT"], d["ws"], out_dtype=torch.float32)
+        dw16 = J.jet_fp8_linear_wgrad(d["dyqT"], d["dysT"], d["xqT"], d["xsT"], M,
+                                      out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        check_f32_output(host(y32), y_ref, y_abs, f"fwd f32 {tag}")
+        check_f32_output(host(dx32), dx_ref, oracle_absprod(a_dy, b_w.T), f"dgrad f32 {tag}")
+        check_bf16_output(host(dw16), dw_ref, oracle_absprod(a_dyT, a_xT), f"wgrad bf16 {tag}")
+    return d, r
+
+
+def test_config_single_layer_256x512x512(gpu_lib):
+    """The small parity configuration: M=256 tokens, K=512, N=512, seed 0."""
+    M, N, K = 256, 512, 512
+    x = inputs.normal_bf16((M, K), 1.0, seed=0, tensor_id=inputs.ID_X)
+    w = inputs.normal_bf16((N, K), 0.02, seed=0, tensor_id=inputs.ID_W)
+    dy = inputs.normal_bf16((M, N), 1e-3, seed=0, tensor_id=inputs.ID_DY)
+    d, r = quantize_all(gpu_lib, x, w, dy)
+    y = gpu_lib.jet_fp8_linear_fwd(d["xq"], d["xs"], d["wq"], d["ws"], out_dtype=torch.float32)
+    dx = gpu_lib.jet_fp8_linear_dgrad(d["dyq"], d["dys"], d["wqT"], d["ws"], out_dtype=torch.float32)
+    dw = gpu_lib.jet_fp8_linear_wgrad(d["dyqT"], d["dysT"], d["xqT"], d["xsT"], M)
+    torch.cuda.synchronize()
+    a_x, b_w = O.dequant_1x128(r["xq"], r["xs"]), O.dequant_128x128(r["wq"], r["ws"])
+    check_f32_output(host(y), O.gemm_fwd(r["xq"], r["xs"], r["wq"], r["ws"]),
+                     oracle_absprod(a_x, b_w), "fwd")
+    a_dy = O.dequant_1x128(r["dyq"], r["dys"])
+    check_f32_output(host(dx), O.gemm_dgrad(r["dyq"], r["dys"], r["wq"], r["ws"]),
+                     oracle_absprod(a_dy, b_w.T), "dgrad")
+    a_dyT = O.dequant_128x1_T(r["dyqT"], r["dysT"], M)
+    a_xT = O.dequant_128x1_T(r["xqT"], r["xsT"], M)
+    check_f32_output(host(dw), O.gemm_wgrad(r["dyqT"], r["dysT"], r["xqT"], r["xsT"], M),
+                     oracle_absprod(a_dyT, a_xT), "wgrad")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (63, 256, 384), (65, 384, 256), (200, 256, 512),
+                                   (129, 128, 1024), (384, 640, 384)])
+def test_ragged_shapes_all_gemms(gpu_lib, M, N, K):
+    run_and_check(gpu_lib, M, N, K, seed=M + N + K)
+
+
+def anchored_small_int(rng, rows, cols):
+    """Integers in [-7, 7] with +-7 on the diagonal rows == cols (mod 128), so
+    every 1x128, 128x1 and 128x128 group holds a +-7: every scale is exactly
+    7/448 = 2^-6 and every code is exact (64*v)."""
+    v = rng.integers(-7, 8, size=(rows, cols)).astype(np.float32)
+    diag = (np.arange(rows)[:, None] % 128) == (np.arange(cols)[None, :] % 128)
+    v[diag] = np.where(rng.integers(0, 2, size=int(diag.sum())) == 1, 7.0, -7.0)
+    return v
+
+
+def test_integer_case_bit_exact(gpu_lib):
+    """Every product of codes is a multiple of 64*64 = 4096, far above the
+    MFMA's internal sub-block resolution, every per-step partial and every
+    FP32 partial sum is exactly representable, and the scales are powers of
+    two: the FP32 results must equal the integer matrix products exactly.
+    A single dropped, duplicated or misplaced product would show."""
+    rng = np.random.default_rng(0)
+    M, N, K = 256, 384, 1024
+    x, w, dy = anchored_small_int(rng, M, K), anchored_small_int(rng, N, K), anchored_small_int(rng, M, N)
+    d, r = quantize_all(gpu_lib, x, w, dy)
+    for key in ("xs", "ws", "dys", "dysT", "xsT"):
+        assert np.all(r[key] == np.float32(2.0 ** -6))
+    y = gpu_lib.jet_fp8_linear_fwd(d["xq"], d["xs"], d["wq"], d["ws"], out_dtype=torch.float32)
+    dx = gpu_lib.jet_fp8_linear_dgrad(d["dyq"], d["dys"], d["wqT"], d["ws"], out_dtype=torch.float32)
+    dw = gpu_lib.jet_fp8_linear_wgrad(d["dyqT"], d["dysT"], d["xqT"], d["xsT"], M)
+    torch.cuda.synchronize()
+    xi, wi, dyi = x.astype(np.int64), w.astype(np.int64), dy.astype(np.int64)
+    assert_bits_equal(host(y), (xi @ wi.T).astype(np.float32), "fwd integer")
+    assert_bits_equal(host(dx), (dyi @ wi).astype(np.float32), "dgrad integer")
+    assert_bits_equal(host(dw), (dyi.T @ xi).astype(np.float32), "wgrad integer")
+
+
+def test_wgrad_accumulate_and_empty_tokens(gpu_lib):
+    M, N, K = 200, 256, 384
+    x, w, dy = layer_inputs(M, N, K, 9)
+    d, r = quantize_all(gpu_lib, x, w, dy)
+    c0 = torch.randn(N, K, device="cuda")
+    dw = c0.clone()
+    gpu_lib.jet_fp8_linear_wgrad(d["dyqT"], d["dysT"], d["xqT"], d["xsT"], M, dw=dw, accumulate=True)
+    ref = O.gemm_wgrad(r["dyqT"], r["dysT"], r["xqT"], r["xsT"], M)
+    # M = 0 tokens: the weight gradient is zero (or unchanged when accumulating)
+    z = torch.full((N, K), 7.0, device="cuda")
+    gpu_lib.jet_fp8_linear_wgrad(d["dyqT"][:, :0], d["dysT"][:0], d["xqT"][:, :0], d["xsT"][:0], 0, dw=z)
+    torch.cuda.synchronize()
+    a_dyT = O.dequant_128x1_T(r["dyqT"], r["dysT"], M)
+    a_xT = O.dequant_128x1_T(r["xqT"], r["xsT"], M)
+    absprod = oracle_absprod(a_dyT, a_xT) + np.abs(host(c0))
+    check_f32_output(host(dw), host(c0).astype(np.float64) + ref, absprod, "wgrad accumulate")
+    assert not host(z).any()
+
+
+def test_gemms_deterministic(gpu_lib):
+    M, N, K = 512, 512, 1024
+    x, w, dy = layer_inputs(M, N, K, 4)
+    d, _ = quantize_all(gpu_lib, x, w, dy)
+    outs = []
+    for _ in range(2):
+        outs.append((gpu_lib.jet_fp8_linear_fwd(d["xq"], d["xs"], d["wq"], d["ws"]),
+                     gpu_lib.jet_fp8_linear_dgrad(d["dyq"], d["dys"], d["wqT"], d["ws"]),
+                     gpu_lib.jet_fp8_linear_wgrad(d["dyqT"], d["dysT"], d["xqT"], d["xsT"], M)))
+    torch.cuda.synchronize()
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+# --- Llama-3.1-8B shapes ----------------------------------------------------
+
+LLAMA = {"qkv": (6144, 4096), "o": (4096, 4096), "gate_up": (28672, 4096), "down": (4096, 14336)}
+
+
+@pytest.mark.parametrize("name", list(LLAMA))
+def test_decode_forward_llama_shapes(gpu_lib, name):
+    """Rollout decode: M=64 tokens, forward only, full check."""
+    N, K = LLAMA[name]
+    M = 64
+    x = inputs.activations_with_outliers(M, K, seed=0)
+    w = inputs.normal_bf16((N, K), 0.02, seed=0, tensor_id=inputs.ID_W)
+    xq, xs = gpu_lib.jet_quant_act_1x128(dev_bf16(x))
+    wq, ws, _ = gpu_lib.jet_quant_weight_128x128(dev_bf16(w), transposed=False)
+    y = gpu_lib.jet_fp8_linear_fwd(xq, xs, wq, ws)
+    torch.cuda.synchronize()
+    q1, s1 = O.quant_1x128(x)
+    assert_bits_equal(host(xq), q1, "decode x codes")
+    rng = np.random.default_rng(N)
+    cols = np.sort(rng.choice(N, 512, replace=False))
+    wsub = w[cols]
+    # oracle on 512 sampled output columns: their weight rows re-quantized by block
+    wq_h, ws_h = host(wq), host(ws)
+    b = O.e4m3_decode(wq_h[cols]) * np.repeat(ws_h[cols // 128], 128, axis=1)
+    a = O.dequant_1x128(q1, s1)
+    check_bf16_output(host(y)[:, cols], a @ b.T, oracle_absprod(a, b), f"decode fwd {name}")
+    del wsub
+
+
+@pytest.mark.parametrize("name", ["qkv", "down"])
+def test_training_shapes_sampled(gpu_lib, name):
+    """Training M=8192: all three GEMMs at full size, checked on sampled rows."""
+    N, K = LLAMA[name]
+    M = 8192
+    x, w, dy = layer_inputs(M, N, K, 0)
+    xd, wd, dyd = dev_bf16(x), dev_bf16(w), dev_bf16(dy)
+    xq, xs = gpu_lib.jet_quant_act_1x128(xd)
+    wq, ws, wqT = gpu_lib.jet_quant_weight_128x128(wd)
+    dyq, dys = gpu_lib.jet_quant_act_1x128(dyd)
+    dyqT, dysT = gpu_lib.jet_quant_act_128x1_T(dyd)
+    xqT, xsT = gpu_lib.jet_quant_act_128x1_T(xq, src_s=xs)
+    y, yq, ys = gpu_lib.jet_fp8_linear_fwd(xq, xs, wq, ws, fuse_quant=True)
+    dx = gpu_lib.jet_fp8_linear_dgrad(dyq, dys, wqT, ws)
+    dw = gpu_lib.jet_fp8_linear_wgrad(dyqT, dysT, xqT, xsT, M)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    rows = np.sort(rng.choice(M, 64, replace=False))
+    ridx = torch.from_numpy(rows).cuda()
+    # quantizer parity on the sampled rows, then GEMM rows from the GPU's codes
+    qx, sx = O.quant_1x128(x[rows])
+    assert_bits_equal(host(xq[ridx]), qx, "x codes")
+    qd, sd = O.quant_1x128(dy[rows])
+    assert_bits_equal(host(dyq[ridx]), qd, "dy codes")
+    wq_h, ws_h = host(wq), host(ws)
+    bw = O.dequant_128x128(wq_h, ws_h)
+    ax = O.dequant_1x128(qx, sx)
+    check_bf16_output(host(y[ridx]), ax @ bw.T, oracle_absprod(ax, bw), f"fwd {name}")
+    qo, so = O.quant_1x128(host(y[ridx]))
+    assert_bits_equal(host(yq[ridx]), qo, "fused codes")
+    assert_bits_equal(host(ys[:, ridx]), so, "fused scales")
+    ad = O.dequant_1x128(qd, sd)
+    check_bf16_output(host(dx[ridx]), ad @ bw, oracle_absprod(ad, bw.T), f"dgrad {name}")
+    del bw
+    # wgrad: 64 sampled output rows n, all k, from the GPU's 128x1 codes
+    nrows = np.sort(rng.choice(N, 64, replace=False))
+    nidx = torch.from_numpy(nrows).cuda()
+    a = O.dequant_128x1_T(host(dyqT[nidx]), host(dysT[:, nidx]), M)
+    b = O.dequant_128x1_T(host(xqT), host(xsT), M)
+    check_f32_output(host(dw[nidx]), a @ b.T, oracle_absprod(a, b), f"wgrad {name}")
