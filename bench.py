@@ -120,7 +120,7 @@ def copy_probe(torch):
 
 def cpu_baseline():
     """The oracle (untuned) on a bounded sample of the workload: the QKV
-    linear (4096 -> 6144) with its full weight and 512 of the 8192 tokens,
+    linear (4096 -> 6144) with its full weight and 4096 of the 8192 tokens,
     through every step of the path; scaled to TFLOP/s of the sample's GEMMs."""
     from oracle import jet_oracle as O
     from fp8_blockwise_quantized_amd import inputs
@@ -129,7 +129,7 @@ def cpu_baseline():
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = 1
-    Ms, N, K = 512, 6144, 4096
+    Ms, N, K = 4096, 6144, 4096
     x = inputs.activations_with_outliers(Ms, K, seed=0)
     w = inputs.normal_bf16((N, K), 0.02, seed=0, tensor_id=inputs.ID_W)
     dy = inputs.normal_bf16((Ms, N), 1e-3, seed=0, tensor_id=inputs.ID_DY)

@@ -39,6 +39,9 @@ def hipcc() -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(LIBDIR, exist_ok=True)
+    # never leave a library built from older sources behind a failed build
+    if os.path.exists(LIB):
+        os.remove(LIB)
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
     cc = hipcc()
