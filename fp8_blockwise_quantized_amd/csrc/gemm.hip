@@ -29,8 +29,8 @@
 //     scales).  Every load of the K loop is one of these DMAs; one barrier per
 //     K step.
 //   * Tile layout in LDS, either
-//       ROWS: row-major 128-byte rows, 16-byte chunks XOR-swizzled by
-//             (row/2) % 8; each DMA reads 8 whole rows;
+//       ROWS: row-major 128-byte rows, 16-byte chunks XOR-swizzled per row
+//             (see swz); each DMA reads 8 whole rows;
 //       FRAG: MFMA-fragment order, each 16-row slab as two 1 KiB blocks, block
 //             h holding at lane l's 16-byte slot the bytes 64*h + 16*(l/16)
 //             .. +15 of slab row l%16; each fragment read is one contiguous
@@ -67,13 +67,12 @@ struct GemmCfg {
   static constexpr int STAGE = ATILE + BTILE + SA + SB;
   static constexpr int ABLK = ATILE / 1024 / NW;   // A DMA instructions per wave and stage
   static constexpr int BBLK = BTILE / 1024 / NW;
-  static constexpr int SPW = BM / NW;              // row-scale slots per wave
-  static constexpr int CPW = BN / NW;              // column-scale slots per wave
-  static constexpr int LOADS = ABLK + BBLK + 2;    // DMA instructions per wave and stage
+  static constexpr int NCA = BM / 64, NCB = BN / 64;   // 64-slot scale chunks (rows, columns)
+  static constexpr int LOADS = ABLK + BBLK + 1;    // DMA instructions per wave and stage
   static constexpr int EPI_PITCH = BN + 8;         // bf16 per staged output row
   static constexpr int LDS = (STAGES * STAGE > BM * EPI_PITCH * 2) ? STAGES * STAGE : BM * EPI_PITCH * 2;
   static_assert(ABLK * NW * 1024 == ATILE && BBLK * NW * 1024 == BTILE, "DMA split");
-  static_assert(SPW <= 64 && CPW <= 64 && SPW * NW == BM && CPW * NW == BN, "scale split");
+  static_assert(BM % 64 == 0 && BN % 64 == 0 && NCA + NCB <= NW, "scale split");
   static_assert(TM % 4 == 0 && (128 % (TN * 16)) == 0 && BN % 128 == 0, "tile shape");
   static_assert(LDS * OCC <= 160 * 1024, "LDS");
 };
@@ -116,22 +115,25 @@ __device__ __forceinline__ void dma4(uint32_t ldsa, const void* sbase, uint32_t 
 
 #pragma clang diagnostic pop
 
-// Wait until at most `n` of this wave's vector-memory loads are outstanding.
-__device__ __forceinline__ void wait_vmem(int n) {
-  switch (n) {
-    case 0: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); break;
-#define JET_WAIT_CASE(N) \
-    case N: asm volatile("s_waitcnt vmcnt(" #N ") lgkmcnt(0)" ::: "memory"); break;
-    JET_WAIT_CASE(6) JET_WAIT_CASE(8) JET_WAIT_CASE(10) JET_WAIT_CASE(12) JET_WAIT_CASE(14)
-    JET_WAIT_CASE(16) JET_WAIT_CASE(18) JET_WAIT_CASE(20) JET_WAIT_CASE(24) JET_WAIT_CASE(28)
-#undef JET_WAIT_CASE
-    default: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); break;
-  }
+// Wait until at most N of this wave's vector-memory loads are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" :: "i"(N) : "memory");
 }
 
-// Row-major layout: byte offset of 16-byte chunk `chunk` of tile row `row`.
+template <bool B> struct BoolC { static constexpr bool value = B; };
+
+// Row-major layout: 16-byte chunk c of tile row r sits at chunk slot
+// c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1).  A fragment read has lane l read
+// chunk 2*(l/16) (+1) of row l % 16: any 8 consecutive lanes then hit 8
+// different chunk slots (all 32 four-byte banks of a 128-byte row), and any
+// 16 consecutive lanes hit 16 different (row parity, slot) pairs (all 64 banks
+// when rows alternate between the two halves of 64 banks), so the read is
+// conflict-free whether the LDS serves 8 or 16 lanes of a b128 read per cycle.
+__device__ __forceinline__ int swz_f(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
+  return row * 128 + ((chunk ^ swz_f(row)) << 4);
 }
 
 template <bool FRAG>
@@ -161,7 +163,7 @@ __device__ __forceinline__ void dma_src(int g, int lane, int& row, uint32_t& col
     col = (uint32_t)(64 * (g & 1) + 16 * (lane >> 4));
   } else {
     row = g * 8 + (lane >> 3);
-    col = (uint32_t)(((lane & 7) ^ ((row >> 1) & 7)) << 4);
+    col = (uint32_t)(((lane & 7) ^ swz_f(row)) << 4);
   }
 }
 
@@ -224,38 +226,52 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs p)
     dma_src<FRAG>(wave * CFG::BBLK + t, lane, row, col);
     offB[t] = (uint32_t)min(n0 + row, p.N - 1) * (uint32_t)p.ldb + col;
   }
-  // Row scales: within the TM*16 slots of wave row wm, slot 64*q + 4*lrow + e
-  // holds tile row wm*TM*16 + (4q + e)*16 + lrow.  Wave w fills slots
-  // SPW*w .. SPW*w + SPW-1 with lanes 0 .. SPW-1.
-  const int sslot = CFG::SPW * wave + (lane % CFG::SPW);
-  const int sblk = sslot / (TM * 16), sin = sslot % (TM * 16);
-  const int srow = sblk * TM * 16 + ((sin >> 6) * 4 + (sin & 3)) * 16 + ((sin >> 2) & 15);
-  const uint32_t offSA = (uint32_t)min(m0 + srow, p.M - 1) * 4u;
-  const uint32_t offSB = (uint32_t)min(n0 + CFG::CPW * wave + (lane % CFG::CPW), p.N - 1) * 4u;
-  // ROWBLOCK: wave w copies the scale of 128-column block (w % (BN/128)) of the tile to slot w.
-  const int blk = min(n0 / 128 + (wave % (BN / 128)), p.N / 128 - 1);
-  const float* gsbw = p.sB + (int64_t)blk * p.sB_o;
+  // Scales: every wave copies one 64-slot chunk per step with one 4-byte DMA
+  // (all lanes active).  Chunks 0 .. NCA-1 are row scales; within the TM*16
+  // slots of wave row wm, slot 64*q + 4*lrow + e holds tile row
+  // wm*TM*16 + (4q + e)*16 + lrow, so each lane reads its TM row scales with
+  // TM/4 contiguous 16-byte loads.  Chunks NCA .. are column scales (ROWCOL:
+  // slot = tile column; ROWBLOCK: slot s = the scale of the tile's 128-column
+  // block s, clamped).  Waves beyond NCA + NCB repeat a chunk (same values).
+  const int chunk = wave % (CFG::NCA + CFG::NCB);
+  const bool row_chunk = chunk < CFG::NCA;
+  uint32_t offS, ldsS;
+  {
+    const int slot = 64 * (row_chunk ? chunk : chunk - CFG::NCA) + lane;
+    if (row_chunk) {
+      const int sblk = slot / (TM * 16), sin = slot % (TM * 16);
+      const int srow = sblk * TM * 16 + ((sin >> 6) * 4 + (sin & 3)) * 16 + ((sin >> 2) & 15);
+      offS = (uint32_t)min(m0 + srow, p.M - 1) * 4u;
+      ldsS = (uint32_t)(CFG::ATILE + CFG::BTILE + 64 * 4 * chunk);
+    } else {
+      if (MODE == kRowCol) {
+        offS = (uint32_t)min(n0 + slot, p.N - 1) * 4u;
+      } else {
+        const int blk = min(n0 / 128 + slot, p.N / 128 - 1);
+        offS = (uint32_t)blk * (uint32_t)p.sB_o * 4u;
+      }
+      ldsS = (uint32_t)(CFG::ATILE + CFG::BTILE + CFG::SA + 64 * 4 * (chunk - CFG::NCA));
+    }
+  }
+  const float* sbase0 = row_chunk ? p.sA : p.sB;
+  const int64_t sstep = row_chunk ? p.sA_ld : p.sB_c;
 
-#define JET_ISSUE(stage_, kb_)                                                               \
-  do {                                                                                       \
-    const uint32_t sbase_ = lds0 + (uint32_t)((stage_) * CFG::STAGE);                        \
-    const uint8_t* ga_ = p.A + (int64_t)(kb_) * 128;                                         \
-    const uint8_t* gb_ = p.B + (int64_t)(kb_) * 128;                                         \
-    _Pragma("unroll") for (int t_ = 0; t_ < CFG::ABLK; ++t_)                                 \
-      dma16(sbase_ + (uint32_t)((wave * CFG::ABLK + t_) * 1024), ga_, offA[t_]);             \
-    _Pragma("unroll") for (int t_ = 0; t_ < CFG::BBLK; ++t_)                                 \
-      dma16(sbase_ + (uint32_t)(CFG::ATILE + (wave * CFG::BBLK + t_) * 1024), gb_, offB[t_]); \
-    if (lane < CFG::SPW)                                                                     \
-      dma4(sbase_ + (uint32_t)(CFG::ATILE + CFG::BTILE + wave * CFG::SPW * 4),               \
-           p.sA + (int64_t)(kb_) * p.sA_ld, offSA);                                          \
-    if (MODE == kRowCol) {                                                                   \
-      if (lane < CFG::CPW)                                                                   \
-        dma4(sbase_ + (uint32_t)(CFG::ATILE + CFG::BTILE + CFG::SA + wave * CFG::CPW * 4),   \
-             p.sB + (int64_t)(kb_) * p.sB_c, offSB);                                         \
-    } else if (lane == 0) {                                                                  \
-      dma4(sbase_ + (uint32_t)(CFG::ATILE + CFG::BTILE + CFG::SA + wave * 4),                \
-           gsbw + (int64_t)(kb_) * p.sB_c, 0u);                                              \
-    }                                                                                        \
+  // DMA part t of step kb into stage `stage`: t < ABLK + BBLK is one 1 KiB
+  // tile DMA, t == ABLK + BBLK the scale DMA.
+  constexpr int NT = CFG::ABLK + CFG::BBLK;
+#define JET_ISSUE(part_, stage_, kb_)                                                          \
+  do {                                                                                         \
+    const uint32_t sbase_ = lds0 + (uint32_t)((stage_) * CFG::STAGE);                          \
+    if ((part_) < CFG::ABLK) {                                                                 \
+      dma16(sbase_ + (uint32_t)((wave * CFG::ABLK + (part_)) * 1024),                          \
+            p.A + (int64_t)(kb_) * 128, offA[(part_) < CFG::ABLK ? (part_) : 0]);              \
+    } else if ((part_) < NT) {                                                                 \
+      const int t_ = (part_) < NT ? (part_) - CFG::ABLK : 0;                                   \
+      dma16(sbase_ + (uint32_t)(CFG::ATILE + (wave * CFG::BBLK + t_) * 1024),                  \
+            p.B + (int64_t)(kb_) * 128, offB[t_]);                                             \
+    } else {                                                                                   \
+      dma4(sbase_ + ldsS, sbase0 + (int64_t)(kb_) * sstep, offS);                              \
+    }                                                                                          \
   } while (0)
 
   v4f acc[TM][TN];
@@ -267,20 +283,26 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs p)
   constexpr int D = CFG::STAGES - 1;   // prefetch distance in K steps
 #pragma unroll
   for (int s = 0; s < D; ++s)
-    if (s < KB) JET_ISSUE(s, s);
+    if (s < KB) {
+#pragma unroll
+      for (int t = 0; t <= NT; ++t) JET_ISSUE(t, s, s);
+    }
 
-  int st = 0;
-  for (int kb = 0; kb < KB; ++kb) {
-    // In flight: this wave's DMAs of steps kb .. min(kb+D-1, KB-1).  Let the
-    // later ones stay; after the barrier every wave's step-kb data has landed
-    // and every wave is done with step kb-1, whose stage step kb+D refills.
-    wait_vmem(CFG::LOADS * min(D - 1, KB - 1 - kb));
+  int kb = 0, st = 0;
+  // One K step.  REFILL: this step also issues the loads of step kb + D into
+  // the stage step kb - 1 used.  The body has no data-dependent branches, so
+  // the compiler schedules and allocates it as one block.
+  auto step = [&](auto refill_tag) __attribute__((always_inline)) {
+    constexpr bool REFILL = decltype(refill_tag)::value;
+    // In flight: this wave's DMAs of steps kb .. kb+D-1 (fewer in the last
+    // steps: then wait for all).  After the barrier every wave's step-kb data
+    // has landed and every wave is done with step kb-1's stage.
+    if (REFILL) wait_vmem<CFG::LOADS * (D - 1)>();
+    else wait_vmem<0>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (kb + D < KB) {
-      const int stn = (st + D) % CFG::STAGES;
-      JET_ISSUE(stn, kb + D);
-    }
+    const int stn = (st + D) % CFG::STAGES;
+    if (REFILL) JET_ISSUE(NT, stn, kb + D);
 
     const uint8_t* As = lds + st * CFG::STAGE;
     const uint8_t* Bs = As + CFG::ATILE;
@@ -306,24 +328,44 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs p)
       for (int i = 0; i < TM; ++i) rsc[i] *= sbk;
     }
 
+    // Software pipeline over the TM x TN MFMAs of the step, in row order: the
+    // A fragment of row i+1 is read when row i starts, the partial of MFMA n
+    // is folded just before MFMA n + LAG reuses its registers (so no fold
+    // waits on the MFMA right before it), and the next step's tile DMAs are
+    // spread over the rows (a wave issuing them back to back would stall
+    // while the CU's address unit drains them).
+    constexpr int LAG = 3;
+    constexpr int NM = TM * TN;
     v8i bf[TN];
 #pragma unroll
     for (int j = 0; j < TN; ++j) bf[j] = frag32<FRAG>(Bs, wn * TN + j, lane);
+    v8i af[2];
+    af[0] = frag32<FRAG>(As, wm * TM, lane);
+    v4f part[LAG];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const v8i af = frag32<FRAG>(As, wm * TM + i, lane);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const v4f part = mfma_fp8(bf[j], af);
+    for (int n = 0; n < NM + LAG; ++n) {
+      if (n >= LAG) {
+        const int ii = (n - LAG) / TN, jj = (n - LAG) % TN;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float c = (MODE == kRowCol) ? rsc[i] * cb[j][r] : rsc[i];
-          acc[i][j][r] = fmaf(part[r], c, acc[i][j][r]);
+          const float c = (MODE == kRowCol) ? rsc[ii] * cb[jj][r] : rsc[ii];
+          acc[ii][jj][r] = fmaf(part[n % LAG][r], c, acc[ii][jj][r]);
+        }
+      }
+      if (n < NM) {
+        const int i = n / TN, j = n % TN;
+        if (j == 0 && i + 1 < TM) af[(i + 1) & 1] = frag32<FRAG>(As, wm * TM + i + 1, lane);
+        part[n % LAG] = mfma_fp8(bf[j], af[i & 1]);
+        if (REFILL && j == TN - 1) {
+#pragma unroll
+          for (int t = (i * NT) / TM; t < ((i + 1) * NT) / TM; ++t) JET_ISSUE(t, stn, kb + D);
         }
       }
     }
     st = (st + 1 == CFG::STAGES) ? 0 : st + 1;
-  }
+  };
+  for (; kb < KB - D; ++kb) step(BoolC<true>{});
+  for (; kb < KB; ++kb) step(BoolC<false>{});
 #undef JET_ISSUE
 
   // ---- epilogue ----
@@ -408,18 +450,48 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
 
 // 8 wavefronts as 2 x 4, wave tile 128 x 64, block tile 256 x 256, two stages.
 using CfgMain = GemmCfg<2, 4, 8, 4, 2, false>;
+// 4 wavefronts as 2 x 2, wave tile 64 x 64, block tile 128 x 128, two stages,
+// two workgroups per CU: for grids whose 256 x 256 tiles leave a last partial
+// wave of workgroups.
+using CfgSmall = GemmCfg<2, 2, 4, 4, 2, false, 2>;
+
+template <class CFG>
+hipError_t dispatch(const GemmArgs& a, int mode, int out, bool accum, bool fuseq, hipStream_t st) {
+  if (mode == kRowBlock) {
+    if (fuseq) return launch_cfg<CFG, kRowBlock, kOutBf16, false, true>(a, st);
+    if (out == kOutBf16) return launch_cfg<CFG, kRowBlock, kOutBf16, false, false>(a, st);
+    return launch_cfg<CFG, kRowBlock, kOutF32, false, false>(a, st);
+  }
+  if (out == kOutBf16) return launch_cfg<CFG, kRowCol, kOutBf16, false, false>(a, st);
+  if (accum) return launch_cfg<CFG, kRowCol, kOutF32, true, false>(a, st);
+  return launch_cfg<CFG, kRowCol, kOutF32, false, false>(a, st);
+}
+
+// Compute units of the current device (cached per device).
+static int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
 
 hipError_t launch_gemm(const GemmArgs& a, int mode, int out, bool accum, bool fuseq,
                        hipStream_t st) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
-  if (mode == kRowBlock) {
-    if (fuseq) return launch_cfg<CfgMain, kRowBlock, kOutBf16, false, true>(a, st);
-    if (out == kOutBf16) return launch_cfg<CfgMain, kRowBlock, kOutBf16, false, false>(a, st);
-    return launch_cfg<CfgMain, kRowBlock, kOutF32, false, false>(a, st);
-  }
-  if (out == kOutBf16) return launch_cfg<CfgMain, kRowCol, kOutBf16, false, false>(a, st);
-  if (accum) return launch_cfg<CfgMain, kRowCol, kOutF32, true, false>(a, st);
-  return launch_cfg<CfgMain, kRowCol, kOutF32, false, false>(a, st);
+  // The big tile keeps the most work per byte staged; use it unless its last
+  // wave of workgroups would leave more than a tenth of the CUs idle.
+  const int64_t tiles = (int64_t)((a.M + CfgMain::BM - 1) / CfgMain::BM) *
+                        (int64_t)((a.N + CfgMain::BN - 1) / CfgMain::BN);
+  const int64_t cus = cu_count();
+  const int64_t slots = (tiles + cus - 1) / cus * cus;
+  if (tiles * 10 >= slots * 9) return dispatch<CfgMain>(a, mode, out, accum, fuseq, st);
+  return dispatch<CfgSmall>(a, mode, out, accum, fuseq, st);
 }
 
 }  // namespace jet

@@ -150,6 +150,37 @@ def test_integer_case_bit_exact(gpu_lib):
     assert_bits_equal(host(dw), (dyi.T @ xi).astype(np.float32), "wgrad integer")
 
 
+# Shapes whose 256x256-tile grid fills (almost) whole waves of 256 CUs, so all
+# three GEMMs take the large-tile kernel; the small-shape tests above take the
+# 128x128 kernel.  3969 tokens leave a ragged last row tile and 128x1 group.
+BIG_TILE_SHAPE = (3969, 3840, 3968)
+
+
+def test_ragged_big_tile_all_gemms(gpu_lib):
+    M, N, K = BIG_TILE_SHAPE
+    run_and_check(gpu_lib, M, N, K, seed=11, out_f32=False)
+
+
+def test_integer_case_bit_exact_big_tile(gpu_lib):
+    """As test_integer_case_bit_exact, at a shape that takes the 256x256 tile
+    in every GEMM (M a multiple of 128 so every 128x1 group holds a +-7).
+    Integer products below 2^53 make the float64 matmul exact."""
+    rng = np.random.default_rng(1)
+    M, N, K = 3968, 3840, 3968
+    x, w, dy = anchored_small_int(rng, M, K), anchored_small_int(rng, N, K), anchored_small_int(rng, M, N)
+    d, r = quantize_all(gpu_lib, x, w, dy)
+    for key in ("xs", "ws", "dys", "dysT", "xsT"):
+        assert np.all(r[key] == np.float32(2.0 ** -6))
+    y = gpu_lib.jet_fp8_linear_fwd(d["xq"], d["xs"], d["wq"], d["ws"], out_dtype=torch.float32)
+    dx = gpu_lib.jet_fp8_linear_dgrad(d["dyq"], d["dys"], d["wqT"], d["ws"], out_dtype=torch.float32)
+    dw = gpu_lib.jet_fp8_linear_wgrad(d["dyqT"], d["dysT"], d["xqT"], d["xsT"], M)
+    torch.cuda.synchronize()
+    xf, wf, dyf = x.astype(np.float64), w.astype(np.float64), dy.astype(np.float64)
+    assert_bits_equal(host(y), (xf @ wf.T).astype(np.float32), "fwd integer")
+    assert_bits_equal(host(dx), (dyf @ wf).astype(np.float32), "dgrad integer")
+    assert_bits_equal(host(dw), (dyf.T @ xf).astype(np.float32), "wgrad integer")
+
+
 def test_wgrad_accumulate_and_empty_tokens(gpu_lib):
     M, N, K = 200, 256, 384
     x, w, dy = layer_inputs(M, N, K, 9)
