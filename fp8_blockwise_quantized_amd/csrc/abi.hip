@@ -80,6 +80,7 @@ int jet_quant_act_128x1_T(const void* src, int src_dtype, const float* src_s, in
   if (!src || !qT || !sT || (fp8 && !src_s))
     return fail(JET_ERR_NULL, "quant_act_128x1_T: null pointer");
   const int64_t Mp = (M + kG - 1) / kG * kG;
+  if (Mp / kG > 65535) return fail(JET_ERR_SHAPE, "quant_act_128x1_T: ceil(M/128) must be <= 65535");
   if (ldsrc < K || ldqT < Mp)
     return fail(JET_ERR_SHAPE, "quant_act_128x1_T: ldsrc < K or ldqT < ceil(M/128)*128");
   const int64_t ld_bytes = fp8 ? ldsrc : 2 * ldsrc;
@@ -143,7 +144,7 @@ int jet_fp8_linear_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, co
   a.B = wq; a.ldb = K;
   a.sA = xs; a.sA_ld = M;
   a.sB = ws; a.sB_o = K / kG; a.sB_c = 1;
-  a.C = y; a.ldc = N; a.Cq = yq; a.Cs = ys;
+  a.C = y; a.ldc = N; a.Cq = yq; a.Cs = ys; a.ldcs = M;
   a.M = (int)M; a.N = (int)N; a.Kc = (int)K;
   return hip_status(jet::launch_gemm(a, jet::kRowBlock, y_dtype == JET_BF16 ? jet::kOutBf16 : jet::kOutF32,
                                      false, fuse, as_stream(stream)),
@@ -199,6 +200,140 @@ int jet_fp8_linear_wgrad(const uint8_t* dyqT, const float* dysT, const uint8_t* 
   return hip_status(jet::launch_gemm(a, jet::kRowCol, dw_dtype == JET_BF16 ? jet::kOutBf16 : jet::kOutF32,
                                      accumulate != 0, false, as_stream(stream)),
                     "fp8_linear_wgrad");
+}
+
+// ---------------------------------------------------------------------------
+// Grouped (mixture-of-experts) entry points
+// ---------------------------------------------------------------------------
+
+static int64_t grouped_cols(int64_t M, int64_t E) { return ((M + kG - 1) / kG + E) * kG; }
+
+static int check_grouped_common(const char* name, const int32_t* seg_off, int64_t E, int64_t M) {
+  if (E < 1 || E > (int64_t(1) << 20))
+    return fail(JET_ERR_SHAPE, "%s: need 1 <= E <= 2^20 experts (E=%lld)", name, (long long)E);
+  if (M < 0 || M > kMaxDim) return fail(JET_ERR_SHAPE, "%s: need 0 <= M <= 2^30", name);
+  if (!seg_off) return fail(JET_ERR_NULL, "%s: null seg_off", name);
+  if (!aligned(seg_off, 4)) return fail(JET_ERR_ALIGN, "%s: seg_off needs 4-byte alignment", name);
+  return JET_OK;
+}
+
+int jet_quant_act_128x1_T_grouped(const void* src, int src_dtype, const float* src_s, int64_t M,
+                                  int64_t K, int64_t ldsrc, const int32_t* seg_off, int64_t E,
+                                  uint8_t* qT, int64_t ldqT, float* sT, void* stream) {
+  g_last_error[0] = 0;
+  if (src_dtype != JET_BF16 && src_dtype != JET_E4M3)
+    return fail(JET_ERR_DTYPE, "quant_act_128x1_T_grouped: src_dtype must be JET_BF16 or JET_E4M3");
+  if (int st = check_grouped_common("quant_act_128x1_T_grouped", seg_off, E, M)) return st;
+  if (K < 0 || K % kG || K > kMaxDim)
+    return fail(JET_ERR_SHAPE, "quant_act_128x1_T_grouped: K must be a multiple of 128");
+  if (M == 0 || K == 0) return JET_OK;
+  if ((M + kG - 1) / kG + E > 65535)
+    return fail(JET_ERR_SHAPE, "quant_act_128x1_T_grouped: ceil(M/128) + E must be <= 65535");
+  const bool fp8 = src_dtype == JET_E4M3;
+  if (!src || !qT || !sT || (fp8 && !src_s))
+    return fail(JET_ERR_NULL, "quant_act_128x1_T_grouped: null pointer");
+  if (ldsrc < K || ldqT < grouped_cols(M, E))
+    return fail(JET_ERR_SHAPE, "quant_act_128x1_T_grouped: ldsrc < K or ldqT < 128*(ceil(M/128)+E)");
+  const int64_t ld_bytes = fp8 ? ldsrc : 2 * ldsrc;
+  if (!aligned(src, 16) || !aligned(qT, 16) || !aligned(sT, 16) || ld_bytes % 16 || ldqT % 16 ||
+      (fp8 && !aligned(src_s, 4)))
+    return fail(JET_ERR_ALIGN, "quant_act_128x1_T_grouped: src, qT, sT need 16-byte alignment; row strides 16 bytes");
+  return hip_status(jet::launch_quant_128x1_T_grouped(src, fp8, src_s, M, K, ldsrc, seg_off, (int)E,
+                                                      qT, ldqT, sT, as_stream(stream)),
+                    "quant_act_128x1_T_grouped");
+}
+
+int jet_fp8_grouped_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
+                        const int32_t* seg_off, int64_t E, int64_t M, int64_t N, int64_t K, void* y,
+                        int y_dtype, uint8_t* yq, float* ys, void* workspace, size_t ws_bytes,
+                        void* stream) {
+  g_last_error[0] = 0;
+  if (int st = check_grouped_common("fp8_grouped_fwd", seg_off, E, M)) return st;
+  if (int st = check_gemm_common("fp8_grouped_fwd", M, N, K, JET_OP_FWD, ws_bytes, workspace)) return st;
+  if (y_dtype != JET_BF16 && y_dtype != JET_F32)
+    return fail(JET_ERR_DTYPE, "fp8_grouped_fwd: y_dtype must be JET_BF16 or JET_F32");
+  const bool fuse = yq || ys;
+  if (fuse && (!yq || !ys)) return fail(JET_ERR_NULL, "fp8_grouped_fwd: yq and ys go together");
+  if (fuse && y_dtype != JET_BF16)
+    return fail(JET_ERR_DTYPE, "fp8_grouped_fwd: the fused 1x128 output needs y_dtype JET_BF16");
+  if (M == 0 || N == 0) return JET_OK;
+  if (!xq || !xs || !wq || !ws || !y) return fail(JET_ERR_NULL, "fp8_grouped_fwd: null pointer");
+  if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(y, 16) || !aligned(xs, 4) || !aligned(ws, 4) ||
+      (fuse && (!aligned(yq, 16) || !aligned(ys, 4))))
+    return fail(JET_ERR_ALIGN, "fp8_grouped_fwd: operands and outputs need 16-byte alignment");
+  jet::GemmArgs a{};
+  a.A = xq; a.lda = K;
+  a.B = wq; a.ldb = K; a.bE = N * K;
+  a.sA = xs; a.sA_ld = M;
+  a.sB = ws; a.sB_o = K / kG; a.sB_c = 1; a.sbE = (N / kG) * (K / kG);
+  a.C = y; a.ldc = N; a.Cq = yq; a.Cs = ys; a.ldcs = M;
+  a.M = (int)M; a.N = (int)N; a.Kc = (int)K;
+  a.seg = seg_off; a.E = (int)E; a.seg_rows = (int)M;
+  return hip_status(jet::launch_gemm_grouped(a, jet::kGrpRows, jet::kRowBlock,
+                                             y_dtype == JET_BF16 ? jet::kOutBf16 : jet::kOutF32,
+                                             false, fuse, as_stream(stream)),
+                    "fp8_grouped_fwd");
+}
+
+int jet_fp8_grouped_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* wqT, const float* ws,
+                          const int32_t* seg_off, int64_t E, int64_t M, int64_t N, int64_t K,
+                          void* dx, int dx_dtype, void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  if (int st = check_grouped_common("fp8_grouped_dgrad", seg_off, E, M)) return st;
+  if (int st = check_gemm_common("fp8_grouped_dgrad", M, N, K, JET_OP_DGRAD, ws_bytes, workspace)) return st;
+  if (dx_dtype != JET_BF16 && dx_dtype != JET_F32)
+    return fail(JET_ERR_DTYPE, "fp8_grouped_dgrad: dx_dtype must be JET_BF16 or JET_F32");
+  if (M == 0 || K == 0) return JET_OK;
+  if (E * N > kMaxDim) return fail(JET_ERR_SHAPE, "fp8_grouped_dgrad: E*N must be <= 2^30");
+  if (!dyq || !dys || !wqT || !ws || !dx) return fail(JET_ERR_NULL, "fp8_grouped_dgrad: null pointer");
+  if (!aligned(dyq, 16) || !aligned(wqT, 16) || !aligned(dx, 16) || !aligned(dys, 4) || !aligned(ws, 4))
+    return fail(JET_ERR_ALIGN, "fp8_grouped_dgrad: operands and output need 16-byte alignment");
+  jet::GemmArgs a{};
+  a.A = dyq; a.lda = N;
+  a.B = wqT; a.ldb = E * N; a.bE = N;
+  a.sA = dys; a.sA_ld = M;
+  a.sB = ws; a.sB_o = 1; a.sB_c = K / kG; a.sbE = (N / kG) * (K / kG);
+  a.C = dx; a.ldc = K;
+  a.M = (int)M; a.N = (int)K; a.Kc = (int)N;
+  a.seg = seg_off; a.E = (int)E; a.seg_rows = (int)M;
+  return hip_status(jet::launch_gemm_grouped(a, jet::kGrpRows, jet::kRowBlock,
+                                             dx_dtype == JET_BF16 ? jet::kOutBf16 : jet::kOutF32,
+                                             false, false, as_stream(stream)),
+                    "fp8_grouped_dgrad");
+}
+
+int jet_fp8_grouped_wgrad(const uint8_t* dyqT, const float* dysT, const uint8_t* xqT,
+                          const float* xsT, int64_t ldT, const int32_t* seg_off, int64_t E,
+                          int64_t M, int64_t N, int64_t K, void* dw, int dw_dtype, int accumulate,
+                          void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  if (int st = check_grouped_common("fp8_grouped_wgrad", seg_off, E, M)) return st;
+  if (int st = check_gemm_common("fp8_grouped_wgrad", M, N, K, JET_OP_WGRAD, ws_bytes, workspace)) return st;
+  if (dw_dtype != JET_F32 && dw_dtype != JET_BF16)
+    return fail(JET_ERR_DTYPE, "fp8_grouped_wgrad: dw_dtype must be JET_F32 or JET_BF16");
+  if (accumulate && dw_dtype != JET_F32)
+    return fail(JET_ERR_DTYPE, "fp8_grouped_wgrad: accumulate needs dw_dtype JET_F32");
+  if (N == 0 || K == 0) return JET_OK;
+  if (!dw) return fail(JET_ERR_NULL, "fp8_grouped_wgrad: null pointer");
+  if (M > 0 && (!dyqT || !dysT || !xqT || !xsT))
+    return fail(JET_ERR_NULL, "fp8_grouped_wgrad: null pointer");
+  if (ldT < grouped_cols(M, E) || ldT > kMaxDim || ldT % 16)
+    return fail(JET_ERR_SHAPE, "fp8_grouped_wgrad: need 128*(ceil(M/128)+E) <= ldT <= 2^30, ldT %% 16");
+  if (!aligned(dw, 16) || (M > 0 && (!aligned(dyqT, 16) || !aligned(xqT, 16) || !aligned(dysT, 4) ||
+                                     !aligned(xsT, 4))))
+    return fail(JET_ERR_ALIGN, "fp8_grouped_wgrad: operands and output need 16-byte alignment");
+  jet::GemmArgs a{};
+  a.A = dyqT; a.lda = ldT;
+  a.B = xqT; a.ldb = ldT;
+  a.sA = dysT; a.sA_ld = N;
+  a.sB = xsT; a.sB_o = 1; a.sB_c = K;
+  a.C = dw; a.ldc = K; a.cE = N * K;
+  a.M = (int)N; a.N = (int)K; a.Kc = 0;
+  a.seg = seg_off; a.E = (int)E; a.seg_rows = (int)M; a.kcap = (int)(ldT / kG * kG);
+  return hip_status(jet::launch_gemm_grouped(a, jet::kGrpContraction, jet::kRowCol,
+                                             dw_dtype == JET_BF16 ? jet::kOutBf16 : jet::kOutF32,
+                                             accumulate != 0, false, as_stream(stream)),
+                    "fp8_grouped_wgrad");
 }
 
 }  // extern "C"

@@ -192,10 +192,19 @@ __device__ __forceinline__ void tile_of_block(int nbm, int nbn, int& tm, int& tn
 
 }  // namespace
 
-template <class CFG, int MODE, int OUT, bool ACCUM, bool FUSEQ>
-__global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs p) {
+// Grouped grids are rounded up to a multiple of the 8 XCDs; renumber so each
+// XCD takes a contiguous range of slots (one expert's tiles share an L2).
+__device__ __forceinline__ int xcd_slot() {
+  constexpr int kXcds = 8;
+  const int g = (int)gridDim.x, b = (int)blockIdx.x;
+  return (g % kXcds == 0) ? (b % kXcds) * (g / kXcds) + b / kXcds : b;
+}
+
+template <class CFG, int MODE, int OUT, bool ACCUM, bool FUSEQ, int GRP>
+__global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa) {
   constexpr int TM = CFG::TM, TN = CFG::TN, BM = CFG::BM, BN = CFG::BN;
   constexpr bool FRAG = CFG::FRAG;
+  constexpr int64_t kOutBytes = (OUT == kOutF32) ? 4 : 2;
   __shared__ __attribute__((aligned(16))) uint8_t lds[CFG::LDS];
 
   const int tid = threadIdx.x;
@@ -204,10 +213,53 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs p)
   const int wm = wave % CFG::WMW, wn = wave / CFG::WMW;
   const int lrow = lane & 15, kg = lane >> 4;
 
-  const int nbm = (p.M + BM - 1) / BM;
-  const int nbn = (p.N + BN - 1) / BN;
+  // This workgroup's problem: the whole GEMM, or (grouped) one expert's part.
+  GemmArgs p = pa;
   int tm, tn;
-  tile_of_block(nbm, nbn, tm, tn);
+  if constexpr (GRP == kGrpNone) {
+    tile_of_block((p.M + BM - 1) / BM, (p.N + BN - 1) / BN, tm, tn);
+  } else if constexpr (GRP == kGrpRows) {
+    // slot = (row tile of the concatenated segments) x (column tile)
+    const int nbn = (p.N + BN - 1) / BN;
+    const int slot = xcd_slot();
+    const int r = slot / nbn;
+    tn = slot - r * nbn;
+    tm = 0;
+    const SegHit h = seg_find(p.seg, p.E, p.seg_rows, BM, r, false);
+    const int e = __builtin_amdgcn_readfirstlane(h.e);
+    if (e < 0) return;
+    const int row0 = __builtin_amdgcn_readfirstlane(h.lo + (r - h.first) * BM);
+    p.M = __builtin_amdgcn_readfirstlane(h.hi) - row0;
+    p.A += (int64_t)row0 * p.lda;
+    p.sA += row0;
+    p.C = static_cast<uint8_t*>(p.C) + (int64_t)row0 * p.ldc * kOutBytes;
+    if (FUSEQ) {
+      p.Cq += (int64_t)row0 * p.ldc;
+      p.Cs += row0;
+    }
+    p.B += (int64_t)e * p.bE;
+    p.sB += (int64_t)e * p.sbE;
+  } else {
+    // slot = (expert) x (output tile); expert e contracts over its padded columns
+    const int nbm = (p.M + BM - 1) / BM, nbn = (p.N + BN - 1) / BN;
+    const int slot = xcd_slot();
+    const int e = slot / (nbm * nbn);
+    if (e >= p.E) return;
+    const int local = slot - e * (nbm * nbn);
+    tm = local / nbn;
+    tn = local - tm * nbn;
+    const SegHit h = seg_find(p.seg, p.E, p.seg_rows, 128, e, true);
+    const int first = __builtin_amdgcn_readfirstlane(h.first);
+    const int groups = __builtin_amdgcn_readfirstlane((h.hi - h.lo + 127) / 128);
+    const int c0 = min(first * 128, p.kcap);
+    const int c1 = min((first + groups) * 128, p.kcap);
+    p.Kc = c1 - c0;
+    p.A += c0;
+    p.B += c0;
+    p.sA += (int64_t)(c0 / 128) * p.sA_ld;
+    p.sB += (int64_t)(c0 / 128) * p.sB_c;
+    p.C = static_cast<uint8_t*>(p.C) + (int64_t)e * p.cE * kOutBytes;
+  }
   const int m0 = tm * BM, n0 = tn * BN;
   const int KB = p.Kc / 128;
   const uint32_t lds0 = lds_addr(lds);
@@ -431,7 +483,7 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs p)
                                    bf16_lo(v.w) * sp.r, bf16_hi(v.w) * sp.r);
         if (ok) {
           *reinterpret_cast<uint2*>(p.Cq + (int64_t)m * p.ldc + n) = make_uint2(q0, q1);
-          if ((c8 & 15) == 0) p.Cs[(int64_t)(n / 128) * p.M + m] = sp.s;
+          if ((c8 & 15) == 0) p.Cs[(int64_t)(n / 128) * p.ldcs + m] = sp.s;
         }
       }
       if (ok) *reinterpret_cast<uint4*>(C + (int64_t)m * p.ldc + n) = v;
@@ -439,11 +491,19 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs p)
   }
 }
 
-template <class CFG, int MODE, int OUT, bool ACCUM, bool FUSEQ>
+template <class CFG, int MODE, int OUT, bool ACCUM, bool FUSEQ, int GRP = kGrpNone>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
-  const int nbm = (a.M + CFG::BM - 1) / CFG::BM;
-  const int nbn = (a.N + CFG::BN - 1) / CFG::BN;
-  hipLaunchKernelGGL((k_gemm_fp8<CFG, MODE, OUT, ACCUM, FUSEQ>), dim3((unsigned)(nbm * nbn)),
+  const int64_t nbm = (a.M + CFG::BM - 1) / CFG::BM;
+  const int64_t nbn = (a.N + CFG::BN - 1) / CFG::BN;
+  int64_t blocks = nbm * nbn;
+  if (GRP == kGrpRows)            // at most ceil(rows/BM) + E row tiles over all segments
+    blocks = ((int64_t)(a.seg_rows + CFG::BM - 1) / CFG::BM + a.E) * nbn;
+  else if (GRP == kGrpContraction)
+    blocks = (int64_t)a.E * nbm * nbn;
+  if (GRP != kGrpNone) blocks = (blocks + 7) / 8 * 8;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_gemm_fp8<CFG, MODE, OUT, ACCUM, FUSEQ, GRP>), dim3((unsigned)blocks),
                      dim3(CFG::THREADS), 0, st, a);
   return hipGetLastError();
 }
@@ -455,16 +515,16 @@ using CfgMain = GemmCfg<2, 4, 8, 4, 2, false>;
 // wave of workgroups.
 using CfgSmall = GemmCfg<2, 2, 4, 4, 2, false, 2>;
 
-template <class CFG>
+template <class CFG, int GRP = kGrpNone>
 hipError_t dispatch(const GemmArgs& a, int mode, int out, bool accum, bool fuseq, hipStream_t st) {
   if (mode == kRowBlock) {
-    if (fuseq) return launch_cfg<CFG, kRowBlock, kOutBf16, false, true>(a, st);
-    if (out == kOutBf16) return launch_cfg<CFG, kRowBlock, kOutBf16, false, false>(a, st);
-    return launch_cfg<CFG, kRowBlock, kOutF32, false, false>(a, st);
+    if (fuseq) return launch_cfg<CFG, kRowBlock, kOutBf16, false, true, GRP>(a, st);
+    if (out == kOutBf16) return launch_cfg<CFG, kRowBlock, kOutBf16, false, false, GRP>(a, st);
+    return launch_cfg<CFG, kRowBlock, kOutF32, false, false, GRP>(a, st);
   }
-  if (out == kOutBf16) return launch_cfg<CFG, kRowCol, kOutBf16, false, false>(a, st);
-  if (accum) return launch_cfg<CFG, kRowCol, kOutF32, true, false>(a, st);
-  return launch_cfg<CFG, kRowCol, kOutF32, false, false>(a, st);
+  if (out == kOutBf16) return launch_cfg<CFG, kRowCol, kOutBf16, false, false, GRP>(a, st);
+  if (accum) return launch_cfg<CFG, kRowCol, kOutF32, true, false, GRP>(a, st);
+  return launch_cfg<CFG, kRowCol, kOutF32, false, false, GRP>(a, st);
 }
 
 // Compute units of the current device (cached per device).
@@ -492,6 +552,23 @@ hipError_t launch_gemm(const GemmArgs& a, int mode, int out, bool accum, bool fu
   const int64_t slots = (tiles + cus - 1) / cus * cus;
   if (tiles * 10 >= slots * 9) return dispatch<CfgMain>(a, mode, out, accum, fuseq, st);
   return dispatch<CfgSmall>(a, mode, out, accum, fuseq, st);
+}
+
+// Expert segments are short and ragged (a few hundred rows each), so the
+// grouped GEMMs use the 128 x 128 tile.
+hipError_t launch_gemm_grouped(const GemmArgs& a, int grp, int mode, int out, bool accum,
+                               bool fuseq, hipStream_t st) {
+  if (a.N == 0 || a.E == 0) return hipSuccess;
+  if (grp == kGrpRows) {
+    if (a.seg_rows == 0) return hipSuccess;
+    if (mode != kRowBlock || accum) return hipErrorInvalidValue;
+    return dispatch<CfgSmall, kGrpRows>(a, mode, out, false, fuseq, st);
+  }
+  if (grp == kGrpContraction) {
+    if (a.M == 0 || mode != kRowCol || fuseq) return hipErrorInvalidValue;
+    return dispatch<CfgSmall, kGrpContraction>(a, mode, out, accum, false, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace jet

@@ -100,7 +100,76 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// ---------------------------------------------------------------------------
+// Streaming (non-temporal) global accesses for data touched once: the loads
+// and stores bypass the caches' normal allocation, which keeps a kernel that
+// runs after a large producer from first evicting that producer's dirty lines.
+// ---------------------------------------------------------------------------
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_stream8(void* p, uint32_t lo, uint32_t hi) {
+  const u32x2_t v = {lo, hi};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t*>(p));
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// ---------------------------------------------------------------------------
+// Segments of a grouped (mixture-of-experts) problem.  seg[0..E] are the
+// device row offsets of the experts' segments; each bound is clamped to
+// [0, rows] and a segment's end to at least its start, so malformed offsets
+// give wrong results but no access outside the matrices.  Segment e owns
+// ceil(len_e / unit) consecutive slots (row tiles, 128-row groups) starting
+// at slot `first`.  One wavefront computes the prefix sums with shuffles
+// (every wavefront of a block may call it; the result is wave-uniform).
+// ---------------------------------------------------------------------------
+struct SegHit {
+  int e;       // segment, or -1 if no segment owns the slot
+  int first;   // its first slot
+  int lo, hi;  // its rows [lo, hi)
+};
+
+// by_e = false: the segment owning slot `target`; by_e = true: segment `target`.
+__device__ __forceinline__ SegHit seg_find(const int32_t* seg, int E, int rows, int unit,
+                                           int target, bool by_e) {
+  const int lane = threadIdx.x & 63;
+  int base = 0;
+  for (int c = 0; c < E; c += 64) {
+    const int e = c + lane;
+    int lo = 0, hi = 0, cnt = 0;
+    if (e < E) {
+      lo = min(max(seg[e], 0), rows);
+      hi = min(max(seg[e + 1], lo), rows);
+      cnt = (hi - lo + unit - 1) / unit;
+    }
+    int incl = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += v;
+    }
+    const int excl = incl - cnt;
+    const bool hit = by_e ? (e == target)
+                          : (e < E && cnt > 0 && base + excl <= target && target < base + incl);
+    const unsigned long long m = __ballot(hit);
+    if (m != 0ull) {
+      const int l = __ffsll((long long)m) - 1;
+      SegHit h;
+      h.e = c + l;
+      h.first = base + __shfl(excl, l, 64);
+      h.lo = __shfl(lo, l, 64);
+      h.hi = __shfl(hi, l, 64);
+      return h;
+    }
+    base += __shfl(incl, 63, 64);
+  }
+  return SegHit{-1, 0, 0, 0};
+}
 
 }  // namespace jet

@@ -10,6 +10,8 @@ namespace jet {
 enum { kRowBlock = 0, kRowCol = 1 };   // scale modes of the GEMM
 enum { kOutBf16 = 0, kOutF32 = 1 };    // GEMM output element types
 
+enum { kGrpNone = 0, kGrpRows = 1, kGrpContraction = 2 };   // grouped (per-expert) modes
+
 // C[M, N] (+)= sum_kb scale * A[M, Kc-slab] . B[N, Kc-slab]^T ; see gemm.hip.
 struct GemmArgs {
   const uint8_t* A;      // [M, Kc] E4M3, row stride lda bytes
@@ -18,9 +20,18 @@ struct GemmArgs {
   const float* sB;       // ROWBLOCK: sB[(n/128) * sB_o + kb * sB_c]; ROWCOL: sB[kb * sB_c + n]
   void* C;               // [M, N] output, row stride ldc elements
   uint8_t* Cq;           // fused 1x128 quantization of a BF16 C (or null)
-  float* Cs;             //   and its scales [N/128, M]
-  int64_t lda, ldb, sA_ld, sB_o, sB_c, ldc;
+  float* Cs;             //   and its scales: Cs[(n/128) * ldcs + m]
+  int64_t lda, ldb, sA_ld, sB_o, sB_c, ldc, ldcs;
   int M, N, Kc;
+  // Grouped problems (mixture of experts); unused by the dense GEMMs.
+  //   kGrpRows:        the rows of A and C are cut into segments seg[e] .. seg[e+1]-1,
+  //                    segment e multiplies expert e's B (B + e*bE, sB + e*sbE).
+  //   kGrpContraction: expert e contracts over the 128-padded column range of
+  //                    segment e (columns below kcap) and writes C + e*cE.
+  const int32_t* seg;
+  int E, seg_rows;       // experts; rows the segment offsets index (clamp bound)
+  int64_t bE, sbE, cE;
+  int kcap;
 };
 
 hipError_t launch_quant_1x128(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
@@ -32,5 +43,12 @@ hipError_t launch_quant_128x1_T(const void* src, bool fp8src, const float* src_s
                                 hipStream_t st);
 hipError_t launch_gemm(const GemmArgs& a, int mode, int out, bool accum, bool fuseq,
                        hipStream_t st);
+// Grouped GEMMs: grp = kGrpRows (forward, dgrad) or kGrpContraction (wgrad).
+hipError_t launch_gemm_grouped(const GemmArgs& a, int grp, int mode, int out, bool accum,
+                               bool fuseq, hipStream_t st);
+hipError_t launch_quant_128x1_T_grouped(const void* src, bool fp8src, const float* src_s,
+                                        int64_t M, int64_t K, int64_t ldsrc, const int32_t* seg,
+                                        int E, uint8_t* qT, int64_t ldqT, float* sT,
+                                        hipStream_t st);
 
 }  // namespace jet

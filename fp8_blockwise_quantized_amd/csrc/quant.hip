@@ -9,10 +9,15 @@
 //    gradient: explainer "Quantisierungsschema" (128x1 for WGrad); 163.com
 //    write-up section 五 (1x128 activations re-quantized as 128x1).
 //
-// Every kernel reads each input byte once from HBM with 16-byte loads, keeps the
-// group in registers, reduces the group maximum with integer/DPP operations
-// inside one wavefront (plus one LDS exchange for the 128x128 block), and
-// writes codes with 8-byte stores.
+// Every kernel reads each input byte once from HBM with 16-byte loads, keeps
+// the group in registers, reduces the group maximum with integer/DPP
+// operations inside one wavefront (plus one LDS exchange for the 128x128
+// block), and writes codes with 8-byte stores.  Accesses whose wavefront
+// instruction covers whole 128-byte lines that no other wavefront touches use
+// the streaming (non-temporal) forms; partial-line accesses keep the normal
+// forms, so the L2 merges the pieces of a line.
+#include <algorithm>
+
 #include "jet_device.hpp"
 #include "jet_launch.hpp"
 
@@ -20,39 +25,50 @@ namespace jet {
 
 // ---------------------------------------------------------------------------
 // 1x128.  One 16-lane DPP row handles one group of 128 BF16 values (256 bytes,
-// 16 bytes per lane); a 256-thread block handles 16 rows of one column group
-// per pass and PASSES passes, all loads issued before any compute.
+// 16 bytes per lane).  Work is cut into units of 16 consecutive groups of one
+// row (4 KiB of input, one 256-thread block); a block takes UPI consecutive
+// units per round, all loads issued before any compute, and strides over the
+// units by the grid size.  Consecutive units continue along a row, so each
+// round of a block reads UPI*4 KiB of contiguous input (whole rows for
+// K <= 2048*UPI) and writes the codes contiguously.
 // ---------------------------------------------------------------------------
-template <int PASSES>
+template <int UPI>
 __global__ __launch_bounds__(256) void k_quant_1x128(const uint16_t* __restrict__ x, int64_t M,
-                                                     int64_t ldx, uint8_t* __restrict__ q,
-                                                     int64_t ldq, float* __restrict__ s) {
+                                                     int64_t K, int64_t ldx,
+                                                     uint8_t* __restrict__ q, int64_t ldq,
+                                                     float* __restrict__ s) {
+  const int64_t gpr = K / kGroup;          // groups per row
+  const int64_t upr = (gpr + 15) / 16;     // units per row
+  const int64_t units = M * upr;
+  const int gi = threadIdx.x >> 4;         // group within the unit
   const int lane16 = threadIdx.x & 15;
-  const int64_t j = blockIdx.y;
-  const int64_t mrow = (int64_t)blockIdx.x * (16 * PASSES) + (threadIdx.x >> 4);
-  uint4 v[PASSES];
+  for (int64_t u0 = (int64_t)blockIdx.x * UPI; u0 < units; u0 += (int64_t)gridDim.x * UPI) {
+    uint4 v[UPI];
 #pragma unroll
-  for (int p = 0; p < PASSES; ++p) {
-    const int64_t m = mrow + 16 * p;
-    v[p] = make_uint4(0u, 0u, 0u, 0u);
-    if (m < M) v[p] = *reinterpret_cast<const uint4*>(x + m * ldx + j * kGroup + lane16 * 8);
-  }
+    for (int k = 0; k < UPI; ++k) {
+      const int64_t u = u0 + k;
+      const int64_t m = u / upr, j = (u % upr) * 16 + gi;
+      v[k] = make_uint4(0u, 0u, 0u, 0u);
+      if (u < units && j < gpr) v[k] = load_stream16(x + m * ldx + j * kGroup + lane16 * 8);
+    }
 #pragma unroll
-  for (int p = 0; p < PASSES; ++p) {
-    const int64_t m = mrow + 16 * p;
-    uint32_t am = max_abs_bf16x2(0u, v[p].x);
-    am = max_abs_bf16x2(am, v[p].y);
-    am = max_abs_bf16x2(am, v[p].z);
-    am = max_abs_bf16x2(am, v[p].w);
-    am = row16_max_u16x2(am);
-    const ScalePair sp = scale_pair(fold_bf16x2(am));
-    const uint32_t c0 = e4m3x4(bf16_lo(v[p].x) * sp.r, bf16_hi(v[p].x) * sp.r,
-                               bf16_lo(v[p].y) * sp.r, bf16_hi(v[p].y) * sp.r);
-    const uint32_t c1 = e4m3x4(bf16_lo(v[p].z) * sp.r, bf16_hi(v[p].z) * sp.r,
-                               bf16_lo(v[p].w) * sp.r, bf16_hi(v[p].w) * sp.r);
-    if (m < M) {
-      *reinterpret_cast<uint2*>(q + m * ldq + j * kGroup + lane16 * 8) = make_uint2(c0, c1);
-      if (lane16 == 0) s[j * M + m] = sp.s;
+    for (int k = 0; k < UPI; ++k) {
+      const int64_t u = u0 + k;
+      const int64_t m = u / upr, j = (u % upr) * 16 + gi;
+      uint32_t am = max_abs_bf16x2(0u, v[k].x);
+      am = max_abs_bf16x2(am, v[k].y);
+      am = max_abs_bf16x2(am, v[k].z);
+      am = max_abs_bf16x2(am, v[k].w);
+      am = row16_max_u16x2(am);
+      const ScalePair sp = scale_pair(fold_bf16x2(am));
+      const uint32_t c0 = e4m3x4(bf16_lo(v[k].x) * sp.r, bf16_hi(v[k].x) * sp.r,
+                                 bf16_lo(v[k].y) * sp.r, bf16_hi(v[k].y) * sp.r);
+      const uint32_t c1 = e4m3x4(bf16_lo(v[k].z) * sp.r, bf16_hi(v[k].z) * sp.r,
+                                 bf16_lo(v[k].w) * sp.r, bf16_hi(v[k].w) * sp.r);
+      if (u < units && j < gpr) {
+        store_stream8(q + m * ldq + j * kGroup + lane16 * 8, c0, c1);
+        if (lane16 == 0) s[j * M + m] = sp.s;
+      }
     }
   }
 }
@@ -60,9 +76,12 @@ __global__ __launch_bounds__(256) void k_quant_1x128(const uint16_t* __restrict_
 hipError_t launch_quant_1x128(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
                               int64_t ldq, float* s, hipStream_t st) {
   if (M == 0) return hipSuccess;
-  constexpr int kPasses = 4;
-  dim3 grid((unsigned)((M + 16 * kPasses - 1) / (16 * kPasses)), (unsigned)(K / kGroup));
-  hipLaunchKernelGGL(k_quant_1x128<kPasses>, grid, dim3(256), 0, st, x, M, ldx, q, ldq, s);
+  constexpr int kUnitsPerRound = 4;
+  constexpr int64_t kMaxBlocks = 4096;
+  const int64_t units = M * ((K / kGroup + 15) / 16);
+  const int64_t blocks = std::min<int64_t>((units + kUnitsPerRound - 1) / kUnitsPerRound, kMaxBlocks);
+  hipLaunchKernelGGL(k_quant_1x128<kUnitsPerRound>, dim3((unsigned)blocks), dim3(256), 0, st, x, M,
+                     K, ldx, q, ldq, s);
   return hipGetLastError();
 }
 
@@ -86,7 +105,7 @@ __global__ __launch_bounds__(256) void k_quant_128x128(const uint16_t* __restric
   const int64_t k0 = kb * kGroup + 8 * c;
   uint4 v[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = *reinterpret_cast<const uint4*>(w + (n0 + i) * ldw + k0);
+  for (int i = 0; i < 8; ++i) v[i] = load_stream16(w + (n0 + i) * ldw + k0);
   uint32_t am = 0u;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -116,7 +135,7 @@ __global__ __launch_bounds__(256) void k_quant_128x128(const uint16_t* __restric
   for (int i = 0; i < 8; ++i) {
     const uint32_t lo = e4m3x4(f[i][0], f[i][1], f[i][2], f[i][3]);
     const uint32_t hi = e4m3x4(f[i][4], f[i][5], f[i][6], f[i][7]);
-    *reinterpret_cast<uint2*>(q + (n0 + i) * K + k0) = make_uint2(lo, hi);
+    store_stream8(q + (n0 + i) * K + k0, lo, hi);
   }
   if (qT != nullptr) {
 #pragma unroll
@@ -149,26 +168,40 @@ hipError_t launch_quant_128x128(const uint16_t* w, int64_t N, int64_t K, int64_t
 // FP8SRC: the source is the 1x128-quantized activation (codes + [K/128, M]
 // scales); the value re-quantized is fl32(E4M3value(code) * scale).
 // ---------------------------------------------------------------------------
-template <bool FP8SRC>
+//
+// GROUPED: the rows are expert segments seg[e] .. seg[e+1]-1 and groups restart
+// at each segment; blockIdx.y is the group's slot g over all segments
+// (segment e owns slots first_e .. first_e + ceil(len_e/128) - 1), which is
+// also its output column block: the padded layout of the grouped WGrad.
+template <bool FP8SRC, bool GROUPED>
 __global__ __launch_bounds__(256) void k_quant_128x1_T(const void* __restrict__ src,
                                                        const float* __restrict__ src_s,
                                                        int64_t M, int64_t K, int64_t ldsrc,
+                                                       const int32_t* __restrict__ seg, int E,
                                                        uint8_t* __restrict__ qT, int64_t ldqT,
                                                        float* __restrict__ sT) {
   constexpr int CW = FP8SRC ? 16 : 8;
   const int ri = threadIdx.x & 15;
   const int c = threadIdx.x >> 4;
   const int64_t g = blockIdx.y;
+  int64_t row_begin = g * kGroup, row_end = M;
+  if constexpr (GROUPED) {
+    const SegHit h = seg_find(seg, E, (int)M, kGroup, (int)g, false);
+    if (h.e < 0) return;
+    row_begin = h.lo + (int64_t)(g - h.first) * kGroup;
+    row_end = h.hi;
+  }
   const int64_t col0 = (int64_t)blockIdx.x * (16 * CW) + (int64_t)c * CW;
   const bool colok = col0 < K;
-  const int64_t m0 = g * kGroup + 8 * ri;
+  const int64_t m0 = row_begin + 8 * ri;      // first source row of this thread
+  const int64_t o0 = g * kGroup + 8 * ri;     // its first output column
 
   float f[8][CW];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int64_t m = m0 + i;
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (colok && m < M) {
+    if (colok && m < row_end) {
       if (FP8SRC)
         v = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(src) + m * ldsrc + col0);
       else
@@ -176,7 +209,7 @@ __global__ __launch_bounds__(256) void k_quant_128x1_T(const void* __restrict__ 
     }
     if constexpr (FP8SRC) {
       float sc = 0.0f;
-      if (colok && m < M) sc = src_s[(col0 / kGroup) * M + m];
+      if (colok && m < row_end) sc = src_s[(col0 / kGroup) * M + m];
       const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
@@ -219,8 +252,25 @@ __global__ __launch_bounds__(256) void k_quant_128x1_T(const void* __restrict__ 
     const float r = rr[jj];
     const uint32_t lo = e4m3x4(f[0][jj] * r, f[1][jj] * r, f[2][jj] * r, f[3][jj] * r);
     const uint32_t hi = e4m3x4(f[4][jj] * r, f[5][jj] * r, f[6][jj] * r, f[7][jj] * r);
-    *reinterpret_cast<uint2*>(qT + (col0 + jj) * ldqT + m0) = make_uint2(lo, hi);
+    store_stream8(qT + (col0 + jj) * ldqT + o0, lo, hi);
   }
+}
+
+template <bool GROUPED>
+static hipError_t launch_128x1_T(const void* src, bool fp8src, const float* src_s, int64_t M,
+                                 int64_t K, int64_t ldsrc, const int32_t* seg, int E,
+                                 unsigned groups, uint8_t* qT, int64_t ldqT, float* sT,
+                                 hipStream_t st) {
+  if (fp8src) {
+    dim3 grid((unsigned)((K + 255) / 256), groups);
+    hipLaunchKernelGGL((k_quant_128x1_T<true, GROUPED>), grid, dim3(256), 0, st, src, src_s, M, K,
+                       ldsrc, seg, E, qT, ldqT, sT);
+  } else {
+    dim3 grid((unsigned)(K / kGroup), groups);
+    hipLaunchKernelGGL((k_quant_128x1_T<false, GROUPED>), grid, dim3(256), 0, st, src, src_s, M,
+                       K, ldsrc, seg, E, qT, ldqT, sT);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_quant_128x1_T(const void* src, bool fp8src, const float* src_s, int64_t M,
@@ -228,16 +278,18 @@ hipError_t launch_quant_128x1_T(const void* src, bool fp8src, const float* src_s
                                 hipStream_t st) {
   if (M == 0 || K == 0) return hipSuccess;
   const unsigned groups = (unsigned)((M + kGroup - 1) / kGroup);
-  if (fp8src) {
-    dim3 grid((unsigned)((K + 255) / 256), groups);
-    hipLaunchKernelGGL(k_quant_128x1_T<true>, grid, dim3(256), 0, st, src, src_s, M, K, ldsrc,
-                       qT, ldqT, sT);
-  } else {
-    dim3 grid((unsigned)(K / kGroup), groups);
-    hipLaunchKernelGGL(k_quant_128x1_T<false>, grid, dim3(256), 0, st, src, src_s, M, K, ldsrc,
-                       qT, ldqT, sT);
-  }
-  return hipGetLastError();
+  return launch_128x1_T<false>(src, fp8src, src_s, M, K, ldsrc, nullptr, 0, groups, qT, ldqT, sT,
+                               st);
+}
+
+hipError_t launch_quant_128x1_T_grouped(const void* src, bool fp8src, const float* src_s,
+                                        int64_t M, int64_t K, int64_t ldsrc, const int32_t* seg,
+                                        int E, uint8_t* qT, int64_t ldqT, float* sT,
+                                        hipStream_t st) {
+  if (M == 0 || K == 0) return hipSuccess;
+  // at most ceil(M/128) + E groups over all segments
+  const unsigned slots = (unsigned)((M + kGroup - 1) / kGroup + E);
+  return launch_128x1_T<true>(src, fp8src, src_s, M, K, ldsrc, seg, E, slots, qT, ldqT, sT, st);
 }
 
 }  // namespace jet

@@ -35,6 +35,11 @@ SIGNATURES = {
     "jet_fp8_linear_dgrad": [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _p, _sz, _p],
     "jet_fp8_linear_wgrad": [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _i32, _p, _sz, _p],
     "jet_workspace_bytes": [_i32, _i64, _i64, _i64],
+    "jet_quant_act_128x1_T_grouped": [_p, _i32, _p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _p],
+    "jet_fp8_grouped_fwd": [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p, _i32, _p, _p, _p, _sz, _p],
+    "jet_fp8_grouped_dgrad": [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p, _i32, _p, _sz, _p],
+    "jet_fp8_grouped_wgrad": [_p, _p, _p, _p, _i64, _p, _i64, _i64, _i64, _i64, _p, _i32, _i32, _p,
+                              _sz, _p],
 }
 _RESTYPES = {"jet_status_string": ctypes.c_char_p, "jet_last_error": ctypes.c_char_p,
              "jet_workspace_bytes": _sz}
@@ -225,4 +230,99 @@ def jet_fp8_linear_wgrad(dyqT, dysT, xqT, xsT, M, dw=None, out_dtype=torch.float
         _ptr(dyqT), _ptr(dysT), _ptr(xqT), _ptr(xsT), M, N, K, _ptr(dw), _dtype_code(dw.dtype),
         1 if accumulate else 0, _ptr(workspace), 0 if workspace is None else workspace.numel(),
         _stream(stream)))
+    return dw
+
+
+# ---------------------------------------------------------------------------
+# Grouped (mixture-of-experts) layer: seg_off is a device int32 tensor [E+1]
+# ---------------------------------------------------------------------------
+def grouped_columns(M: int, E: int) -> int:
+    """Column capacity of the padded transposed grouped layout: 128*(ceil(M/128)+E)."""
+    return (-(-M // 128) + E) * 128
+
+
+def _seg(seg_off):
+    if seg_off.dtype != torch.int32 or seg_off.dim() != 1 or not seg_off.is_contiguous():
+        raise TypeError("seg_off must be a contiguous 1-D int32 device tensor [E+1]")
+    return seg_off, seg_off.numel() - 1
+
+
+def jet_quant_act_128x1_T_grouped(src, seg_off, src_s=None, qT=None, sT=None, stream=None):
+    """Grouped 128x1 transposed quantization.  Returns (qT uint8 [K, P], sT float32 [P/128, K]),
+    P = grouped_columns(M, E); columns past the padded total are left as allocated."""
+    _rowmajor(src, "src")
+    seg_off, E = _seg(seg_off)
+    M, K = src.shape
+    if src_s is None:
+        if src.dtype != torch.bfloat16:
+            raise TypeError("src must be bfloat16 when src_s is None")
+        dt = JET_BF16
+    else:
+        src = _codes(src)
+        dt = JET_E4M3
+    P = grouped_columns(M, E)
+    qT = _codes(qT) if qT is not None else _empty((K, P), torch.uint8, src)
+    sT = sT if sT is not None else _empty((qT.stride(0) // 128, K), torch.float32, src)
+    _rowmajor(qT, "qT")
+    _check("jet_quant_act_128x1_T_grouped", _lib.jet_quant_act_128x1_T_grouped(
+        _ptr(src), dt, _ptr(src_s), M, K, src.stride(0), _ptr(seg_off), E, _ptr(qT), qT.stride(0),
+        _ptr(sT), _stream(stream)))
+    return qT, sT
+
+
+def jet_fp8_grouped_fwd(xq, xs, wq, ws, seg_off, y=None, out_dtype=torch.bfloat16,
+                        fuse_quant=False, yq=None, ys=None, workspace=None, stream=None):
+    """Y rows of expert e = deq(xq_e) . deq(wq[e])^T; wq [E, N, K], ws [E, N/128, K/128]."""
+    xq, wq = _codes(xq), _codes(wq)
+    seg_off, E = _seg(seg_off)
+    M, K = xq.shape
+    N = wq.shape[1]
+    y = y if y is not None else _empty((M, N), out_dtype, xq)
+    if fuse_quant:
+        yq = _codes(yq) if yq is not None else _empty((M, N), torch.uint8, xq)
+        ys = ys if ys is not None else _empty((N // 128, M), torch.float32, xq)
+    need = jet_workspace_bytes(JET_OP_FWD, M, N, K)
+    if workspace is None and need:
+        workspace = _empty((need,), torch.uint8, xq)
+    _check("jet_fp8_grouped_fwd", _lib.jet_fp8_grouped_fwd(
+        _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(seg_off), E, M, N, K, _ptr(y),
+        _dtype_code(y.dtype), _ptr(yq), _ptr(ys), _ptr(workspace),
+        0 if workspace is None else workspace.numel(), _stream(stream)))
+    return (y, yq, ys) if fuse_quant else y
+
+
+def jet_fp8_grouped_dgrad(dyq, dys, wqT, ws, seg_off, dx=None, out_dtype=torch.bfloat16,
+                          workspace=None, stream=None):
+    """dX rows of expert e = deq(dyq_e) . deq(W_e); wqT [K, E*N] (stacked transposed codes)."""
+    dyq, wqT = _codes(dyq), _codes(wqT)
+    seg_off, E = _seg(seg_off)
+    M, N = dyq.shape
+    K = wqT.shape[0]
+    dx = dx if dx is not None else _empty((M, K), out_dtype, dyq)
+    need = jet_workspace_bytes(JET_OP_DGRAD, M, N, K)
+    if workspace is None and need:
+        workspace = _empty((need,), torch.uint8, dyq)
+    _check("jet_fp8_grouped_dgrad", _lib.jet_fp8_grouped_dgrad(
+        _ptr(dyq), _ptr(dys), _ptr(wqT), _ptr(ws), _ptr(seg_off), E, M, N, K, _ptr(dx),
+        _dtype_code(dx.dtype), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+        _stream(stream)))
+    return dx
+
+
+def jet_fp8_grouped_wgrad(dyqT, dysT, xqT, xsT, seg_off, M, dw=None, out_dtype=torch.float32,
+                          accumulate=False, workspace=None, stream=None):
+    """dW_e (+)= deq(dyqT_e) . deq(xqT_e)^T; operands in the padded grouped layout [N, P], [K, P]."""
+    dyqT, xqT = _codes(dyqT), _codes(xqT)
+    seg_off, E = _seg(seg_off)
+    N, K = dyqT.shape[0], xqT.shape[0]
+    if dyqT.stride(0) != xqT.stride(0):
+        raise ValueError("dyqT and xqT need the same row stride")
+    dw = dw if dw is not None else _empty((E, N, K), out_dtype, dyqT)
+    need = jet_workspace_bytes(JET_OP_WGRAD, M, N, K)
+    if workspace is None and need:
+        workspace = _empty((need,), torch.uint8, dyqT)
+    _check("jet_fp8_grouped_wgrad", _lib.jet_fp8_grouped_wgrad(
+        _ptr(dyqT), _ptr(dysT), _ptr(xqT), _ptr(xsT), dyqT.stride(0), _ptr(seg_off), E, M, N, K,
+        _ptr(dw), _dtype_code(dw.dtype), 1 if accumulate else 0, _ptr(workspace),
+        0 if workspace is None else workspace.numel(), _stream(stream)))
     return dw

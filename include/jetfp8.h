@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define JET_ABI_VERSION 1
+#define JET_ABI_VERSION 2
 
 typedef enum {
   JET_OK = 0,
@@ -178,6 +178,82 @@ int jet_fp8_linear_wgrad(const uint8_t* dyqT, const float* dysT,
 
 /* Workspace bytes the GEMM `op` (jet_op) needs at this shape (0 = none). */
 size_t jet_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
+
+/*
+ * Grouped (mixture-of-experts) layer.  The pages apply the FP8 recipe to MoE
+ * models (66260.cn FP8-RL item: expert layers in the compressed format;
+ * nmedialink section on the Qwen3-30B MoE experiment) without a layout, so:
+ * the M routed rows are sorted by expert and expert e owns the contiguous
+ * segment of rows seg_off[e] .. seg_off[e+1]-1; every step of the dense layer
+ * applies per segment with expert e's weights.
+ *
+ *   seg_off : DEVICE int32 [E+1], seg_off[0] = 0, nondecreasing,
+ *             seg_off[E] = M.  It is read on the device only (no host sync).
+ *             Offsets that break these rules give unspecified results, but
+ *             every access stays inside the buffers described here.
+ *   1 <= E <= 2^20.  The 1x128 quantization of X and dY, and the 128x128
+ *   quantization of the stacked weights [E*N, K], are the dense entry points
+ *   (their groups never cross a row or an expert).
+ *
+ * Padded transposed layout of the grouped WGrad operands: segment e owns the
+ * columns col[e] .. col[e+1]-1 with col[e] = 128 * sum_{e'<e} ceil(len_e'/128);
+ * its 128x1 groups start at its first row; columns past its rows hold zero
+ * codes.  Buffers are sized for the largest possible total,
+ * P = 128 * (ceil(M/128) + E) columns; columns past col[E] are not written.
+ */
+
+/*
+ *   src, src_dtype, src_s, M, K, ldsrc : as jet_quant_act_128x1_T (M = all rows).
+ *   qT : E4M3 [K, ldqT] with ldqT >= P (ldqT % 16 == 0);  sT : FP32 [ldqT/128, K],
+ *        the scale of slot g (columns 128g..128g+127) of column k at sT[g*K + k].
+ *   ceil(M/128) + E <= 65535.
+ */
+int jet_quant_act_128x1_T_grouped(const void* src, int src_dtype, const float* src_s,
+                                  int64_t M, int64_t K, int64_t ldsrc,
+                                  const int32_t* seg_off, int64_t E,
+                                  uint8_t* qT, int64_t ldqT, float* sT, void* stream);
+
+/*
+ * Y rows of segment e = Xhat_e . What_e^T.
+ *   xq, xs : as jet_fp8_linear_fwd over all M rows (xs [K/128, M]).
+ *   wq : E4M3 [E, N, K] dense; ws : FP32 [E, N/128, K/128].
+ *   y, yq, ys : as jet_fp8_linear_fwd ([M, N], ys [N/128, M]).
+ */
+int jet_fp8_grouped_fwd(const uint8_t* xq, const float* xs,
+                        const uint8_t* wq, const float* ws,
+                        const int32_t* seg_off, int64_t E,
+                        int64_t M, int64_t N, int64_t K,
+                        void* y, int y_dtype, uint8_t* yq, float* ys,
+                        void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * dX rows of segment e = dYhat_e . What_e.
+ *   dyq, dys : as jet_fp8_linear_dgrad over all M rows.
+ *   wqT : E4M3 [K, E*N] dense -- the transposed codes jet_quant_weight_128x128
+ *         writes for the stacked weights [E*N, K] (expert e: columns e*N..e*N+N-1);
+ *   ws  : FP32 [E, N/128, K/128].  E*N <= 2^30.
+ *   dx  : [M, K] dense, dx_dtype JET_BF16 or JET_F32.
+ */
+int jet_fp8_grouped_dgrad(const uint8_t* dyq, const float* dys,
+                          const uint8_t* wqT, const float* ws,
+                          const int32_t* seg_off, int64_t E,
+                          int64_t M, int64_t N, int64_t K,
+                          void* dx, int dx_dtype,
+                          void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * dW_e (+)= dYhat_e^T . Xhat_e for every expert (an empty segment gives 0).
+ *   dyqT : E4M3 [N, ldT], dysT : FP32 [ldT/128, N]   (jet_quant_act_128x1_T_grouped of dY)
+ *   xqT  : E4M3 [K, ldT], xsT  : FP32 [ldT/128, K]   (of the 1x128-quantized X)
+ *   ldT >= P, ldT % 16 == 0, ldT <= 2^30.
+ *   dw : [E, N, K] dense, dw_dtype JET_F32 or JET_BF16; accumulate as jet_fp8_linear_wgrad.
+ */
+int jet_fp8_grouped_wgrad(const uint8_t* dyqT, const float* dysT,
+                          const uint8_t* xqT, const float* xsT, int64_t ldT,
+                          const int32_t* seg_off, int64_t E,
+                          int64_t M, int64_t N, int64_t K,
+                          void* dw, int dw_dtype, int accumulate,
+                          void* workspace, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

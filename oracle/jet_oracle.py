@@ -55,6 +55,15 @@ R5  A partial 128x1 group at the token tail uses only its valid rows; the
 R6  GEMM reference = float64 product of the exactly dequantized operands;
     BF16 outputs are the round-to-nearest-even BF16 of the FP32 rounding of
     that product.
+R7  Mixture-of-experts layers ([FP8-RL]: expert layers run in the compressed
+    format; [NV-RL] section on the Qwen3-30B MoE experiment: the same FP8
+    recipe on an MoE model).  The pages give no grouped layout, so: the rows
+    routed to expert e form the contiguous segment seg_off[e]..seg_off[e+1]-1
+    of the token matrix; every step of the dense layer applies to each
+    segment with expert e's weights; 128x1 groups restart at each segment
+    start; the transposed 128x1 outputs give segment e the column range
+    starting at 128 * sum_{e'<e} ceil(len_e'/128), zero-padded to a multiple
+    of 128 columns.  An empty segment contributes nothing (dW_e = 0).
 """
 from __future__ import annotations
 
@@ -276,6 +285,82 @@ def gemm_wgrad(dyqT, dysT, xqT, xsT, M) -> np.ndarray:
     reading R4: both operands grouped 128x1 along the M tokens.
     """
     return dequant_128x1_T(dyqT, dysT, M) @ dequant_128x1_T(xqT, xsT, M).T
+
+
+# ---------------------------------------------------------------------------
+# Grouped (mixture-of-experts) layer, reading R7: the dense steps per segment
+# ---------------------------------------------------------------------------
+
+def segment_columns(seg_off) -> np.ndarray:
+    """Start column of each segment in the transposed 128x1 layout, int64 [E+1]
+    (entry E = the padded total)."""
+    seg_off = np.asarray(seg_off, dtype=np.int64)
+    lens = seg_off[1:] - seg_off[:-1]
+    col = np.zeros(len(lens) + 1, dtype=np.int64)
+    col[1:] = np.cumsum(-(-lens // GROUP) * GROUP)
+    return col
+
+
+def quant_128x1_T_grouped(a, seg_off) -> tuple[np.ndarray, np.ndarray]:
+    """128x1 transposed quantization with groups restarting at each segment.
+
+    a : [M, C] float32, seg_off : [E+1].  returns codesT [C, P] and scales
+    [P/128, C], P = segment_columns(seg_off)[E]; segment e occupies columns
+    col[e] .. col[e+1]-1 (its own quant_128x1_T output).
+    """
+    a = np.asarray(a, dtype=np.float32)
+    col = segment_columns(seg_off)
+    C = a.shape[1]
+    codesT = np.zeros((C, int(col[-1])), dtype=np.uint8)
+    scales = np.zeros((int(col[-1]) // GROUP, C), dtype=np.float32)
+    for e in range(len(col) - 1):
+        lo, hi = int(seg_off[e]), int(seg_off[e + 1])
+        if hi == lo:
+            continue
+        qT, sT = quant_128x1_T(a[lo:hi])
+        codesT[:, col[e]:col[e + 1]] = qT
+        scales[col[e] // GROUP: col[e + 1] // GROUP] = sT
+    return codesT, scales
+
+
+def requant_128x1_T_grouped_from_1x128(codes, scales, seg_off) -> tuple[np.ndarray, np.ndarray]:
+    """Grouped form of requant_128x1_T_from_1x128 (readings R4, R7)."""
+    return quant_128x1_T_grouped(dequant_1x128_fl32(codes, scales), seg_off)
+
+
+def gemm_grouped_fwd(xq, xs, wq, ws, seg_off) -> np.ndarray:
+    """Y rows of segment e = X_e W_e^T (float64 [M, N]); wq [E, N, K], ws [E, N/128, K/128]."""
+    a = dequant_1x128(xq, xs)
+    y = np.zeros((a.shape[0], wq.shape[1]))
+    for e in range(wq.shape[0]):
+        lo, hi = int(seg_off[e]), int(seg_off[e + 1])
+        y[lo:hi] = a[lo:hi] @ dequant_128x128(wq[e], ws[e]).T
+    return y
+
+
+def gemm_grouped_dgrad(dyq, dys, wq, ws, seg_off) -> np.ndarray:
+    """dX rows of segment e = dY_e W_e (float64 [M, K])."""
+    a = dequant_1x128(dyq, dys)
+    dx = np.zeros((a.shape[0], wq.shape[2]))
+    for e in range(wq.shape[0]):
+        lo, hi = int(seg_off[e]), int(seg_off[e + 1])
+        dx[lo:hi] = a[lo:hi] @ dequant_128x128(wq[e], ws[e])
+    return dx
+
+
+def gemm_grouped_wgrad(dyqT, dysT, xqT, xsT, seg_off) -> np.ndarray:
+    """dW_e = dY_e^T X_e (float64 [E, N, K]) from the grouped transposed operands."""
+    col = segment_columns(seg_off)
+    E = len(col) - 1
+    dw = np.zeros((E, dyqT.shape[0], xqT.shape[0]))
+    for e in range(E):
+        n = int(seg_off[e + 1] - seg_off[e])
+        if n == 0:
+            continue
+        c0, c1 = int(col[e]), int(col[e + 1])
+        g0, g1 = c0 // GROUP, c1 // GROUP
+        dw[e] = gemm_wgrad(dyqT[:, c0:c1], dysT[g0:g1], xqT[:, c0:c1], xsT[g0:g1], n)
+    return dw
 
 
 # ---------------------------------------------------------------------------

@@ -28,7 +28,9 @@ def J():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["jet_quant_act_1x128", "jet_quant_act_128x1_T", "jet_quant_weight_128x128",
-              "jet_fp8_linear_fwd", "jet_fp8_linear_dgrad", "jet_fp8_linear_wgrad"]:
+              "jet_fp8_linear_fwd", "jet_fp8_linear_dgrad", "jet_fp8_linear_wgrad",
+              "jet_quant_act_128x1_T_grouped", "jet_fp8_grouped_fwd", "jet_fp8_grouped_dgrad",
+              "jet_fp8_grouped_wgrad"]:
         assert n in names
 
 
@@ -46,7 +48,7 @@ def test_binding_covers_header(J):
 
 
 def test_version_and_status_strings(J):
-    assert J.jet_abi_version() == 1
+    assert J.jet_abi_version() == 2
     assert J.jet_status_string(J.JET_ERR_SHAPE) == "JET_ERR_SHAPE"
     assert J.jet_status_string(99) == "JET_ERR_UNKNOWN"
 
@@ -89,3 +91,33 @@ def test_gemm_validation(J):
     assert L.jet_fp8_linear_fwd(None, None, None, None, 0, 128, 128, None, J.JET_BF16, None, None, None, 0,
                                 None) == J.JET_OK
     assert J.jet_workspace_bytes(J.JET_OP_FWD, 64, 4096, 4096) >= 0
+
+
+def test_grouped_validation(J):
+    L = J._lib
+    a = [P16, P16, P16, P16]
+    # quantizer: E range, null seg_off, capacity of qT, grid limit
+    assert L.jet_quant_act_128x1_T_grouped(P16, J.JET_BF16, None, 300, 128, 128, P16, 0, P16, 1024, P16,
+                                           None) == J.JET_ERR_SHAPE
+    assert L.jet_quant_act_128x1_T_grouped(P16, J.JET_BF16, None, 300, 128, 128, None, 4, P16, 1024, P16,
+                                           None) == J.JET_ERR_NULL
+    assert L.jet_quant_act_128x1_T_grouped(P16, J.JET_BF16, None, 300, 128, 128, P16, 4, P16, 880, P16,
+                                           None) == J.JET_ERR_SHAPE        # needs 128*(3+4) = 896
+    assert L.jet_quant_act_128x1_T_grouped(P16, J.JET_BF16, None, 300, 128, 128, P17, 4, P16, 896, P16,
+                                           None) == J.JET_ERR_ALIGN
+    assert L.jet_quant_act_128x1_T_grouped(P16, J.JET_BF16, None, 128, 128, 128, P16, 65535, P16,
+                                           128 * 65536, P16, None) == J.JET_ERR_SHAPE
+    # GEMMs
+    assert L.jet_fp8_grouped_fwd(*a, P16, 0, 64, 128, 128, P16, J.JET_BF16, None, None, None, 0,
+                                 None) == J.JET_ERR_SHAPE
+    assert L.jet_fp8_grouped_fwd(*a, None, 2, 64, 128, 128, P16, J.JET_BF16, None, None, None, 0,
+                                 None) == J.JET_ERR_NULL
+    assert L.jet_fp8_grouped_fwd(*a, P16, 2, 64, 100, 128, P16, J.JET_BF16, None, None, None, 0,
+                                 None) == J.JET_ERR_SHAPE
+    assert L.jet_fp8_grouped_dgrad(*a, P16, 2, 64, 128, 128, P16, 5, None, 0, None) == J.JET_ERR_DTYPE
+    assert L.jet_fp8_grouped_wgrad(*a, 256, P16, 2, 64, 128, 128, P16, J.JET_F32, 0, None, 0,
+                                   None) == J.JET_ERR_SHAPE                  # ldT < 128*(1+2)
+    assert L.jet_fp8_grouped_wgrad(*a, 384, P16, 2, 64, 128, 128, P16, J.JET_BF16, 1, None, 0,
+                                   None) == J.JET_ERR_DTYPE
+    assert L.jet_fp8_grouped_fwd(None, None, None, None, P16, 2, 0, 128, 128, None, J.JET_BF16, None,
+                                 None, None, 0, None) == J.JET_OK          # no rows: no-op
