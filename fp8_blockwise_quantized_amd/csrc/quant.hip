@@ -156,23 +156,27 @@ hipError_t launch_quant_128x128(const uint16_t* w, int64_t N, int64_t K, int64_t
 }
 
 // ---------------------------------------------------------------------------
-// 128x1, transposed.  A block handles one 128-row group g and 16*CW columns;
-// thread t owns rows 8*(t%16)..+7 of the group and columns CW*(t/16)..+CW-1
-// (16 source bytes per row).  The 16 lanes of a DPP row share the columns and
-// cover all 128 rows, so each column's maximum is a DPP-row reduction.  Codes
-// of column k for the thread's 8 rows are packed into one 8-byte store at
-// qT[k][128g + 8*(t%16)], so a wavefront store writes 128 contiguous bytes of
-// four qT rows.  Rows past M are zeros: they do not change a column maximum
-// and they encode to 0x00 in the padding columns.
+// 128x1, transposed.  A block handles one 128-row group g and 16*CW columns
+// (256 source bytes per row).  Thread t owns rows 8*ri .. 8*ri+7 of the group
+// and the CW columns of 16-byte chunk c (ri, c in 0..15), with lane
+// (c % 8) + 8 * (ri % 8) of wavefront (ri / 8) + 2 * (c / 8): each wavefront
+// load covers 8 rows x 128 contiguous bytes (whole cache lines).  A column's
+// maximum is reduced over the thread's 8 rows, across the 8 row slabs of the
+// wavefront (lane-index xor 8, 16, 32), then with the one other wavefront
+// holding the same columns through LDS.  Codes of column k for the thread's 8
+// rows are packed into one 8-byte store at qT[k][128g + 8*ri]; the two
+// wavefronts that share columns write the two halves of each 128-byte qT row
+// segment.  Rows past the group's end are zeros: they do not change a column
+// maximum and they encode to 0x00 in the padding columns.
 //
 // FP8SRC: the source is the 1x128-quantized activation (codes + [K/128, M]
 // scales); the value re-quantized is fl32(E4M3value(code) * scale).
-// ---------------------------------------------------------------------------
 //
 // GROUPED: the rows are expert segments seg[e] .. seg[e+1]-1 and groups restart
 // at each segment; blockIdx.y is the group's slot g over all segments
 // (segment e owns slots first_e .. first_e + ceil(len_e/128) - 1), which is
 // also its output column block: the padded layout of the grouped WGrad.
+// ---------------------------------------------------------------------------
 template <bool FP8SRC, bool GROUPED>
 __global__ __launch_bounds__(256) void k_quant_128x1_T(const void* __restrict__ src,
                                                        const float* __restrict__ src_s,
@@ -181,8 +185,11 @@ __global__ __launch_bounds__(256) void k_quant_128x1_T(const void* __restrict__ 
                                                        uint8_t* __restrict__ qT, int64_t ldqT,
                                                        float* __restrict__ sT) {
   constexpr int CW = FP8SRC ? 16 : 8;
-  const int ri = threadIdx.x & 15;
-  const int c = threadIdx.x >> 4;
+  __shared__ float red[4][8][CW];     // per wavefront: column maxima of its 8 chunks
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int ri = (lane >> 3) + 8 * (wave & 1);
+  const int c = (lane & 7) + 8 * (wave >> 1);
   const int64_t g = blockIdx.y;
   int64_t row_begin = g * kGroup, row_end = M;
   if constexpr (GROUPED) {
@@ -203,9 +210,9 @@ __global__ __launch_bounds__(256) void k_quant_128x1_T(const void* __restrict__ 
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
     if (colok && m < row_end) {
       if (FP8SRC)
-        v = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(src) + m * ldsrc + col0);
+        v = load_stream16(static_cast<const uint8_t*>(src) + m * ldsrc + col0);
       else
-        v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + m * ldsrc + col0);
+        v = load_stream16(static_cast<const uint16_t*>(src) + m * ldsrc + col0);
     }
     if constexpr (FP8SRC) {
       float sc = 0.0f;
@@ -228,15 +235,30 @@ __global__ __launch_bounds__(256) void k_quant_128x1_T(const void* __restrict__ 
     }
   }
 
-  float rr[CW];
-  float ss[CW];
+  // column maxima (non-negative floats compared as unsigned integers)
+  uint32_t am[CW];
 #pragma unroll
   for (int jj = 0; jj < CW; ++jj) {
     float a = fabsf(f[0][jj]);
 #pragma unroll
     for (int i = 1; i < 8; ++i) a = fmaxf(a, fabsf(f[i][jj]));
-    a = row16_max_f32(a);
-    const ScalePair sp = scale_pair(a);
+    uint32_t u = __float_as_uint(a);
+    u = max(u, (uint32_t)__shfl_xor((int)u, 8, 64));
+    u = max(u, (uint32_t)__shfl_xor((int)u, 16, 64));
+    u = max(u, (uint32_t)__shfl_xor((int)u, 32, 64));
+    am[jj] = u;
+  }
+  if (lane < 8) {
+#pragma unroll
+    for (int jj = 0; jj < CW; ++jj) red[wave][lane][jj] = __uint_as_float(am[jj]);
+  }
+  __syncthreads();
+  float rr[CW];
+  float ss[CW];
+#pragma unroll
+  for (int jj = 0; jj < CW; ++jj) {
+    const uint32_t other = __float_as_uint(red[wave ^ 1][lane & 7][jj]);
+    const ScalePair sp = scale_pair(__uint_as_float(max(am[jj], other)));
     rr[jj] = sp.r;
     ss[jj] = sp.s;
   }
@@ -252,7 +274,7 @@ __global__ __launch_bounds__(256) void k_quant_128x1_T(const void* __restrict__ 
     const float r = rr[jj];
     const uint32_t lo = e4m3x4(f[0][jj] * r, f[1][jj] * r, f[2][jj] * r, f[3][jj] * r);
     const uint32_t hi = e4m3x4(f[4][jj] * r, f[5][jj] * r, f[6][jj] * r, f[7][jj] * r);
-    store_stream8(qT + (col0 + jj) * ldqT + o0, lo, hi);
+    *reinterpret_cast<uint2*>(qT + (col0 + jj) * ldqT + o0) = make_uint2(lo, hi);
   }
 }
 
