@@ -120,8 +120,9 @@ def copy_probe(torch):
 
 def cpu_baseline():
     """The oracle (untuned) on a bounded sample of the workload: the QKV
-    linear (4096 -> 6144) with its full weight and 4096 of the 8192 tokens,
-    through every step of the path; scaled to TFLOP/s of the sample's GEMMs."""
+    linear (4096 -> 6144) with its full weight and all 8192 tokens (one of
+    the four layers), through every step of the path; scaled to TFLOP/s of
+    the sample's GEMMs."""
     from oracle import jet_oracle as O
     from fp8_blockwise_quantized_amd import inputs
     try:
@@ -129,7 +130,7 @@ def cpu_baseline():
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = 1
-    Ms, N, K = 4096, 6144, 4096
+    Ms, N, K = M_TOKENS, 6144, 4096
     x = inputs.activations_with_outliers(Ms, K, seed=0)
     w = inputs.normal_bf16((N, K), 0.02, seed=0, tensor_id=inputs.ID_W)
     dy = inputs.normal_bf16((Ms, N), 1e-3, seed=0, tensor_id=inputs.ID_DY)
@@ -170,7 +171,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: this build runs on exactly one GPU "
-              f"(the path shards by tokens; see DESIGN.md for the multi-GPU design).", file=sys.stderr)
+              f"(the path shards by tokens; a multi-GPU run is not part of it).", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():

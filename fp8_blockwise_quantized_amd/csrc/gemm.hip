@@ -63,17 +63,21 @@ struct GemmCfg {
   static constexpr int THREADS = 64 * NW;
   static constexpr int BM = WMW * TM * 16, BN = WNW * TN * 16;
   static constexpr int ATILE = BM * 128, BTILE = BN * 128;
-  static constexpr int SA = BM * 4, SB = BN * 4;
-  static constexpr int STAGE = ATILE + BTILE + SA + SB;
   static constexpr int ABLK = ATILE / 1024 / NW;   // A DMA instructions per wave and stage
   static constexpr int BBLK = BTILE / 1024 / NW;
-  static constexpr int NCA = BM / 64, NCB = BN / 64;   // 64-slot scale chunks (rows, columns)
-  static constexpr int LOADS = ABLK + BBLK + 1;    // DMA instructions per wave and stage
-  static constexpr int EPI_PITCH = BN + 8;         // bf16 per staged output row
+  static constexpr int OA = TM / WNW, OB = TN / WMW;   // a wave's own A and B slabs (its DMA share)
+  static constexpr int RSW = TM * 16, CSW = TN * 16;   // private row / column scale slots per wave
+  static constexpr int SPRIV = (RSW + CSW) * 4;        // private scale bytes per wave and stage
+  static constexpr int NRS = RSW / 64;                 // row-scale DMAs per wave and stage
+  static constexpr int STAGE = ATILE + BTILE + NW * SPRIV;
+  static constexpr int LOADS = ABLK + BBLK + NRS + 1;  // DMA instructions per wave and stage
+  static constexpr int EPI_PITCH = BN + 8;             // bf16 per staged output row
   static constexpr int LDS = (STAGES * STAGE > BM * EPI_PITCH * 2) ? STAGES * STAGE : BM * EPI_PITCH * 2;
   static_assert(ABLK * NW * 1024 == ATILE && BBLK * NW * 1024 == BTILE, "DMA split");
-  static_assert(BM % 64 == 0 && BN % 64 == 0 && NCA + NCB <= NW, "scale split");
+  static_assert(ABLK * 8 == OA * 16 && BBLK * 8 == OB * 16, "a wave's DMA rows are its own slabs");
+  static_assert(RSW % 64 == 0 && CSW == 64, "scale DMA shape");
   static_assert(TM % 4 == 0 && (128 % (TN * 16)) == 0 && BN % 128 == 0, "tile shape");
+  static_assert((TM & (TM - 1)) == 0 && (TN & (TN - 1)) == 0, "power-of-two slab counts");
   static_assert(LDS * OCC <= 160 * 1024, "LDS");
 };
 
@@ -264,65 +268,71 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
   const int KB = p.Kc / 128;
   const uint32_t lds0 = lds_addr(lds);
 
-  // ---- per-lane DMA source offsets (bytes from the step's base pointers) ----
+  // ---- the wave's own share of every stage ----
+  // Wave (wm, wn) DMAs the OA 16-row A slabs wn*OA .. of its wave row and the
+  // OB 16-row B slabs wm*OB .. of its wave column: exactly the operands of
+  // its first OA x OB MFMAs.  Local slab i (j) of the wave is physical slab
+  // (i + wn*OA) % TM ((j + wm*OB) % TN), so local slabs 0.. are its own.
+  constexpr int OA = CFG::OA, OB = CFG::OB;
+  const int rotA0 = __builtin_amdgcn_readfirstlane(wn * OA);
+  const int rotB0 = __builtin_amdgcn_readfirstlane(wm * OB);
+  const int gA0 = (wm * TM * 16 + rotA0 * 16) / 8;   // first 1 KiB DMA block (8 rows) of own A rows
+  const int gB0 = (wn * TN * 16 + rotB0 * 16) / 8;
   uint32_t offA[CFG::ABLK], offB[CFG::BBLK];
 #pragma unroll
   for (int t = 0; t < CFG::ABLK; ++t) {
     int row; uint32_t col;
-    dma_src<FRAG>(wave * CFG::ABLK + t, lane, row, col);
+    dma_src<FRAG>(gA0 + t, lane, row, col);
     offA[t] = (uint32_t)min(m0 + row, p.M - 1) * (uint32_t)p.lda + col;
   }
 #pragma unroll
   for (int t = 0; t < CFG::BBLK; ++t) {
     int row; uint32_t col;
-    dma_src<FRAG>(wave * CFG::BBLK + t, lane, row, col);
+    dma_src<FRAG>(gB0 + t, lane, row, col);
     offB[t] = (uint32_t)min(n0 + row, p.N - 1) * (uint32_t)p.ldb + col;
   }
-  // Scales: every wave copies one 64-slot chunk per step with one 4-byte DMA
-  // (all lanes active).  Chunks 0 .. NCA-1 are row scales; within the TM*16
-  // slots of wave row wm, slot 64*q + 4*lrow + e holds tile row
-  // wm*TM*16 + (4q + e)*16 + lrow, so each lane reads its TM row scales with
-  // TM/4 contiguous 16-byte loads.  Chunks NCA .. are column scales (ROWCOL:
-  // slot = tile column; ROWBLOCK: slot s = the scale of the tile's 128-column
-  // block s, clamped).  Waves beyond NCA + NCB repeat a chunk (same values).
-  const int chunk = wave % (CFG::NCA + CFG::NCB);
-  const bool row_chunk = chunk < CFG::NCA;
-  uint32_t offS, ldsS;
-  {
-    const int slot = 64 * (row_chunk ? chunk : chunk - CFG::NCA) + lane;
-    if (row_chunk) {
-      const int sblk = slot / (TM * 16), sin = slot % (TM * 16);
-      const int srow = sblk * TM * 16 + ((sin >> 6) * 4 + (sin & 3)) * 16 + ((sin >> 2) & 15);
-      offS = (uint32_t)min(m0 + srow, p.M - 1) * 4u;
-      ldsS = (uint32_t)(CFG::ATILE + CFG::BTILE + 64 * 4 * chunk);
-    } else {
-      if (MODE == kRowCol) {
-        offS = (uint32_t)min(n0 + slot, p.N - 1) * 4u;
-      } else {
-        const int blk = min(n0 / 128 + slot, p.N / 128 - 1);
-        offS = (uint32_t)blk * (uint32_t)p.sB_o * 4u;
-      }
-      ldsS = (uint32_t)(CFG::ATILE + CFG::BTILE + CFG::SA + 64 * 4 * (chunk - CFG::NCA));
-    }
+  // Private scale copies (each wave DMAs the scales it folds with, so it can
+  // use them before the workgroup barrier).  Row slots, in local order: slot
+  // 64*(i/4) + 4*lrow + (i%4) holds the row of local slab i, lane row lrow
+  // (each lane reads its TM scales with TM/4 16-byte loads).  Column slots:
+  // ROWCOL slot 16*j + c holds column c of local B slab j; ROWBLOCK every slot
+  // holds the scale of the wave's 128-column block.
+  const uint32_t sprv = (uint32_t)(CFG::ATILE + CFG::BTILE + wave * CFG::SPRIV);
+  uint32_t offR[CFG::NRS];
+#pragma unroll
+  for (int q = 0; q < CFG::NRS; ++q) {
+    const int sl = 64 * q + lane;
+    const int li = 4 * (sl >> 6) + (sl & 3), lr = (sl >> 2) & 15;
+    const int row = wm * TM * 16 + ((li + rotA0) & (TM - 1)) * 16 + lr;
+    offR[q] = (uint32_t)min(m0 + row, p.M - 1) * 4u;
   }
-  const float* sbase0 = row_chunk ? p.sA : p.sB;
-  const int64_t sstep = row_chunk ? p.sA_ld : p.sB_c;
+  uint32_t offC;
+  if (MODE == kRowCol) {
+    const int lj = lane >> 4, c16 = lane & 15;
+    offC = (uint32_t)min(n0 + wn * TN * 16 + ((lj + rotB0) & (TN - 1)) * 16 + c16, p.N - 1) * 4u;
+  } else {
+    const int blk = min((n0 + wn * TN * 16) / 128, p.N / 128 - 1);
+    offC = (uint32_t)blk * (uint32_t)p.sB_o * 4u;
+  }
 
   // DMA part t of step kb into stage `stage`: t < ABLK + BBLK is one 1 KiB
-  // tile DMA, t == ABLK + BBLK the scale DMA.
+  // tile DMA, then NRS row-scale DMAs and one column-scale DMA.
   constexpr int NT = CFG::ABLK + CFG::BBLK;
 #define JET_ISSUE(part_, stage_, kb_)                                                          \
   do {                                                                                         \
     const uint32_t sbase_ = lds0 + (uint32_t)((stage_) * CFG::STAGE);                          \
     if ((part_) < CFG::ABLK) {                                                                 \
-      dma16(sbase_ + (uint32_t)((wave * CFG::ABLK + (part_)) * 1024),                          \
-            p.A + (int64_t)(kb_) * 128, offA[(part_) < CFG::ABLK ? (part_) : 0]);              \
+      dma16(sbase_ + (uint32_t)((gA0 + (part_)) * 1024), p.A + (int64_t)(kb_) * 128,           \
+            offA[(part_) < CFG::ABLK ? (part_) : 0]);                                          \
     } else if ((part_) < NT) {                                                                 \
       const int t_ = (part_) < NT ? (part_) - CFG::ABLK : 0;                                   \
-      dma16(sbase_ + (uint32_t)(CFG::ATILE + (wave * CFG::BBLK + t_) * 1024),                  \
-            p.B + (int64_t)(kb_) * 128, offB[t_]);                                             \
+      dma16(sbase_ + (uint32_t)(CFG::ATILE + (gB0 + t_) * 1024), p.B + (int64_t)(kb_) * 128,  \
+            offB[t_]);                                                                         \
+    } else if ((part_) < NT + CFG::NRS) {                                                      \
+      const int q_ = ((part_) < NT + CFG::NRS && (part_) >= NT) ? (part_) - NT : 0;            \
+      dma4(sbase_ + sprv + (uint32_t)(256 * q_), p.sA + (int64_t)(kb_) * p.sA_ld, offR[q_]);   \
     } else {                                                                                   \
-      dma4(sbase_ + ldsS, sbase0 + (int64_t)(kb_) * sstep, offS);                              \
+      dma4(sbase_ + sprv + (uint32_t)(CFG::RSW * 4), p.sB + (int64_t)(kb_) * p.sB_c, offC);    \
     }                                                                                          \
   } while (0)
 
@@ -332,12 +342,42 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
+  // MFMA order of a step (local slabs): the own OA x OB block first, then the
+  // rest of rows 0..OA-1, then rows OA.. in order.  A fragments live in a
+  // ring of R buffers (local row i in buffer i % R); a row whose buffer is
+  // still unused is read right after the barrier, any other row right after
+  // the last MFMA of row i-R.  (With 8 row slabs the outer-product scales of
+  // ROWCOL leave no registers for the extra buffer.)
+  constexpr int NM = TM * TN;
+  constexpr int R = (MODE == kRowCol && TM >= 8) ? OA : OA + 1;
+  struct Order { int i[NM]; int j[NM]; int load_after[TM]; };
+  constexpr Order ORD = []() {
+    Order o{};
+    int n = 0;
+    for (int i = 0; i < OA; ++i)
+      for (int j = 0; j < OB; ++j) { o.i[n] = i; o.j[n] = j; ++n; }
+    for (int i = 0; i < OA; ++i)
+      for (int j = OB; j < TN; ++j) { o.i[n] = i; o.j[n] = j; ++n; }
+    for (int i = OA; i < TM; ++i)
+      for (int j = 0; j < TN; ++j) { o.i[n] = i; o.j[n] = j; ++n; }
+    for (int i = 0; i < TM; ++i) o.load_after[i] = -1;        // -1: own (phase 1)
+    for (int i = OA; i < TM; ++i) {
+      int last = OA * OB - 1;                                   // right after the barrier
+      for (int m = 0; m < NM; ++m)
+        if (i - R >= 0 && o.i[m] == i - R) last = m;
+      o.load_after[i] = last;
+    }
+    return o;
+  }();
+  constexpr int NOWN = OA * OB;   // MFMAs before the barrier
+  constexpr int LAG = 3;
+
   constexpr int D = CFG::STAGES - 1;   // prefetch distance in K steps
 #pragma unroll
   for (int s = 0; s < D; ++s)
     if (s < KB) {
 #pragma unroll
-      for (int t = 0; t <= NT; ++t) JET_ISSUE(t, s, s);
+      for (int t = 0; t < NT + CFG::NRS + 1; ++t) JET_ISSUE(t, s, s);
     }
 
   int kb = 0, st = 0;
@@ -346,58 +386,49 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
   // the compiler schedules and allocates it as one block.
   auto step = [&](auto refill_tag) __attribute__((always_inline)) {
     constexpr bool REFILL = decltype(refill_tag)::value;
-    // In flight: this wave's DMAs of steps kb .. kb+D-1 (fewer in the last
-    // steps: then wait for all).  After the barrier every wave's step-kb data
-    // has landed and every wave is done with step kb-1's stage.
+    // This wave's own DMAs of step kb have landed (the later steps' may stay).
     if (REFILL) wait_vmem<CFG::LOADS * (D - 1)>();
     else wait_vmem<0>();
-    __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     const int stn = (st + D) % CFG::STAGES;
-    if (REFILL) JET_ISSUE(NT, stn, kb + D);
-
     const uint8_t* As = lds + st * CFG::STAGE;
     const uint8_t* Bs = As + CFG::ATILE;
-    const float* sAs = reinterpret_cast<const float*>(Bs + CFG::BTILE);
-    const float* sBs = sAs + BM;
+    const float* Sp = reinterpret_cast<const float*>(As + sprv);   // private scales
+    // Opaque per step: the fragment addresses are recomputed in the loop body
+    // (a few VALU adds) instead of being kept live across it in VGPRs.
+    int rotA = rotA0, rotB = rotB0;
+    asm volatile("" : "+s"(rotA), "+s"(rotB));
 
+    v8i bf[TN];
+    v8i af[R];
+#pragma unroll
+    for (int j = 0; j < OB; ++j) bf[j] = frag32<FRAG>(Bs, wn * TN + ((j + rotB) & (TN - 1)), lane);
+#pragma unroll
+    for (int i = 0; i < OA; ++i) af[i] = frag32<FRAG>(As, wm * TM + ((i + rotA) & (TM - 1)), lane);
     float rsc[TM];
 #pragma unroll
     for (int q = 0; q < TM / 4; ++q) {
-      const float4 r4 = *reinterpret_cast<const float4*>(sAs + wm * TM * 16 + q * 64 + lrow * 4);
+      const float4 r4 = *reinterpret_cast<const float4*>(Sp + 64 * q + 4 * lrow);
       rsc[4 * q + 0] = r4.x; rsc[4 * q + 1] = r4.y; rsc[4 * q + 2] = r4.z; rsc[4 * q + 3] = r4.w;
     }
     float cb[TN][4];
     if (MODE == kRowCol) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const float4 c4 = *reinterpret_cast<const float4*>(sBs + wn * TN * 16 + j * 16 + 4 * kg);
+        const float4 c4 = *reinterpret_cast<const float4*>(Sp + CFG::RSW + 16 * j + 4 * kg);
         cb[j][0] = c4.x; cb[j][1] = c4.y; cb[j][2] = c4.z; cb[j][3] = c4.w;
       }
     } else {
-      const float sbk = sBs[(wn * TN * 16) / 128];
+      const float sbk = Sp[CFG::RSW];
 #pragma unroll
       for (int i = 0; i < TM; ++i) rsc[i] *= sbk;
     }
 
-    // Software pipeline over the TM x TN MFMAs of the step, in row order: the
-    // A fragment of row i+1 is read when row i starts, the partial of MFMA n
-    // is folded just before MFMA n + LAG reuses its registers (so no fold
-    // waits on the MFMA right before it), and the next step's tile DMAs are
-    // spread over the rows (a wave issuing them back to back would stall
-    // while the CU's address unit drains them).
-    constexpr int LAG = 3;
-    constexpr int NM = TM * TN;
-    v8i bf[TN];
-#pragma unroll
-    for (int j = 0; j < TN; ++j) bf[j] = frag32<FRAG>(Bs, wn * TN + j, lane);
-    v8i af[2];
-    af[0] = frag32<FRAG>(As, wm * TM, lane);
     v4f part[LAG];
 #pragma unroll
     for (int n = 0; n < NM + LAG; ++n) {
       if (n >= LAG) {
-        const int ii = (n - LAG) / TN, jj = (n - LAG) % TN;
+        const int ii = ORD.i[n - LAG], jj = ORD.j[n - LAG];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float c = (MODE == kRowCol) ? rsc[ii] * cb[jj][r] : rsc[ii];
@@ -405,14 +436,36 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
         }
       }
       if (n < NM) {
-        const int i = n / TN, j = n % TN;
-        if (j == 0 && i + 1 < TM) af[(i + 1) & 1] = frag32<FRAG>(As, wm * TM + i + 1, lane);
-        part[n % LAG] = mfma_fp8(bf[j], af[i & 1]);
-        if (REFILL && j == TN - 1) {
+        const int i = ORD.i[n], j = ORD.j[n];
+        part[n % LAG] = mfma_fp8(bf[j], af[i % R]);
+        if (n == NOWN - 1) {
+          // Every wave's step-kb data has landed and every wave is done with
+          // step kb-1, whose stage step kb+D refills.
+          __builtin_amdgcn_s_barrier();
+          asm volatile("" ::: "memory");
+          if (REFILL) {
 #pragma unroll
-          for (int t = (i * NT) / TM; t < ((i + 1) * NT) / TM; ++t) JET_ISSUE(t, stn, kb + D);
+            for (int t = NT; t < NT + CFG::NRS + 1; ++t) JET_ISSUE(t, stn, kb + D);
+          }
+#pragma unroll
+          for (int jb = OB; jb < TN; ++jb)
+            bf[jb] = frag32<FRAG>(Bs, wn * TN + ((jb + rotB) & (TN - 1)), lane);
+        }
+        if (n >= NOWN - 1) {
+#pragma unroll
+          for (int ia = OA; ia < TM; ++ia)
+            if (ORD.load_after[ia] == n)
+              af[ia % R] = frag32<FRAG>(As, wm * TM + ((ia + rotA) & (TM - 1)), lane);
+        }
+        if (n >= NOWN) {
+          if (REFILL && ((n - NOWN) & 1) == 0 && (n - NOWN) / 2 < NT) JET_ISSUE((n - NOWN) / 2, stn, kb + D);
         }
       }
+    }
+    // tile DMAs not yet issued (more DMAs than MFMA slots)
+    if (REFILL) {
+#pragma unroll
+      for (int t = (NM - NOWN + 1) / 2; t < NT; ++t) JET_ISSUE(t, stn, kb + D);
     }
     st = (st + 1 == CFG::STAGES) ? 0 : st + 1;
   };
@@ -421,7 +474,8 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
 #undef JET_ISSUE
 
   // ---- epilogue ----
-  // Lane element (i, j, r) is C[m0 + wm*TM*16 + i*16 + lrow][n0 + wn*TN*16 + j*16 + 4*kg + r].
+  // Lane element (i, j, r) of local slabs (i, j) is
+  // C[m0 + wm*TM*16 + pa(i)*16 + lrow][n0 + wn*TN*16 + pb(j)*16 + 4*kg + r].
   const int mrow = m0 + wm * TM * 16 + lrow;
   const int ncol = n0 + wn * TN * 16 + 4 * kg;
   if (OUT == kOutF32) {
@@ -429,11 +483,11 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
     float* C = static_cast<float*>(p.C);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      const int m = mrow + i * 16;
+      const int m = mrow + ((i + rotA0) & (TM - 1)) * 16;
       if (m >= p.M) continue;
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int n = ncol + j * 16;
+        const int n = ncol + ((j + rotB0) & (TN - 1)) * 16;
         if (n >= p.N) continue;
         float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
         float4* dst = reinterpret_cast<float4*>(C + (int64_t)m * p.ldc + n);
@@ -454,8 +508,8 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
       for (int j = 0; j < TN; ++j) {
         const uint32_t lo = bf16_rne(acc[i][j][0]) | (bf16_rne(acc[i][j][1]) << 16);
         const uint32_t hi = bf16_rne(acc[i][j][2]) | (bf16_rne(acc[i][j][3]) << 16);
-        *reinterpret_cast<uint2*>(t + (wm * TM * 16 + i * 16 + lrow) * CFG::EPI_PITCH +
-                                  wn * TN * 16 + j * 16 + 4 * kg) = make_uint2(lo, hi);
+        *reinterpret_cast<uint2*>(t + (wm * TM * 16 + ((i + rotA0) & (TM - 1)) * 16 + lrow) * CFG::EPI_PITCH +
+                                  wn * TN * 16 + ((j + rotB0) & (TN - 1)) * 16 + 4 * kg) = make_uint2(lo, hi);
       }
     __syncthreads();
     uint16_t* C = static_cast<uint16_t*>(p.C);

@@ -37,7 +37,7 @@ Sources, cited by page title and section:
           The pages name the format only as "E4M3"; the +-448 range is the
           OCP E4M3 range.
 
-Readings taken where the pages are silent (each is also listed in the design doc):
+Readings taken where the pages are silent:
 
 R1  E4M3 is OCP E4M3FN ([OCP]); not the FNUZ variant (max 240).
 R2  Scale per group: amax_c = max(max|x|, 2^-96); stored scale
