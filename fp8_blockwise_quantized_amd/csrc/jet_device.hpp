@@ -116,6 +116,10 @@ __device__ __forceinline__ void store_stream8(void* p, uint32_t lo, uint32_t hi)
   const u32x2_t v = {lo, hi};
   __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t*>(p));
 }
+__device__ __forceinline__ void store_stream16(void* p, uint4 w) {
+  const u32x4_t v = {w.x, w.y, w.z, w.w};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
+}
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }

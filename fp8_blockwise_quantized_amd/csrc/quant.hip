@@ -25,63 +25,68 @@ namespace jet {
 
 // ---------------------------------------------------------------------------
 // 1x128.  One 16-lane DPP row handles one group of 128 BF16 values (256 bytes,
-// 16 bytes per lane).  Work is cut into units of 16 consecutive groups of one
-// row (4 KiB of input, one 256-thread block); a block takes UPI consecutive
-// units per round, all loads issued before any compute, and strides over the
-// units by the grid size.  Consecutive units continue along a row, so each
-// round of a block reads UPI*4 KiB of contiguous input (whole rows for
-// K <= 2048*UPI) and writes the codes contiguously.
+// 16 bytes per lane).  Work is cut into units of 32 rows x 4 consecutive
+// groups (32 KiB of input): in each of a 256-thread block's 8 passes, the 4
+// DPP rows of a wavefront take 4 rows of the same group (whole 128-byte
+// lines), all loads issued before any compute.  The unit's 128 scales are
+// staged in LDS (double-buffered, one barrier per unit) and written as 4 runs
+// of 32 consecutive rows, so the scale stores are whole lines as well.  A
+// block strides over the units by the grid size; consecutive units continue
+// along the rows.
 // ---------------------------------------------------------------------------
-template <int UPI>
 __global__ __launch_bounds__(256) void k_quant_1x128(const uint16_t* __restrict__ x, int64_t M,
                                                      int64_t K, int64_t ldx,
                                                      uint8_t* __restrict__ q, int64_t ldq,
                                                      float* __restrict__ s) {
-  const int64_t gpr = K / kGroup;          // groups per row
-  const int64_t upr = (gpr + 15) / 16;     // units per row
-  const int64_t units = M * upr;
-  const int gi = threadIdx.x >> 4;         // group within the unit
-  const int lane16 = threadIdx.x & 15;
-  for (int64_t u0 = (int64_t)blockIdx.x * UPI; u0 < units; u0 += (int64_t)gridDim.x * UPI) {
-    uint4 v[UPI];
+  __shared__ float stg[2][4][32];
+  const int64_t G = K / kGroup;
+  const int64_t ugc = (G + 3) / 4;                 // units along a row block
+  const int64_t units = ((M + 31) / 32) * ugc;
+  const int dr = threadIdx.x >> 4, lane16 = threadIdx.x & 15;
+  int buf = 0;
+  for (int64_t u = blockIdx.x; u < units; u += gridDim.x, buf ^= 1) {
+    const int64_t m0 = (u / ugc) * 32, j0 = (u % ugc) * 4;
+    uint4 v[8];
 #pragma unroll
-    for (int k = 0; k < UPI; ++k) {
-      const int64_t u = u0 + k;
-      const int64_t m = u / upr, j = (u % upr) * 16 + gi;
-      v[k] = make_uint4(0u, 0u, 0u, 0u);
-      if (u < units && j < gpr) v[k] = load_stream16(x + m * ldx + j * kGroup + lane16 * 8);
+    for (int p = 0; p < 8; ++p) {
+      const int64_t m = m0 + 16 * (p & 1) + dr, j = j0 + (p >> 1);
+      v[p] = make_uint4(0u, 0u, 0u, 0u);
+      if (m < M && j < G) v[p] = load_stream16(x + m * ldx + j * kGroup + lane16 * 8);
     }
 #pragma unroll
-    for (int k = 0; k < UPI; ++k) {
-      const int64_t u = u0 + k;
-      const int64_t m = u / upr, j = (u % upr) * 16 + gi;
-      uint32_t am = max_abs_bf16x2(0u, v[k].x);
-      am = max_abs_bf16x2(am, v[k].y);
-      am = max_abs_bf16x2(am, v[k].z);
-      am = max_abs_bf16x2(am, v[k].w);
+    for (int p = 0; p < 8; ++p) {
+      const int r = 16 * (p & 1) + dr, g = p >> 1;
+      const int64_t m = m0 + r, j = j0 + g;
+      uint32_t am = max_abs_bf16x2(0u, v[p].x);
+      am = max_abs_bf16x2(am, v[p].y);
+      am = max_abs_bf16x2(am, v[p].z);
+      am = max_abs_bf16x2(am, v[p].w);
       am = row16_max_u16x2(am);
       const ScalePair sp = scale_pair(fold_bf16x2(am));
-      const uint32_t c0 = e4m3x4(bf16_lo(v[k].x) * sp.r, bf16_hi(v[k].x) * sp.r,
-                                 bf16_lo(v[k].y) * sp.r, bf16_hi(v[k].y) * sp.r);
-      const uint32_t c1 = e4m3x4(bf16_lo(v[k].z) * sp.r, bf16_hi(v[k].z) * sp.r,
-                                 bf16_lo(v[k].w) * sp.r, bf16_hi(v[k].w) * sp.r);
-      if (u < units && j < gpr) {
-        store_stream8(q + m * ldq + j * kGroup + lane16 * 8, c0, c1);
-        if (lane16 == 0) s[j * M + m] = sp.s;
-      }
+      const uint32_t c0 = e4m3x4(bf16_lo(v[p].x) * sp.r, bf16_hi(v[p].x) * sp.r,
+                                 bf16_lo(v[p].y) * sp.r, bf16_hi(v[p].y) * sp.r);
+      const uint32_t c1 = e4m3x4(bf16_lo(v[p].z) * sp.r, bf16_hi(v[p].z) * sp.r,
+                                 bf16_lo(v[p].w) * sp.r, bf16_hi(v[p].w) * sp.r);
+      if (m < M && j < G) store_stream8(q + m * ldq + j * kGroup + lane16 * 8, c0, c1);
+      if (lane16 == 0) stg[buf][g][r] = sp.s;
+    }
+    __syncthreads();
+    if (threadIdx.x < 128) {
+      const int g = threadIdx.x >> 5, r = threadIdx.x & 31;
+      const int64_t m = m0 + r, j = j0 + g;
+      if (m < M && j < G) s[j * M + m] = stg[buf][g][r];
     }
   }
 }
 
 hipError_t launch_quant_1x128(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
                               int64_t ldq, float* s, hipStream_t st) {
-  if (M == 0) return hipSuccess;
-  constexpr int kUnitsPerRound = 4;
-  constexpr int64_t kMaxBlocks = 4096;
-  const int64_t units = M * ((K / kGroup + 15) / 16);
-  const int64_t blocks = std::min<int64_t>((units + kUnitsPerRound - 1) / kUnitsPerRound, kMaxBlocks);
-  hipLaunchKernelGGL(k_quant_1x128<kUnitsPerRound>, dim3((unsigned)blocks), dim3(256), 0, st, x, M,
-                     K, ldx, q, ldq, s);
+  if (M == 0 || K == 0) return hipSuccess;
+  constexpr int64_t kMaxBlocks = 2048;
+  const int64_t units = ((M + 31) / 32) * ((K / kGroup + 3) / 4);
+  const int64_t blocks = std::min<int64_t>(units, kMaxBlocks);
+  hipLaunchKernelGGL(k_quant_1x128, dim3((unsigned)blocks), dim3(256), 0, st, x, M, K, ldx, q, ldq,
+                     s);
   return hipGetLastError();
 }
 
@@ -92,12 +97,18 @@ hipError_t launch_quant_1x128(const uint16_t* x, int64_t M, int64_t K, int64_t l
 // row, then one LDS exchange between the 16 DPP rows of the block.  Row-major
 // codes are packed along the tile's rows, transposed codes along its columns.
 // ---------------------------------------------------------------------------
+// Byte offset in the staged transposed weight tile of byte `b` of row k.
+__device__ __forceinline__ int tT_off(int k, int b) {
+  return (k ^ ((k >> 3) & 1)) * kGroup + (b ^ (((k >> 3) & 7) << 4));
+}
+
 __global__ __launch_bounds__(256) void k_quant_128x128(const uint16_t* __restrict__ w, int64_t N,
                                                        int64_t K, int64_t ldw,
                                                        uint8_t* __restrict__ q,
                                                        float* __restrict__ s,
                                                        uint8_t* __restrict__ qT) {
   __shared__ uint32_t red[16];
+  __shared__ __attribute__((aligned(16))) uint8_t tT[kGroup * kGroup];
   const int c = threadIdx.x & 15;
   const int ri = threadIdx.x >> 4;
   const int64_t kb = blockIdx.x, nb = blockIdx.y;
@@ -138,11 +149,24 @@ __global__ __launch_bounds__(256) void k_quant_128x128(const uint16_t* __restric
     store_stream8(q + (n0 + i) * K + k0, lo, hi);
   }
   if (qT != nullptr) {
+    // Transposed codes through LDS, so every global store covers whole
+    // 128-byte lines of qT: a thread holds 8 bytes of each of its 8 qT rows;
+    // the block's 128 x 128 qT tile is staged with rows permuted
+    // (k ^ ((k >> 3) & 1)) and 16-byte chunks XOR-swizzled by (k >> 3) & 7 to
+    // spread the LDS banks, then written back 8 lanes per row.
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
+      const int kl = 8 * c + jj;
       const uint32_t lo = e4m3x4(f[0][jj], f[1][jj], f[2][jj], f[3][jj]);
       const uint32_t hi = e4m3x4(f[4][jj], f[5][jj], f[6][jj], f[7][jj]);
-      *reinterpret_cast<uint2*>(qT + (k0 + jj) * N + n0) = make_uint2(lo, hi);
+      *reinterpret_cast<uint2*>(tT + tT_off(kl, 8 * ri)) = make_uint2(lo, hi);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      const int kl = pass * 32 + (threadIdx.x >> 3), chunk = threadIdx.x & 7;
+      const uint4 v16 = *reinterpret_cast<const uint4*>(tT + tT_off(kl, 16 * chunk));
+      store_stream16(qT + (kb * kGroup + kl) * N + nb * kGroup + 16 * chunk, v16);
     }
   }
 }
