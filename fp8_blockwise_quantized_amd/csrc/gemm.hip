@@ -27,7 +27,10 @@
 //     (ordered so each lane reads its TM rows with TM/4 contiguous 16-byte
 //     loads) and column scales (or, for ROWBLOCK, the 128-column block
 //     scales).  Every load of the K loop is one of these DMAs; one barrier per
-//     K step.
+//     K step, at its start.  The next step's DMAs are issued between this
+//     step's MFMAs (one after every other MFMA), so they have almost a whole
+//     step to land.  Fragment addresses are compile-time LDS offsets from
+//     per-lane bases (no per-step address arithmetic).
 //   * Tile layout in LDS, either
 //       ROWS: row-major 128-byte rows, 16-byte chunks XOR-swizzled per row
 //             (see swz); each DMA reads 8 whole rows;
@@ -65,7 +68,7 @@ struct GemmCfg {
   static constexpr int ATILE = BM * 128, BTILE = BN * 128;
   static constexpr int ABLK = ATILE / 1024 / NW;   // A DMA instructions per wave and stage
   static constexpr int BBLK = BTILE / 1024 / NW;
-  static constexpr int OA = TM / WNW, OB = TN / WMW;   // a wave's own A and B slabs (its DMA share)
+  static constexpr int OA = TM / WNW, OB = TN / WMW;   // A and B slabs of a wave's DMA share
   static constexpr int RSW = TM * 16, CSW = TN * 16;   // private row / column scale slots per wave
   static constexpr int SPRIV = (RSW + CSW) * 4;        // private scale bytes per wave and stage
   static constexpr int NRS = RSW / 64;                 // row-scale DMAs per wave and stage
@@ -74,7 +77,7 @@ struct GemmCfg {
   static constexpr int EPI_PITCH = BN + 8;             // bf16 per staged output row
   static constexpr int LDS = (STAGES * STAGE > BM * EPI_PITCH * 2) ? STAGES * STAGE : BM * EPI_PITCH * 2;
   static_assert(ABLK * NW * 1024 == ATILE && BBLK * NW * 1024 == BTILE, "DMA split");
-  static_assert(ABLK * 8 == OA * 16 && BBLK * 8 == OB * 16, "a wave's DMA rows are its own slabs");
+  static_assert(ABLK * 8 == OA * 16 && BBLK * 8 == OB * 16, "a wave's DMA rows are whole slabs");
   static_assert(RSW % 64 == 0 && CSW == 64, "scale DMA shape");
   static_assert(TM % 4 == 0 && (128 % (TN * 16)) == 0 && BN % 128 == 0, "tile shape");
   static_assert((TM & (TM - 1)) == 0 && (TN & (TN - 1)) == 0, "power-of-two slab counts");
@@ -268,16 +271,13 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
   const int KB = p.Kc / 128;
   const uint32_t lds0 = lds_addr(lds);
 
-  // ---- the wave's own share of every stage ----
-  // Wave (wm, wn) DMAs the OA 16-row A slabs wn*OA .. of its wave row and the
-  // OB 16-row B slabs wm*OB .. of its wave column: exactly the operands of
-  // its first OA x OB MFMAs.  Local slab i (j) of the wave is physical slab
-  // (i + wn*OA) % TM ((j + wm*OB) % TN), so local slabs 0.. are its own.
+  // ---- the wave's share of every stage ----
+  // Wave (wm, wn) DMAs the OA 16-row A slabs wn*OA .. wn*OA+OA-1 of its wave
+  // row and the OB 16-row B slabs wm*OB .. of its wave column; the workgroup
+  // barrier at the top of each step makes every wave's share visible to all.
   constexpr int OA = CFG::OA, OB = CFG::OB;
-  const int rotA0 = __builtin_amdgcn_readfirstlane(wn * OA);
-  const int rotB0 = __builtin_amdgcn_readfirstlane(wm * OB);
-  const int gA0 = (wm * TM * 16 + rotA0 * 16) / 8;   // first 1 KiB DMA block (8 rows) of own A rows
-  const int gB0 = (wn * TN * 16 + rotB0 * 16) / 8;
+  const int gA0 = (wm * TM * 16 + wn * OA * 16) / 8;   // first 1 KiB DMA block (8 rows) of the share
+  const int gB0 = (wn * TN * 16 + wm * OB * 16) / 8;
   uint32_t offA[CFG::ABLK], offB[CFG::BBLK];
 #pragma unroll
   for (int t = 0; t < CFG::ABLK; ++t) {
@@ -291,25 +291,25 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
     dma_src<FRAG>(gB0 + t, lane, row, col);
     offB[t] = (uint32_t)min(n0 + row, p.N - 1) * (uint32_t)p.ldb + col;
   }
-  // Private scale copies (each wave DMAs the scales it folds with, so it can
-  // use them before the workgroup barrier).  Row slots, in local order: slot
-  // 64*(i/4) + 4*lrow + (i%4) holds the row of local slab i, lane row lrow
-  // (each lane reads its TM scales with TM/4 16-byte loads).  Column slots:
-  // ROWCOL slot 16*j + c holds column c of local B slab j; ROWBLOCK every slot
-  // holds the scale of the wave's 128-column block.
+  // Private scale copies (each wave DMAs the scales it folds with, laid out
+  // for its reads).  Row slots: slot 64*(i/4) + 4*lrow + (i%4) holds the row
+  // of the wave's slab i, lane row lrow (each lane reads its TM scales with
+  // TM/4 16-byte loads).  Column slots: ROWCOL slot 16*j + c holds column c of
+  // the wave's B slab j; ROWBLOCK every slot holds the scale of the wave's
+  // 128-column block.
   const uint32_t sprv = (uint32_t)(CFG::ATILE + CFG::BTILE + wave * CFG::SPRIV);
   uint32_t offR[CFG::NRS];
 #pragma unroll
   for (int q = 0; q < CFG::NRS; ++q) {
     const int sl = 64 * q + lane;
     const int li = 4 * (sl >> 6) + (sl & 3), lr = (sl >> 2) & 15;
-    const int row = wm * TM * 16 + ((li + rotA0) & (TM - 1)) * 16 + lr;
+    const int row = wm * TM * 16 + li * 16 + lr;
     offR[q] = (uint32_t)min(m0 + row, p.M - 1) * 4u;
   }
   uint32_t offC;
   if (MODE == kRowCol) {
     const int lj = lane >> 4, c16 = lane & 15;
-    offC = (uint32_t)min(n0 + wn * TN * 16 + ((lj + rotB0) & (TN - 1)) * 16 + c16, p.N - 1) * 4u;
+    offC = (uint32_t)min(n0 + wn * TN * 16 + lj * 16 + c16, p.N - 1) * 4u;
   } else {
     const int blk = min((n0 + wn * TN * 16) / 128, p.N / 128 - 1);
     offC = (uint32_t)blk * (uint32_t)p.sB_o * 4u;
@@ -342,12 +342,13 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // MFMA order of a step (local slabs): the own OA x OB block first, then the
-  // rest of rows 0..OA-1, then rows OA.. in order.  A fragments live in a
-  // ring of R buffers (local row i in buffer i % R); a row whose buffer is
-  // still unused is read right after the barrier, any other row right after
-  // the last MFMA of row i-R.  (With 8 row slabs the outer-product scales of
-  // ROWCOL leave no registers for the extra buffer.)
+  // MFMA order of a step (slab indices of the wave tile): the OA x OB corner
+  // block first (its fragments are read first), then the rest of rows
+  // 0..OA-1, then rows OA.. in order.  A fragments live in a ring of R buffers
+  // (row i in buffer i % R); a row whose buffer is still unused is read after
+  // the corner block, any other row right after the last MFMA of row i-R.
+  // (With 8 row slabs the outer-product scales of ROWCOL leave no registers
+  // for the extra buffer.)
   constexpr int NM = TM * TN;
   constexpr int R = (MODE == kRowCol && TM >= 8) ? OA : OA + 1;
   struct Order { int i[NM]; int j[NM]; int load_after[TM]; };
@@ -360,16 +361,16 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
       for (int j = OB; j < TN; ++j) { o.i[n] = i; o.j[n] = j; ++n; }
     for (int i = OA; i < TM; ++i)
       for (int j = 0; j < TN; ++j) { o.i[n] = i; o.j[n] = j; ++n; }
-    for (int i = 0; i < TM; ++i) o.load_after[i] = -1;        // -1: own (phase 1)
+    for (int i = 0; i < TM; ++i) o.load_after[i] = -1;        // -1: read at the step start
     for (int i = OA; i < TM; ++i) {
-      int last = OA * OB - 1;                                   // right after the barrier
+      int last = OA * OB - 1;                                   // after the corner block
       for (int m = 0; m < NM; ++m)
         if (i - R >= 0 && o.i[m] == i - R) last = m;
       o.load_after[i] = last;
     }
     return o;
   }();
-  constexpr int NOWN = OA * OB;   // MFMAs before the barrier
+  constexpr int NCORNER = OA * OB;   // MFMAs of the corner block
   constexpr int LAG = 3;
 
   constexpr int D = CFG::STAGES - 1;   // prefetch distance in K steps
@@ -386,25 +387,24 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
   // the compiler schedules and allocates it as one block.
   auto step = [&](auto refill_tag) __attribute__((always_inline)) {
     constexpr bool REFILL = decltype(refill_tag)::value;
-    // This wave's own DMAs of step kb have landed (the later steps' may stay).
+    // This wave's DMAs of step kb have landed (the later steps' may stay);
+    // after the barrier every wave's have, and every wave is done with step
+    // kb-1, whose stage step kb+D refills.
     if (REFILL) wait_vmem<CFG::LOADS * (D - 1)>();
     else wait_vmem<0>();
+    __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     const int stn = (st + D) % CFG::STAGES;
     const uint8_t* As = lds + st * CFG::STAGE;
     const uint8_t* Bs = As + CFG::ATILE;
     const float* Sp = reinterpret_cast<const float*>(As + sprv);   // private scales
-    // Opaque per step: the fragment addresses are recomputed in the loop body
-    // (a few VALU adds) instead of being kept live across it in VGPRs.
-    int rotA = rotA0, rotB = rotB0;
-    asm volatile("" : "+s"(rotA), "+s"(rotB));
 
     v8i bf[TN];
     v8i af[R];
 #pragma unroll
-    for (int j = 0; j < OB; ++j) bf[j] = frag32<FRAG>(Bs, wn * TN + ((j + rotB) & (TN - 1)), lane);
+    for (int j = 0; j < OB; ++j) bf[j] = frag32<FRAG>(Bs, wn * TN + j, lane);
 #pragma unroll
-    for (int i = 0; i < OA; ++i) af[i] = frag32<FRAG>(As, wm * TM + ((i + rotA) & (TM - 1)), lane);
+    for (int i = 0; i < OA; ++i) af[i] = frag32<FRAG>(As, wm * TM + i, lane);
     float rsc[TM];
 #pragma unroll
     for (int q = 0; q < TM / 4; ++q) {
@@ -438,34 +438,29 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
       if (n < NM) {
         const int i = ORD.i[n], j = ORD.j[n];
         part[n % LAG] = mfma_fp8(bf[j], af[i % R]);
-        if (n == NOWN - 1) {
-          // Every wave's step-kb data has landed and every wave is done with
-          // step kb-1, whose stage step kb+D refills.
-          __builtin_amdgcn_s_barrier();
-          asm volatile("" ::: "memory");
+        if (n == 0) {
+          // after the first MFMA: the next step's scale DMAs, the remaining
+          // B fragments
           if (REFILL) {
 #pragma unroll
             for (int t = NT; t < NT + CFG::NRS + 1; ++t) JET_ISSUE(t, stn, kb + D);
           }
 #pragma unroll
-          for (int jb = OB; jb < TN; ++jb)
-            bf[jb] = frag32<FRAG>(Bs, wn * TN + ((jb + rotB) & (TN - 1)), lane);
+          for (int jb = OB; jb < TN; ++jb) bf[jb] = frag32<FRAG>(Bs, wn * TN + jb, lane);
         }
-        if (n >= NOWN - 1) {
+        if (n >= NCORNER - 1) {
 #pragma unroll
           for (int ia = OA; ia < TM; ++ia)
-            if (ORD.load_after[ia] == n)
-              af[ia % R] = frag32<FRAG>(As, wm * TM + ((ia + rotA) & (TM - 1)), lane);
+            if (ORD.load_after[ia] == n) af[ia % R] = frag32<FRAG>(As, wm * TM + ia, lane);
         }
-        if (n >= NOWN) {
-          if (REFILL && ((n - NOWN) & 1) == 0 && (n - NOWN) / 2 < NT) JET_ISSUE((n - NOWN) / 2, stn, kb + D);
-        }
+        // the next step's tile DMAs, one after every other MFMA
+        if (REFILL && n >= 1 && ((n - 1) & 1) == 0 && (n - 1) / 2 < NT) JET_ISSUE((n - 1) / 2, stn, kb + D);
       }
     }
     // tile DMAs not yet issued (more DMAs than MFMA slots)
     if (REFILL) {
 #pragma unroll
-      for (int t = (NM - NOWN + 1) / 2; t < NT; ++t) JET_ISSUE(t, stn, kb + D);
+      for (int t = NM / 2; t < NT; ++t) JET_ISSUE(t, stn, kb + D);
     }
     st = (st + 1 == CFG::STAGES) ? 0 : st + 1;
   };
@@ -474,8 +469,8 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
 #undef JET_ISSUE
 
   // ---- epilogue ----
-  // Lane element (i, j, r) of local slabs (i, j) is
-  // C[m0 + wm*TM*16 + pa(i)*16 + lrow][n0 + wn*TN*16 + pb(j)*16 + 4*kg + r].
+  // Lane element (i, j, r) of slabs (i, j) is
+  // C[m0 + wm*TM*16 + i*16 + lrow][n0 + wn*TN*16 + j*16 + 4*kg + r].
   const int mrow = m0 + wm * TM * 16 + lrow;
   const int ncol = n0 + wn * TN * 16 + 4 * kg;
   if (OUT == kOutF32) {
@@ -483,11 +478,11 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
     float* C = static_cast<float*>(p.C);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      const int m = mrow + ((i + rotA0) & (TM - 1)) * 16;
+      const int m = mrow + i * 16;
       if (m >= p.M) continue;
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int n = ncol + ((j + rotB0) & (TN - 1)) * 16;
+        const int n = ncol + j * 16;
         if (n >= p.N) continue;
         float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
         float4* dst = reinterpret_cast<float4*>(C + (int64_t)m * p.ldc + n);
@@ -508,8 +503,8 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
       for (int j = 0; j < TN; ++j) {
         const uint32_t lo = bf16_rne(acc[i][j][0]) | (bf16_rne(acc[i][j][1]) << 16);
         const uint32_t hi = bf16_rne(acc[i][j][2]) | (bf16_rne(acc[i][j][3]) << 16);
-        *reinterpret_cast<uint2*>(t + (wm * TM * 16 + ((i + rotA0) & (TM - 1)) * 16 + lrow) * CFG::EPI_PITCH +
-                                  wn * TN * 16 + ((j + rotB0) & (TN - 1)) * 16 + 4 * kg) = make_uint2(lo, hi);
+        *reinterpret_cast<uint2*>(t + (wm * TM * 16 + i * 16 + lrow) * CFG::EPI_PITCH +
+                                  wn * TN * 16 + j * 16 + 4 * kg) = make_uint2(lo, hi);
       }
     __syncthreads();
     uint16_t* C = static_cast<uint16_t*>(p.C);
