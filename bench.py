@@ -4,9 +4,9 @@ One step = the whole path over the four Llama-3.1-8B decoder linears at the
 training batch of M = 8192 tokens (8 sequences x 1024):
   for each of QKV (4096->6144), O (4096->4096), gate+up (4096->28672), down (14336->4096):
     128x128 re-quantization of the BF16 master weight (+ transposed codes),
-    1x128 quantization of X, forward GEMM with the fused 1x128 quantization of Y,
-    1x128 quantization of dY, dgrad GEMM, 128x1 quantization of dY (transposed),
-    128x1 re-quantization of X from its FP8 codes (transposed), wgrad GEMM.
+    X quantized 1x128 and re-quantized 128x1 from those codes (transposed) in
+    one read, forward GEMM with the fused 1x128 quantization of Y, dY
+    quantized 1x128 and 128x1 (transposed) in one read, dgrad GEMM, wgrad GEMM.
 Inputs are seeded synthetic tensors resident in HBM before timing starts.
 `value` = GEMM FLOPs of the step (3 x 2*M*N*K per linear) / step time.
 
@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="run 1 GiB device copies first (HBM counter calibration)")
     ap.add_argument("--events", type=int, default=1, help="per-kernel HIP events in the timed loop")
+    ap.add_argument("--quant", choices=("both", "separate"), default="both",
+                    help="activation quantizers: one read for both groupings (default), or the "
+                         "separate 1x128 and 128x1 kernels")
     return ap.parse_args()
 
 
@@ -59,6 +62,11 @@ def q_bytes_128x1_bf16(M, K):
 
 def q_bytes_128x1_fp8(M, K):  # E4M3 + 1x128 scales in, E4M3 + 128x1 scales out
     return M * K + M * K // 128 * 4 + M * K + M * K // 128 * 4
+
+
+def q_bytes_both(M, K):       # BF16 in; 1x128 and 128x1-transposed codes and scales out
+    Mp = -(-M // 128) * 128
+    return M * K * 2 + M * K + M * K // 128 * 4 + Mp * K + Mp // 128 * K * 4
 
 
 class Layer:
@@ -83,8 +91,32 @@ class Layer:
         self.dw = e((N, K), f32)
         self.flops = 2.0 * M * N * K
 
-    def ops(self, J):
+    def ops(self, J, separate=False):
         """(kernel kind, algorithmic work, unit, callable) in path order."""
+        M, N, K = self.M, self.N, self.K
+        if separate:
+            return self.ops_separate(J)
+        return [
+            ("quant_w128x128", q_bytes_w(N, K), "B",
+             lambda: J.jet_quant_weight_128x128(self.w, q=self.wq, s=self.ws, qT=self.wqT)),
+            ("quant_1x128_128x1_T_requant", q_bytes_both(M, K), "B",
+             lambda: J.jet_quant_act_1x128_128x1_T(self.x, True, q=self.xq, s=self.xs,
+                                                   qT=self.xqT, sT=self.xsT)),
+            ("gemm_fwd", self.flops, "F",
+             lambda: J.jet_fp8_linear_fwd(self.xq, self.xs, self.wq, self.ws, y=self.y,
+                                          fuse_quant=True, yq=self.yq, ys=self.ys)),
+            ("quant_1x128_128x1_T_bf16", q_bytes_both(M, N), "B",
+             lambda: J.jet_quant_act_1x128_128x1_T(self.dy, False, q=self.dyq, s=self.dys,
+                                                   qT=self.dyqT, sT=self.dysT)),
+            ("gemm_dgrad", self.flops, "F",
+             lambda: J.jet_fp8_linear_dgrad(self.dyq, self.dys, self.wqT, self.ws, dx=self.dx)),
+            ("gemm_wgrad", self.flops, "F",
+             lambda: J.jet_fp8_linear_wgrad(self.dyqT, self.dysT, self.xqT, self.xsT, M, dw=self.dw)),
+        ]
+
+
+    def ops_separate(self, J):
+        """The same step with the separate 1x128 and 128x1 quantizers."""
         M, N, K = self.M, self.N, self.K
         return [
             ("quant_w128x128", q_bytes_w(N, K), "B",
@@ -182,7 +214,8 @@ def main():
     if args.copy_probe:
         copy_probe(torch)
     layers = [Layer(J, torch, n, N, K, M_TOKENS, seed=0) for (n, N, K) in LAYERS]
-    plan = [(l.name, kind, work, unit, fn) for l in layers for (kind, work, unit, fn) in l.ops(J)]
+    plan = [(l.name, kind, work, unit, fn) for l in layers
+            for (kind, work, unit, fn) in l.ops(J, separate=args.quant == "separate")]
     torch.cuda.synchronize()
 
     def step(evs=None):
@@ -256,7 +289,7 @@ def main():
                                "gate+up 4096->28672, down 14336->4096), training batch M=8192 tokens, "
                                "fwd + dgrad + wgrad with every quantizer and the BF16-master weight "
                                "re-quantization per step",
-                   "M": M_TOKENS, "parallelism": "none (1 GPU)"},
+                   "M": M_TOKENS, "activation_quantizers": args.quant, "parallelism": "none (1 GPU)"},
         "frac_fp8_peak_step": round(value / PEAK_FP8_TFLOPS, 4),
         "quantizer_gbs_step": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1) if quant_ms else None,
         "roofline": roofline,

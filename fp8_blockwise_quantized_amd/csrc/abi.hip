@@ -92,6 +92,30 @@ int jet_quant_act_128x1_T(const void* src, int src_dtype, const float* src_s, in
                     "quant_act_128x1_T");
 }
 
+int jet_quant_act_1x128_128x1_T(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                                int64_t ldq, float* s, uint8_t* qT, int64_t ldqT, float* sT,
+                                int requant, void* stream) {
+  g_last_error[0] = 0;
+  if (requant != 0 && requant != 1)
+    return fail(JET_ERR_DTYPE, "quant_act_1x128_128x1_T: requant must be 0 or 1");
+  if (M < 0 || K < 0 || K % kG || M > kMaxDim || K > kMaxDim)
+    return fail(JET_ERR_SHAPE, "quant_act_1x128_128x1_T: need M >= 0 and K a multiple of 128");
+  if (M == 0 || K == 0) return JET_OK;
+  if (!x || !q || !s || !qT || !sT) return fail(JET_ERR_NULL, "quant_act_1x128_128x1_T: null pointer");
+  const int64_t Mp = (M + kG - 1) / kG * kG;
+  if (Mp / kG > 65535)
+    return fail(JET_ERR_SHAPE, "quant_act_1x128_128x1_T: ceil(M/128) must be <= 65535");
+  if (ldx < K || ldq < K || ldqT < Mp)
+    return fail(JET_ERR_SHAPE, "quant_act_1x128_128x1_T: ldx < K, ldq < K or ldqT < ceil(M/128)*128");
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(qT, 16) || !aligned(sT, 16) || !aligned(s, 4) ||
+      ldx % 8 || ldq % 16 || ldqT % 16)
+    return fail(JET_ERR_ALIGN,
+                "quant_act_1x128_128x1_T: x, q, qT, sT need 16-byte alignment, ldx %% 8, ldq %% 16, ldqT %% 16");
+  return hip_status(jet::launch_quant_1x128_128x1_T(static_cast<const uint16_t*>(x), M, K, ldx, q, ldq,
+                                                    s, qT, ldqT, sT, requant == 1, as_stream(stream)),
+                    "quant_act_1x128_128x1_T");
+}
+
 int jet_quant_weight_128x128(const void* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q, float* s,
                              uint8_t* qT, void* stream) {
   g_last_error[0] = 0;

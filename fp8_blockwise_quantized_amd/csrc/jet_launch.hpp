@@ -41,6 +41,11 @@ hipError_t launch_quant_128x128(const uint16_t* w, int64_t N, int64_t K, int64_t
 hipError_t launch_quant_128x1_T(const void* src, bool fp8src, const float* src_s, int64_t M,
                                 int64_t K, int64_t ldsrc, uint8_t* qT, int64_t ldqT, float* sT,
                                 hipStream_t st);
+// 1x128 (q, s) and 128x1 transposed (qT, sT) of one BF16 activation in one read;
+// requant: the 128x1 groups quantize the dequantized 1x128 values.
+hipError_t launch_quant_1x128_128x1_T(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                      uint8_t* q, int64_t ldq, float* s, uint8_t* qT,
+                                      int64_t ldqT, float* sT, bool requant, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs& a, int mode, int out, bool accum, bool fuseq,
                        hipStream_t st);
 // Grouped GEMMs: grp = kGrpRows (forward, dgrad) or kGrpContraction (wgrad).

@@ -180,6 +180,142 @@ hipError_t launch_quant_128x128(const uint16_t* w, int64_t N, int64_t K, int64_t
 }
 
 // ---------------------------------------------------------------------------
+// 1x128 and 128x1 (transposed) from one read of a BF16 activation.  One
+// 256-thread block per 128x128 tile (row group g, column block kb); thread t
+// owns rows 8*(t/16)..+7 and columns 8*(t%16)..+7, an 8x8 tile in registers,
+// as in the 128x128 kernel.  1x128: each of the thread's rows is a group
+// spread over one 16-lane DPP row; its codes are 8-byte pieces of whole
+// 128-byte lines.  128x1: a column's maximum reduces over the thread's 8
+// rows, the wavefront's 4 row slabs (lane xor 16, 32) and the 4 wavefronts
+// (LDS); the transposed codes are staged in LDS and leave as whole lines.
+//
+// REQUANT (activations): the 128x1 groups quantize the dequantized 1x128
+// values fl32(E4M3value(code) * scale), i.e. exactly what the 128x1 kernel
+// computes from the 1x128 codes.  Otherwise (output gradients) they quantize
+// the BF16 values themselves.  Both sets of outputs equal those of the two
+// separate quantizers bit for bit.  Rows at or past M are zeros: they have no
+// 1x128 output and encode to zero codes in the transposed padding columns.
+// ---------------------------------------------------------------------------
+template <bool REQUANT>
+__global__ __launch_bounds__(256) void k_quant_1x128_128x1_T(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, uint8_t* __restrict__ q,
+    int64_t ldq, float* __restrict__ s, uint8_t* __restrict__ qT, int64_t ldqT,
+    float* __restrict__ sT) {
+  __shared__ uint32_t cred[4][16][8];     // per wavefront: column maxima of its 16 chunks
+  __shared__ __attribute__((aligned(16))) uint8_t tT[kGroup * kGroup];
+  const int c = threadIdx.x & 15;
+  const int ri = threadIdx.x >> 4;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t kb = blockIdx.x, g = blockIdx.y;
+  const int64_t m0 = g * kGroup + 8 * ri;
+  const int64_t k0 = kb * kGroup + 8 * c;
+  uint4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (m0 + i < M) v[i] = load_stream16(x + (m0 + i) * ldx + k0);
+  }
+
+  // 1x128 groups (one per row), and the values the 128x1 groups quantize
+  float f[8][8];
+  float rs[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t am = max_abs_bf16x2(0u, v[i].x);
+    am = max_abs_bf16x2(am, v[i].y);
+    am = max_abs_bf16x2(am, v[i].z);
+    am = max_abs_bf16x2(am, v[i].w);
+    am = row16_max_u16x2(am);
+    const ScalePair sp = scale_pair(fold_bf16x2(am));
+    rs[i] = sp.s;
+    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      f[i][2 * d] = bf16_lo(w[d]);
+      f[i][2 * d + 1] = bf16_hi(w[d]);
+    }
+    const uint32_t c0 = e4m3x4(f[i][0] * sp.r, f[i][1] * sp.r, f[i][2] * sp.r, f[i][3] * sp.r);
+    const uint32_t c1 = e4m3x4(f[i][4] * sp.r, f[i][5] * sp.r, f[i][6] * sp.r, f[i][7] * sp.r);
+    if (m0 + i < M) store_stream8(q + (m0 + i) * ldq + k0, c0, c1);
+    if (REQUANT) {
+      f[i][0] = e4m3_at<0>(c0) * sp.s; f[i][1] = e4m3_at<1>(c0) * sp.s;
+      f[i][2] = e4m3_at<2>(c0) * sp.s; f[i][3] = e4m3_at<3>(c0) * sp.s;
+      f[i][4] = e4m3_at<0>(c1) * sp.s; f[i][5] = e4m3_at<1>(c1) * sp.s;
+      f[i][6] = e4m3_at<2>(c1) * sp.s; f[i][7] = e4m3_at<3>(c1) * sp.s;
+    }
+  }
+  if (c == 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (m0 + i < M) s[kb * M + m0 + i] = rs[i];
+  }
+
+  // 128x1 column maxima (non-negative floats compared as unsigned integers)
+  uint32_t am[8];
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    float a = fabsf(f[0][jj]);
+#pragma unroll
+    for (int i = 1; i < 8; ++i) a = fmaxf(a, fabsf(f[i][jj]));
+    uint32_t u = __float_as_uint(a);
+    u = max(u, (uint32_t)__shfl_xor((int)u, 16, 64));
+    u = max(u, (uint32_t)__shfl_xor((int)u, 32, 64));
+    am[jj] = u;
+  }
+  if (lane < 16) {
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) cred[wave][c][jj] = am[jj];
+  }
+  __syncthreads();
+  float rT[8];
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    uint32_t u = cred[0][c][jj];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) u = max(u, cred[w][c][jj]);
+    const ScalePair sp = scale_pair(__uint_as_float(u));
+    rT[jj] = sp.r;
+    am[jj] = __float_as_uint(sp.s);
+  }
+  if (ri == 0) {
+    float* dst = sT + g * K + k0;
+    *reinterpret_cast<float4*>(dst) = make_float4(__uint_as_float(am[0]), __uint_as_float(am[1]),
+                                                  __uint_as_float(am[2]), __uint_as_float(am[3]));
+    *reinterpret_cast<float4*>(dst + 4) = make_float4(__uint_as_float(am[4]), __uint_as_float(am[5]),
+                                                      __uint_as_float(am[6]), __uint_as_float(am[7]));
+  }
+  // transposed codes through LDS (layout of the 128x128 kernel's staging)
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    const float r = rT[jj];
+    const uint32_t lo = e4m3x4(f[0][jj] * r, f[1][jj] * r, f[2][jj] * r, f[3][jj] * r);
+    const uint32_t hi = e4m3x4(f[4][jj] * r, f[5][jj] * r, f[6][jj] * r, f[7][jj] * r);
+    *reinterpret_cast<uint2*>(tT + tT_off(8 * c + jj, 8 * ri)) = make_uint2(lo, hi);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int kl = pass * 32 + (threadIdx.x >> 3), chunk = threadIdx.x & 7;
+    const uint4 v16 = *reinterpret_cast<const uint4*>(tT + tT_off(kl, 16 * chunk));
+    store_stream16(qT + (kb * kGroup + kl) * ldqT + g * kGroup + 16 * chunk, v16);
+  }
+}
+
+hipError_t launch_quant_1x128_128x1_T(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                      uint8_t* q, int64_t ldq, float* s, uint8_t* qT,
+                                      int64_t ldqT, float* sT, bool requant, hipStream_t st) {
+  if (M == 0 || K == 0) return hipSuccess;
+  dim3 grid((unsigned)(K / kGroup), (unsigned)((M + kGroup - 1) / kGroup));
+  if (requant)
+    hipLaunchKernelGGL(k_quant_1x128_128x1_T<true>, grid, dim3(256), 0, st, x, M, K, ldx, q, ldq, s,
+                       qT, ldqT, sT);
+  else
+    hipLaunchKernelGGL(k_quant_1x128_128x1_T<false>, grid, dim3(256), 0, st, x, M, K, ldx, q, ldq,
+                       s, qT, ldqT, sT);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // 128x1, transposed.  A block handles one 128-row group g and 16*CW columns
 // (256 source bytes per row).  Thread t owns rows 8*ri .. 8*ri+7 of the group
 // and the CW columns of 16-byte chunk c (ri, c in 0..15), with lane

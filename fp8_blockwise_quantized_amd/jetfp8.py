@@ -30,6 +30,7 @@ SIGNATURES = {
     "jet_last_error": [],
     "jet_quant_act_1x128": [_p, _i64, _i64, _i64, _p, _i64, _p, _p],
     "jet_quant_act_128x1_T": [_p, _i32, _p, _i64, _i64, _i64, _p, _i64, _p, _p],
+    "jet_quant_act_1x128_128x1_T": [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _i32, _p],
     "jet_quant_weight_128x128": [_p, _i64, _i64, _i64, _p, _p, _p, _p],
     "jet_fp8_linear_fwd": [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _p, _p, _p, _sz, _p],
     "jet_fp8_linear_dgrad": [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _p, _sz, _p],
@@ -159,6 +160,31 @@ def jet_quant_act_128x1_T(src, src_s=None, qT=None, sT=None, stream=None):
         _ptr(src), dt, _ptr(src_s), M, K, src.stride(0), _ptr(qT), qT.stride(0), _ptr(sT),
         _stream(stream)))
     return qT, sT
+
+
+def jet_quant_act_1x128_128x1_T(x, requant, q=None, s=None, qT=None, sT=None, stream=None):
+    """Both groupings of a BF16 [M, K] tensor from one read.
+
+    Returns (q uint8 [M, K], s float32 [K/128, M], qT uint8 [K, Mp],
+    sT float32 [Mp/128, K]), equal to jet_quant_act_1x128(x) and to
+    jet_quant_act_128x1_T(x) (requant False) or jet_quant_act_128x1_T(q, s)
+    (requant True).
+    """
+    _rowmajor(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    M, K = x.shape
+    Mp = -(-M // 128) * 128
+    q = _codes(q) if q is not None else _empty((M, K), torch.uint8, x)
+    s = s if s is not None else _empty((K // 128, M), torch.float32, x)
+    qT = _codes(qT) if qT is not None else _empty((K, Mp), torch.uint8, x)
+    sT = sT if sT is not None else _empty((Mp // 128, K), torch.float32, x)
+    _rowmajor(q, "q")
+    _rowmajor(qT, "qT")
+    _check("jet_quant_act_1x128_128x1_T", _lib.jet_quant_act_1x128_128x1_T(
+        _ptr(x), M, K, x.stride(0), _ptr(q), q.stride(0), _ptr(s), _ptr(qT), qT.stride(0),
+        _ptr(sT), 1 if requant else 0, _stream(stream)))
+    return q, s, qT, sT
 
 
 def jet_quant_weight_128x128(w, q=None, s=None, qT=None, transposed=True, stream=None):

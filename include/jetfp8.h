@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define JET_ABI_VERSION 2
+#define JET_ABI_VERSION 3
 
 typedef enum {
   JET_OK = 0,
@@ -99,6 +99,31 @@ int jet_quant_act_1x128(const void* x, int64_t M, int64_t K, int64_t ldx,
 int jet_quant_act_128x1_T(const void* src, int src_dtype, const float* src_s,
                           int64_t M, int64_t K, int64_t ldsrc,
                           uint8_t* qT, int64_t ldqT, float* sT, void* stream);
+
+/*
+ * Both activation groupings from one read of a BF16 activation or output
+ * gradient: the 1x128 outputs of jet_quant_act_1x128 and the 128x1 transposed
+ * outputs of jet_quant_act_128x1_T, bit for bit, in one pass over x.  The
+ * forward needs the 1x128 form and the weight gradient the 128x1 form of the
+ * same tensor (explainer "Quantisierungsschema"; 163.com write-up section 五);
+ * producing both together saves a read of the tensor in HBM.
+ *
+ *   x, M, K, ldx, q, ldq, s : as jet_quant_act_1x128.
+ *   qT, ldqT, sT            : as jet_quant_act_128x1_T (columns M..Mp-1 of qT
+ *                             receive zero codes).
+ *   requant == 0 : the 128x1 groups quantize the BF16 values of x (as
+ *                  jet_quant_act_128x1_T with src_dtype JET_BF16: output
+ *                  gradients).
+ *   requant == 1 : they quantize the dequantized 1x128 values
+ *                  fl32(E4M3value(q) * s) (as jet_quant_act_128x1_T with
+ *                  src_dtype JET_E4M3 on this call's q, s: activations).
+ *   M >= 0, K % 128 == 0, ceil(M/128) <= 65535.  x, q, qT, sT 16-byte
+ *   aligned, s 4-byte aligned; ldx % 8, ldq % 16, ldqT % 16.
+ */
+int jet_quant_act_1x128_128x1_T(const void* x, int64_t M, int64_t K, int64_t ldx,
+                                uint8_t* q, int64_t ldq, float* s,
+                                uint8_t* qT, int64_t ldqT, float* sT,
+                                int requant, void* stream);
 
 /*
  * 128x128 block quantization of a BF16 master weight (run on every weight

@@ -48,7 +48,7 @@ def test_binding_covers_header(J):
 
 
 def test_version_and_status_strings(J):
-    assert J.jet_abi_version() == 2
+    assert J.jet_abi_version() == 3
     assert J.jet_status_string(J.JET_ERR_SHAPE) == "JET_ERR_SHAPE"
     assert J.jet_status_string(99) == "JET_ERR_UNKNOWN"
 
@@ -70,6 +70,19 @@ def test_quantizer_validation(J):
     assert L.jet_quant_act_128x1_T(P16, 7, None, 4, 128, 128, P16, 128, P16, None) == J.JET_ERR_DTYPE
     assert L.jet_quant_act_128x1_T(P16, J.JET_E4M3, None, 4, 128, 128, P16, 128, P16, None) == J.JET_ERR_NULL
     assert L.jet_quant_act_128x1_T(P16, J.JET_BF16, None, 200, 128, 128, P16, 200, P16, None) == J.JET_ERR_SHAPE
+    # both groupings in one call: every argument error is reported before any launch
+    Q2 = L.jet_quant_act_1x128_128x1_T
+    assert Q2(P16, 4, 128, 128, P16, 128, P16, P16, 128, P16, 2, None) == J.JET_ERR_DTYPE
+    assert Q2(P16, 4, 100, 128, P16, 128, P16, P16, 128, P16, 0, None) == J.JET_ERR_SHAPE
+    assert Q2(P16, 4, 128, 128, P16, 128, P16, None, 128, P16, 1, None) == J.JET_ERR_NULL
+    assert Q2(P16, 4, 128, 128, P16, 128, None, P16, 128, P16, 0, None) == J.JET_ERR_NULL
+    assert Q2(P16, 200, 128, 128, P16, 128, P16, P16, 200, P16, 0, None) == J.JET_ERR_SHAPE   # ldqT < 256
+    assert Q2(P16, 4, 128, 64, P16, 128, P16, P16, 128, P16, 0, None) == J.JET_ERR_SHAPE     # ldx < K
+    assert Q2(P16, 4, 128, 128, P16, 128, P16, P17, 128, P16, 0, None) == J.JET_ERR_ALIGN
+    assert Q2(P16, 4, 128, 128, P16, 136, P16, P16, 128, P16, 0, None) == J.JET_ERR_ALIGN    # ldq % 16
+    assert Q2(P16, 4, 128, 128, P16, 128, P16, P16, 136, P16, 0, None) == J.JET_ERR_ALIGN    # ldqT % 16
+    assert Q2(P16, 128 * 65536, 128, 128, P16, 128, P16, P16, 128 * 65536, P16, 0, None) == J.JET_ERR_SHAPE
+    assert Q2(None, 0, 128, 128, None, 128, None, None, 0, None, 0, None) == J.JET_OK    # empty: no-op
     assert L.jet_quant_weight_128x128(P16, 100, 128, 128, P16, P16, None, None) == J.JET_ERR_SHAPE
     assert L.jet_quant_weight_128x128(P16, 128, 128, 128, P16, P16, P17, None) == J.JET_ERR_ALIGN
 

@@ -107,6 +107,29 @@ def test_quant_128x1_T_requant_from_fp8_parity(gpu_lib, M, K):
     assert_bits_equal(host(sT), so, f"requant scales M={M} K={K}")
 
 
+@pytest.mark.parametrize("M", RAGGED_M)
+@pytest.mark.parametrize("requant", [False, True])
+def test_quant_1x128_128x1_T_parity(gpu_lib, M, requant):
+    """One read, both groupings: the 1x128 outputs equal quant_1x128 and the
+    128x1 outputs quant_128x1_T of the BF16 values (output gradients) or of
+    the dequantized 1x128 values (activations), bit for bit."""
+    K = 512
+    x = inputs.activations_with_outliers(M, K, seed=M + 7)
+    if M >= 9:
+        x[:9] = edge_matrix(K)
+    Mp = -(-M // 128) * 128
+    qbuf = torch.full((K, Mp + 16), 0xAB, dtype=torch.uint8, device="cuda")
+    q, s, qT, sT = gpu_lib.jet_quant_act_1x128_128x1_T(dev_bf16(x), requant, qT=qbuf[:, :Mp])
+    torch.cuda.synchronize()
+    q1, s1 = O.quant_1x128(x)
+    assert_bits_equal(host(q), q1, f"1x128 codes M={M}")
+    assert_bits_equal(host(s), s1, f"1x128 scales M={M}")
+    qo, so = O.requant_128x1_T_from_1x128(q1, s1) if requant else O.quant_128x1_T(x)
+    assert_bits_equal(host(qT), qo, f"128x1 codes M={M} requant={requant}")
+    assert_bits_equal(host(sT), so, f"128x1 scales M={M} requant={requant}")
+    assert np.all(host(qbuf)[:, Mp:] == 0xAB), "write past the padded row"
+
+
 def test_quantizers_deterministic(gpu_lib):
     x = dev_bf16(inputs.activations_with_outliers(1000, 1024, seed=3))
     a = [gpu_lib.jet_quant_act_1x128(x) for _ in range(2)]
@@ -166,3 +189,25 @@ def test_full_size_dy_128x1_sampled(gpu_lib):
         qo, so = O.quant_128x1_T(dy[sl])
         assert_bits_equal(host(qT[:, sl]), qo, "sampled dY 128x1 codes")
         assert_bits_equal(host(sT[g]), so[0], "sampled dY 128x1 scales")
+
+
+@pytest.mark.parametrize("M,K,requant", [(8192, 4096, True), (8192, 14336, True), (8192, 6144, False)])
+def test_full_size_both_groupings_match_separate_quantizers(gpu_lib, M, K, requant):
+    """At full Llama sizes, the one-read quantizer equals the two separate
+    quantizers on every byte (both are pinned to the oracle above), and a
+    sampled 128-row group equals the oracle directly."""
+    x = (inputs.activations_with_outliers(M, K, seed=1) if requant
+         else inputs.normal_bf16((M, K), 1e-3, seed=1, tensor_id=inputs.ID_DY))
+    xd = dev_bf16(x)
+    q, s, qT, sT = gpu_lib.jet_quant_act_1x128_128x1_T(xd, requant)
+    q1, s1 = gpu_lib.jet_quant_act_1x128(xd)
+    qT1, sT1 = gpu_lib.jet_quant_act_128x1_T(q1, src_s=s1) if requant else gpu_lib.jet_quant_act_128x1_T(xd)
+    torch.cuda.synchronize()
+    assert torch.equal(q, q1) and torch.equal(s.view(torch.int32), s1.view(torch.int32))
+    assert torch.equal(qT, qT1) and torch.equal(sT.view(torch.int32), sT1.view(torch.int32))
+    g = int(np.random.default_rng(K).integers(0, M // 128))
+    sl = slice(g * 128, g * 128 + 128)
+    cq, cs = O.quant_1x128(x[sl])
+    qo, so = O.requant_128x1_T_from_1x128(cq, cs) if requant else O.quant_128x1_T(x[sl])
+    assert_bits_equal(host(qT[:, sl]), qo, "sampled group codes")
+    assert_bits_equal(host(sT[g]), so[0], "sampled group scales")
