@@ -66,6 +66,20 @@ __device__ __forceinline__ float row16_max_f32(float f) {
   return __uint_as_float(v);
 }
 
+// out[i] = the value of lane i of the caller's 16-lane DPP row, i = 0..7
+// (row_newbcast; every lane of the row must be active).
+__device__ __forceinline__ void row_bcast8(float v, float out[8]) {
+  const int b = __float_as_int(v);
+  out[0] = __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0x150, 0xF, 0xF, false));
+  out[1] = __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0x151, 0xF, 0xF, false));
+  out[2] = __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0x152, 0xF, 0xF, false));
+  out[3] = __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0x153, 0xF, 0xF, false));
+  out[4] = __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0x154, 0xF, 0xF, false));
+  out[5] = __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0x155, 0xF, 0xF, false));
+  out[6] = __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0x156, 0xF, 0xF, false));
+  out[7] = __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0x157, 0xF, 0xF, false));
+}
+
 // ---------------------------------------------------------------------------
 // Scale pair of a group.
 // ---------------------------------------------------------------------------

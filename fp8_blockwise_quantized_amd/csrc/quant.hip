@@ -180,14 +180,17 @@ hipError_t launch_quant_128x128(const uint16_t* w, int64_t N, int64_t K, int64_t
 }
 
 // ---------------------------------------------------------------------------
-// 1x128 and 128x1 (transposed) from one read of a BF16 activation.  One
-// 256-thread block per 128x128 tile (row group g, column block kb); thread t
-// owns rows 8*(t/16)..+7 and columns 8*(t%16)..+7, an 8x8 tile in registers,
-// as in the 128x128 kernel.  1x128: each of the thread's rows is a group
-// spread over one 16-lane DPP row; its codes are 8-byte pieces of whole
-// 128-byte lines.  128x1: a column's maximum reduces over the thread's 8
-// rows, the wavefront's 4 row slabs (lane xor 16, 32) and the 4 wavefronts
-// (LDS); the transposed codes are staged in LDS and leave as whole lines.
+// 1x128 and 128x1 (transposed) from one read of a BF16 activation.  A block
+// of 256*RG threads takes RG 128-row groups of one 128-column block kb; thread
+// t owns rows 8*(t/16)..+7 and columns 8*(t%16)..+7, an 8x8 tile in
+// registers, as in the 128x128 kernel.  1x128: each of the thread's rows is a
+// group spread over one 16-lane DPP row; each lane computes one row's scale
+// pair and a DPP broadcast hands it to the row; the codes are 8-byte pieces
+// of whole 128-byte lines.  128x1: a column's maximum reduces over the
+// thread's 8 rows, the wavefront's 4 row slabs (lane xor 16, 32) and the row
+// group's 4 wavefronts (LDS, one thread per column for the scale pair); the
+// transposed codes are staged in LDS and leave as whole lines, 128*RG
+// contiguous bytes per qT row.
 //
 // REQUANT (activations): the 128x1 groups quantize the dequantized 1x128
 // values fl32(E4M3value(code) * scale), i.e. exactly what the 128x1 kernel
@@ -196,18 +199,22 @@ hipError_t launch_quant_128x128(const uint16_t* w, int64_t N, int64_t K, int64_t
 // separate quantizers bit for bit.  Rows at or past M are zeros: they have no
 // 1x128 output and encode to zero codes in the transposed padding columns.
 // ---------------------------------------------------------------------------
-template <bool REQUANT>
-__global__ __launch_bounds__(256) void k_quant_1x128_128x1_T(
+template <bool REQUANT, int RG>
+__global__ __launch_bounds__(256 * RG) void k_quant_1x128_128x1_T(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, uint8_t* __restrict__ q,
     int64_t ldq, float* __restrict__ s, uint8_t* __restrict__ qT, int64_t ldqT,
     float* __restrict__ sT) {
-  __shared__ uint32_t cred[4][16][8];     // per wavefront: column maxima of its 16 chunks
-  __shared__ __attribute__((aligned(16))) uint8_t tT[kGroup * kGroup];
+  constexpr int CR = REQUANT ? 8 : 4;       // column-maximum words per thread
+  __shared__ uint32_t cred[4 * RG][16][CR]; // per wavefront: column maxima of its 16 chunks
+  __shared__ float colR[RG][kGroup];        // 128x1 quantisation multipliers of the tile's columns
+  __shared__ __attribute__((aligned(16))) uint8_t tT[RG][kGroup * kGroup];
   const int c = threadIdx.x & 15;
-  const int ri = threadIdx.x >> 4;
+  const int ri = threadIdx.x >> 4;          // 8-row slab of the block's 128*RG rows
+  const int gi = ri >> 4;                   // row group within the block (wavefronts 4gi..4gi+3)
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t kb = blockIdx.x, g = blockIdx.y;
-  const int64_t m0 = g * kGroup + 8 * ri;
+  const int64_t G = (M + kGroup - 1) / kGroup;
+  const int64_t kb = blockIdx.x;
+  const int64_t m0 = (int64_t)blockIdx.y * RG * kGroup + 8 * ri;
   const int64_t k0 = kb * kGroup + 8 * c;
   uint4 v[8];
 #pragma unroll
@@ -216,88 +223,139 @@ __global__ __launch_bounds__(256) void k_quant_1x128_128x1_T(
     if (m0 + i < M) v[i] = load_stream16(x + (m0 + i) * ldx + k0);
   }
 
-  // 1x128 groups (one per row), and the values the 128x1 groups quantize
-  float f[8][8];
-  float rs[8];
+  // 1x128: the maximum of each of the thread's 8 rows over its DPP row; lane
+  // c computes the scale pair of row c % 8 and row_newbcast hands each row's
+  // pair to the whole DPP row (one division pair per lane instead of eight).
+  uint32_t amr[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     uint32_t am = max_abs_bf16x2(0u, v[i].x);
     am = max_abs_bf16x2(am, v[i].y);
     am = max_abs_bf16x2(am, v[i].z);
     am = max_abs_bf16x2(am, v[i].w);
-    am = row16_max_u16x2(am);
-    const ScalePair sp = scale_pair(fold_bf16x2(am));
-    rs[i] = sp.s;
-    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      f[i][2 * d] = bf16_lo(w[d]);
-      f[i][2 * d + 1] = bf16_hi(w[d]);
-    }
-    const uint32_t c0 = e4m3x4(f[i][0] * sp.r, f[i][1] * sp.r, f[i][2] * sp.r, f[i][3] * sp.r);
-    const uint32_t c1 = e4m3x4(f[i][4] * sp.r, f[i][5] * sp.r, f[i][6] * sp.r, f[i][7] * sp.r);
-    if (m0 + i < M) store_stream8(q + (m0 + i) * ldq + k0, c0, c1);
-    if (REQUANT) {
-      f[i][0] = e4m3_at<0>(c0) * sp.s; f[i][1] = e4m3_at<1>(c0) * sp.s;
-      f[i][2] = e4m3_at<2>(c0) * sp.s; f[i][3] = e4m3_at<3>(c0) * sp.s;
-      f[i][4] = e4m3_at<0>(c1) * sp.s; f[i][5] = e4m3_at<1>(c1) * sp.s;
-      f[i][6] = e4m3_at<2>(c1) * sp.s; f[i][7] = e4m3_at<3>(c1) * sp.s;
-    }
+    amr[i] = row16_max_u16x2(am);
   }
-  if (c == 0) {
+  uint32_t mine = amr[0];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (m0 + i < M) s[kb * M + m0 + i] = rs[i];
-  }
+  for (int i = 1; i < 8; ++i) mine = ((c & 7) == i) ? amr[i] : mine;
+  const ScalePair own = scale_pair(fold_bf16x2(mine));
+  if (c < 8 && m0 + c < M) s[kb * M + m0 + c] = own.s;
+  float rr[8], rs[8];
+  row_bcast8(own.r, rr);
+  row_bcast8(own.s, rs);
 
-  // 128x1 column maxima (non-negative floats compared as unsigned integers)
-  uint32_t am[8];
+  // 1x128 codes.  The tile is kept as raw BF16 words (or, for the
+  // re-quantisation, as codes and row scales) and its FP32 values are
+  // recomputed in each phase: 64 live floats would halve the resident blocks.
+  uint32_t cw[8][2];
 #pragma unroll
-  for (int jj = 0; jj < 8; ++jj) {
-    float a = fabsf(f[0][jj]);
+  for (int i = 0; i < 8; ++i) {
+    const float r = rr[i];
+    cw[i][0] = e4m3x4(bf16_lo(v[i].x) * r, bf16_hi(v[i].x) * r, bf16_lo(v[i].y) * r, bf16_hi(v[i].y) * r);
+    cw[i][1] = e4m3x4(bf16_lo(v[i].z) * r, bf16_hi(v[i].z) * r, bf16_lo(v[i].w) * r, bf16_hi(v[i].w) * r);
+    if (m0 + i < M) store_stream8(q + (m0 + i) * ldq + k0, cw[i][0], cw[i][1]);
+  }
+  // value of row i, column jj of the thread's tile (jj a compile-time index)
+  auto value = [&](int i, int jj) __attribute__((always_inline)) -> float {
+    if constexpr (REQUANT) {
+      const uint32_t wd = cw[i][jj >> 2];
+      float d;
+      switch (jj & 3) {
+        case 0: d = e4m3_at<0>(wd); break;
+        case 1: d = e4m3_at<1>(wd); break;
+        case 2: d = e4m3_at<2>(wd); break;
+        default: d = e4m3_at<3>(wd); break;
+      }
+      return d * rs[i];
+    } else {
+      const uint32_t wd = (jj >> 1) == 0 ? v[i].x : (jj >> 1) == 1 ? v[i].y : (jj >> 1) == 2 ? v[i].z : v[i].w;
+      return (jj & 1) ? bf16_hi(wd) : bf16_lo(wd);
+    }
+  };
+
+  // 128x1 column maxima over the thread's 8 rows and the wavefront's 4 row
+  // slabs: packed BF16 magnitudes, or FP32 magnitude bits (re-quantisation)
+  uint32_t cm[CR];
 #pragma unroll
-    for (int i = 1; i < 8; ++i) a = fmaxf(a, fabsf(f[i][jj]));
-    uint32_t u = __float_as_uint(a);
-    u = max(u, (uint32_t)__shfl_xor((int)u, 16, 64));
-    u = max(u, (uint32_t)__shfl_xor((int)u, 32, 64));
-    am[jj] = u;
+  for (int d = 0; d < CR; ++d) {
+    uint32_t u;
+    if constexpr (REQUANT) {
+      float a = fabsf(value(0, d));
+#pragma unroll
+      for (int i = 1; i < 8; ++i) a = fmaxf(a, fabsf(value(i, d)));
+      u = __float_as_uint(a);
+      u = max(u, (uint32_t)__shfl_xor((int)u, 16, 64));
+      u = max(u, (uint32_t)__shfl_xor((int)u, 32, 64));
+    } else {
+      u = 0u;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        u = max_abs_bf16x2(u, d == 0 ? v[i].x : d == 1 ? v[i].y : d == 2 ? v[i].z : v[i].w);
+      u = max_abs_bf16x2(u, (uint32_t)__shfl_xor((int)u, 16, 64));
+      u = max_abs_bf16x2(u, (uint32_t)__shfl_xor((int)u, 32, 64));
+    }
+    cm[d] = u;
   }
   if (lane < 16) {
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) cred[wave][c][jj] = am[jj];
+    for (int d = 0; d < CR; ++d) cred[wave][c][d] = cm[d];
+  }
+  __syncthreads();
+  // one thread per column of each row group: its maximum over the group's 4
+  // wavefronts and its scale pair
+  if (threadIdx.x < kGroup * RG) {
+    const int cg = threadIdx.x >> 7, col = threadIdx.x & (kGroup - 1), cc = col >> 3, jj = col & 7;
+    float amax;
+    if constexpr (REQUANT) {
+      uint32_t u = cred[4 * cg][cc][jj];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) u = max(u, cred[4 * cg + w][cc][jj]);
+      amax = __uint_as_float(u);
+    } else {
+      uint32_t u = cred[4 * cg][cc][jj >> 1];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) u = max_abs_bf16x2(u, cred[4 * cg + w][cc][jj >> 1]);
+      amax = __uint_as_float(((jj & 1) ? (u >> 16) : (u & 0xFFFFu)) << 16);
+    }
+    const ScalePair sp = scale_pair(amax);
+    colR[cg][col] = sp.r;
+    const int64_t gg = (int64_t)blockIdx.y * RG + cg;
+    if (gg < G) sT[gg * K + kb * kGroup + col] = sp.s;
   }
   __syncthreads();
   float rT[8];
-#pragma unroll
-  for (int jj = 0; jj < 8; ++jj) {
-    uint32_t u = cred[0][c][jj];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) u = max(u, cred[w][c][jj]);
-    const ScalePair sp = scale_pair(__uint_as_float(u));
-    rT[jj] = sp.r;
-    am[jj] = __float_as_uint(sp.s);
+  {
+    const float4 r0 = *reinterpret_cast<const float4*>(&colR[gi][8 * c]);
+    const float4 r1 = *reinterpret_cast<const float4*>(&colR[gi][8 * c + 4]);
+    rT[0] = r0.x; rT[1] = r0.y; rT[2] = r0.z; rT[3] = r0.w;
+    rT[4] = r1.x; rT[5] = r1.y; rT[6] = r1.z; rT[7] = r1.w;
   }
-  if (ri == 0) {
-    float* dst = sT + g * K + k0;
-    *reinterpret_cast<float4*>(dst) = make_float4(__uint_as_float(am[0]), __uint_as_float(am[1]),
-                                                  __uint_as_float(am[2]), __uint_as_float(am[3]));
-    *reinterpret_cast<float4*>(dst + 4) = make_float4(__uint_as_float(am[4]), __uint_as_float(am[5]),
-                                                      __uint_as_float(am[6]), __uint_as_float(am[7]));
+  // transposed codes through LDS (layout of the 128x128 kernel's staging);
+  // the tile's values are recomputed here, not kept live across the barriers
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if constexpr (REQUANT) {
+      asm volatile("" : "+v"(cw[i][0]), "+v"(cw[i][1]));
+    } else {
+      asm volatile("" : "+v"(v[i].x), "+v"(v[i].y), "+v"(v[i].z), "+v"(v[i].w));
+    }
   }
-  // transposed codes through LDS (layout of the 128x128 kernel's staging)
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) {
     const float r = rT[jj];
-    const uint32_t lo = e4m3x4(f[0][jj] * r, f[1][jj] * r, f[2][jj] * r, f[3][jj] * r);
-    const uint32_t hi = e4m3x4(f[4][jj] * r, f[5][jj] * r, f[6][jj] * r, f[7][jj] * r);
-    *reinterpret_cast<uint2*>(tT + tT_off(8 * c + jj, 8 * ri)) = make_uint2(lo, hi);
+    const uint32_t lo = e4m3x4(value(0, jj) * r, value(1, jj) * r, value(2, jj) * r, value(3, jj) * r);
+    const uint32_t hi = e4m3x4(value(4, jj) * r, value(5, jj) * r, value(6, jj) * r, value(7, jj) * r);
+    *reinterpret_cast<uint2*>(&tT[gi][tT_off(8 * c + jj, 8 * (ri & 15))]) = make_uint2(lo, hi);
   }
   __syncthreads();
+  // each qT row takes 128*RG contiguous bytes (the block's row groups side by side)
 #pragma unroll
   for (int pass = 0; pass < 4; ++pass) {
-    const int kl = pass * 32 + (threadIdx.x >> 3), chunk = threadIdx.x & 7;
-    const uint4 v16 = *reinterpret_cast<const uint4*>(tT + tT_off(kl, 16 * chunk));
-    store_stream16(qT + (kb * kGroup + kl) * ldqT + g * kGroup + 16 * chunk, v16);
+    const int kl = pass * 32 + (threadIdx.x >> (3 + (RG == 2))), chunk = threadIdx.x & (8 * RG - 1);
+    const int h = chunk >> 3;
+    const uint4 v16 = *reinterpret_cast<const uint4*>(&tT[h][tT_off(kl, 16 * (chunk & 7))]);
+    if ((int64_t)blockIdx.y * RG + h < G)
+      store_stream16(qT + (kb * kGroup + kl) * ldqT + (int64_t)blockIdx.y * RG * kGroup + 16 * chunk, v16);
   }
 }
 
@@ -305,13 +363,15 @@ hipError_t launch_quant_1x128_128x1_T(const uint16_t* x, int64_t M, int64_t K, i
                                       uint8_t* q, int64_t ldq, float* s, uint8_t* qT,
                                       int64_t ldqT, float* sT, bool requant, hipStream_t st) {
   if (M == 0 || K == 0) return hipSuccess;
-  dim3 grid((unsigned)(K / kGroup), (unsigned)((M + kGroup - 1) / kGroup));
+  constexpr int RG = 2;   // two row groups per block: 256-byte runs in every qT row
+  const int64_t G = (M + kGroup - 1) / kGroup;
+  dim3 grid((unsigned)(K / kGroup), (unsigned)((G + RG - 1) / RG));
   if (requant)
-    hipLaunchKernelGGL(k_quant_1x128_128x1_T<true>, grid, dim3(256), 0, st, x, M, K, ldx, q, ldq, s,
-                       qT, ldqT, sT);
+    hipLaunchKernelGGL((k_quant_1x128_128x1_T<true, RG>), grid, dim3(256 * RG), 0, st, x, M, K, ldx,
+                       q, ldq, s, qT, ldqT, sT);
   else
-    hipLaunchKernelGGL(k_quant_1x128_128x1_T<false>, grid, dim3(256), 0, st, x, M, K, ldx, q, ldq,
-                       s, qT, ldqT, sT);
+    hipLaunchKernelGGL((k_quant_1x128_128x1_T<false, RG>), grid, dim3(256 * RG), 0, st, x, M, K, ldx,
+                       q, ldq, s, qT, ldqT, sT);
   return hipGetLastError();
 }
 
