@@ -132,16 +132,19 @@ int jet_quant_weight_128x128(const void* w, int64_t N, int64_t K, int64_t ldw, u
 }
 
 size_t jet_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {
-  (void)op; (void)M; (void)N; (void)K;
+  // the dense forward at M <= 128 keeps split-K partial sums in the workspace
+  if (op == JET_OP_FWD && M > 0 && M <= jet::kSkinnyMaxM && N > 0 && K > 0 && N % kG == 0 &&
+      K % kG == 0 && N <= kMaxDim && K <= kMaxDim)
+    return jet::skinny_workspace_bytes(M, N, K);
   return 0;
 }
 
-static int check_gemm_common(const char* name, int64_t M, int64_t N, int64_t K, int op,
+// need: the workspace bytes this call requires (0 for the grouped GEMMs)
+static int check_gemm_common(const char* name, int64_t M, int64_t N, int64_t K, size_t need,
                              size_t ws_bytes, const void* workspace) {
   if (M < 0 || N < 0 || K < 0 || N % kG || K % kG || M > kMaxDim || N > kMaxDim || K > kMaxDim)
     return fail(JET_ERR_SHAPE, "%s: need M >= 0, N and K multiples of 128 (M=%lld N=%lld K=%lld)",
                 name, (long long)M, (long long)N, (long long)K);
-  const size_t need = jet_workspace_bytes(op, M, N, K);
   if (ws_bytes < need || (need && !workspace))
     return fail(JET_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", name, need);
   return JET_OK;
@@ -151,7 +154,9 @@ int jet_fp8_linear_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, co
                        int64_t M, int64_t N, int64_t K, void* y, int y_dtype, uint8_t* yq, float* ys,
                        void* workspace, size_t ws_bytes, void* stream) {
   g_last_error[0] = 0;
-  if (int st = check_gemm_common("fp8_linear_fwd", M, N, K, JET_OP_FWD, ws_bytes, workspace)) return st;
+  if (int st = check_gemm_common("fp8_linear_fwd", M, N, K, jet_workspace_bytes(JET_OP_FWD, M, N, K),
+                                 ws_bytes, workspace))
+    return st;
   if (y_dtype != JET_BF16 && y_dtype != JET_F32)
     return fail(JET_ERR_DTYPE, "fp8_linear_fwd: y_dtype must be JET_BF16 or JET_F32");
   const bool fuse = yq || ys;
@@ -170,8 +175,10 @@ int jet_fp8_linear_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, co
   a.sB = ws; a.sB_o = K / kG; a.sB_c = 1;
   a.C = y; a.ldc = N; a.Cq = yq; a.Cs = ys; a.ldcs = M;
   a.M = (int)M; a.N = (int)N; a.Kc = (int)K;
-  return hip_status(jet::launch_gemm(a, jet::kRowBlock, y_dtype == JET_BF16 ? jet::kOutBf16 : jet::kOutF32,
-                                     false, fuse, as_stream(stream)),
+  const int out = y_dtype == JET_BF16 ? jet::kOutBf16 : jet::kOutF32;
+  if (M <= jet::kSkinnyMaxM)   // rollout decode: weight-streaming, split-K into the workspace
+    return hip_status(jet::launch_gemm_skinny(a, out, fuse, workspace, as_stream(stream)), "fp8_linear_fwd");
+  return hip_status(jet::launch_gemm(a, jet::kRowBlock, out, false, fuse, as_stream(stream)),
                     "fp8_linear_fwd");
 }
 
@@ -179,7 +186,9 @@ int jet_fp8_linear_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* wq
                          int64_t M, int64_t N, int64_t K, void* dx, int dx_dtype, void* workspace,
                          size_t ws_bytes, void* stream) {
   g_last_error[0] = 0;
-  if (int st = check_gemm_common("fp8_linear_dgrad", M, N, K, JET_OP_DGRAD, ws_bytes, workspace)) return st;
+  if (int st = check_gemm_common("fp8_linear_dgrad", M, N, K, jet_workspace_bytes(JET_OP_DGRAD, M, N, K),
+                                 ws_bytes, workspace))
+    return st;
   if (dx_dtype != JET_BF16 && dx_dtype != JET_F32)
     return fail(JET_ERR_DTYPE, "fp8_linear_dgrad: dx_dtype must be JET_BF16 or JET_F32");
   if (M == 0 || K == 0) return JET_OK;
@@ -202,7 +211,9 @@ int jet_fp8_linear_wgrad(const uint8_t* dyqT, const float* dysT, const uint8_t* 
                          int64_t M, int64_t N, int64_t K, void* dw, int dw_dtype, int accumulate,
                          void* workspace, size_t ws_bytes, void* stream) {
   g_last_error[0] = 0;
-  if (int st = check_gemm_common("fp8_linear_wgrad", M, N, K, JET_OP_WGRAD, ws_bytes, workspace)) return st;
+  if (int st = check_gemm_common("fp8_linear_wgrad", M, N, K, jet_workspace_bytes(JET_OP_WGRAD, M, N, K),
+                                 ws_bytes, workspace))
+    return st;
   if (dw_dtype != JET_F32 && dw_dtype != JET_BF16)
     return fail(JET_ERR_DTYPE, "fp8_linear_wgrad: dw_dtype must be JET_F32 or JET_BF16");
   if (accumulate && dw_dtype != JET_F32)
@@ -273,7 +284,7 @@ int jet_fp8_grouped_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, c
                         void* stream) {
   g_last_error[0] = 0;
   if (int st = check_grouped_common("fp8_grouped_fwd", seg_off, E, M)) return st;
-  if (int st = check_gemm_common("fp8_grouped_fwd", M, N, K, JET_OP_FWD, ws_bytes, workspace)) return st;
+  if (int st = check_gemm_common("fp8_grouped_fwd", M, N, K, 0, ws_bytes, workspace)) return st;
   if (y_dtype != JET_BF16 && y_dtype != JET_F32)
     return fail(JET_ERR_DTYPE, "fp8_grouped_fwd: y_dtype must be JET_BF16 or JET_F32");
   const bool fuse = yq || ys;
@@ -304,7 +315,7 @@ int jet_fp8_grouped_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* w
                           void* dx, int dx_dtype, void* workspace, size_t ws_bytes, void* stream) {
   g_last_error[0] = 0;
   if (int st = check_grouped_common("fp8_grouped_dgrad", seg_off, E, M)) return st;
-  if (int st = check_gemm_common("fp8_grouped_dgrad", M, N, K, JET_OP_DGRAD, ws_bytes, workspace)) return st;
+  if (int st = check_gemm_common("fp8_grouped_dgrad", M, N, K, 0, ws_bytes, workspace)) return st;
   if (dx_dtype != JET_BF16 && dx_dtype != JET_F32)
     return fail(JET_ERR_DTYPE, "fp8_grouped_dgrad: dx_dtype must be JET_BF16 or JET_F32");
   if (M == 0 || K == 0) return JET_OK;
@@ -332,7 +343,7 @@ int jet_fp8_grouped_wgrad(const uint8_t* dyqT, const float* dysT, const uint8_t*
                           void* workspace, size_t ws_bytes, void* stream) {
   g_last_error[0] = 0;
   if (int st = check_grouped_common("fp8_grouped_wgrad", seg_off, E, M)) return st;
-  if (int st = check_gemm_common("fp8_grouped_wgrad", M, N, K, JET_OP_WGRAD, ws_bytes, workspace)) return st;
+  if (int st = check_gemm_common("fp8_grouped_wgrad", M, N, K, 0, ws_bytes, workspace)) return st;
   if (dw_dtype != JET_F32 && dw_dtype != JET_BF16)
     return fail(JET_ERR_DTYPE, "fp8_grouped_wgrad: dw_dtype must be JET_F32 or JET_BF16");
   if (accumulate && dw_dtype != JET_F32)

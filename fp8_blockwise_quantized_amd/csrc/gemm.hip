@@ -603,6 +603,258 @@ hipError_t launch_gemm(const GemmArgs& a, int mode, int out, bool accum, bool fu
   return dispatch<CfgSmall>(a, mode, out, accum, fuseq, st);
 }
 
+// ---------------------------------------------------------------------------
+// Small-M forward (rollout decode, M <= 128): Y = Xq . Wq^T streams the whole
+// weight once for a handful of rows, so it is bound by HBM bandwidth and needs
+// many weight bytes in flight.  The output is cut into 64*WS-column blocks
+// and the K steps into S contiguous ranges; a workgroup (4 wavefronts) computes
+// the FP32 partial sum of one (block, range) through an NST-stage ring of
+// direct global->LDS loads (NST-1 steps of prefetch) and writes it to the
+// caller's workspace P[S][M][N].  k_skinny_finish then sums the S partials in
+// order s = 0..S-1 (deterministic) and writes Y (BF16 or FP32) and, for BF16,
+// the fused 1x128 quantization of Y.  Per 128-K step the numerics are those
+// of the main kernel: one MFMA per 16x16 sub-tile from zero, folded into FP32
+// with the product of the row scale and the weight block scale.
+//
+// Stage layout: the X tile (MT*16 rows x 128 bytes, swizzled rows), the W
+// tile (64 rows x 128 bytes), then four 256-byte scale slots, one DMA per
+// wavefront: slots q < MT/4 hold X row scales (float 4r + t of slot q is row
+// (4q + t)*16 + r, so lane r reads its rows i*16 + r, i < MT, as MT/4 16-byte
+// loads); the other slots hold 64 copies of the W block scale.
+// Wavefront w multiplies W slab w (output columns 16w..16w+15 of the block)
+// with the MT X slabs.
+template <int MT, int NST, int WS>
+struct SkinnyCfg {
+  static constexpr int BN = 64 * WS;                   // output columns per workgroup
+  static constexpr int XT = MT * 16 * 128, WT = BN * 128;
+  static constexpr int STAGE = XT + WT + 1024;
+  static constexpr int XBLK = XT / 1024, WBLK = WT / 1024;
+  static constexpr int BPW = (XBLK + WBLK) / 4;        // tile DMAs per wavefront and stage
+  static constexpr int NSX = MT / 4;                   // scale slots holding X row scales
+  static constexpr int LOADS = BPW + 1;
+  static constexpr int LDS = NST * STAGE;
+  static_assert((XBLK + WBLK) % 4 == 0 && NSX >= 1 && NSX < 4, "DMA split");
+  static_assert(BN <= 128, "one weight block scale per workgroup");
+  static_assert(LDS <= 160 * 1024, "LDS");
+};
+
+template <int MT, int NST, int WS>
+__global__ __launch_bounds__(256) void k_gemm_fp8_skinny(GemmArgs p, float* __restrict__ part,
+                                                         int splits) {
+  using C = SkinnyCfg<MT, NST, WS>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lrow = lane & 15, kg = lane >> 4;
+  const int n0 = blockIdx.x * C::BN;
+  const int sidx = blockIdx.y;
+  const int KB = p.Kc / 128;
+  const int kb0 = (int)((int64_t)KB * sidx / splits), kb1 = (int)((int64_t)KB * (sidx + 1) / splits);
+  const int nsteps = kb1 - kb0;
+  const uint32_t lds0 = lds_addr(lds);
+
+  // this wavefront's DMA blocks: global blocks wave*BPW .. ; X blocks first, then W
+  uint32_t off[C::BPW], dst[C::BPW];
+  bool isx[C::BPW];
+#pragma unroll
+  for (int t = 0; t < C::BPW; ++t) {
+    const int gb = wave * C::BPW + t;
+    int row; uint32_t col;
+    if (gb < C::XBLK) {
+      dma_src<false>(gb, lane, row, col);
+      off[t] = (uint32_t)min(row, p.M - 1) * (uint32_t)p.lda + col;
+      dst[t] = (uint32_t)(gb * 1024);
+      isx[t] = true;
+    } else {
+      dma_src<false>(gb - C::XBLK, lane, row, col);
+      off[t] = (uint32_t)(n0 + row) * (uint32_t)p.ldb + col;
+      dst[t] = (uint32_t)(C::XT + (gb - C::XBLK) * 1024);
+      isx[t] = false;
+    }
+  }
+  uint32_t soff;   // the wavefront's scale DMA
+  if (wave < C::NSX) {
+    // slot 64q + 4r + t (q = wave, r = lane/4, t = lane%4) holds row (4q + t)*16 + r
+    const int row = (4 * wave + (lane & 3)) * 16 + (lane >> 2);
+    soff = (uint32_t)min(row, p.M - 1) * 4u;
+  } else {
+    soff = (uint32_t)(n0 / 128) * (uint32_t)p.sB_o * 4u;
+  }
+  const uint32_t sdst = (uint32_t)(C::XT + C::WT + 256 * wave);
+
+  auto issue = [&](int stage, int kb) __attribute__((always_inline)) {
+    const uint32_t sb = lds0 + (uint32_t)(stage * C::STAGE);
+#pragma unroll
+    for (int t = 0; t < C::BPW; ++t)
+      dma16(sb + dst[t], (isx[t] ? p.A : p.B) + (int64_t)kb * 128, off[t]);
+    if (wave < C::NSX) dma4(sb + sdst, p.sA + (int64_t)kb * p.sA_ld, soff);
+    else dma4(sb + sdst, p.sB + (int64_t)kb * p.sB_c, soff);
+  };
+
+  constexpr int D = NST - 1;
+#pragma unroll
+  for (int s = 0; s < D; ++s)
+    if (s < nsteps) issue(s, kb0 + s);
+
+  v4f acc[WS][MT];
+#pragma unroll
+  for (int j = 0; j < WS; ++j)
+#pragma unroll
+    for (int i = 0; i < MT; ++i) acc[j][i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  int st = 0;
+  for (int k = 0; k < nsteps; ++k) {
+    // this wavefront's loads of step k have landed once at most those of the
+    // (up to D-1) later steps already issued are outstanding
+    const int later = min(nsteps - 1 - k, D - 1);
+    if (later >= D - 1) wait_vmem<C::LOADS * (D - 1)>();
+    else wait_vmem<0>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const uint8_t* Xs = lds + st * C::STAGE;
+    const uint8_t* Ws = Xs + C::XT;
+    const float* Sc = reinterpret_cast<const float*>(Xs + C::XT + C::WT);
+    // the stage step k-1 used is free: refill it with step k + D
+    if (k + D < nsteps) issue((st + D) % NST, kb0 + k + D);
+    float sx[MT];
+#pragma unroll
+    for (int q = 0; q < MT / 4; ++q) {
+      const float4 r4 = *reinterpret_cast<const float4*>(Sc + 64 * q + 4 * lrow);
+      sx[4 * q] = r4.x; sx[4 * q + 1] = r4.y; sx[4 * q + 2] = r4.z; sx[4 * q + 3] = r4.w;
+    }
+    const float swb = Sc[64 * C::NSX + lane];
+#pragma unroll
+    for (int j = 0; j < WS; ++j) {
+      const v8i bfr = frag32<false>(Ws, wave * WS + j, lane);
+      v4f pr[MT];
+#pragma unroll
+      for (int i = 0; i < MT; ++i) pr[i] = mfma_fp8(bfr, frag32<false>(Xs, i, lane));
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        const float c = sx[i] * swb;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[j][i][r] = fmaf(pr[i][r], c, acc[j][i][r]);
+      }
+    }
+    st = (st + 1 == NST) ? 0 : st + 1;
+  }
+  wait_vmem<0>();
+
+  // partial sums: lane holds row i*16 + lrow, columns n0 + 16*(wave*WS + j) + 4*kg + r
+  float* P = part + (int64_t)sidx * p.M * p.N;
+#pragma unroll
+  for (int j = 0; j < WS; ++j) {
+    const int n = n0 + 16 * (wave * WS + j) + 4 * kg;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int m = i * 16 + lrow;
+      if (m < p.M)
+        *reinterpret_cast<float4*>(P + (int64_t)m * p.N + n) =
+            make_float4(acc[j][i][0], acc[j][i][1], acc[j][i][2], acc[j][i][3]);
+    }
+  }
+}
+
+// Sum of the S partials, then the output: 16 rows x 128 columns per block, a
+// DPP row of 16 lanes per row (8 columns per lane, one 1x128 group per row).
+template <int OUT, bool FUSEQ>
+__global__ __launch_bounds__(256) void k_skinny_finish(GemmArgs p, const float* __restrict__ part,
+                                                       int splits) {
+  const int c = threadIdx.x & 15;
+  const int m = blockIdx.y * 16 + (threadIdx.x >> 4);
+  const int n = blockIdx.x * 128 + 8 * c;
+  const bool ok = m < p.M;
+  const int mm = ok ? m : p.M - 1;
+  float v[8];
+  {
+    const float* src = part + (int64_t)mm * p.N + n;
+    const float4 a = *reinterpret_cast<const float4*>(src);
+    const float4 b = *reinterpret_cast<const float4*>(src + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  for (int s = 1; s < splits; ++s) {
+    const float* src = part + ((int64_t)s * p.M + mm) * p.N + n;
+    const float4 a = *reinterpret_cast<const float4*>(src);
+    const float4 b = *reinterpret_cast<const float4*>(src + 4);
+    v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w; v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
+  }
+  if (OUT == kOutF32) {
+    if (ok) {
+      float* Cf = static_cast<float*>(p.C) + (int64_t)m * p.ldc + n;
+      *reinterpret_cast<float4*>(Cf) = make_float4(v[0], v[1], v[2], v[3]);
+      *reinterpret_cast<float4*>(Cf + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    }
+    return;
+  }
+  uint4 w;
+  w.x = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
+  w.y = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
+  w.z = bf16_rne(v[4]) | (bf16_rne(v[5]) << 16);
+  w.w = bf16_rne(v[6]) | (bf16_rne(v[7]) << 16);
+  if (FUSEQ) {
+    // 1x128 quantization of the BF16 output, as in the main kernel's epilogue
+    uint32_t am = max_abs_bf16x2(0u, w.x);
+    am = max_abs_bf16x2(am, w.y);
+    am = max_abs_bf16x2(am, w.z);
+    am = max_abs_bf16x2(am, w.w);
+    am = row16_max_u16x2(am);
+    const ScalePair sp = scale_pair(fold_bf16x2(am));
+    const uint32_t q0 = e4m3x4(bf16_lo(w.x) * sp.r, bf16_hi(w.x) * sp.r, bf16_lo(w.y) * sp.r, bf16_hi(w.y) * sp.r);
+    const uint32_t q1 = e4m3x4(bf16_lo(w.z) * sp.r, bf16_hi(w.z) * sp.r, bf16_lo(w.w) * sp.r, bf16_hi(w.w) * sp.r);
+    if (ok) {
+      *reinterpret_cast<uint2*>(p.Cq + (int64_t)m * p.ldc + n) = make_uint2(q0, q1);
+      if (c == 0) p.Cs[(int64_t)(n / 128) * p.ldcs + m] = sp.s;
+    }
+  }
+  if (ok) *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.C) + (int64_t)m * p.ldc + n) = w;
+}
+
+// Small-M configuration (measured on the Llama-8B decode shapes: 4, 6 or 8
+// stages, 64 or 128 columns per workgroup and 128..1024 target workgroups all
+// land within 10 %; this one needs the fewest ranges, so the least workspace).
+constexpr int kSkWS = 2;        // W slabs per wavefront: 128 output columns per workgroup
+constexpr int kSkNST = 6;       // ring stages for M <= 64 (4 for M <= 128)
+constexpr int kSkTarget = 128;  // workgroups aimed at over all column blocks and K ranges
+
+// K-step ranges of the small-M forward: about kSkTarget workgroups in total,
+// at least one K step per range, at most 16 ranges.
+int skinny_splits(int64_t M, int64_t N, int64_t K) {
+  (void)M;
+  const int64_t blocks = N / (64 * kSkWS), kb = K / 128;
+  int64_t s = (kSkTarget + blocks - 1) / blocks;
+  if (s > 16) s = 16;
+  if (s > kb) s = kb;
+  return (int)(s < 1 ? 1 : s);
+}
+
+size_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || M > kSkinnyMaxM || N <= 0 || K <= 0) return 0;
+  return (size_t)skinny_splits(M, N, K) * (size_t)M * (size_t)N * sizeof(float);
+}
+
+template <int MT, int NST, int WS>
+static hipError_t launch_skinny_mt(const GemmArgs& a, int out, bool fuseq, float* part, int S,
+                                   hipStream_t st) {
+  hipLaunchKernelGGL((k_gemm_fp8_skinny<MT, NST, WS>), dim3((unsigned)(a.N / (64 * WS)), (unsigned)S),
+                     dim3(256), 0, st, a, part, S);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 g((unsigned)(a.N / 128), (unsigned)((a.M + 15) / 16));
+  if (out == kOutF32) hipLaunchKernelGGL((k_skinny_finish<kOutF32, false>), g, dim3(256), 0, st, a, part, S);
+  else if (fuseq) hipLaunchKernelGGL((k_skinny_finish<kOutBf16, true>), g, dim3(256), 0, st, a, part, S);
+  else hipLaunchKernelGGL((k_skinny_finish<kOutBf16, false>), g, dim3(256), 0, st, a, part, S);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_skinny(const GemmArgs& a, int out, bool fuseq, void* workspace, hipStream_t st) {
+  if (a.M == 0 || a.N == 0) return hipSuccess;
+  if (a.M > kSkinnyMaxM || a.Kc <= 0 || a.N % (64 * kSkWS)) return hipErrorInvalidValue;
+  const int S = skinny_splits(a.M, a.N, a.Kc);
+  float* part = static_cast<float*>(workspace);
+  if (a.M <= 64) return launch_skinny_mt<4, kSkNST, kSkWS>(a, out, fuseq, part, S, st);
+  return launch_skinny_mt<8, 4, kSkWS>(a, out, fuseq, part, S, st);
+}
+
 // Expert segments are short and ragged (a few hundred rows each), so the
 // grouped GEMMs use the 128 x 128 tile.
 hipError_t launch_gemm_grouped(const GemmArgs& a, int grp, int mode, int out, bool accum,

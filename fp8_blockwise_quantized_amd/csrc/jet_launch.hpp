@@ -48,6 +48,12 @@ hipError_t launch_quant_1x128_128x1_T(const uint16_t* x, int64_t M, int64_t K, i
                                       int64_t ldqT, float* sT, bool requant, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs& a, int mode, int out, bool accum, bool fuseq,
                        hipStream_t st);
+// Small-M forward (M <= kSkinnyMaxM): split-K partial sums in the caller's
+// workspace (skinny_workspace_bytes), then a deterministic finishing pass.
+constexpr int64_t kSkinnyMaxM = 128;
+int skinny_splits(int64_t M, int64_t N, int64_t K);
+size_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_skinny(const GemmArgs& a, int out, bool fuseq, void* workspace, hipStream_t st);
 // Grouped GEMMs: grp = kGrpRows (forward, dgrad) or kGrpContraction (wgrad).
 hipError_t launch_gemm_grouped(const GemmArgs& a, int grp, int mode, int out, bool accum,
                                bool fuseq, hipStream_t st);

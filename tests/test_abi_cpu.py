@@ -90,20 +90,33 @@ def test_quantizer_validation(J):
 def test_gemm_validation(J):
     L = J._lib
     a = [P16, P16, P16, P16]
-    assert L.jet_fp8_linear_fwd(*a, 64, 100, 128, P16, J.JET_BF16, None, None, None, 0, None) == J.JET_ERR_SHAPE
-    assert L.jet_fp8_linear_fwd(*a, 64, 128, 128, P16, 9, None, None, None, 0, None) == J.JET_ERR_DTYPE
-    assert L.jet_fp8_linear_fwd(*a, 64, 128, 128, P16, J.JET_BF16, P16, None, None, 0, None) == J.JET_ERR_NULL
-    assert L.jet_fp8_linear_fwd(*a, 64, 128, 128, P16, J.JET_F32, P16, P16, None, 0, None) == J.JET_ERR_DTYPE
-    assert L.jet_fp8_linear_fwd(P16, P16, None, P16, 64, 128, 128, P16, J.JET_BF16, None, None, None, 0,
+    assert L.jet_fp8_linear_fwd(*a, 256, 100, 128, P16, J.JET_BF16, None, None, None, 0, None) == J.JET_ERR_SHAPE
+    assert L.jet_fp8_linear_fwd(*a, 256, 128, 128, P16, 9, None, None, None, 0, None) == J.JET_ERR_DTYPE
+    assert L.jet_fp8_linear_fwd(*a, 256, 128, 128, P16, J.JET_BF16, P16, None, None, 0, None) == J.JET_ERR_NULL
+    assert L.jet_fp8_linear_fwd(*a, 256, 128, 128, P16, J.JET_F32, P16, P16, None, 0, None) == J.JET_ERR_DTYPE
+    assert L.jet_fp8_linear_fwd(P16, P16, None, P16, 256, 128, 128, P16, J.JET_BF16, None, None, None, 0,
                                 None) == J.JET_ERR_NULL
-    assert L.jet_fp8_linear_fwd(P17, P16, P16, P16, 64, 128, 128, P16, J.JET_BF16, None, None, None, 0,
+    assert L.jet_fp8_linear_fwd(P17, P16, P16, P16, 256, 128, 128, P16, J.JET_BF16, None, None, None, 0,
                                 None) == J.JET_ERR_ALIGN
+    # small M (rollout decode) keeps split-K partial sums in the caller's workspace
+    need = J.jet_workspace_bytes(J.JET_OP_FWD, 64, 4096, 4096)
+    assert need == 4 * 64 * 4096 * 4                    # 4 K ranges: 128 workgroups over 32 column blocks
+    assert J.jet_workspace_bytes(J.JET_OP_FWD, 64, 28672, 4096) == 1 * 64 * 28672 * 4
+    assert J.jet_workspace_bytes(J.JET_OP_FWD, 128, 4096, 256) == 2 * 128 * 4096 * 4   # at most one range per K step
+    assert J.jet_workspace_bytes(J.JET_OP_FWD, 129, 4096, 4096) == 0
+    assert J.jet_workspace_bytes(J.JET_OP_DGRAD, 64, 4096, 4096) == 0
+    assert J.jet_workspace_bytes(J.JET_OP_WGRAD, 64, 4096, 4096) == 0
+    assert L.jet_fp8_linear_fwd(*a, 64, 4096, 4096, P16, J.JET_BF16, None, None, None, 0, None) == J.JET_ERR_WORKSPACE
+    assert L.jet_fp8_linear_fwd(*a, 64, 4096, 4096, P16, J.JET_BF16, None, None, P16, need - 1,
+                                None) == J.JET_ERR_WORKSPACE
+    assert L.jet_fp8_linear_fwd(*a, 64, 4096, 4096, P16, J.JET_BF16, None, None, None, need,
+                                None) == J.JET_ERR_WORKSPACE      # size without a pointer
+    assert "workspace" in J.jet_last_error()
     assert L.jet_fp8_linear_dgrad(*a, 64, 128, 96, P16, J.JET_BF16, None, 0, None) == J.JET_ERR_SHAPE
     assert L.jet_fp8_linear_wgrad(*a, 64, 128, 128, P16, J.JET_BF16, 1, None, 0, None) == J.JET_ERR_DTYPE
     assert L.jet_fp8_linear_wgrad(*a, 64, 128, 128, None, J.JET_F32, 0, None, 0, None) == J.JET_ERR_NULL
     assert L.jet_fp8_linear_fwd(None, None, None, None, 0, 128, 128, None, J.JET_BF16, None, None, None, 0,
                                 None) == J.JET_OK
-    assert J.jet_workspace_bytes(J.JET_OP_FWD, 64, 4096, 4096) >= 0
 
 
 def test_grouped_validation(J):

@@ -214,6 +214,59 @@ def test_gemms_deterministic(gpu_lib):
         assert torch.equal(a, b)
 
 
+# --- small M: the split-K forward (rollout decode) ---------------------------
+
+@pytest.mark.parametrize("M", [1, 16, 64, 100, 128])
+@pytest.mark.parametrize("K", [128, 1280])
+def test_small_m_forward(gpu_lib, M, K):
+    """M <= 128 takes the split-K forward (64-row and 128-row variants; one K
+    step, and ten steps in up to ten ranges): BF16 with the fused 1x128 output
+    and FP32 against the oracle, deterministic, and an explicit workspace of
+    the reported size gives the same bits."""
+    N = 384
+    x = inputs.activations_with_outliers(M, K, seed=M + K)
+    w = inputs.normal_bf16((N, K), 0.02, seed=M, tensor_id=inputs.ID_W)
+    xq, xs = gpu_lib.jet_quant_act_1x128(dev_bf16(x))
+    wq, ws, _ = gpu_lib.jet_quant_weight_128x128(dev_bf16(w), transposed=False)
+    need = gpu_lib.jet_workspace_bytes(gpu_lib.JET_OP_FWD, M, N, K)
+    assert need > 0
+    y16, yq, ys = gpu_lib.jet_fp8_linear_fwd(xq, xs, wq, ws, fuse_quant=True)
+    y32 = gpu_lib.jet_fp8_linear_fwd(xq, xs, wq, ws, out_dtype=torch.float32)
+    wsp = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")
+    y16b = gpu_lib.jet_fp8_linear_fwd(xq, xs, wq, ws, workspace=wsp)
+    torch.cuda.synchronize()
+    a = O.dequant_1x128(host(xq), host(xs))
+    b = O.dequant_128x128(host(wq), host(ws))
+    ref, absp = a @ b.T, oracle_absprod(a, b)
+    tag = f"M={M} K={K}"
+    check_bf16_output(host(y16), ref, absp, f"small-M fwd bf16 {tag}")
+    check_f32_output(host(y32), ref, absp, f"small-M fwd f32 {tag}")
+    qo, so = O.quant_1x128(host(y16))
+    assert_bits_equal(host(yq), qo, f"small-M fused codes {tag}")
+    assert_bits_equal(host(ys), so, f"small-M fused scales {tag}")
+    assert torch.equal(y16, y16b), "explicit workspace changed the result"
+
+
+def test_small_m_matches_exact_integer_case(gpu_lib):
+    """Integer operands with +-7 anchors (every scale 2^-6): the split-K sums
+    are exact, so the small-M forward equals the int64 matmul bit for bit."""
+    M, N, K = 48, 256, 2048
+    rng = np.random.default_rng(5)
+    def anchored(rows, cols):
+        v = rng.integers(-7, 8, size=(rows, cols)).astype(np.float32)
+        v[:, ::128] = 7.0
+        return v
+    x, w = anchored(M, K), anchored(N, K)
+    w[np.arange(N)[:, None] % 128 == np.arange(K)[None, :] % 128] = -7.0
+    xq, xs = gpu_lib.jet_quant_act_1x128(dev_bf16(x))
+    wq, ws, _ = gpu_lib.jet_quant_weight_128x128(dev_bf16(w), transposed=False)
+    y = gpu_lib.jet_fp8_linear_fwd(xq, xs, wq, ws, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert np.all(host(xs) == np.float32(2.0 ** -6)) and np.all(host(ws) == np.float32(2.0 ** -6))
+    assert_bits_equal(host(y), (x.astype(np.int64) @ w.astype(np.int64).T).astype(np.float32),
+                      "small-M integer fwd")
+
+
 # --- Llama-3.1-8B shapes ----------------------------------------------------
 
 LLAMA = {"qkv": (6144, 4096), "o": (4096, 4096), "gate_up": (28672, 4096), "down": (4096, 14336)}
