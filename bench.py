@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="run 1 GiB device copies first (HBM counter calibration)")
     ap.add_argument("--events", type=int, default=1, help="per-kernel HIP events in the timed loop")
+    ap.add_argument("--workload", choices=("train", "decode"), default="train",
+                    help="train: the M=8192 fwd+bwd step (the headline line); decode: the rollout "
+                         "forward at M=64 over the same four linears")
     ap.add_argument("--quant", choices=("both", "separate"), default="both",
                     help="activation quantizers: one read for both groupings (default), or the "
                          "separate 1x128 and 128x1 kernels")
@@ -199,6 +202,88 @@ def counters_for(kernel: str):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
+DECODE_M = 64
+DECODE_COPIES = 4      # weight copies cycled per step: 4 x 218 MB exceeds the 256 MB MALL
+
+
+def decode_bench(args, torch, J):
+    """Rollout decode: forward of the four linears at M=64, one weight copy per
+    step (cycling DECODE_COPIES copies, so weights stream from HBM), with the
+    fused 1x128 output.  value = weight bytes streamed / time."""
+    from fp8_blockwise_quantized_amd import inputs
+    bf = lambda a: torch.from_numpy(a).to(torch.bfloat16).cuda()
+    M = DECODE_M
+    copies = []
+    for c in range(DECODE_COPIES):
+        layer = []
+        for (name, N, K) in LAYERS:
+            x = bf(inputs.activations_with_outliers(M, K, seed=c))
+            w = bf(inputs.normal_bf16((N, K), 0.02, seed=c, tensor_id=inputs.ID_W))
+            xq, xs = J.jet_quant_act_1x128(x)
+            wq, ws, _ = J.jet_quant_weight_128x128(w, transposed=False)
+            del x, w
+            y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+            yq = torch.empty(M, N, dtype=torch.uint8, device="cuda")
+            ys = torch.empty(N // 128, M, dtype=torch.float32, device="cuda")
+            wsp = torch.empty(max(J.jet_workspace_bytes(J.JET_OP_FWD, M, N, K), 16), dtype=torch.uint8,
+                              device="cuda")
+            layer.append((name, N, K, lambda xq=xq, xs=xs, wq=wq, ws=ws, y=y, yq=yq, ys=ys, wsp=wsp:
+                          J.jet_fp8_linear_fwd(xq, xs, wq, ws, y=y, fuse_quant=True, yq=yq, ys=ys,
+                                               workspace=wsp)))
+        copies.append(layer)
+    torch.cuda.synchronize()
+    E = torch.cuda.Event
+    def step(s, evs=None):
+        for i, (_, _, _, fn) in enumerate(copies[s % DECODE_COPIES]):
+            if evs is not None:
+                evs[i][0].record()
+            fn()
+            if evs is not None:
+                evs[i][1].record()
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    # the timed steps run without per-call events (at ~10 us per call the host
+    # cost of recording them would show); the per-layer breakdown comes from a
+    # second pass with events
+    t0, t1 = E(enable_timing=True), E(enable_timing=True)
+    t0.record()
+    for s in range(args.steps):
+        step(s)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    per = [[[E(enable_timing=True), E(enable_timing=True)] for _ in LAYERS] for _ in range(args.steps)]
+    if args.events:
+        for s in range(args.steps):
+            step(s, per[s])
+        torch.cuda.synchronize()
+    wbytes = sum(N * K + N * K // 16384 * 4 for (_, N, K) in LAYERS)
+    flops = sum(2.0 * M * N * K for (_, N, K) in LAYERS)
+    kernels = {}
+    if args.events:
+        for i, (name, N, K) in enumerate(LAYERS):
+            us = sum(per[s][i][0].elapsed_time(per[s][i][1]) for s in range(args.steps)) / args.steps * 1e3
+            kernels[f"fwd_{name}"] = {"avg_us": round(us, 2), "weight_gbs": round((N * K) / (us * 1e-6) / 1e9, 1)}
+    dom = max(kernels, key=lambda k: kernels[k]["avg_us"]) if kernels else None
+    out = {
+        "metric": "FP8 linear decode forward weight-stream GB/s, Llama-8B shapes, M=64",
+        "value": round(wbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "e4m3",
+        "data": "synthetic",
+        "config": {"workload": "Llama-3.1-8B decoder linears (QKV, O, gate+up, down) at rollout decode "
+                               "batch M=64, forward with the fused 1x128 output, weights cycled over "
+                               f"{DECODE_COPIES} copies", "M": M, "parallelism": "none (1 GPU)"},
+        "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+        "roofline": None if dom is None else {
+            "bound": "hbm", "kernel": dom, "achieved": kernels[dom]["weight_gbs"], "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(kernels[dom]["weight_gbs"] / PEAK_HBM_GBS, 4), "traffic": None},
+        "kernels": kernels,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -211,6 +296,9 @@ def main():
         sys.exit(1)
     from fp8_blockwise_quantized_amd import jetfp8 as J
 
+    if args.workload == "decode":
+        decode_bench(args, torch, J)
+        return
     if args.copy_probe:
         copy_probe(torch)
     layers = [Layer(J, torch, n, N, K, M_TOKENS, seed=0) for (n, N, K) in LAYERS]

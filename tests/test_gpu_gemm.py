@@ -336,3 +336,67 @@ def test_training_shapes_sampled(gpu_lib, name):
     a = O.dequant_128x1_T(host(dyqT[nidx]), host(dysT[:, nidx]), M)
     b = O.dequant_128x1_T(host(xqT), host(xsT), M)
     check_f32_output(host(dw[nidx]), a @ b.T, oracle_absprod(a, b), f"wgrad {name}")
+
+
+# --- Qwen-14B/32B shapes at M=16384 (sampled) ---------------------------------
+
+QWEN = {"qkv": (7168, 5120), "down_32b": (5120, 27648), "gate_up_14b": (34816, 5120)}
+
+
+@pytest.mark.parametrize("name", ["qkv", "down_32b"])
+def test_qwen_shapes_sampled(gpu_lib, name):
+    """Qwen-14B/32B-shaped linears (hidden 5120; QKV 5120->7168 with 40 query
+    and 8 key/value heads of 128; the 32B down projection 27648->5120) at
+    M=16384 training tokens: the step's quantizers (both activation groupings
+    from one read) and all three GEMMs at full size, checked on sampled rows
+    and columns against the oracle."""
+    N, K = QWEN[name]
+    M = 16384
+    x, w, dy = layer_inputs(M, N, K, 3)
+    xd, wd, dyd = dev_bf16(x), dev_bf16(w), dev_bf16(dy)
+    xq, xs, xqT, xsT = gpu_lib.jet_quant_act_1x128_128x1_T(xd, True)
+    dyq, dys, dyqT, dysT = gpu_lib.jet_quant_act_1x128_128x1_T(dyd, False)
+    wq, ws, wqT = gpu_lib.jet_quant_weight_128x128(wd)
+    y, yq, ys = gpu_lib.jet_fp8_linear_fwd(xq, xs, wq, ws, fuse_quant=True)
+    dx = gpu_lib.jet_fp8_linear_dgrad(dyq, dys, wqT, ws)
+    dw = gpu_lib.jet_fp8_linear_wgrad(dyqT, dysT, xqT, xsT, M)
+    torch.cuda.synchronize()
+    del xd, wd, dyd
+    rng = np.random.default_rng(17)
+    rows = np.sort(rng.choice(M, 32, replace=False))
+    ncols = np.sort(rng.choice(N, 256, replace=False))
+    kcols = np.sort(rng.choice(K, 256, replace=False))
+    ridx, nidx, kidx = (torch.from_numpy(a).cuda() for a in (rows, ncols, kcols))
+    # quantizers on the sampled rows (1x128) and one 128-row group (128x1)
+    qx, sx = O.quant_1x128(x[rows])
+    assert_bits_equal(host(xq[ridx]), qx, "x codes")
+    assert_bits_equal(host(xs[:, ridx]), sx, "x scales")
+    qd, sd = O.quant_1x128(dy[rows])
+    assert_bits_equal(host(dyq[ridx]), qd, "dy codes")
+    g = int(rng.integers(0, M // 128))
+    gs = slice(g * 128, g * 128 + 128)
+    cq, cs = O.quant_1x128(x[gs])
+    rq, rs = O.requant_128x1_T_from_1x128(cq, cs)
+    assert_bits_equal(host(xqT[:, gs]), rq, "x 128x1 codes")
+    assert_bits_equal(host(xsT[g]), rs[0], "x 128x1 scales")
+    tq, ts = O.quant_128x1_T(dy[gs])
+    assert_bits_equal(host(dyqT[:, gs]), tq, "dy 128x1 codes")
+    bi, bj = int(rng.integers(0, N // 128)), int(rng.integers(0, K // 128))
+    wb = w[bi * 128:(bi + 1) * 128, bj * 128:(bj + 1) * 128]
+    wqo, wso = O.quant_128x128(wb)
+    assert_bits_equal(host(wq[bi * 128:(bi + 1) * 128, bj * 128:(bj + 1) * 128]), wqo, "w block codes")
+    del x, w, dy
+    # GEMMs from the GPU's own codes, on sampled rows x sampled columns
+    wq_h, ws_h = host(wq), host(ws)
+    bw_n = O.e4m3_decode(wq_h[ncols]) * np.repeat(ws_h[ncols // 128], 128, axis=1)          # [256, K]
+    ax = O.dequant_1x128(qx, sx)
+    check_bf16_output(host(y[ridx][:, nidx]), ax @ bw_n.T, oracle_absprod(ax, bw_n), f"fwd {name}")
+    qo, so = O.quant_1x128(host(y[ridx]))
+    assert_bits_equal(host(yq[ridx]), qo, "fused codes")
+    bw_k = (O.e4m3_decode(wq_h[:, kcols]) * np.repeat(ws_h[:, kcols // 128], 128, axis=0)).T  # [256, N]
+    ad = O.dequant_1x128(qd, sd)
+    check_bf16_output(host(dx[ridx][:, kidx]), ad @ bw_k.T, oracle_absprod(ad, bw_k), f"dgrad {name}")
+    del wq_h, bw_n, bw_k
+    a = O.dequant_128x1_T(host(dyqT[nidx[:32]]), host(dysT[:, nidx[:32]]), M)
+    b = O.dequant_128x1_T(host(xqT[kidx]), host(xsT[:, kidx]), M)
+    check_f32_output(host(dw[nidx[:32]][:, kidx]), a @ b.T, oracle_absprod(a, b), f"wgrad {name}")
