@@ -69,16 +69,18 @@ struct GemmCfg {
   static constexpr int ABLK = ATILE / 1024 / NW;   // A DMA instructions per wave and stage
   static constexpr int BBLK = BTILE / 1024 / NW;
   static constexpr int OA = TM / WNW, OB = TN / WMW;   // A and B slabs of a wave's DMA share
-  static constexpr int RSW = TM * 16, CSW = TN * 16;   // private row / column scale slots per wave
-  static constexpr int SPRIV = (RSW + CSW) * 4;        // private scale bytes per wave and stage
-  static constexpr int NRS = RSW / 64;                 // row-scale DMAs per wave and stage
-  static constexpr int STAGE = ATILE + BTILE + NW * SPRIV;
-  static constexpr int LOADS = ABLK + BBLK + NRS + 1;  // DMA instructions per wave and stage
+  static constexpr int RQ = BM / 64;                   // row-scale DMAs (64 rows each) per stage
+  static constexpr int CQ = BN / 64;                   // column-scale DMAs (ROWCOL) per stage
+  static constexpr int SCL = BM * 4 + 1024;            // scale bytes per stage: rows, then columns
+  static constexpr int STAGE = ATILE + BTILE + SCL;
+  static constexpr int LOADS = ABLK + BBLK;            // tile DMAs per wave and stage (+1 scale DMA
+                                                       // for waves 0 .. RQ+CQ-1)
   static constexpr int EPI_PITCH = BN + 8;             // bf16 per staged output row
   static constexpr int LDS = (STAGES * STAGE > BM * EPI_PITCH * 2) ? STAGES * STAGE : BM * EPI_PITCH * 2;
   static_assert(ABLK * NW * 1024 == ATILE && BBLK * NW * 1024 == BTILE, "DMA split");
   static_assert(ABLK * 8 == OA * 16 && BBLK * 8 == OB * 16, "a wave's DMA rows are whole slabs");
-  static_assert(RSW % 64 == 0 && CSW == 64, "scale DMA shape");
+  static_assert(BM % 64 == 0 && BN % 64 == 0 && BN * 4 <= 1024 && NW >= RQ + CQ, "scale DMA shape");
+  static_assert((TM * 16) % 64 == 0 || TM * 16 == 64, "row-scale regions of whole DMAs");
   static_assert(TM % 4 == 0 && (128 % (TN * 16)) == 0 && BN % 128 == 0, "tile shape");
   static_assert((TM & (TM - 1)) == 0 && (TN & (TN - 1)) == 0, "power-of-two slab counts");
   static_assert(LDS * OCC <= 160 * 1024, "LDS");
@@ -291,32 +293,39 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
     dma_src<FRAG>(gB0 + t, lane, row, col);
     offB[t] = (uint32_t)min(n0 + row, p.N - 1) * (uint32_t)p.ldb + col;
   }
-  // Private scale copies (each wave DMAs the scales it folds with, laid out
-  // for its reads).  Row slots: slot 64*(i/4) + 4*lrow + (i%4) holds the row
-  // of the wave's slab i, lane row lrow (each lane reads its TM scales with
-  // TM/4 16-byte loads).  Column slots: ROWCOL slot 16*j + c holds column c of
-  // the wave's B slab j; ROWBLOCK every slot holds the scale of the wave's
-  // 128-column block.
-  const uint32_t sprv = (uint32_t)(CFG::ATILE + CFG::BTILE + wave * CFG::SPRIV);
-  uint32_t offR[CFG::NRS];
-#pragma unroll
-  for (int q = 0; q < CFG::NRS; ++q) {
-    const int sl = 64 * q + lane;
-    const int li = 4 * (sl >> 6) + (sl & 3), lr = (sl >> 2) & 15;
-    const int row = wm * TM * 16 + li * 16 + lr;
-    offR[q] = (uint32_t)min(m0 + row, p.M - 1) * 4u;
-  }
-  uint32_t offC;
-  if (MODE == kRowCol) {
-    const int lj = lane >> 4, c16 = lane & 15;
-    offC = (uint32_t)min(n0 + wn * TN * 16 + lj * 16 + c16, p.N - 1) * 4u;
+  // Scales of the stage, shared by the workgroup (the barrier at the top of a
+  // step covers them).  Rows: the region of wave row wm holds its TM*16 rows
+  // with slot 64*(i/4) + 4*lrow + (i%4) = row i*16 + lrow, so each lane reads
+  // its TM row scales as TM/4 16-byte loads.  Columns (after the BM row
+  // slots): ROWCOL in natural column order, ROWBLOCK the tile's 128-column
+  // block scales (one copy per remaining wave, read from the first).  Every
+  // wave issues exactly one scale DMA per stage, its source chosen without a
+  // branch, so the K-step body stays one basic block: waves 0..RQ-1 the row
+  // scales (64 each), the others the column scales.
+  static_assert(MODE == kRowBlock ? (CFG::NW > CFG::RQ && CFG::NW - CFG::RQ <= 4)
+                                  : CFG::NW - CFG::RQ == CFG::CQ, "one scale DMA per wave");
+  const bool srow = wave < CFG::RQ;
+  uint32_t offS, sdst;
+  if (srow) {
+    const int sl = 64 * wave + lane;
+    const int wm_ = sl / (TM * 16), w_ = sl % (TM * 16);
+    const int i_ = 4 * (w_ >> 6) + (w_ & 3), lr_ = (w_ >> 2) & 15;
+    offS = (uint32_t)min(m0 + wm_ * TM * 16 + i_ * 16 + lr_, p.M - 1) * 4u;
+    sdst = (uint32_t)(CFG::ATILE + CFG::BTILE + 256 * wave);
   } else {
-    const int blk = min((n0 + wn * TN * 16) / 128, p.N / 128 - 1);
-    offC = (uint32_t)blk * (uint32_t)p.sB_o * 4u;
+    const int c_ = wave - CFG::RQ;
+    if (MODE == kRowCol) {
+      offS = (uint32_t)min(n0 + 64 * c_ + lane, p.N - 1) * 4u;
+    } else {
+      // lanes 0..BN/128-1 the tile's blocks; the rest repeat the last one
+      const int blk = min(n0 / 128 + min(lane, CFG::BN / 128 - 1), p.N / 128 - 1);
+      offS = (uint32_t)blk * (uint32_t)p.sB_o * 4u;
+    }
+    sdst = (uint32_t)(CFG::ATILE + CFG::BTILE + CFG::BM * 4 + 256 * c_);
   }
 
   // DMA part t of step kb into stage `stage`: t < ABLK + BBLK is one 1 KiB
-  // tile DMA, then NRS row-scale DMAs and one column-scale DMA.
+  // tile DMA, t == ABLK + BBLK the wave's scale DMA (if it has one).
   constexpr int NT = CFG::ABLK + CFG::BBLK;
 #define JET_ISSUE(part_, stage_, kb_)                                                          \
   do {                                                                                         \
@@ -328,11 +337,9 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
       const int t_ = (part_) < NT ? (part_) - CFG::ABLK : 0;                                   \
       dma16(sbase_ + (uint32_t)(CFG::ATILE + (gB0 + t_) * 1024), p.B + (int64_t)(kb_) * 128,  \
             offB[t_]);                                                                         \
-    } else if ((part_) < NT + CFG::NRS) {                                                      \
-      const int q_ = ((part_) < NT + CFG::NRS && (part_) >= NT) ? (part_) - NT : 0;            \
-      dma4(sbase_ + sprv + (uint32_t)(256 * q_), p.sA + (int64_t)(kb_) * p.sA_ld, offR[q_]);   \
     } else {                                                                                   \
-      dma4(sbase_ + sprv + (uint32_t)(CFG::RSW * 4), p.sB + (int64_t)(kb_) * p.sB_c, offC);    \
+      const float* sp_ = srow ? p.sA + (int64_t)(kb_) * p.sA_ld : p.sB + (int64_t)(kb_) * p.sB_c; \
+      dma4(sbase_ + sdst, sp_, offS);                                                          \
     }                                                                                          \
   } while (0)
 
@@ -378,7 +385,7 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
   for (int s = 0; s < D; ++s)
     if (s < KB) {
 #pragma unroll
-      for (int t = 0; t < NT + CFG::NRS + 1; ++t) JET_ISSUE(t, s, s);
+      for (int t = 0; t < NT + 1; ++t) JET_ISSUE(t, s, s);
     }
 
   int kb = 0, st = 0;
@@ -397,7 +404,8 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
     const int stn = (st + D) % CFG::STAGES;
     const uint8_t* As = lds + st * CFG::STAGE;
     const uint8_t* Bs = As + CFG::ATILE;
-    const float* Sp = reinterpret_cast<const float*>(As + sprv);   // private scales
+    const float* Sr = reinterpret_cast<const float*>(Bs + CFG::BTILE) + wm * TM * 16;   // row scales
+    const float* Sc = reinterpret_cast<const float*>(Bs + CFG::BTILE) + CFG::BM;        // column scales
 
     v8i bf[TN];
     v8i af[R];
@@ -408,18 +416,18 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
     float rsc[TM];
 #pragma unroll
     for (int q = 0; q < TM / 4; ++q) {
-      const float4 r4 = *reinterpret_cast<const float4*>(Sp + 64 * q + 4 * lrow);
+      const float4 r4 = *reinterpret_cast<const float4*>(Sr + 64 * q + 4 * lrow);
       rsc[4 * q + 0] = r4.x; rsc[4 * q + 1] = r4.y; rsc[4 * q + 2] = r4.z; rsc[4 * q + 3] = r4.w;
     }
     float cb[TN][4];
     if (MODE == kRowCol) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const float4 c4 = *reinterpret_cast<const float4*>(Sp + CFG::RSW + 16 * j + 4 * kg);
+        const float4 c4 = *reinterpret_cast<const float4*>(Sc + wn * TN * 16 + 16 * j + 4 * kg);
         cb[j][0] = c4.x; cb[j][1] = c4.y; cb[j][2] = c4.z; cb[j][3] = c4.w;
       }
     } else {
-      const float sbk = Sp[CFG::RSW];
+      const float sbk = Sc[(wn * TN * 16) / 128];
 #pragma unroll
       for (int i = 0; i < TM; ++i) rsc[i] *= sbk;
     }
@@ -443,7 +451,7 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
           // B fragments
           if (REFILL) {
 #pragma unroll
-            for (int t = NT; t < NT + CFG::NRS + 1; ++t) JET_ISSUE(t, stn, kb + D);
+            for (int t = NT; t < NT + 1; ++t) JET_ISSUE(t, stn, kb + D);
           }
 #pragma unroll
           for (int jb = OB; jb < TN; ++jb) bf[jb] = frag32<FRAG>(Bs, wn * TN + jb, lane);
