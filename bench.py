@@ -10,6 +10,11 @@ training batch of M = 8192 tokens (8 sequences x 1024):
 Inputs are seeded synthetic tensors resident in HBM before timing starts.
 `value` = GEMM FLOPs of the step (3 x 2*M*N*K per linear) / step time.
 
+`--workload decode` times the rollout forward of the same linears at M = 64;
+`--workload moe` the grouped (mixture-of-experts) layer of Qwen3-30B-A3B shape
+(hidden 2048, expert intermediate 768, 128 experts, top-8 of 8192 tokens with
+Zipf(1.1) expert load), fwd + dgrad + wgrad with every quantizer.
+
 Prints ONE JSON line.  --gpus above 1 is refused: this build runs on one GPU.
 """
 from __future__ import annotations
@@ -33,6 +38,11 @@ COUNTERS = os.path.join(ROOT, "profiles", "gemm_counters.json")
 GEMM_SRC = os.path.join(ROOT, "fp8_blockwise_quantized_amd", "csrc", "gemm.hip")
 
 
+def log(msg):
+    """Progress on stderr (stdout carries only the JSON line)."""
+    print(f"bench.py: {msg}", file=sys.stderr, flush=True)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -42,9 +52,10 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="run 1 GiB device copies first (HBM counter calibration)")
     ap.add_argument("--events", type=int, default=1, help="per-kernel HIP events in the timed loop")
-    ap.add_argument("--workload", choices=("train", "decode"), default="train",
+    ap.add_argument("--workload", choices=("train", "decode", "moe"), default="train",
                     help="train: the M=8192 fwd+bwd step (the headline line); decode: the rollout "
-                         "forward at M=64 over the same four linears")
+                         "forward at M=64 over the same four linears; moe: the grouped expert "
+                         "layer (Qwen3-30B-A3B shapes) fwd+bwd")
     ap.add_argument("--quant", choices=("both", "separate"), default="both",
                     help="activation quantizers: one read for both groupings (default), or the "
                          "separate 1x128 and 128x1 kernels")
@@ -70,6 +81,76 @@ def q_bytes_128x1_fp8(M, K):  # E4M3 + 1x128 scales in, E4M3 + 128x1 scales out
 def q_bytes_both(M, K):       # BF16 in; 1x128 and 128x1-transposed codes and scales out
     Mp = -(-M // 128) * 128
     return M * K * 2 + M * K + M * K // 128 * 4 + Mp * K + Mp // 128 * K * 4
+
+
+def q_bytes_128x1_grouped(M, K, P, fp8_src):
+    """Grouped 128x1-transposed quantizer: M rows in (BF16, or E4M3 + 1x128
+    scales), P padded columns of codes and P/128 scale rows out."""
+    src = M * K + M * K // 128 * 4 if fp8_src else M * K * 2
+    return src + P * K + P // 128 * K * 4
+
+
+MOE_TOKENS, MOE_EXPERTS, MOE_TOPK, MOE_ALPHA = 8192, 128, 8, 1.1
+MOE_LAYERS = [("gate_up", 1536, 2048), ("down", 2048, 768)]   # per expert: (N, K)
+
+
+class MoELayer:
+    """One grouped expert layer: rows sorted by expert (seg), weights [E, N, K]."""
+
+    def __init__(self, J, torch, name, N, K, seg, seed):
+        from fp8_blockwise_quantized_amd import inputs
+        E, M = len(seg) - 1, int(seg[-1])
+        self.name, self.N, self.K, self.M, self.E = name, N, K, M, E
+        dev = "cuda"
+        bf = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(dev)
+        self.seg = torch.from_numpy(np.asarray(seg, np.int32)).to(dev)
+        self.x = bf(inputs.activations_with_outliers(M, K, seed=seed))
+        self.w = bf(inputs.normal_bf16((E * N, K), 0.02, seed=seed, tensor_id=inputs.ID_W))
+        self.dy = bf(inputs.normal_bf16((M, N), 1e-3, seed=seed, tensor_id=inputs.ID_DY))
+        u8, f32 = torch.uint8, torch.float32
+        e = lambda shape, dt: torch.empty(shape, dtype=dt, device=dev)
+        self.P = P = J.grouped_columns(M, E)
+        self.wq, self.ws, self.wqT = e((E * N, K), u8), e((E * N // 128, K // 128), f32), e((K, E * N), u8)
+        self.xq, self.xs = e((M, K), u8), e((K // 128, M), f32)
+        self.y, self.yq, self.ys = e((M, N), torch.bfloat16), e((M, N), u8), e((N // 128, M), f32)
+        self.dyq, self.dys = e((M, N), u8), e((N // 128, M), f32)
+        self.dx = e((M, K), torch.bfloat16)
+        self.dyqT, self.dysT = e((N, P), u8), e((P // 128, N), f32)
+        self.xqT, self.xsT = e((K, P), u8), e((P // 128, K), f32)
+        self.dw = e((E, N, K), f32)
+        self.flops = 2.0 * M * N * K
+
+    def ops(self, J):
+        M, N, K, E, P = self.M, self.N, self.K, self.E, self.P
+        wq3 = self.wq.view(E, N, K)
+        ws3 = self.ws.view(E, N // 128, K // 128)
+        return [
+            ("quant_w128x128", q_bytes_w(E * N, K), "B",
+             lambda: J.jet_quant_weight_128x128(self.w, q=self.wq, s=self.ws, qT=self.wqT)),
+            ("quant_1x128", q_bytes_1x128(M, K), "B",
+             lambda: J.jet_quant_act_1x128(self.x, q=self.xq, s=self.xs)),
+            ("quant_128x1_T_grouped_fp8", q_bytes_128x1_grouped(M, K, P, True), "B",
+             lambda: J.jet_quant_act_128x1_T_grouped(self.xq, self.seg, src_s=self.xs,
+                                                     qT=self.xqT, sT=self.xsT)),
+            ("grouped_fwd", self.flops, "F",
+             lambda: J.jet_fp8_grouped_fwd(self.xq, self.xs, wq3, ws3, self.seg, y=self.y,
+                                           fuse_quant=True, yq=self.yq, ys=self.ys)),
+            ("quant_1x128", q_bytes_1x128(M, N), "B",
+             lambda: J.jet_quant_act_1x128(self.dy, q=self.dyq, s=self.dys)),
+            ("grouped_dgrad", self.flops, "F",
+             lambda: J.jet_fp8_grouped_dgrad(self.dyq, self.dys, self.wqT, ws3, self.seg, dx=self.dx)),
+            ("quant_128x1_T_grouped_bf16", q_bytes_128x1_grouped(M, N, P, False), "B",
+             lambda: J.jet_quant_act_128x1_T_grouped(self.dy, self.seg, qT=self.dyqT, sT=self.dysT)),
+            ("grouped_wgrad", self.flops, "F",
+             lambda: J.jet_fp8_grouped_wgrad(self.dyqT, self.dysT, self.xqT, self.xsT, self.seg, M,
+                                             dw=self.dw)),
+        ]
+
+
+def moe_routing():
+    from fp8_blockwise_quantized_amd import inputs
+    ids = inputs.zipf_top8_routing(MOE_TOKENS, MOE_EXPERTS, MOE_TOPK, MOE_ALPHA, seed=0)
+    return inputs.segment_offsets(ids, MOE_EXPERTS)
 
 
 class Layer:
@@ -188,6 +269,53 @@ def cpu_baseline():
                       f"host cpu_count={os.cpu_count()}"}
 
 
+MOE_SAMPLE_EXPERTS = 16
+
+
+def cpu_baseline_moe():
+    """The oracle (untuned) on a bounded sample of the MoE workload: the
+    gate+up expert layer (2048 -> 1536) restricted to the first
+    MOE_SAMPLE_EXPERTS experts' segments of the same routing (their full
+    weights and routed rows), through every step of the path; scaled to
+    TFLOP/s of the sample's GEMMs."""
+    from oracle import jet_oracle as O
+    from fp8_blockwise_quantized_amd import inputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    seg_all = moe_routing()
+    E = MOE_SAMPLE_EXPERTS
+    seg = seg_all[:E + 1].astype(np.int32)
+    M = int(seg[-1])
+    _, N, K = MOE_LAYERS[0]
+    x = inputs.activations_with_outliers(M, K, seed=0)
+    w = inputs.normal_bf16((E, N, K), 0.02, seed=0, tensor_id=inputs.ID_W)
+    dy = inputs.normal_bf16((M, N), 1e-3, seed=0, tensor_id=inputs.ID_DY)
+    t0 = time.perf_counter()
+    wq = np.empty((E, N, K), np.uint8)
+    ws = np.empty((E, N // 128, K // 128), np.float32)
+    for e in range(E):
+        wq[e], ws[e] = O.quant_128x128(w[e])
+    xq, xs = O.quant_1x128(x)
+    xqT, xsT = O.requant_128x1_T_grouped_from_1x128(xq, xs, seg)
+    y = O.bf16_rne(O.fl32(O.gemm_grouped_fwd(xq, xs, wq, ws, seg)))
+    O.quant_1x128(y)
+    dyq, dys = O.quant_1x128(dy)
+    O.gemm_grouped_dgrad(dyq, dys, wq, ws, seg)
+    dyqT, dysT = O.quant_128x1_T_grouped(dy, seg)
+    O.gemm_grouped_wgrad(dyqT, dysT, xqT, xsT, seg)
+    dt = time.perf_counter() - t0
+    flops = 3 * 2.0 * M * N * K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"gate+up expert layer 2048->1536, the first {E} of {MOE_EXPERTS} experts "
+                      f"({M} of {int(seg_all[-1])} routed rows), full expert weights, all path steps "
+                      f"(weight/act quantizers, grouped fwd+fused quant, dgrad, grouped 128x1 "
+                      f"quantizers, wgrad); host cpu_count={os.cpu_count()}"}
+
+
 def counters_for(kernel: str):
     """HBM traffic per launch of `kernel` from the committed rocprofv3 counter
     summary, or None if absent or taken on a different gemm.hip."""
@@ -301,9 +429,16 @@ def main():
         return
     if args.copy_probe:
         copy_probe(torch)
-    layers = [Layer(J, torch, n, N, K, M_TOKENS, seed=0) for (n, N, K) in LAYERS]
-    plan = [(l.name, kind, work, unit, fn) for l in layers
-            for (kind, work, unit, fn) in l.ops(J, separate=args.quant == "separate")]
+    moe = args.workload == "moe"
+    log(f"building the {args.workload} inputs")
+    if moe:
+        seg = moe_routing()
+        layers = [MoELayer(J, torch, n, N, K, seg, seed=0) for (n, N, K) in MOE_LAYERS]
+        plan = [(l.name, kind, work, unit, fn) for l in layers for (kind, work, unit, fn) in l.ops(J)]
+    else:
+        layers = [Layer(J, torch, n, N, K, M_TOKENS, seed=0) for (n, N, K) in LAYERS]
+        plan = [(l.name, kind, work, unit, fn) for l in layers
+                for (kind, work, unit, fn) in l.ops(J, separate=args.quant == "separate")]
     torch.cuda.synchronize()
 
     def step(evs=None):
@@ -314,6 +449,7 @@ def main():
             if evs is not None:
                 evs[i][1].record()
 
+    log(f"{args.warmup} warm-up steps, then {args.steps} timed steps")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -363,28 +499,41 @@ def main():
         achieved = a["work"] / a["launches"] / (a["ms"] / a["launches"] * 1e-3) / 1e12
         roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
-                    "traffic": counters_for(dom),
+                    "traffic": None if moe else counters_for(dom),
                     "flops_per_launch": a["work"] / a["launches"]}
 
     quant_bytes = sum(agg[k]["work"] for k in agg if agg[k]["unit"] == "B") / args.steps
     quant_ms = sum(agg[k]["ms"] for k in agg if agg[k]["unit"] == "B") / args.steps
+    if moe:
+        metric = "FP8 grouped MoE expert layers fwd+bwd TFLOP/s, Qwen3-30B-A3B shapes"
+        config = {"workload": f"Qwen3-30B-A3B-shaped MoE expert layers (gate+up 2048->1536 and down "
+                              f"768->2048 per expert), {MOE_EXPERTS} experts, top-{MOE_TOPK} of "
+                              f"{MOE_TOKENS} tokens with Zipf({MOE_ALPHA}) expert load, grouped fwd + "
+                              f"dgrad + wgrad with every quantizer and the weight re-quantization per step",
+                  "routed_rows": int(seg[-1]), "experts": MOE_EXPERTS,
+                  "largest_segment": int(np.diff(seg).max()), "smallest_segment": int(np.diff(seg).min()),
+                  "parallelism": "none (1 GPU)"}
+    else:
+        metric = METRIC
+        config = {"workload": "Llama-3.1-8B decoder linears (QKV 4096->6144, O 4096->4096, "
+                              "gate+up 4096->28672, down 14336->4096), training batch M=8192 tokens, "
+                              "fwd + dgrad + wgrad with every quantizer and the BF16-master weight "
+                              "re-quantization per step",
+                  "M": M_TOKENS, "activation_quantizers": args.quant, "parallelism": "none (1 GPU)"}
     out = {
-        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "metric": metric, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "e4m3",
         "data": "synthetic",
-        "config": {"workload": "Llama-3.1-8B decoder linears (QKV 4096->6144, O 4096->4096, "
-                               "gate+up 4096->28672, down 14336->4096), training batch M=8192 tokens, "
-                               "fwd + dgrad + wgrad with every quantizer and the BF16-master weight "
-                               "re-quantization per step",
-                   "M": M_TOKENS, "activation_quantizers": args.quant, "parallelism": "none (1 GPU)"},
+        "config": config,
         "frac_fp8_peak_step": round(value / PEAK_FP8_TFLOPS, 4),
         "quantizer_gbs_step": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1) if quant_ms else None,
         "roofline": roofline,
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline()
+        log("timing the oracle on its bounded sample")
+        out["cpu_baseline"] = cpu_baseline_moe() if moe else cpu_baseline()
     print(json.dumps(out), flush=True)
 
 

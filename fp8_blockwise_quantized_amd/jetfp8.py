@@ -307,9 +307,7 @@ def jet_fp8_grouped_fwd(xq, xs, wq, ws, seg_off, y=None, out_dtype=torch.bfloat1
     if fuse_quant:
         yq = _codes(yq) if yq is not None else _empty((M, N), torch.uint8, xq)
         ys = ys if ys is not None else _empty((N // 128, M), torch.float32, xq)
-    need = jet_workspace_bytes(JET_OP_FWD, M, N, K)
-    if workspace is None and need:
-        workspace = _empty((need,), torch.uint8, xq)
+    # the grouped GEMMs take no workspace (a caller's buffer is passed through)
     _check("jet_fp8_grouped_fwd", _lib.jet_fp8_grouped_fwd(
         _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(seg_off), E, M, N, K, _ptr(y),
         _dtype_code(y.dtype), _ptr(yq), _ptr(ys), _ptr(workspace),
@@ -325,9 +323,7 @@ def jet_fp8_grouped_dgrad(dyq, dys, wqT, ws, seg_off, dx=None, out_dtype=torch.b
     M, N = dyq.shape
     K = wqT.shape[0]
     dx = dx if dx is not None else _empty((M, K), out_dtype, dyq)
-    need = jet_workspace_bytes(JET_OP_DGRAD, M, N, K)
-    if workspace is None and need:
-        workspace = _empty((need,), torch.uint8, dyq)
+    # the grouped GEMMs take no workspace (a caller's buffer is passed through)
     _check("jet_fp8_grouped_dgrad", _lib.jet_fp8_grouped_dgrad(
         _ptr(dyq), _ptr(dys), _ptr(wqT), _ptr(ws), _ptr(seg_off), E, M, N, K, _ptr(dx),
         _dtype_code(dx.dtype), _ptr(workspace), 0 if workspace is None else workspace.numel(),
@@ -344,9 +340,7 @@ def jet_fp8_grouped_wgrad(dyqT, dysT, xqT, xsT, seg_off, M, dw=None, out_dtype=t
     if dyqT.stride(0) != xqT.stride(0):
         raise ValueError("dyqT and xqT need the same row stride")
     dw = dw if dw is not None else _empty((E, N, K), out_dtype, dyqT)
-    need = jet_workspace_bytes(JET_OP_WGRAD, M, N, K)
-    if workspace is None and need:
-        workspace = _empty((need,), torch.uint8, dyqT)
+    # the grouped GEMMs take no workspace (a caller's buffer is passed through)
     _check("jet_fp8_grouped_wgrad", _lib.jet_fp8_grouped_wgrad(
         _ptr(dyqT), _ptr(dysT), _ptr(xqT), _ptr(xsT), dyqT.stride(0), _ptr(seg_off), E, M, N, K,
         _ptr(dw), _dtype_code(dw.dtype), 1 if accumulate else 0, _ptr(workspace),
