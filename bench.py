@@ -35,6 +35,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 LAYERS = [("qkv", 6144, 4096), ("o", 4096, 4096), ("gate_up", 28672, 4096), ("down", 4096, 14336)]
 M_TOKENS = 8192
 COUNTERS = os.path.join(ROOT, "profiles", "gemm_counters.json")
+MOE_COUNTERS = os.path.join(ROOT, "profiles", "moe_counters.json")
 GEMM_SRC = os.path.join(ROOT, "fp8_blockwise_quantized_amd", "csrc", "gemm.hip")
 
 
@@ -120,6 +121,17 @@ class MoELayer:
         self.dw = e((E, N, K), f32)
         self.flops = 2.0 * M * N * K
 
+    def gemm_bytes(self, kind):
+        """Algorithmic HBM bytes of one grouped GEMM launch (as Layer.gemm_bytes;
+        the wgrad operands in their padded layout of P columns)."""
+        M, N, K, E, P = self.M, self.N, self.K, self.E, self.P
+        w = E * (N * K + N * K // 16384 * 4)
+        if kind == "grouped_fwd":
+            return M * K + M * K // 128 * 4 + w + M * N * 2 + M * N + M * N // 128 * 4
+        if kind == "grouped_dgrad":
+            return M * N + M * N // 128 * 4 + w + M * K * 2
+        return (N + K) * P + P // 128 * (N + K) * 4 + E * N * K * 4
+
     def ops(self, J):
         M, N, K, E, P = self.M, self.N, self.K, self.E, self.P
         wq3 = self.wq.view(E, N, K)
@@ -174,6 +186,18 @@ class Layer:
         self.xqT, self.xsT = e((K, Mp), u8), e((Mp // 128, K), f32)
         self.dw = e((N, K), f32)
         self.flops = 2.0 * M * N * K
+
+    def gemm_bytes(self, kind):
+        """Algorithmic HBM bytes of one GEMM launch: operand codes and scales
+        read once, outputs written once."""
+        M, N, K = self.M, self.N, self.K
+        Mp = -(-M // 128) * 128
+        w = N * K + N * K // 16384 * 4
+        if kind == "gemm_fwd":
+            return M * K + M * K // 128 * 4 + w + M * N * 2 + M * N + M * N // 128 * 4
+        if kind == "gemm_dgrad":
+            return M * N + M * N // 128 * 4 + w + M * K * 2
+        return (N + K) * Mp + Mp // 128 * (N + K) * 4 + N * K * 4
 
     def ops(self, J, separate=False):
         """(kernel kind, algorithmic work, unit, callable) in path order."""
@@ -316,11 +340,11 @@ def cpu_baseline_moe():
                       f"quantizers, wgrad); host cpu_count={os.cpu_count()}"}
 
 
-def counters_for(kernel: str):
+def counters_for(kernel: str, path: str = COUNTERS):
     """HBM traffic per launch of `kernel` from the committed rocprofv3 counter
     summary, or None if absent or taken on a different gemm.hip."""
     try:
-        c = json.load(open(COUNTERS))
+        c = json.load(open(path))
     except (OSError, ValueError):
         return None
     sha = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
@@ -494,13 +518,26 @@ def main():
     gemm_kinds = [k for k in agg if agg[k]["unit"] == "F"]
     roofline = None
     if gemm_kinds:
+        # The dominant GEMM kind, priced against the roofline its arithmetic
+        # intensity (FLOP per algorithmic byte) puts it under: MFMA above the
+        # ridge (5.0 PF / 8 TB/s = 625 FLOP/B), HBM below it.
         dom = max(gemm_kinds, key=lambda k: agg[k]["ms"])
         a = agg[dom]
-        achieved = a["work"] / a["launches"] / (a["ms"] / a["launches"] * 1e-3) / 1e12
-        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
-                    "traffic": None if moe else counters_for(dom),
-                    "flops_per_launch": a["work"] / a["launches"]}
+        sec = a["ms"] / a["launches"] * 1e-3
+        flops = a["work"] / a["launches"]
+        nbytes = sum(l.gemm_bytes(dom) for l in layers) / len(layers)
+        intensity = flops / nbytes
+        common = {"kernel": dom, "traffic": counters_for(dom, MOE_COUNTERS if moe else COUNTERS),
+                  "flops_per_launch": flops, "bytes_per_launch": nbytes,
+                  "intensity_flop_per_byte": round(intensity, 1)}
+        if intensity >= PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+            achieved = flops / sec / 1e12
+            roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4), **common}
+        else:
+            achieved = nbytes / sec / 1e9
+            roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), **common}
 
     quant_bytes = sum(agg[k]["work"] for k in agg if agg[k]["unit"] == "B") / args.steps
     quant_ms = sum(agg[k]["ms"] for k in agg if agg[k]["unit"] == "B") / args.steps
