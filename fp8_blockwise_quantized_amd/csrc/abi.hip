@@ -147,6 +147,8 @@ static int check_gemm_common(const char* name, int64_t M, int64_t N, int64_t K, 
                 name, (long long)M, (long long)N, (long long)K);
   if (ws_bytes < need || (need && !workspace))
     return fail(JET_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", name, need);
+  if (need && !aligned(workspace, 16))
+    return fail(JET_ERR_ALIGN, "%s: the workspace needs 16-byte alignment", name);
   return JET_OK;
 }
 
@@ -176,7 +178,7 @@ int jet_fp8_linear_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, co
   a.C = y; a.ldc = N; a.Cq = yq; a.Cs = ys; a.ldcs = M;
   a.M = (int)M; a.N = (int)N; a.Kc = (int)K;
   const int out = y_dtype == JET_BF16 ? jet::kOutBf16 : jet::kOutF32;
-  if (M <= jet::kSkinnyMaxM)   // rollout decode: weight-streaming, split-K into the workspace
+  if (M <= jet::kSkinnyMaxM)   // rollout decode: weight-streaming, split-K through the workspace
     return hip_status(jet::launch_gemm_skinny(a, out, fuse, workspace, as_stream(stream)), "fp8_linear_fwd");
   return hip_status(jet::launch_gemm(a, jet::kRowBlock, out, false, fuse, as_stream(stream)),
                     "fp8_linear_fwd");

@@ -623,13 +623,19 @@ hipError_t launch_gemm(const GemmArgs& a, int mode, int out, bool accum, bool fu
 // weight once for a handful of rows, so it is bound by HBM bandwidth and needs
 // many weight bytes in flight.  The output is cut into 64*WS-column blocks
 // and the K steps into S contiguous ranges; a workgroup (4 wavefronts) computes
-// the FP32 partial sum of one (block, range) through an NST-stage ring of
-// direct global->LDS loads (NST-1 steps of prefetch) and writes it to the
-// caller's workspace P[S][M][N].  k_skinny_finish then sums the S partials in
-// order s = 0..S-1 (deterministic) and writes Y (BF16 or FP32) and, for BF16,
-// the fused 1x128 quantization of Y.  Per 128-K step the numerics are those
-// of the main kernel: one MFMA per 16x16 sub-tile from zero, folded into FP32
-// with the product of the row scale and the weight block scale.
+// the FP32 sum of one (block, range) through an NST-stage ring of direct
+// global->LDS loads (NST-1 steps of prefetch).  With S = 1 it writes Y (BF16
+// or FP32) and, for BF16, the fused 1x128 quantization of Y itself.  With
+// S > 1 it writes its partial sum to the caller's workspace P[S][M][N] and
+// k_skinny_finish sums the S partials in order s = 0..S-1 (deterministic)
+// and writes the same outputs.  (Finishing inside the split kernel, the last
+// workgroup of a column block summing the others' partials, measured slower:
+// the partials then have to cross the XCDs' separate L2 caches through memory,
+// three dependent memory round trips at the end of every workgroup, where the
+// second kernel reads them from L2 after one kernel boundary.)  Per 128-K step
+// the numerics are those of the main kernel: one MFMA per 16x16 sub-tile from
+// zero, folded into FP32 with the product of the row scale and the weight
+// block scale.
 //
 // Stage layout: the X tile (MT*16 rows x 128 bytes, swizzled rows), the W
 // tile (64 rows x 128 bytes), then four 256-byte scale slots, one DMA per
@@ -648,12 +654,14 @@ struct SkinnyCfg {
   static constexpr int NSX = MT / 4;                   // scale slots holding X row scales
   static constexpr int LOADS = BPW + 1;
   static constexpr int LDS = NST * STAGE;
+  static constexpr int TP = BN + 4;                    // FP32 output tile pitch (floats)
   static_assert((XBLK + WBLK) % 4 == 0 && NSX >= 1 && NSX < 4, "DMA split");
-  static_assert(BN <= 128, "one weight block scale per workgroup");
+  static_assert(BN == 128, "one 1x128 output group and one weight block scale per workgroup");
+  static_assert(MT * 16 * TP * 4 <= LDS, "output tile fits the stage ring");
   static_assert(LDS <= 160 * 1024, "LDS");
 };
 
-template <int MT, int NST, int WS>
+template <int MT, int NST, int WS, int OUT, bool FUSEQ>
 __global__ __launch_bounds__(256) void k_gemm_fp8_skinny(GemmArgs p, float* __restrict__ part,
                                                          int splits) {
   using C = SkinnyCfg<MT, NST, WS>;
@@ -755,18 +763,75 @@ __global__ __launch_bounds__(256) void k_gemm_fp8_skinny(GemmArgs p, float* __re
   }
   wait_vmem<0>();
 
-  // partial sums: lane holds row i*16 + lrow, columns n0 + 16*(wave*WS + j) + 4*kg + r
-  float* P = part + (int64_t)sidx * p.M * p.N;
+  if (splits > 1) {
+    // partial sums: lane holds row i*16 + lrow, columns n0 + 16*(wave*WS + j) + 4*kg + r
+    float* P = part + (int64_t)sidx * p.M * p.N;
 #pragma unroll
-  for (int j = 0; j < WS; ++j) {
-    const int n = n0 + 16 * (wave * WS + j) + 4 * kg;
+    for (int j = 0; j < WS; ++j) {
+      const int n = n0 + 16 * (wave * WS + j) + 4 * kg;
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      const int m = i * 16 + lrow;
-      if (m < p.M)
-        *reinterpret_cast<float4*>(P + (int64_t)m * p.N + n) =
-            make_float4(acc[j][i][0], acc[j][i][1], acc[j][i][2], acc[j][i][3]);
+      for (int i = 0; i < MT; ++i) {
+        const int m = i * 16 + lrow;
+        if (m < p.M)
+          *reinterpret_cast<float4*>(P + (int64_t)m * p.N + n) =
+              make_float4(acc[j][i][0], acc[j][i][1], acc[j][i][2], acc[j][i][3]);
+      }
     }
+    return;
+  }
+
+  // ---- S = 1: the block's FP32 values into an LDS tile T[MT*16][TP], then
+  // the outputs.  Lane element (j, i, r) is row i*16 + lrow, column
+  // 16*(wave*WS + j) + 4*kg + r. ----
+  float* T = reinterpret_cast<float*>(lds);
+  __syncthreads();   // every wavefront is done with the stage ring
+#pragma unroll
+  for (int j = 0; j < WS; ++j)
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+      *reinterpret_cast<float4*>(T + (i * 16 + lrow) * C::TP + 16 * (wave * WS + j) + 4 * kg) =
+          make_float4(acc[j][i][0], acc[j][i][1], acc[j][i][2], acc[j][i][3]);
+  __syncthreads();
+
+  // ---- outputs: 16 rows per pass, a DPP row of 16 lanes per row (8 columns
+  // per lane, one 1x128 group per row) ----
+  const int c = tid & 15;
+  const int n = n0 + 8 * c;
+  for (int m0r = 0; m0r < p.M; m0r += 16) {
+    const int m = m0r + (tid >> 4);
+    const bool ok = m < p.M;
+    const float* src = T + (ok ? m : p.M - 1) * C::TP + 8 * c;
+    const float4 a = *reinterpret_cast<const float4*>(src);
+    const float4 b = *reinterpret_cast<const float4*>(src + 4);
+    if (OUT == kOutF32) {
+      if (ok) {
+        float* Cf = static_cast<float*>(p.C) + (int64_t)m * p.ldc + n;
+        *reinterpret_cast<float4*>(Cf) = a;
+        *reinterpret_cast<float4*>(Cf + 4) = b;
+      }
+      continue;
+    }
+    uint4 w;
+    w.x = bf16_rne(a.x) | (bf16_rne(a.y) << 16);
+    w.y = bf16_rne(a.z) | (bf16_rne(a.w) << 16);
+    w.z = bf16_rne(b.x) | (bf16_rne(b.y) << 16);
+    w.w = bf16_rne(b.z) | (bf16_rne(b.w) << 16);
+    if (FUSEQ) {
+      // 1x128 quantization of the BF16 output, as in the main kernel's epilogue
+      uint32_t am = max_abs_bf16x2(0u, w.x);
+      am = max_abs_bf16x2(am, w.y);
+      am = max_abs_bf16x2(am, w.z);
+      am = max_abs_bf16x2(am, w.w);
+      am = row16_max_u16x2(am);
+      const ScalePair sp = scale_pair(fold_bf16x2(am));
+      const uint32_t q0 = e4m3x4(bf16_lo(w.x) * sp.r, bf16_hi(w.x) * sp.r, bf16_lo(w.y) * sp.r, bf16_hi(w.y) * sp.r);
+      const uint32_t q1 = e4m3x4(bf16_lo(w.z) * sp.r, bf16_hi(w.z) * sp.r, bf16_lo(w.w) * sp.r, bf16_hi(w.w) * sp.r);
+      if (ok) {
+        *reinterpret_cast<uint2*>(p.Cq + (int64_t)m * p.ldc + n) = make_uint2(q0, q1);
+        if (c == 0) p.Cs[(int64_t)(n / 128) * p.ldcs + m] = sp.s;
+      }
+    }
+    if (ok) *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.C) + (int64_t)m * p.ldc + n) = w;
   }
 }
 
@@ -825,8 +890,8 @@ __global__ __launch_bounds__(256) void k_skinny_finish(GemmArgs p, const float* 
 }
 
 // Small-M configuration (measured on the Llama-8B decode shapes: 4, 6 or 8
-// stages, 64 or 128 columns per workgroup and 128..1024 target workgroups all
-// land within 10 %; this one needs the fewest ranges, so the least workspace).
+// stages and 128..1024 target workgroups all land within 10 %; this one needs
+// the fewest ranges, so the least workspace).
 constexpr int kSkWS = 2;        // W slabs per wavefront: 128 output columns per workgroup
 constexpr int kSkNST = 6;       // ring stages for M <= 64 (4 for M <= 128)
 constexpr int kSkTarget = 128;  // workgroups aimed at over all column blocks and K ranges
@@ -842,32 +907,40 @@ int skinny_splits(int64_t M, int64_t N, int64_t K) {
   return (int)(s < 1 ? 1 : s);
 }
 
+// Workspace: the S partial sums (S*M*N floats); none when the K steps are not split.
 size_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || M > kSkinnyMaxM || N <= 0 || K <= 0) return 0;
-  return (size_t)skinny_splits(M, N, K) * (size_t)M * (size_t)N * sizeof(float);
+  const int S = skinny_splits(M, N, K);
+  return S == 1 ? 0 : (size_t)S * (size_t)M * (size_t)N * sizeof(float);
 }
 
-template <int MT, int NST, int WS>
-static hipError_t launch_skinny_mt(const GemmArgs& a, int out, bool fuseq, float* part, int S,
-                                   hipStream_t st) {
-  hipLaunchKernelGGL((k_gemm_fp8_skinny<MT, NST, WS>), dim3((unsigned)(a.N / (64 * WS)), (unsigned)S),
-                     dim3(256), 0, st, a, part, S);
+template <int MT, int NST, int WS, int OUT, bool FUSEQ>
+static hipError_t launch_skinny_mt(const GemmArgs& a, float* part, int S, hipStream_t st) {
+  hipLaunchKernelGGL((k_gemm_fp8_skinny<MT, NST, WS, OUT, FUSEQ>),
+                     dim3((unsigned)(a.N / (64 * WS)), (unsigned)S), dim3(256), 0, st, a, part, S);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || S == 1) return e;
   const dim3 g((unsigned)(a.N / 128), (unsigned)((a.M + 15) / 16));
-  if (out == kOutF32) hipLaunchKernelGGL((k_skinny_finish<kOutF32, false>), g, dim3(256), 0, st, a, part, S);
-  else if (fuseq) hipLaunchKernelGGL((k_skinny_finish<kOutBf16, true>), g, dim3(256), 0, st, a, part, S);
-  else hipLaunchKernelGGL((k_skinny_finish<kOutBf16, false>), g, dim3(256), 0, st, a, part, S);
+  hipLaunchKernelGGL((k_skinny_finish<OUT, FUSEQ>), g, dim3(256), 0, st, a, part, S);
   return hipGetLastError();
+}
+
+template <int MT, int NST>
+static hipError_t launch_skinny_out(const GemmArgs& a, int out, bool fuseq, float* part, int S,
+                                    hipStream_t st) {
+  if (out == kOutF32) return launch_skinny_mt<MT, NST, kSkWS, kOutF32, false>(a, part, S, st);
+  if (fuseq) return launch_skinny_mt<MT, NST, kSkWS, kOutBf16, true>(a, part, S, st);
+  return launch_skinny_mt<MT, NST, kSkWS, kOutBf16, false>(a, part, S, st);
 }
 
 hipError_t launch_gemm_skinny(const GemmArgs& a, int out, bool fuseq, void* workspace, hipStream_t st) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
   if (a.M > kSkinnyMaxM || a.Kc <= 0 || a.N % (64 * kSkWS)) return hipErrorInvalidValue;
   const int S = skinny_splits(a.M, a.N, a.Kc);
+  if (S > 1 && workspace == nullptr) return hipErrorInvalidValue;
   float* part = static_cast<float*>(workspace);
-  if (a.M <= 64) return launch_skinny_mt<4, kSkNST, kSkWS>(a, out, fuseq, part, S, st);
-  return launch_skinny_mt<8, 4, kSkWS>(a, out, fuseq, part, S, st);
+  if (a.M <= 64) return launch_skinny_out<4, kSkNST>(a, out, fuseq, part, S, st);
+  return launch_skinny_out<8, 4>(a, out, fuseq, part, S, st);
 }
 
 // Grouped GEMMs use the 256 x 256 tile too: measured on the Qwen3-30B-A3B

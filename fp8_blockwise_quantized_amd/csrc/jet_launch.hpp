@@ -48,8 +48,9 @@ hipError_t launch_quant_1x128_128x1_T(const uint16_t* x, int64_t M, int64_t K, i
                                       int64_t ldqT, float* sT, bool requant, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs& a, int mode, int out, bool accum, bool fuseq,
                        hipStream_t st);
-// Small-M forward (M <= kSkinnyMaxM): split-K partial sums in the caller's
-// workspace (skinny_workspace_bytes), then a deterministic finishing pass.
+// Small-M forward (M <= kSkinnyMaxM): one kernel when the K steps are not
+// split; otherwise split-K partial sums in the caller's workspace
+// (skinny_workspace_bytes) and a deterministic finishing pass.
 constexpr int64_t kSkinnyMaxM = 128;
 int skinny_splits(int64_t M, int64_t N, int64_t K);
 size_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K);

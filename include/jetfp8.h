@@ -155,13 +155,14 @@ int jet_quant_weight_128x128(const void* w, int64_t N, int64_t K, int64_t ldw,
  *        jet_quant_act_1x128 of the BF16 Y -- the next layer's FP8 input
  *        (163.com section 五: quantization fused with the preceding operator).
  *   workspace : device scratch of at least jet_workspace_bytes(JET_OP_FWD, M, N, K)
- *        bytes (may be NULL when that is 0).  For M <= 128 (rollout decode,
- *        explainer "Kernarchitektur": rollout runs the same forward) the call
- *        splits the contraction into ranges whose FP32 partial sums live in
- *        the workspace, then sums them in a fixed order: the result is
- *        deterministic, and within the GEMM tolerance of the large-M kernel
- *        (the FP32 summation order differs).  The caller owns the workspace;
- *        calls that share one workspace must not overlap.
+ *        bytes, 16-byte aligned (may be NULL when that is 0).  For M <= 128
+ *        (rollout decode, explainer "Kernarchitektur": rollout runs the same
+ *        forward) the call may split the contraction into ranges whose FP32
+ *        partial sums live in the workspace, then sums them in a fixed order:
+ *        the result is deterministic, and within the GEMM tolerance of the
+ *        large-M kernel (the FP32 summation order differs).  Its contents on
+ *        entry are ignored and unspecified on return.  The caller owns the
+ *        workspace; calls that share one workspace must not overlap.
  *   M >= 0, N % 128 == 0, K % 128 == 0, all pointers 16-byte aligned.
  */
 int jet_fp8_linear_fwd(const uint8_t* xq, const float* xs,
@@ -208,8 +209,9 @@ int jet_fp8_linear_wgrad(const uint8_t* dyqT, const float* dysT,
                          void* workspace, size_t ws_bytes, void* stream);
 
 /* Workspace bytes the GEMM `op` (jet_op) needs at this shape (0 = none):
- * nonzero only for the dense forward with 0 < M <= 128 (split-K partial sums,
- * at most 16 * M * N * 4 bytes).  The grouped GEMMs need none. */
+ * nonzero only for the dense forward with 0 < M <= 128 when its contraction is
+ * split (S ranges, S <= 16: S * M * N * 4 bytes of partial sums).  The grouped
+ * GEMMs need none. */
 size_t jet_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
 
 /*

@@ -229,10 +229,10 @@ def test_small_m_forward(gpu_lib, M, K):
     xq, xs = gpu_lib.jet_quant_act_1x128(dev_bf16(x))
     wq, ws, _ = gpu_lib.jet_quant_weight_128x128(dev_bf16(w), transposed=False)
     need = gpu_lib.jet_workspace_bytes(gpu_lib.JET_OP_FWD, M, N, K)
-    assert need > 0
+    assert (need > 0) == (K > 128)          # a single K step is never split
     y16, yq, ys = gpu_lib.jet_fp8_linear_fwd(xq, xs, wq, ws, fuse_quant=True)
     y32 = gpu_lib.jet_fp8_linear_fwd(xq, xs, wq, ws, out_dtype=torch.float32)
-    wsp = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")
+    wsp = torch.full((max(need, 16),), 0x7F, dtype=torch.uint8, device="cuda")
     y16b = gpu_lib.jet_fp8_linear_fwd(xq, xs, wq, ws, workspace=wsp)
     torch.cuda.synchronize()
     a = O.dequant_1x128(host(xq), host(xs))
@@ -245,6 +245,71 @@ def test_small_m_forward(gpu_lib, M, K):
     assert_bits_equal(host(yq), qo, f"small-M fused codes {tag}")
     assert_bits_equal(host(ys), so, f"small-M fused scales {tag}")
     assert torch.equal(y16, y16b), "explicit workspace changed the result"
+
+
+def _small_m_problem(gpu_lib, M, N, K, seed):
+    x = inputs.activations_with_outliers(M, K, seed=seed)
+    w = inputs.normal_bf16((N, K), 0.02, seed=seed, tensor_id=inputs.ID_W)
+    xq, xs = gpu_lib.jet_quant_act_1x128(dev_bf16(x))
+    wq, ws, _ = gpu_lib.jet_quant_weight_128x128(dev_bf16(w), transposed=False)
+    return xq, xs, wq, ws
+
+
+def test_small_m_workspace_reuse_and_stale_contents(gpu_lib):
+    """One workspace filled with random bytes, shared by shapes with 10, 8 and
+    4 K ranges called in an interleaved order, gives every call the bits of a
+    call on its own fresh workspace (no state is carried between calls)."""
+    shapes = [(64, 384, 1280), (64, 2048, 2048), (32, 4096, 512)]
+    needs = [gpu_lib.jet_workspace_bytes(gpu_lib.JET_OP_FWD, *sh) for sh in shapes]
+    assert min(needs) > 0
+    probs = [_small_m_problem(gpu_lib, *sh, seed=i) for i, sh in enumerate(shapes)]
+    refs = []
+    for (xq, xs, wq, ws) in probs:
+        y, yq, ys = gpu_lib.jet_fp8_linear_fwd(xq, xs, wq, ws, fuse_quant=True)
+        refs.append((y, yq, ys))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    shared = torch.randint(0, 256, (max(needs),), dtype=torch.uint8, device="cuda", generator=g)
+    for it, i in enumerate([0, 1, 2, 0, 2, 1, 1, 0]):
+        xq, xs, wq, ws = probs[i]
+        y, yq, ys = gpu_lib.jet_fp8_linear_fwd(xq, xs, wq, ws, fuse_quant=True, workspace=shared)
+        torch.cuda.synchronize()
+        for a, b, what in zip((y, yq, ys), refs[i], ("Y", "codes", "scales")):
+            assert torch.equal(a, b), f"call {it} (shape {shapes[i]}): {what} differ on a shared workspace"
+
+
+def test_small_m_graph_replay(gpu_lib):
+    """A captured split-K forward (the split kernel and its finishing pass)
+    replays correctly: eager work on the same workspace and a synchronization
+    run between the replays; every replay equals the eager result."""
+    M, N, K = 64, 4096, 4096
+    xq, xs, wq, ws = _small_m_problem(gpu_lib, M, N, K, seed=3)
+    need = gpu_lib.jet_workspace_bytes(gpu_lib.JET_OP_FWD, M, N, K)
+    assert need > 0
+    wsp = torch.empty(need, dtype=torch.uint8, device="cuda")
+    y_eager, yq_eager, ys_eager = gpu_lib.jet_fp8_linear_fwd(xq, xs, wq, ws, fuse_quant=True, workspace=wsp)
+    y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    yq = torch.empty(M, N, dtype=torch.uint8, device="cuda")
+    ys = torch.empty(N // 128, M, dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):     # warm-up on the capture stream
+        gpu_lib.jet_fp8_linear_fwd(xq, xs, wq, ws, y=y, fuse_quant=True, yq=yq, ys=ys, workspace=wsp)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gpu_lib.jet_fp8_linear_fwd(xq, xs, wq, ws, y=y, fuse_quant=True, yq=yq, ys=ys, workspace=wsp)
+    torch.cuda.synchronize()
+    for r in range(4):
+        y.zero_(); yq.zero_(); ys.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager) and torch.equal(yq, yq_eager) and torch.equal(ys, ys_eager), \
+            f"graph replay {r} differs from the eager call"
+        # eager work on the same workspace between replays (fresh tags)
+        gpu_lib.jet_fp8_linear_fwd(xq, xs, wq, ws, fuse_quant=True, workspace=wsp)
+        torch.cuda.synchronize()
 
 
 def test_small_m_matches_exact_integer_case(gpu_lib):
