@@ -68,6 +68,50 @@ int jet_quant_act_1x128(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_
                     "quant_act_1x128");
 }
 
+int jet_rmsnorm_quant_1x128(const void* x, const void* gamma, int64_t M, int64_t H, int64_t ldx,
+                            float eps, void* y, int64_t ldy, uint8_t* q, int64_t ldq, float* s,
+                            void* stream) {
+  g_last_error[0] = 0;
+  if (M < 0 || H <= 0 || H % kG || H > 8192 || M > kMaxDim)
+    return fail(JET_ERR_SHAPE, "rmsnorm_quant_1x128: need M >= 0 and 0 < H <= 8192, H %% 128 == 0 "
+                               "(M=%lld H=%lld)", (long long)M, (long long)H);
+  if (!(eps >= 0.0f) || eps > 3.0e38f)
+    return fail(JET_ERR_SHAPE, "rmsnorm_quant_1x128: eps must be finite and >= 0");
+  if (M == 0) return JET_OK;
+  if (!x || !gamma || !q || !s) return fail(JET_ERR_NULL, "rmsnorm_quant_1x128: null pointer");
+  if (ldx < H || ldq < H || (y && ldy < H))
+    return fail(JET_ERR_SHAPE, "rmsnorm_quant_1x128: leading dimension < H");
+  if (!aligned(x, 16) || !aligned(gamma, 16) || !aligned(q, 16) || !aligned(s, 4) || ldx % 8 ||
+      ldq % 16 || (y && (!aligned(y, 16) || ldy % 8)))
+    return fail(JET_ERR_ALIGN, "rmsnorm_quant_1x128: x, gamma, y, q need 16-byte alignment, "
+                               "ldx %% 8, ldy %% 8, ldq %% 16");
+  return hip_status(jet::launch_rmsnorm_quant_1x128(static_cast<const uint16_t*>(x),
+                                                    static_cast<const uint16_t*>(gamma), M, H, ldx, eps,
+                                                    static_cast<uint16_t*>(y), ldy, q, ldq, s,
+                                                    as_stream(stream)),
+                    "rmsnorm_quant_1x128");
+}
+
+int jet_swiglu_quant_1x128(const void* gu, int64_t M, int64_t I, int64_t ldgu, void* h, int64_t ldh,
+                           uint8_t* q, int64_t ldq, float* s, void* stream) {
+  g_last_error[0] = 0;
+  if (M < 0 || I < 0 || I % kG || M > kMaxDim || I > kMaxDim)
+    return fail(JET_ERR_SHAPE, "swiglu_quant_1x128: need M >= 0 and I a multiple of 128 (M=%lld I=%lld)",
+                (long long)M, (long long)I);
+  if (M == 0 || I == 0) return JET_OK;
+  if (!gu || !q || !s) return fail(JET_ERR_NULL, "swiglu_quant_1x128: null pointer");
+  if (ldgu < 2 * I || ldq < I || (h && ldh < I))
+    return fail(JET_ERR_SHAPE, "swiglu_quant_1x128: need ldgu >= 2*I, ldq >= I, ldh >= I");
+  if (!aligned(gu, 16) || !aligned(q, 16) || !aligned(s, 4) || ldgu % 8 || ldq % 16 ||
+      (h && (!aligned(h, 16) || ldh % 8)))
+    return fail(JET_ERR_ALIGN, "swiglu_quant_1x128: gu, h, q need 16-byte alignment, ldgu %% 8, "
+                               "ldh %% 8, ldq %% 16");
+  return hip_status(jet::launch_swiglu_quant_1x128(static_cast<const uint16_t*>(gu), M, I, ldgu,
+                                                   static_cast<uint16_t*>(h), ldh, q, ldq, s,
+                                                   as_stream(stream)),
+                    "swiglu_quant_1x128");
+}
+
 int jet_quant_act_128x1_T(const void* src, int src_dtype, const float* src_s, int64_t M, int64_t K,
                           int64_t ldsrc, uint8_t* qT, int64_t ldqT, float* sT, void* stream) {
   g_last_error[0] = 0;

@@ -46,6 +46,13 @@ hipError_t launch_quant_128x1_T(const void* src, bool fp8src, const float* src_s
 hipError_t launch_quant_1x128_128x1_T(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                       uint8_t* q, int64_t ldq, float* s, uint8_t* qT,
                                       int64_t ldqT, float* sT, bool requant, hipStream_t st);
+// Fused producers of the 1x128 input: RMSNorm (H <= 8192) and SwiGLU; y / h
+// (the BF16 tensor) may be null.
+hipError_t launch_rmsnorm_quant_1x128(const uint16_t* x, const uint16_t* gamma, int64_t M, int64_t H,
+                                      int64_t ldx, float eps, uint16_t* y, int64_t ldy, uint8_t* q,
+                                      int64_t ldq, float* s, hipStream_t st);
+hipError_t launch_swiglu_quant_1x128(const uint16_t* gu, int64_t M, int64_t I, int64_t ldgu, uint16_t* h,
+                                     int64_t ldh, uint8_t* q, int64_t ldq, float* s, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs& a, int mode, int out, bool accum, bool fuseq,
                        hipStream_t st);
 // Small-M forward (M <= kSkinnyMaxM): one kernel when the K steps are not

@@ -21,7 +21,7 @@ JET_OK, JET_ERR_NULL, JET_ERR_SHAPE, JET_ERR_ALIGN, JET_ERR_DTYPE, JET_ERR_WORKS
 JET_BF16, JET_F32, JET_E4M3 = 1, 2, 3
 JET_OP_FWD, JET_OP_DGRAD, JET_OP_WGRAD = 0, 1, 2
 
-_p, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+_p, _i64, _i32, _sz, _f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
 
 # name -> argtypes, in header order
 SIGNATURES = {
@@ -32,6 +32,8 @@ SIGNATURES = {
     "jet_quant_act_128x1_T": [_p, _i32, _p, _i64, _i64, _i64, _p, _i64, _p, _p],
     "jet_quant_act_1x128_128x1_T": [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _i32, _p],
     "jet_quant_weight_128x128": [_p, _i64, _i64, _i64, _p, _p, _p, _p],
+    "jet_rmsnorm_quant_1x128": [_p, _p, _i64, _i64, _i64, _f32, _p, _i64, _p, _i64, _p, _p],
+    "jet_swiglu_quant_1x128": [_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _p],
     "jet_fp8_linear_fwd": [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _p, _p, _p, _sz, _p],
     "jet_fp8_linear_dgrad": [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _p, _sz, _p],
     "jet_fp8_linear_wgrad": [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _i32, _p, _sz, _p],
@@ -134,6 +136,54 @@ def jet_quant_act_1x128(x, q=None, s=None, stream=None):
     _check("jet_quant_act_1x128", _lib.jet_quant_act_1x128(
         _ptr(x), M, K, x.stride(0), _ptr(q), q.stride(0), _ptr(s), _stream(stream)))
     return q, s
+
+
+def jet_rmsnorm_quant_1x128(x, gamma, eps, y=None, return_y=False, q=None, s=None, stream=None):
+    """RMSNorm of each row of x BF16 [M, H] with weight gamma BF16 [H], fused
+    with its 1x128 quantization.  Returns (q uint8 [M, H], s float32 [H/128, M]),
+    or (y, q, s) with the BF16 RMSNorm output y when return_y (or y given)."""
+    _rowmajor(x, "x")
+    if x.dtype != torch.bfloat16 or gamma.dtype != torch.bfloat16:
+        raise TypeError("x and gamma must be bfloat16")
+    if gamma.dim() != 1 or not gamma.is_contiguous():
+        raise ValueError("gamma must be a contiguous 1-D tensor")
+    M, H = x.shape
+    if gamma.numel() != H:
+        raise ValueError("gamma must have H elements")
+    if y is None and return_y:
+        y = _empty((M, H), torch.bfloat16, x)
+    if y is not None:
+        _rowmajor(y, "y")
+    q = _codes(q) if q is not None else _empty((M, H), torch.uint8, x)
+    s = s if s is not None else _empty((H // 128, M), torch.float32, x)
+    _rowmajor(q, "q")
+    _check("jet_rmsnorm_quant_1x128", _lib.jet_rmsnorm_quant_1x128(
+        _ptr(x), _ptr(gamma), M, H, x.stride(0), float(eps), _ptr(y), 0 if y is None else y.stride(0),
+        _ptr(q), q.stride(0), _ptr(s), _stream(stream)))
+    return (y, q, s) if y is not None else (q, s)
+
+
+def jet_swiglu_quant_1x128(gu, inter=None, h=None, return_h=False, q=None, s=None, stream=None):
+    """SwiGLU of the fused gate+up output gu BF16 [M, 2I] (gate = columns
+    0..I-1, up = I..2I-1), fused with its 1x128 quantization.  Returns
+    (q uint8 [M, I], s float32 [I/128, M]), or (h, q, s) with the BF16 h when
+    return_h (or h given)."""
+    _rowmajor(gu, "gu")
+    if gu.dtype != torch.bfloat16:
+        raise TypeError("gu must be bfloat16")
+    M = gu.shape[0]
+    I = gu.shape[1] // 2 if inter is None else int(inter)
+    if h is None and return_h:
+        h = _empty((M, I), torch.bfloat16, gu)
+    if h is not None:
+        _rowmajor(h, "h")
+    q = _codes(q) if q is not None else _empty((M, I), torch.uint8, gu)
+    s = s if s is not None else _empty((I // 128, M), torch.float32, gu)
+    _rowmajor(q, "q")
+    _check("jet_swiglu_quant_1x128", _lib.jet_swiglu_quant_1x128(
+        _ptr(gu), M, I, gu.stride(0), _ptr(h), 0 if h is None else h.stride(0), _ptr(q), q.stride(0),
+        _ptr(s), _stream(stream)))
+    return (h, q, s) if h is not None else (q, s)
 
 
 def jet_quant_act_128x1_T(src, src_s=None, qT=None, sT=None, stream=None):

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define JET_ABI_VERSION 3
+#define JET_ABI_VERSION 4
 
 typedef enum {
   JET_OK = 0,
@@ -99,6 +99,54 @@ int jet_quant_act_1x128(const void* x, int64_t M, int64_t K, int64_t ldx,
 int jet_quant_act_128x1_T(const void* src, int src_dtype, const float* src_s,
                           int64_t M, int64_t K, int64_t ldsrc,
                           uint8_t* qT, int64_t ldqT, float* sT, void* stream);
+
+/*
+ * Fused producer: RMSNorm + 1x128 quantization.  The input of the QKV and
+ * gate+up projections comes out of an RMSNorm; this call writes its 1x128 FP8
+ * codes and scales directly (explainer "Implementierung": fused RMSNorm
+ * kernels; "Quantisierungsschema" and 163.com write-up section 五: the
+ * quantization runs fused with the operator that produces the activation).
+ * Per row m (the pages give no formula; the Llama RMSNorm is taken):
+ *   r = 1 / sqrt(mean_k(x[m,k]^2) + eps)            (FP32)
+ *   y[m,k] = bf16((x[m,k] * r) * gamma[k])          (FP32 products, one RNE rounding)
+ * and q, s are the 1x128 quantization of y, bit for bit what
+ * jet_quant_act_1x128 gives for that BF16 y.
+ *
+ *   x     : BF16 [M, H], row stride ldx elements (ldx >= H, ldx % 8 == 0)
+ *   gamma : BF16 [H]
+ *   eps   : finite, >= 0
+ *   y     : optional BF16 [M, H] output (NULL: not written), row stride ldy
+ *   q     : E4M3 [M, H], row stride ldq bytes (ldq >= H, ldq % 16 == 0)
+ *   s     : FP32 [H/128, M]
+ *   0 < H <= 8192, H % 128 == 0, M >= 0; x, gamma, y, q 16-byte aligned.
+ *   The mean square is summed in FP32 (as in an FP32 RMSNorm): rows whose
+ *   squares overflow FP32 (|x| above about 1e19) give a zero scale r.
+ *   A row of x is read once; the results are independent of M and of the
+ *   other rows.  JET_ERR_SHAPE / NULL / ALIGN as for the quantizers.
+ */
+int jet_rmsnorm_quant_1x128(const void* x, const void* gamma, int64_t M, int64_t H,
+                            int64_t ldx, float eps, void* y, int64_t ldy,
+                            uint8_t* q, int64_t ldq, float* s, void* stream);
+
+/*
+ * Fused producer: SwiGLU + 1x128 quantization, the input of the down
+ * projection (explainer "Implementierung": fused activation kernels).  From
+ * the fused gate+up projection's output gu = [gate | up]:
+ *   h[m,i] = bf16(gate * sigmoid(gate) * up),  gate = gu[m,i], up = gu[m,I+i]
+ * (FP32: sigmoid(g) = 1/(1+e) for g >= 0 and e/(1+e) for g < 0 with
+ * e = expf(-|g|); one RNE rounding), and q, s are the 1x128 quantization of h,
+ * bit for bit what jet_quant_act_1x128 gives for that BF16 h.
+ *
+ *   gu : BF16 [M, 2I] (columns 0..I-1 gate, I..2I-1 up), row stride ldgu
+ *        elements (ldgu >= 2I, ldgu % 8 == 0)
+ *   h  : optional BF16 [M, I] output (NULL: not written), row stride ldh
+ *   q  : E4M3 [M, I], row stride ldq bytes (ldq >= I, ldq % 16 == 0)
+ *   s  : FP32 [I/128, M]
+ *   I % 128 == 0, M >= 0; gu, h, q 16-byte aligned.
+ */
+int jet_swiglu_quant_1x128(const void* gu, int64_t M, int64_t I, int64_t ldgu,
+                           void* h, int64_t ldh, uint8_t* q, int64_t ldq, float* s,
+                           void* stream);
 
 /*
  * Both activation groupings from one read of a BF16 activation or output

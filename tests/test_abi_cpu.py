@@ -48,7 +48,7 @@ def test_binding_covers_header(J):
 
 
 def test_version_and_status_strings(J):
-    assert J.jet_abi_version() == 3
+    assert J.jet_abi_version() == 4
     assert J.jet_status_string(J.JET_ERR_SHAPE) == "JET_ERR_SHAPE"
     assert J.jet_status_string(99) == "JET_ERR_UNKNOWN"
 
@@ -85,6 +85,38 @@ def test_quantizer_validation(J):
     assert Q2(None, 0, 128, 128, None, 128, None, None, 0, None, 0, None) == J.JET_OK    # empty: no-op
     assert L.jet_quant_weight_128x128(P16, 100, 128, 128, P16, P16, None, None) == J.JET_ERR_SHAPE
     assert L.jet_quant_weight_128x128(P16, 128, 128, 128, P16, P16, P17, None) == J.JET_ERR_ALIGN
+
+
+def test_fused_producer_validation(J):
+    L = J._lib
+    # RMSNorm + 1x128: shapes, eps, nulls, alignment -- all rejected before any launch
+    assert L.jet_rmsnorm_quant_1x128(P16, P16, 4, 100, 128, 1e-5, None, 0, P16, 128, P16, None) == J.JET_ERR_SHAPE
+    assert L.jet_rmsnorm_quant_1x128(P16, P16, 4, 8320, 8320, 1e-5, None, 0, P16, 8320, P16, None) == J.JET_ERR_SHAPE
+    assert L.jet_rmsnorm_quant_1x128(P16, P16, -1, 128, 128, 1e-5, None, 0, P16, 128, P16, None) == J.JET_ERR_SHAPE
+    assert L.jet_rmsnorm_quant_1x128(P16, P16, 4, 128, 128, -1.0, None, 0, P16, 128, P16, None) == J.JET_ERR_SHAPE
+    assert L.jet_rmsnorm_quant_1x128(P16, P16, 4, 128, 128, float("nan"), None, 0, P16, 128, P16, None) == J.JET_ERR_SHAPE
+    assert L.jet_rmsnorm_quant_1x128(P16, P16, 0, 128, 128, 1e-5, None, 0, None, 0, None, None) == J.JET_OK
+    assert L.jet_rmsnorm_quant_1x128(P16, None, 4, 128, 128, 1e-5, None, 0, P16, 128, P16, None) == J.JET_ERR_NULL
+    assert L.jet_rmsnorm_quant_1x128(P16, P16, 4, 256, 128, 1e-5, None, 0, P16, 256, P16, None) == J.JET_ERR_SHAPE
+    assert L.jet_rmsnorm_quant_1x128(P16, P16, 4, 128, 128, 1e-5, P16, 64, P16, 128, P16, None) == J.JET_ERR_SHAPE
+    assert L.jet_rmsnorm_quant_1x128(P17, P16, 4, 128, 128, 1e-5, None, 0, P16, 128, P16, None) == J.JET_ERR_ALIGN
+    assert L.jet_rmsnorm_quant_1x128(P16, P17, 4, 128, 128, 1e-5, None, 0, P16, 128, P16, None) == J.JET_ERR_ALIGN
+    assert L.jet_rmsnorm_quant_1x128(P16, P16, 4, 128, 128, 1e-5, P17, 128, P16, 128, P16, None) == J.JET_ERR_ALIGN
+    assert L.jet_rmsnorm_quant_1x128(P16, P16, 4, 128, 132, 1e-5, None, 0, P16, 128, P16, None) == J.JET_ERR_ALIGN
+    assert "rmsnorm" in J.jet_last_error()
+    # SwiGLU + 1x128
+    assert L.jet_swiglu_quant_1x128(P16, 4, 100, 256, None, 0, P16, 128, P16, None) == J.JET_ERR_SHAPE
+    assert L.jet_swiglu_quant_1x128(P16, 0, 128, 256, None, 0, None, 0, None, None) == J.JET_OK
+    assert L.jet_swiglu_quant_1x128(P16, 4, 0, 0, None, 0, None, 0, None, None) == J.JET_OK
+    assert L.jet_swiglu_quant_1x128(None, 4, 128, 256, None, 0, P16, 128, P16, None) == J.JET_ERR_NULL
+    assert L.jet_swiglu_quant_1x128(P16, 4, 128, 255, None, 0, P16, 128, P16, None) == J.JET_ERR_SHAPE
+    assert L.jet_swiglu_quant_1x128(P16, 4, 128, 256, P16, 64, P16, 128, P16, None) == J.JET_ERR_SHAPE
+    assert L.jet_swiglu_quant_1x128(P16, 4, 128, 256, None, 0, P16, 120, P16, None) == J.JET_ERR_SHAPE
+    assert L.jet_swiglu_quant_1x128(P17, 4, 128, 256, None, 0, P16, 128, P16, None) == J.JET_ERR_ALIGN
+    assert L.jet_swiglu_quant_1x128(P16, 4, 128, 260, None, 0, P16, 128, P16, None) == J.JET_ERR_ALIGN
+    assert L.jet_swiglu_quant_1x128(P16, 4, 128, 256, P17, 128, P16, 128, P16, None) == J.JET_ERR_ALIGN
+    assert L.jet_swiglu_quant_1x128(P16, 4, 128, 256, None, 0, P16, 136, P16, None) == J.JET_ERR_ALIGN
+    assert "swiglu" in J.jet_last_error()
 
 
 def test_gemm_validation(J):
