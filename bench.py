@@ -10,6 +10,8 @@ training batch of M = 8192 tokens (8 sequences x 1024):
 Inputs are seeded synthetic tensors resident in HBM before timing starts.
 `value` = GEMM FLOPs of the step (3 x 2*M*N*K per linear) / step time.
 
+`--workload fused` the fused producers of the linear inputs of one layer
+(RMSNorm + 1x128 twice, SwiGLU + 1x128 once) at M = 8192;
 `--workload decode` times the rollout forward of the same linears at M = 64;
 `--workload moe` the grouped (mixture-of-experts) layer of Qwen3-30B-A3B shape
 (hidden 2048, expert intermediate 768, 128 experts, top-8 of 8192 tokens with
@@ -53,10 +55,12 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="run 1 GiB device copies first (HBM counter calibration)")
     ap.add_argument("--events", type=int, default=1, help="per-kernel HIP events in the timed loop")
-    ap.add_argument("--workload", choices=("train", "decode", "moe"), default="train",
+    ap.add_argument("--workload", choices=("train", "decode", "moe", "fused"), default="train",
                     help="train: the M=8192 fwd+bwd step (the headline line); decode: the rollout "
                          "forward at M=64 over the same four linears; moe: the grouped expert "
-                         "layer (Qwen3-30B-A3B shapes) fwd+bwd")
+                         "layer (Qwen3-30B-A3B shapes) fwd+bwd; fused: the fused RMSNorm/SwiGLU "
+                         "producers of the 1x128 inputs of one Llama-8B layer")
+    ap.add_argument("--fused-m", type=int, default=8192, help="tokens for --workload fused")
     ap.add_argument("--quant", choices=("both", "separate"), default="both",
                     help="activation quantizers: one read for both groupings (default), or the "
                          "separate 1x128 and 128x1 kernels")
@@ -436,6 +440,133 @@ def decode_bench(args, torch, J):
     print(json.dumps(out), flush=True)
 
 
+FUSED_H, FUSED_I, FUSED_EPS = 4096, 14336, 1e-5
+
+
+def cpu_baseline_fused():
+    """The oracle (untuned) on a bounded sample of the fused workload: 2048
+    rows through RMSNorm + 1x128 (H=4096) and through SwiGLU + 1x128
+    (I=14336); scaled to GB/s of the sample's algorithmic bytes."""
+    from oracle import fused_producers as F
+    from fp8_blockwise_quantized_amd import inputs
+    rows = 2048
+    x = inputs.activations_with_outliers(rows, FUSED_H, seed=0)
+    g = inputs.normal_bf16((FUSED_H,), 0.1, seed=0, tensor_id=inputs.ID_W) + np.float32(1.0)
+    gu = inputs.normal_bf16((rows, 2 * FUSED_I), 1.3, seed=0, tensor_id=inputs.ID_X)
+    t0 = time.perf_counter()
+    F.rmsnorm_quant_1x128(x, g, FUSED_EPS)
+    F.swiglu_quant_1x128(gu, FUSED_I)
+    dt = time.perf_counter() - t0
+    nbytes = fused_bytes_rms(rows, FUSED_H) + fused_bytes_swiglu(rows, FUSED_I)
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"{rows} rows: RMSNorm+1x128 at H={FUSED_H} and SwiGLU+1x128 at I={FUSED_I} "
+                      f"(element-wise NumPy, one thread); host cpu_count={os.cpu_count()}"}
+
+
+def fused_bytes_rms(M, H):      # x and gamma in; codes and scales out
+    return M * H * 2 + H * 2 + M * H + M * H // 128 * 4
+
+
+def fused_bytes_swiglu(M, I):   # gate and up in; codes and scales out
+    return M * 2 * I * 2 + M * I + M * I // 128 * 4
+
+
+def fused_bench(args, torch, J):
+    """Fused producers of one Llama-3.1-8B layer's linear inputs at M tokens:
+    RMSNorm + 1x128 for the attention and MLP inputs (H=4096), SwiGLU + 1x128
+    for the down projection's input (I=14336).  value = algorithmic bytes /
+    time.  For context, the unfused sequence (torch's BF16 operator, then the
+    1x128 quantizer) is timed on the same inputs."""
+    from fp8_blockwise_quantized_amd import inputs
+    M, H, I = args.fused_m, FUSED_H, FUSED_I
+    bf = lambda a: torch.from_numpy(a).to(torch.bfloat16).cuda()
+    log(f"building the fused-producer inputs (M={M})")
+    xs = [bf(inputs.activations_with_outliers(M, H, seed=i)) for i in range(2)]
+    gs = [bf(inputs.normal_bf16((H,), 0.1, seed=i, tensor_id=inputs.ID_W) + np.float32(1.0)) for i in range(2)]
+    gu = bf(inputs.normal_bf16((M, 2 * I), 1.3, seed=0, tensor_id=inputs.ID_X))
+    e = lambda shape, dt: torch.empty(shape, dtype=dt, device="cuda")
+    qx = [e((M, H), torch.uint8) for _ in range(2)]
+    sx = [e((H // 128, M), torch.float32) for _ in range(2)]
+    qh, sh = e((M, I), torch.uint8), e((I // 128, M), torch.float32)
+    plan = [("rmsnorm_quant_1x128", fused_bytes_rms(M, H),
+             lambda i=i: J.jet_rmsnorm_quant_1x128(xs[i], gs[i], FUSED_EPS, q=qx[i], s=sx[i])) for i in range(2)]
+    plan.append(("swiglu_quant_1x128", fused_bytes_swiglu(M, I),
+                 lambda: J.jet_swiglu_quant_1x128(gu, q=qh, s=sh)))
+    yb, hb = e((M, H), torch.bfloat16), e((M, I), torch.bfloat16)
+    def unfused():
+        for i in range(2):
+            yb.copy_(torch.nn.functional.rms_norm(xs[i], (H,), weight=gs[i], eps=FUSED_EPS))
+            J.jet_quant_act_1x128(yb, q=qx[i], s=sx[i])
+        hb.copy_(torch.nn.functional.silu(gu[:, :I]) * gu[:, I:])
+        J.jet_quant_act_1x128(hb, q=qh, s=sh)
+    E = torch.cuda.Event
+    def step(evs=None):
+        for i, (_, _, fn) in enumerate(plan):
+            if evs is not None:
+                evs[i][0].record()
+            fn()
+            if evs is not None:
+                evs[i][1].record()
+    for _ in range(args.warmup):
+        step()
+        unfused()
+    torch.cuda.synchronize()
+    log(f"{args.warmup} warm-up steps, then {args.steps} timed steps")
+    per = [[[E(enable_timing=True), E(enable_timing=True)] for _ in plan] for _ in range(args.steps)]
+    t0, t1 = E(enable_timing=True), E(enable_timing=True)
+    t0.record()
+    for st in range(args.steps):
+        step(per[st] if args.events else None)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    u0, u1 = E(enable_timing=True), E(enable_timing=True)
+    u0.record()
+    for _ in range(args.steps):
+        unfused()
+    u1.record()
+    torch.cuda.synchronize()
+    ms_unfused = u0.elapsed_time(u1) / args.steps
+    total = sum(b for (_, b, _) in plan)
+    kernels = {}
+    if args.events:
+        for i, (kind, b, _) in enumerate(plan):
+            us = sum(per[st][i][0].elapsed_time(per[st][i][1]) for st in range(args.steps)) / args.steps * 1e3
+            k = kernels.setdefault(kind, {"avg_us": 0.0, "launches_per_step": 0, "bytes": 0})
+            k["avg_us"] += us
+            k["launches_per_step"] += 1
+            k["bytes"] += b
+        for k in kernels.values():
+            k["gbs"] = round(k["bytes"] / (k["avg_us"] * 1e-6) / 1e9, 1)
+            k["avg_us"] = round(k["avg_us"] / k["launches_per_step"], 2)
+            k["frac_hbm_peak"] = round(k["gbs"] / PEAK_HBM_GBS, 4)
+    dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches_per_step"]) if kernels else None
+    out = {
+        "metric": "Fused RMSNorm/SwiGLU + 1x128 FP8 producers GB/s, Llama-8B layer inputs",
+        "value": round(total / (ms * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"Llama-3.1-8B layer, M={M} tokens: RMSNorm+1x128 of the attention and "
+                               f"MLP inputs (H={H}), SwiGLU+1x128 of the down projection's input "
+                               f"(I={I}, from the fused gate+up output)", "M": M,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": None if dom is None else {
+            "bound": "hbm", "kernel": dom, "achieved": kernels[dom]["gbs"], "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(kernels[dom]["gbs"] / PEAK_HBM_GBS, 4), "traffic": None,
+            "bytes_per_launch": kernels[dom]["bytes"] // kernels[dom]["launches_per_step"]},
+        "kernels": kernels,
+        "unfused_context": {"ms_per_step": round(ms_unfused, 4),
+                            "what": "torch BF16 rms_norm / silu*mul, then jet_quant_act_1x128",
+                            "speedup_of_fused": round(ms_unfused / ms, 2)},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on its bounded sample")
+        out["cpu_baseline"] = cpu_baseline_fused()
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -450,6 +581,9 @@ def main():
 
     if args.workload == "decode":
         decode_bench(args, torch, J)
+        return
+    if args.workload == "fused":
+        fused_bench(args, torch, J)
         return
     if args.copy_probe:
         copy_probe(torch)

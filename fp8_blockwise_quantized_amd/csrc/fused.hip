@@ -14,10 +14,11 @@
 //    gu = [gate | up] (columns 0..I-1 and I..2I-1):
 //      h = bf16(gate * sigmoid(gate) * up), then the 1x128 quantization of h.
 //
-// The arithmetic is FP32 (IEEE division and square root, accurate expf) and
-// the BF16 tensor is rounded once; its 1x128 codes and scales are computed
-// exactly as jet_quant_act_1x128 would compute them from that BF16 tensor, and
-// the BF16 tensor itself is written too when the caller asks for it.
+// The arithmetic is FP32 (RMSNorm: IEEE division and square root; SwiGLU: the
+// hardware exp2 and reciprocal, see swiglu1) and the BF16 tensor is rounded
+// once; its 1x128 codes and scales are computed exactly as
+// jet_quant_act_1x128 would compute them from that BF16 tensor, and the BF16
+// tensor itself is written too when the caller asks for it.
 #include <algorithm>
 
 #include "jet_device.hpp"
@@ -61,18 +62,20 @@ __device__ __forceinline__ Codes8 quant_row16(const uint32_t w[4]) {
 // RMSNorm + 1x128.  One wavefront per row; lane l holds columns 512c + 8l ..
 // +7 of every 512-column chunk c (16-byte loads, each instruction a whole
 // 1 KiB of the row), so the 16 lanes of a DPP row hold one 128-column group.
-// A 256-thread block takes kRmsRowsPerBlock consecutive rows (each wavefront
-// kRmsRowsPerBlock/4 of them); the block's scales are staged in LDS and
-// written as runs of consecutive rows per group.
+// The row and gamma are loaded together (one memory latency per row).  A
+// block of kRmsRowsPerBlock wavefronts takes as many consecutive rows; its
+// scales are staged in LDS and written as runs of consecutive rows per group.
 // ---------------------------------------------------------------------------
 constexpr int kRmsMaxChunks = 16;                  // H <= 8192
-constexpr int kRmsRowsPerBlock = 8;
+constexpr int kRmsRowsPerBlock = 8;                // = wavefronts per block
 
-__global__ __launch_bounds__(256) void k_rmsnorm_quant_1x128(
+// CH: 512-column chunks held in registers (H <= 512*CH)
+template <int CH>
+__global__ __launch_bounds__(64 * kRmsRowsPerBlock) void k_rmsnorm_quant_1x128(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma, int64_t M, int64_t H,
     int64_t ldx, float eps, uint16_t* __restrict__ y, int64_t ldy, uint8_t* __restrict__ q,
     int64_t ldq, float* __restrict__ s) {
-  __shared__ float stg[kRmsMaxChunks * 4][kRmsRowsPerBlock];
+  __shared__ float stg[CH * 4][kRmsRowsPerBlock];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nb = (int)gridDim.x, b = (int)blockIdx.x;
   // consecutive blocks on one XCD (blocks are dealt round-robin to the 8 XCDs),
@@ -83,20 +86,24 @@ __global__ __launch_bounds__(256) void k_rmsnorm_quant_1x128(
   const int G = (int)(H / kGroup);
   const float inv_h = 1.0f / (float)H;
 
-  for (int rr = wave; rr < kRmsRowsPerBlock; rr += 4) {
-    const int64_t m = m0 + rr;
-    if (m >= M) break;
+  const int rr = wave;
+  const int64_t m = m0 + rr;
+  if (m < M) {
     const uint16_t* xr = x + m * ldx;
-    uint4 v[kRmsMaxChunks];
+    uint4 v[CH], gv[CH];
 #pragma unroll
-    for (int c = 0; c < kRmsMaxChunks; ++c) {
+    for (int c = 0; c < CH; ++c) {
       v[c] = make_uint4(0u, 0u, 0u, 0u);
+      gv[c] = v[c];
       const int64_t col = 512 * c + 8 * lane;
-      if (c < chunks && col < H) v[c] = load_stream16(xr + col);
+      if (c < chunks && col < H) {
+        v[c] = load_stream16(xr + col);
+        gv[c] = *reinterpret_cast<const uint4*>(gamma + col);
+      }
     }
     float ss = 0.0f;
 #pragma unroll
-    for (int c = 0; c < kRmsMaxChunks; ++c) {
+    for (int c = 0; c < CH; ++c) {
       const uint32_t w[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -108,14 +115,12 @@ __global__ __launch_bounds__(256) void k_rmsnorm_quant_1x128(
     const float ms = wave_sum(ss) * inv_h;
     const float r = 1.0f / sqrtf(ms + eps);
 #pragma unroll
-    for (int c = 0; c < kRmsMaxChunks; ++c) {
-      if (c >= chunks) break;
+    for (int c = 0; c < CH; ++c) {
+      if (c >= chunks) continue;                   // uniform; keeps the loop fully unrolled
       const int64_t col = 512 * c + 8 * lane;
       const bool ok = col < H;                     // uniform per DPP row (H % 128 == 0)
-      uint4 gv = make_uint4(0u, 0u, 0u, 0u);
-      if (ok) gv = *reinterpret_cast<const uint4*>(gamma + col);
       const uint32_t xw[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
-      const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+      const uint32_t gw[4] = {gv[c].x, gv[c].y, gv[c].z, gv[c].w};
       uint32_t yw[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -133,10 +138,10 @@ __global__ __launch_bounds__(256) void k_rmsnorm_quant_1x128(
   }
   __syncthreads();
   // scales: group j of rows m0 .. m0 + kRmsRowsPerBlock - 1 at s[j*M + m]
-  for (int i = threadIdx.x; i < G * kRmsRowsPerBlock; i += 256) {
-    const int j = i / kRmsRowsPerBlock, rr = i % kRmsRowsPerBlock;
-    const int64_t m = m0 + rr;
-    if (m < M) s[(int64_t)j * M + m] = stg[j][rr];
+  for (int i = threadIdx.x; i < G * kRmsRowsPerBlock; i += 64 * kRmsRowsPerBlock) {
+    const int j = i / kRmsRowsPerBlock, r2 = i % kRmsRowsPerBlock;
+    const int64_t m2 = m0 + r2;
+    if (m2 < M) s[(int64_t)j * M + m2] = stg[j][r2];
   }
 }
 
@@ -147,8 +152,14 @@ hipError_t launch_rmsnorm_quant_1x128(const uint16_t* x, const uint16_t* gamma, 
   if (H <= 0 || H % kGroup || H > 512 * kRmsMaxChunks) return hipErrorInvalidValue;
   const int64_t blocks = (M + kRmsRowsPerBlock - 1) / kRmsRowsPerBlock;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_rmsnorm_quant_1x128, dim3((unsigned)blocks), dim3(256), 0, st, x, gamma, M, H,
-                     ldx, eps, y, ldy, q, ldq, s);
+  const dim3 grid((unsigned)blocks), block(64 * kRmsRowsPerBlock);
+  if (H <= 2048)
+    hipLaunchKernelGGL(k_rmsnorm_quant_1x128<4>, grid, block, 0, st, x, gamma, M, H, ldx, eps, y, ldy, q, ldq, s);
+  else if (H <= 4096)
+    hipLaunchKernelGGL(k_rmsnorm_quant_1x128<8>, grid, block, 0, st, x, gamma, M, H, ldx, eps, y, ldy, q, ldq, s);
+  else
+    hipLaunchKernelGGL(k_rmsnorm_quant_1x128<16>, grid, block, 0, st, x, gamma, M, H, ldx, eps, y, ldy, q, ldq,
+                       s);
   return hipGetLastError();
 }
 
@@ -158,11 +169,17 @@ hipError_t launch_rmsnorm_quant_1x128(const uint16_t* x, const uint16_t* gamma, 
 // DPP rows of a wavefront take 4 rows of one group, each lane 8 columns of
 // gate and the same 8 columns of up (all loads issued before any compute).
 // sigmoid(g) = 1/(1 + e) for g >= 0 and e/(1 + e) for g < 0 with
-// e = exp(-|g|), which never overflows.
+// e = exp(-|g|), which never overflows.  exp(-|g|) = 2^(-|g| * log2(e)) on the
+// hardware base-2 exponential and 1/(1 + e) on the hardware reciprocal (each
+// within about 1 ulp): the element stays within a few 2^-24 relative of the
+// exact value for the gate values that matter (|g| up to a few tens), far
+// inside half a BF16 step, at a fraction of the instructions of a libm exp and
+// an IEEE division (this kernel is otherwise bound by VALU issue).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float swiglu1(float g, float u) {
-  const float e = expf(-fabsf(g));
-  const float inv = 1.0f / (1.0f + e);
+  constexpr float kLog2e = 1.4426950408889634f;
+  const float e = __builtin_amdgcn_exp2f(-fabsf(g) * kLog2e);
+  const float inv = __builtin_amdgcn_rcpf(1.0f + e);
   const float sg = g >= 0.0f ? inv : e * inv;
   return (g * sg) * u;
 }

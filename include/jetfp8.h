@@ -134,8 +134,10 @@ int jet_rmsnorm_quant_1x128(const void* x, const void* gamma, int64_t M, int64_t
  * the fused gate+up projection's output gu = [gate | up]:
  *   h[m,i] = bf16(gate * sigmoid(gate) * up),  gate = gu[m,i], up = gu[m,I+i]
  * (FP32: sigmoid(g) = 1/(1+e) for g >= 0 and e/(1+e) for g < 0 with
- * e = expf(-|g|); one RNE rounding), and q, s are the 1x128 quantization of h,
- * bit for bit what jet_quant_act_1x128 gives for that BF16 h.
+ * e = 2^(-|g| log2(e)) on the hardware exp2 and 1/(1+e) on the hardware
+ * reciprocal, each within about 1 ulp; one RNE rounding), and q, s are the
+ * 1x128 quantization of h, bit for bit what jet_quant_act_1x128 gives for
+ * that BF16 h.
  *
  *   gu : BF16 [M, 2I] (columns 0..I-1 gate, I..2I-1 up), row stride ldgu
  *        elements (ldgu >= 2I, ldgu % 8 == 0)

@@ -15,15 +15,15 @@ every quantization can run fused with the computation before it.
 The pages name the operators but give no formula, so the plainest readings,
 those of the Llama decoder the pages' models use, are taken:
 
-R8  RMSNorm of one token's hidden vector x (length H) with weight gamma:
+R12 RMSNorm of one token's hidden vector x (length H) with weight gamma:
     y = x / sqrt(mean(x^2) + eps) * gamma, computed exactly (float64) and
     rounded once: BF16 round-to-nearest-even of the FP32 rounding (the same
     output convention as the GEMMs, reading R6 of jet_oracle).
-R9  The gated activation of the MLP (SwiGLU): the fused gate+up projection
+R13 The gated activation of the MLP (SwiGLU): the fused gate+up projection
     gives [M, 2I]; gate = columns 0..I-1, up = columns I..2I-1;
     h = silu(gate) * up with silu(g) = g / (1 + exp(-g)), computed exactly
-    and rounded once as in R8.
-R10 The fused producer's FP8 output is the 1x128 quantization (jet_oracle
+    and rounded once as in R12.
+R14 The fused producer's FP8 output is the 1x128 quantization (jet_oracle
     steps 3-5) of that BF16 tensor: fusing changes where the quantization
     runs, not what it computes.
 """
@@ -35,7 +35,7 @@ from oracle.jet_oracle import bf16_rne, fl32, quant_1x128
 
 
 def rmsnorm_bf16(x, gamma, eps: float) -> np.ndarray:
-    """R8: BF16 RMSNorm of each row of x [M, H] (float32 holding BF16 values)
+    """R12: BF16 RMSNorm of each row of x [M, H] (float32 holding BF16 values)
     with weight gamma [H]; float32 holding BF16 values out."""
     x64 = np.asarray(x, dtype=np.float64)
     g64 = np.asarray(gamma, dtype=np.float64)
@@ -52,7 +52,7 @@ def silu(g) -> np.ndarray:
 
 
 def swiglu_bf16(gu, inter: int) -> np.ndarray:
-    """R9: BF16 h = silu(gate) * up from the fused gate+up output gu [M, 2*inter]."""
+    """R13: BF16 h = silu(gate) * up from the fused gate+up output gu [M, 2*inter]."""
     gu64 = np.asarray(gu, dtype=np.float64)
     if gu64.shape[1] < 2 * inter:
         raise ValueError("gu must hold gate and up: at least 2*inter columns")
@@ -61,14 +61,14 @@ def swiglu_bf16(gu, inter: int) -> np.ndarray:
 
 
 def rmsnorm_quant_1x128(x, gamma, eps: float):
-    """R8 + R10: (BF16 y, codes [M, H], scales [H/128, M])."""
+    """R12 + R14: (BF16 y, codes [M, H], scales [H/128, M])."""
     y = rmsnorm_bf16(x, gamma, eps)
     q, s = quant_1x128(y)
     return y, q, s
 
 
 def swiglu_quant_1x128(gu, inter: int):
-    """R9 + R10: (BF16 h, codes [M, inter], scales [inter/128, M])."""
+    """R13 + R14: (BF16 h, codes [M, inter], scales [inter/128, M])."""
     h = swiglu_bf16(gu, inter)
     q, s = quant_1x128(h)
     return h, q, s

@@ -6,12 +6,15 @@ The bar:
     GPU's own BF16 output (both sides take the rounding decisions on the same
     BF16 values);
   * the BF16 output: within one BF16 spacing of the oracle's float64 value
-    rounded to BF16 (elementwise).  The kernels compute in FP32 (IEEE divide
-    and square root, an accurate exp, a 64-term per-lane sum then a butterfly
-    for the mean square), which stays within a few 2^-24 relative of the exact
-    value; BF16 keeps 8 bits, so the two roundings can differ only where the
-    exact value lies that close to a BF16 midpoint, and then by one step.
-    Results below the FP32 normal range are allowed an absolute 2^-126.
+    rounded to BF16 (elementwise).  The kernels compute in FP32 (RMSNorm: IEEE
+    divide and square root, a 64-term per-lane sum then a butterfly for the
+    mean square; SwiGLU: the hardware exp2 of -|g|*log2(e) and the hardware
+    reciprocal, each within about 1 ulp), which stays within a few 2^-24
+    relative of the exact value for the values that occur (the exp2 argument's
+    rounding adds |g|*2^-24); BF16 keeps 8 bits, so the two roundings can
+    differ only where the exact value lies that close to a BF16 midpoint, and
+    then by one step.  Results below the FP32 normal range are allowed an
+    absolute 2^-126.
 """
 import numpy as np
 import pytest

@@ -1,4 +1,4 @@
-"""Pins of the fused-producer oracle (RMSNorm and SwiGLU, readings R8-R10 of
+"""Pins of the fused-producer oracle (RMSNorm and SwiGLU, readings R12-R14 of
 oracle/fused_producers.py) against things other than itself: hand-worked
 values, closed forms and invariants, and torch's own rms_norm and silu in
 float64.  CPU only.
