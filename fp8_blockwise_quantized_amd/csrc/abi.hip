@@ -28,6 +28,9 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 constexpr int64_t kG = 128;
 constexpr int64_t kMaxDim = int64_t(1) << 30;   // GEMM tile indices are 32-bit
+// Row stride (bytes) of an FP8 GEMM operand: the kernels address a tile's rows
+// with 32-bit offsets from a 64-bit per-tile base, at most 256 rows apart.
+constexpr int64_t kMaxLd = int64_t(1) << 24;
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
@@ -189,6 +192,8 @@ static int check_gemm_common(const char* name, int64_t M, int64_t N, int64_t K, 
   if (M < 0 || N < 0 || K < 0 || N % kG || K % kG || M > kMaxDim || N > kMaxDim || K > kMaxDim)
     return fail(JET_ERR_SHAPE, "%s: need M >= 0, N and K multiples of 128 (M=%lld N=%lld K=%lld)",
                 name, (long long)M, (long long)N, (long long)K);
+  if (N > kMaxLd || K > kMaxLd)
+    return fail(JET_ERR_SHAPE, "%s: N and K must be <= 2^24 (FP8 operand row strides)", name);
   if (ws_bytes < need || (need && !workspace))
     return fail(JET_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", name, need);
   if (need && !aligned(workspace, 16))
@@ -268,6 +273,8 @@ int jet_fp8_linear_wgrad(const uint8_t* dyqT, const float* dysT, const uint8_t* 
   if (!dw) return fail(JET_ERR_NULL, "fp8_linear_wgrad: null pointer");
   if (M > 0 && (!dyqT || !dysT || !xqT || !xsT)) return fail(JET_ERR_NULL, "fp8_linear_wgrad: null pointer");
   const int64_t Mp = (M + kG - 1) / kG * kG;
+  if (Mp > kMaxLd)
+    return fail(JET_ERR_SHAPE, "fp8_linear_wgrad: M must be <= 2^24 (row stride of the transposed operands)");
   if (!aligned(dw, 16) || (M > 0 && (!aligned(dyqT, 16) || !aligned(xqT, 16) || !aligned(dysT, 4) ||
                                      !aligned(xsT, 4))))
     return fail(JET_ERR_ALIGN, "fp8_linear_wgrad: operands and output need 16-byte alignment");
@@ -365,7 +372,7 @@ int jet_fp8_grouped_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* w
   if (dx_dtype != JET_BF16 && dx_dtype != JET_F32)
     return fail(JET_ERR_DTYPE, "fp8_grouped_dgrad: dx_dtype must be JET_BF16 or JET_F32");
   if (M == 0 || K == 0) return JET_OK;
-  if (E * N > kMaxDim) return fail(JET_ERR_SHAPE, "fp8_grouped_dgrad: E*N must be <= 2^30");
+  if (E * N > kMaxLd) return fail(JET_ERR_SHAPE, "fp8_grouped_dgrad: E*N must be <= 2^24 (row stride of wqT)");
   if (!dyq || !dys || !wqT || !ws || !dx) return fail(JET_ERR_NULL, "fp8_grouped_dgrad: null pointer");
   if (!aligned(dyq, 16) || !aligned(wqT, 16) || !aligned(dx, 16) || !aligned(dys, 4) || !aligned(ws, 4))
     return fail(JET_ERR_ALIGN, "fp8_grouped_dgrad: operands and output need 16-byte alignment");
@@ -398,8 +405,8 @@ int jet_fp8_grouped_wgrad(const uint8_t* dyqT, const float* dysT, const uint8_t*
   if (!dw) return fail(JET_ERR_NULL, "fp8_grouped_wgrad: null pointer");
   if (M > 0 && (!dyqT || !dysT || !xqT || !xsT))
     return fail(JET_ERR_NULL, "fp8_grouped_wgrad: null pointer");
-  if (ldT < grouped_cols(M, E) || ldT > kMaxDim || ldT % 16)
-    return fail(JET_ERR_SHAPE, "fp8_grouped_wgrad: need 128*(ceil(M/128)+E) <= ldT <= 2^30, ldT %% 16");
+  if (ldT < grouped_cols(M, E) || ldT > kMaxLd || ldT % 16)
+    return fail(JET_ERR_SHAPE, "fp8_grouped_wgrad: need 128*(ceil(M/128)+E) <= ldT <= 2^24, ldT %% 16");
   if (!aligned(dw, 16) || (M > 0 && (!aligned(dyqT, 16) || !aligned(xqT, 16) || !aligned(dysT, 4) ||
                                      !aligned(xsT, 4))))
     return fail(JET_ERR_ALIGN, "fp8_grouped_wgrad: operands and output need 16-byte alignment");

@@ -279,6 +279,13 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
   const int m0 = tm * BM, n0 = tn * BN;
   const int KB = p.Kc / 128;
   const uint32_t lds0 = lds_addr(lds);
+  // 64-bit bases at the tile's first row of A and of B (and, for ROWBLOCK, its
+  // first weight-block scale row): the 32-bit per-lane DMA offsets then stay
+  // below 256 rows times the row stride (< 2^32 for strides up to 2^24 bytes,
+  // the limit the entry points check), whatever the operand's size.
+  p.A += (int64_t)m0 * p.lda;
+  p.B += (int64_t)n0 * p.ldb;
+  if (MODE == kRowBlock) p.sB += (int64_t)(n0 / 128) * p.sB_o;
 
   // ---- the wave's share of every stage ----
   // Wave (wm, wn) DMAs the OA 16-row A slabs wn*OA .. wn*OA+OA-1 of its wave
@@ -292,13 +299,13 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
   for (int t = 0; t < CFG::ABLK; ++t) {
     int row; uint32_t col;
     dma_src<FRAG>(gA0 + t, lane, row, col);
-    offA[t] = (uint32_t)min(m0 + row, p.M - 1) * (uint32_t)p.lda + col;
+    offA[t] = (uint32_t)min(row, p.M - 1 - m0) * (uint32_t)p.lda + col;
   }
 #pragma unroll
   for (int t = 0; t < CFG::BBLK; ++t) {
     int row; uint32_t col;
     dma_src<FRAG>(gB0 + t, lane, row, col);
-    offB[t] = (uint32_t)min(n0 + row, p.N - 1) * (uint32_t)p.ldb + col;
+    offB[t] = (uint32_t)min(row, p.N - 1 - n0) * (uint32_t)p.ldb + col;
   }
   // Scales of the stage, shared by the workgroup (the barrier at the top of a
   // step covers them).  Rows: the region of wave row wm holds its TM*16 rows
@@ -324,8 +331,9 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
     if (MODE == kRowCol) {
       offS = (uint32_t)min(n0 + 64 * c_ + lane, p.N - 1) * 4u;
     } else {
-      // lanes 0..BN/128-1 the tile's blocks; the rest repeat the last one
-      const int blk = min(n0 / 128 + min(lane, CFG::BN / 128 - 1), p.N / 128 - 1);
+      // lanes 0..BN/128-1 the tile's blocks (relative to its first); the rest
+      // repeat the last one
+      const int blk = min(min(lane, CFG::BN / 128 - 1), p.N / 128 - 1 - n0 / 128);
       offS = (uint32_t)blk * (uint32_t)p.sB_o * 4u;
     }
     sdst = (uint32_t)(CFG::ATILE + CFG::BTILE + CFG::BM * 4 + 256 * c_);
@@ -675,6 +683,10 @@ __global__ __launch_bounds__(256) void k_gemm_fp8_skinny(GemmArgs p, float* __re
   const int kb0 = (int)((int64_t)KB * sidx / splits), kb1 = (int)((int64_t)KB * (sidx + 1) / splits);
   const int nsteps = kb1 - kb0;
   const uint32_t lds0 = lds_addr(lds);
+  // 64-bit bases at the block's first weight row and weight-block scale row
+  // (32-bit per-lane offsets: at most 128 rows times the row stride)
+  p.B += (int64_t)n0 * p.ldb;
+  p.sB += (int64_t)(n0 / 128) * p.sB_o;
 
   // this wavefront's DMA blocks: global blocks wave*BPW .. ; X blocks first, then W
   uint32_t off[C::BPW], dst[C::BPW];
@@ -690,7 +702,7 @@ __global__ __launch_bounds__(256) void k_gemm_fp8_skinny(GemmArgs p, float* __re
       isx[t] = true;
     } else {
       dma_src<false>(gb - C::XBLK, lane, row, col);
-      off[t] = (uint32_t)(n0 + row) * (uint32_t)p.ldb + col;
+      off[t] = (uint32_t)row * (uint32_t)p.ldb + col;
       dst[t] = (uint32_t)(C::XT + (gb - C::XBLK) * 1024);
       isx[t] = false;
     }
@@ -701,7 +713,7 @@ __global__ __launch_bounds__(256) void k_gemm_fp8_skinny(GemmArgs p, float* __re
     const int row = (4 * wave + (lane & 3)) * 16 + (lane >> 2);
     soff = (uint32_t)min(row, p.M - 1) * 4u;
   } else {
-    soff = (uint32_t)(n0 / 128) * (uint32_t)p.sB_o * 4u;
+    soff = 0u;
   }
   const uint32_t sdst = (uint32_t)(C::XT + C::WT + 256 * wave);
 

@@ -213,7 +213,8 @@ int jet_quant_weight_128x128(const void* w, int64_t N, int64_t K, int64_t ldw,
  *        large-M kernel (the FP32 summation order differs).  Its contents on
  *        entry are ignored and unspecified on return.  The caller owns the
  *        workspace; calls that share one workspace must not overlap.
- *   M >= 0, N % 128 == 0, K % 128 == 0, all pointers 16-byte aligned.
+ *   M >= 0, N % 128 == 0, K % 128 == 0, N and K <= 2^24 (row strides of the
+ *   FP8 operands), all pointers 16-byte aligned.
  */
 int jet_fp8_linear_fwd(const uint8_t* xq, const float* xs,
                        const uint8_t* wq, const float* ws,
@@ -231,7 +232,8 @@ int jet_fp8_linear_fwd(const uint8_t* xq, const float* xs,
  *         jet_quant_weight_128x128 (its qT output); ws : FP32 [N/128, K/128]
  *         (the same block scales as the forward).
  *   dx  : [M, K] dense, dx_dtype JET_BF16 or JET_F32
- *   M >= 0, N % 128 == 0, K % 128 == 0, all pointers 16-byte aligned.
+ *   M >= 0, N % 128 == 0, K % 128 == 0, N and K <= 2^24, all pointers
+ *   16-byte aligned.
  */
 int jet_fp8_linear_dgrad(const uint8_t* dyq, const float* dys,
                          const uint8_t* wqT, const float* ws,
@@ -250,7 +252,8 @@ int jet_fp8_linear_dgrad(const uint8_t* dyq, const float* dys,
  *          (both as written by jet_quant_act_128x1_T; padding columns hold zeros)
  *   dw   : [N, K] dense, dw_dtype JET_F32 or JET_BF16; accumulate != 0 adds
  *          to the existing contents (JET_F32 only).
- *   M >= 0, N % 128 == 0, K % 128 == 0, all pointers 16-byte aligned.
+ *   M >= 0, N % 128 == 0, K % 128 == 0; M, N and K <= 2^24 (M sets the row
+ *   stride of the transposed operands), all pointers 16-byte aligned.
  */
 int jet_fp8_linear_wgrad(const uint8_t* dyqT, const float* dysT,
                          const uint8_t* xqT, const float* xsT,
@@ -316,7 +319,7 @@ int jet_fp8_grouped_fwd(const uint8_t* xq, const float* xs,
  *   dyq, dys : as jet_fp8_linear_dgrad over all M rows.
  *   wqT : E4M3 [K, E*N] dense -- the transposed codes jet_quant_weight_128x128
  *         writes for the stacked weights [E*N, K] (expert e: columns e*N..e*N+N-1);
- *   ws  : FP32 [E, N/128, K/128].  E*N <= 2^30.
+ *   ws  : FP32 [E, N/128, K/128].  E*N <= 2^24.
  *   dx  : [M, K] dense, dx_dtype JET_BF16 or JET_F32.
  */
 int jet_fp8_grouped_dgrad(const uint8_t* dyq, const float* dys,
@@ -330,7 +333,7 @@ int jet_fp8_grouped_dgrad(const uint8_t* dyq, const float* dys,
  * dW_e (+)= dYhat_e^T . Xhat_e for every expert (an empty segment gives 0).
  *   dyqT : E4M3 [N, ldT], dysT : FP32 [ldT/128, N]   (jet_quant_act_128x1_T_grouped of dY)
  *   xqT  : E4M3 [K, ldT], xsT  : FP32 [ldT/128, K]   (of the 1x128-quantized X)
- *   ldT >= P, ldT % 16 == 0, ldT <= 2^30.
+ *   ldT >= P, ldT % 16 == 0, ldT <= 2^24.
  *   dw : [E, N, K] dense, dw_dtype JET_F32 or JET_BF16; accumulate as jet_fp8_linear_wgrad.
  */
 int jet_fp8_grouped_wgrad(const uint8_t* dyqT, const float* dysT,

@@ -87,6 +87,18 @@ def test_quantizer_validation(J):
     assert L.jet_quant_weight_128x128(P16, 128, 128, 128, P16, P16, P17, None) == J.JET_ERR_ALIGN
 
 
+def test_gemm_operand_stride_limit(J):
+    """The GEMM kernels address a tile's rows with 32-bit offsets from a 64-bit
+    per-tile base: every FP8 operand row stride must stay <= 2^24 bytes."""
+    L = J._lib
+    a = (P16, P16, P16, P16)
+    big = (1 << 24) + 128
+    assert L.jet_fp8_linear_fwd(*a, 256, 128, big, P16, J.JET_BF16, None, None, None, 0, None) == J.JET_ERR_SHAPE
+    assert L.jet_fp8_linear_dgrad(*a, 256, big, 128, P16, J.JET_BF16, None, 0, None) == J.JET_ERR_SHAPE
+    assert L.jet_fp8_linear_wgrad(*a, big, 128, 128, P16, J.JET_F32, 0, None, 0, None) == J.JET_ERR_SHAPE
+    assert "2^24" in J.jet_last_error()
+
+
 def test_fused_producer_validation(J):
     L = J._lib
     # RMSNorm + 1x128: shapes, eps, nulls, alignment -- all rejected before any launch
