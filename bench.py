@@ -61,6 +61,8 @@ def parse():
                          "layer (Qwen3-30B-A3B shapes) fwd+bwd; fused: the fused RMSNorm/SwiGLU "
                          "producers of the 1x128 inputs of one Llama-8B layer")
     ap.add_argument("--fused-m", type=int, default=8192, help="tokens for --workload fused")
+    ap.add_argument("--invariant", action="store_true",
+                    help="decode: the batch-invariant forward (one K range, bit-identical to training)")
     ap.add_argument("--quant", choices=("both", "separate"), default="both",
                     help="activation quantizers: one read for both groupings (default), or the "
                          "separate 1x128 and 128x1 kernels")
@@ -383,9 +385,13 @@ def decode_bench(args, torch, J):
             ys = torch.empty(N // 128, M, dtype=torch.float32, device="cuda")
             wsp = torch.empty(max(J.jet_workspace_bytes(J.JET_OP_FWD, M, N, K), 16), dtype=torch.uint8,
                               device="cuda")
-            layer.append((name, N, K, lambda xq=xq, xs=xs, wq=wq, ws=ws, y=y, yq=yq, ys=ys, wsp=wsp:
-                          J.jet_fp8_linear_fwd(xq, xs, wq, ws, y=y, fuse_quant=True, yq=yq, ys=ys,
-                                               workspace=wsp)))
+            if args.invariant:
+                fn = (lambda xq=xq, xs=xs, wq=wq, ws=ws, y=y, yq=yq, ys=ys:
+                      J.jet_fp8_linear_fwd_batch_invariant(xq, xs, wq, ws, y=y, fuse_quant=True, yq=yq, ys=ys))
+            else:
+                fn = (lambda xq=xq, xs=xs, wq=wq, ws=ws, y=y, yq=yq, ys=ys, wsp=wsp:
+                      J.jet_fp8_linear_fwd(xq, xs, wq, ws, y=y, fuse_quant=True, yq=yq, ys=ys, workspace=wsp))
+            layer.append((name, N, K, fn))
         copies.append(layer)
     torch.cuda.synchronize()
     E = torch.cuda.Event
@@ -430,7 +436,8 @@ def decode_bench(args, torch, J):
         "data": "synthetic",
         "config": {"workload": "Llama-3.1-8B decoder linears (QKV, O, gate+up, down) at rollout decode "
                                "batch M=64, forward with the fused 1x128 output, weights cycled over "
-                               f"{DECODE_COPIES} copies", "M": M, "parallelism": "none (1 GPU)"},
+                               f"{DECODE_COPIES} copies", "M": M, "parallelism": "none (1 GPU)",
+                   "forward": "batch-invariant (one K range)" if args.invariant else "split-K"},
         "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
         "roofline": None if dom is None else {
             "bound": "hbm", "kernel": dom, "achieved": kernels[dom]["weight_gbs"], "peak": PEAK_HBM_GBS,

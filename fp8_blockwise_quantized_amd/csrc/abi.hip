@@ -201,24 +201,25 @@ static int check_gemm_common(const char* name, int64_t M, int64_t N, int64_t K, 
   return JET_OK;
 }
 
-int jet_fp8_linear_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
-                       int64_t M, int64_t N, int64_t K, void* y, int y_dtype, uint8_t* yq, float* ys,
-                       void* workspace, size_t ws_bytes, void* stream) {
+// The forward; invariant: one K range at every M (no workspace), so each
+// output element does not depend on M.
+static int linear_fwd(const char* name, const uint8_t* xq, const float* xs, const uint8_t* wq,
+                      const float* ws, int64_t M, int64_t N, int64_t K, void* y, int y_dtype, uint8_t* yq,
+                      float* ys, void* workspace, size_t ws_bytes, void* stream, bool invariant) {
   g_last_error[0] = 0;
-  if (int st = check_gemm_common("fp8_linear_fwd", M, N, K, jet_workspace_bytes(JET_OP_FWD, M, N, K),
-                                 ws_bytes, workspace))
-    return st;
+  const size_t need = invariant ? 0 : jet_workspace_bytes(JET_OP_FWD, M, N, K);
+  if (int st = check_gemm_common(name, M, N, K, need, ws_bytes, workspace)) return st;
   if (y_dtype != JET_BF16 && y_dtype != JET_F32)
-    return fail(JET_ERR_DTYPE, "fp8_linear_fwd: y_dtype must be JET_BF16 or JET_F32");
+    return fail(JET_ERR_DTYPE, "%s: y_dtype must be JET_BF16 or JET_F32", name);
   const bool fuse = yq || ys;
-  if (fuse && (!yq || !ys)) return fail(JET_ERR_NULL, "fp8_linear_fwd: yq and ys go together");
+  if (fuse && (!yq || !ys)) return fail(JET_ERR_NULL, "%s: yq and ys go together", name);
   if (fuse && y_dtype != JET_BF16)
-    return fail(JET_ERR_DTYPE, "fp8_linear_fwd: the fused 1x128 output needs y_dtype JET_BF16");
+    return fail(JET_ERR_DTYPE, "%s: the fused 1x128 output needs y_dtype JET_BF16", name);
   if (M == 0 || N == 0) return JET_OK;
-  if (!xq || !xs || !wq || !ws || !y) return fail(JET_ERR_NULL, "fp8_linear_fwd: null pointer");
+  if (!xq || !xs || !wq || !ws || !y) return fail(JET_ERR_NULL, "%s: null pointer", name);
   if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(y, 16) || !aligned(xs, 4) || !aligned(ws, 4) ||
       (fuse && (!aligned(yq, 16) || !aligned(ys, 4))))
-    return fail(JET_ERR_ALIGN, "fp8_linear_fwd: operands and outputs need 16-byte alignment");
+    return fail(JET_ERR_ALIGN, "%s: operands and outputs need 16-byte alignment", name);
   jet::GemmArgs a{};
   a.A = xq; a.lda = K;
   a.B = wq; a.ldb = K;
@@ -227,10 +228,23 @@ int jet_fp8_linear_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, co
   a.C = y; a.ldc = N; a.Cq = yq; a.Cs = ys; a.ldcs = M;
   a.M = (int)M; a.N = (int)N; a.Kc = (int)K;
   const int out = y_dtype == JET_BF16 ? jet::kOutBf16 : jet::kOutF32;
-  if (M <= jet::kSkinnyMaxM)   // rollout decode: weight-streaming, split-K through the workspace
-    return hip_status(jet::launch_gemm_skinny(a, out, fuse, workspace, as_stream(stream)), "fp8_linear_fwd");
-  return hip_status(jet::launch_gemm(a, jet::kRowBlock, out, false, fuse, as_stream(stream)),
-                    "fp8_linear_fwd");
+  if (M <= jet::kSkinnyMaxM)   // rollout decode: weight-streaming (split-K through the workspace)
+    return hip_status(jet::launch_gemm_skinny(a, out, fuse, workspace, as_stream(stream), invariant), name);
+  return hip_status(jet::launch_gemm(a, jet::kRowBlock, out, false, fuse, as_stream(stream)), name);
+}
+
+int jet_fp8_linear_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
+                       int64_t M, int64_t N, int64_t K, void* y, int y_dtype, uint8_t* yq, float* ys,
+                       void* workspace, size_t ws_bytes, void* stream) {
+  return linear_fwd("fp8_linear_fwd", xq, xs, wq, ws, M, N, K, y, y_dtype, yq, ys, workspace, ws_bytes,
+                    stream, false);
+}
+
+int jet_fp8_linear_fwd_batch_invariant(const uint8_t* xq, const float* xs, const uint8_t* wq,
+                                       const float* ws, int64_t M, int64_t N, int64_t K, void* y,
+                                       int y_dtype, uint8_t* yq, float* ys, void* stream) {
+  return linear_fwd("fp8_linear_fwd_batch_invariant", xq, xs, wq, ws, M, N, K, y, y_dtype, yq, ys, nullptr,
+                    0, stream, true);
 }
 
 int jet_fp8_linear_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* wqT, const float* ws,

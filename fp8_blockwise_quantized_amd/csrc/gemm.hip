@@ -945,10 +945,13 @@ static hipError_t launch_skinny_out(const GemmArgs& a, int out, bool fuseq, floa
   return launch_skinny_mt<MT, NST, kSkWS, kOutBf16, false>(a, part, S, st);
 }
 
-hipError_t launch_gemm_skinny(const GemmArgs& a, int out, bool fuseq, void* workspace, hipStream_t st) {
+hipError_t launch_gemm_skinny(const GemmArgs& a, int out, bool fuseq, void* workspace, hipStream_t st,
+                              bool unsplit) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
   if (a.M > kSkinnyMaxM || a.Kc <= 0 || a.N % (64 * kSkWS)) return hipErrorInvalidValue;
-  const int S = skinny_splits(a.M, a.N, a.Kc);
+  // unsplit: every output element is the same chain of per-step FMAs, in K
+  // order, as in k_gemm_fp8 (bit-identical to the large-M forward)
+  const int S = unsplit ? 1 : skinny_splits(a.M, a.N, a.Kc);
   if (S > 1 && workspace == nullptr) return hipErrorInvalidValue;
   float* part = static_cast<float*>(workspace);
   if (a.M <= 64) return launch_skinny_out<4, kSkNST>(a, out, fuseq, part, S, st);

@@ -61,7 +61,9 @@ hipError_t launch_gemm(const GemmArgs& a, int mode, int out, bool accum, bool fu
 constexpr int64_t kSkinnyMaxM = 128;
 int skinny_splits(int64_t M, int64_t N, int64_t K);
 size_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K);
-hipError_t launch_gemm_skinny(const GemmArgs& a, int out, bool fuseq, void* workspace, hipStream_t st);
+// unsplit: one K range (no workspace), bit-identical to launch_gemm's forward.
+hipError_t launch_gemm_skinny(const GemmArgs& a, int out, bool fuseq, void* workspace, hipStream_t st,
+                              bool unsplit = false);
 // Grouped GEMMs: grp = kGrpRows (forward, dgrad) or kGrpContraction (wgrad).
 hipError_t launch_gemm_grouped(const GemmArgs& a, int grp, int mode, int out, bool accum,
                                bool fuseq, hipStream_t st);

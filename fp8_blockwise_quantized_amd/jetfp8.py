@@ -35,6 +35,7 @@ SIGNATURES = {
     "jet_rmsnorm_quant_1x128": [_p, _p, _i64, _i64, _i64, _f32, _p, _i64, _p, _i64, _p, _p],
     "jet_swiglu_quant_1x128": [_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _p],
     "jet_fp8_linear_fwd": [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _p, _p, _p, _sz, _p],
+    "jet_fp8_linear_fwd_batch_invariant": [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _p, _p, _p],
     "jet_fp8_linear_dgrad": [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _p, _sz, _p],
     "jet_fp8_linear_wgrad": [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _i32, _p, _sz, _p],
     "jet_workspace_bytes": [_i32, _i64, _i64, _i64],
@@ -273,6 +274,23 @@ def jet_fp8_linear_fwd(xq, xs, wq, ws, y=None, out_dtype=torch.bfloat16, fuse_qu
     _check("jet_fp8_linear_fwd", _lib.jet_fp8_linear_fwd(
         _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), M, N, K, _ptr(y), _dtype_code(y.dtype),
         _ptr(yq), _ptr(ys), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+        _stream(stream)))
+    return (y, yq, ys) if fuse_quant else y
+
+
+def jet_fp8_linear_fwd_batch_invariant(xq, xs, wq, ws, y=None, out_dtype=torch.bfloat16, fuse_quant=False,
+                                       yq=None, ys=None, stream=None):
+    """As jet_fp8_linear_fwd, with each output row bit-identical at every M
+    (no workspace)."""
+    xq, wq = _codes(xq), _codes(wq)
+    M, K = xq.shape
+    N = wq.shape[0]
+    y = y if y is not None else _empty((M, N), out_dtype, xq)
+    if fuse_quant:
+        yq = _codes(yq) if yq is not None else _empty((M, N), torch.uint8, xq)
+        ys = ys if ys is not None else _empty((N // 128, M), torch.float32, xq)
+    _check("jet_fp8_linear_fwd_batch_invariant", _lib.jet_fp8_linear_fwd_batch_invariant(
+        _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), M, N, K, _ptr(y), _dtype_code(y.dtype), _ptr(yq), _ptr(ys),
         _stream(stream)))
     return (y, yq, ys) if fuse_quant else y
 

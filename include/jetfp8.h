@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define JET_ABI_VERSION 4
+#define JET_ABI_VERSION 5
 
 typedef enum {
   JET_OK = 0,
@@ -221,6 +221,27 @@ int jet_fp8_linear_fwd(const uint8_t* xq, const float* xs,
                        int64_t M, int64_t N, int64_t K,
                        void* y, int y_dtype, uint8_t* yq, float* ys,
                        void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * The forward of jet_fp8_linear_fwd with a batch-invariant result: every
+ * output element is computed by the same chain of operations whatever M is
+ * (one MFMA per 128-wide K step from zero, folded into FP32 in K order), so a
+ * token's Y, and its fused 1x128 codes, are bit-identical whether it is
+ * computed in a rollout batch of a few rows or in a training batch of
+ * thousands.  The explainer ("Kernarchitektur") requires the rollout graph to
+ * be the training forward graph at the same granularity and precision; this
+ * entry point makes the two forwards agree bit for bit, not only in format.
+ * For M <= 128 it streams the weight with one K range per output block (no
+ * workspace; the split ranges of jet_fp8_linear_fwd are summed in another
+ * FP32 order), which is slower there when N/128 blocks leave CUs idle; for
+ * M > 128 it is jet_fp8_linear_fwd.  Arguments, layouts and errors as
+ * jet_fp8_linear_fwd without the workspace.
+ */
+int jet_fp8_linear_fwd_batch_invariant(const uint8_t* xq, const float* xs,
+                                       const uint8_t* wq, const float* ws,
+                                       int64_t M, int64_t N, int64_t K,
+                                       void* y, int y_dtype, uint8_t* yq, float* ys,
+                                       void* stream);
 
 /*
  * Data-gradient GEMM  dX[m,k] = sum_n dYhat[m,n] * What[n,k].

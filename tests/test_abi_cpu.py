@@ -48,7 +48,7 @@ def test_binding_covers_header(J):
 
 
 def test_version_and_status_strings(J):
-    assert J.jet_abi_version() == 4
+    assert J.jet_abi_version() == 5
     assert J.jet_status_string(J.JET_ERR_SHAPE) == "JET_ERR_SHAPE"
     assert J.jet_status_string(99) == "JET_ERR_UNKNOWN"
 
@@ -85,6 +85,20 @@ def test_quantizer_validation(J):
     assert Q2(None, 0, 128, 128, None, 128, None, None, 0, None, 0, None) == J.JET_OK    # empty: no-op
     assert L.jet_quant_weight_128x128(P16, 100, 128, 128, P16, P16, None, None) == J.JET_ERR_SHAPE
     assert L.jet_quant_weight_128x128(P16, 128, 128, 128, P16, P16, P17, None) == J.JET_ERR_ALIGN
+
+
+def test_batch_invariant_forward_validation(J):
+    L = J._lib
+    a = (P16, P16, P16, P16)
+    f = L.jet_fp8_linear_fwd_batch_invariant
+    assert f(*a, 64, 100, 128, P16, J.JET_BF16, None, None, None) == J.JET_ERR_SHAPE
+    assert f(*a, 64, 128, 128, P16, 7, None, None, None) == J.JET_ERR_DTYPE
+    assert f(*a, 64, 128, 128, P16, J.JET_F32, P16, P16, None) == J.JET_ERR_DTYPE
+    assert f(*a, 64, 128, 128, P16, J.JET_BF16, P16, None, None) == J.JET_ERR_NULL
+    assert f(None, P16, P16, P16, 64, 128, 128, P16, J.JET_BF16, None, None, None) == J.JET_ERR_NULL
+    assert f(P17, P16, P16, P16, 64, 128, 128, P16, J.JET_BF16, None, None, None) == J.JET_ERR_ALIGN
+    assert f(*a, 0, 128, 128, P16, J.JET_BF16, None, None, None) == J.JET_OK
+    assert "batch_invariant" in J.jet_last_error() or J.jet_last_error() == ""
 
 
 def test_gemm_operand_stride_limit(J):

@@ -465,3 +465,38 @@ def test_qwen_shapes_sampled(gpu_lib, name):
     a = O.dequant_128x1_T(host(dyqT[nidx[:32]]), host(dysT[:, nidx[:32]]), M)
     b = O.dequant_128x1_T(host(xqT[kidx]), host(xsT[:, kidx]), M)
     check_f32_output(host(dw[nidx[:32]][:, kidx]), a @ b.T, oracle_absprod(a, b), f"wgrad {name}")
+
+
+# --- batch invariance (rollout rows == training rows, bit for bit) ------------
+
+@pytest.mark.parametrize("name", list(LLAMA))
+def test_batch_invariant_forward_matches_training_batch(gpu_lib, name):
+    """Rows computed by jet_fp8_linear_fwd_batch_invariant in a rollout-sized
+    batch (M = 1, 37, 64, 128: the weight-streaming kernel) equal the same rows
+    computed in a training-sized batch (M = 2048: the tiled kernel), bit for
+    bit: BF16 Y, its fused 1x128 codes and scales, and FP32 Y.  The default
+    split-K forward of the same rows stays within the GEMM tolerance but is not
+    bit-identical; its mismatch is reported."""
+    N, K = LLAMA[name]
+    Mb = 2048
+    x = inputs.activations_with_outliers(Mb, K, seed=11)
+    w = inputs.normal_bf16((N, K), 0.02, seed=11, tensor_id=inputs.ID_W)
+    xq, xs = gpu_lib.jet_quant_act_1x128(dev_bf16(x))
+    wq, ws, _ = gpu_lib.jet_quant_weight_128x128(dev_bf16(w), transposed=False)
+    yb, yqb, ysb = gpu_lib.jet_fp8_linear_fwd(xq, xs, wq, ws, fuse_quant=True)
+    y32b = gpu_lib.jet_fp8_linear_fwd(xq, xs, wq, ws, out_dtype=torch.float32)
+    report = []
+    for M, r0 in ((1, 5), (37, 100), (64, 1000), (128, 1900)):
+        rows = slice(r0, r0 + M)
+        xq_s, xs_s = xq[rows].contiguous(), xs[:, rows].contiguous()
+        y, yq, ys = gpu_lib.jet_fp8_linear_fwd_batch_invariant(xq_s, xs_s, wq, ws, fuse_quant=True)
+        y32 = gpu_lib.jet_fp8_linear_fwd_batch_invariant(xq_s, xs_s, wq, ws, out_dtype=torch.float32)
+        y_split = gpu_lib.jet_fp8_linear_fwd(xq_s, xs_s, wq, ws, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(y, yb[rows]), f"{name} M={M}: BF16 rows differ from the training batch"
+        assert torch.equal(yq, yqb[rows]) and torch.equal(ys, ysb[:, rows]), f"{name} M={M}: fused codes differ"
+        assert torch.equal(y32, y32b[rows]), f"{name} M={M}: FP32 rows differ from the training batch"
+        diff = (y_split - y32b[rows]).abs()
+        report.append(f"M={M}: split-K differs in {int((diff > 0).sum())}/{diff.numel()} elements, "
+                      f"max {float(diff.max()):.2e}")
+    print(f"{name}: " + "; ".join(report))
