@@ -12,6 +12,8 @@ Inputs are seeded synthetic tensors resident in HBM before timing starts.
 
 `--workload fused` the fused producers of the linear inputs of one layer
 (RMSNorm + 1x128 twice, SwiGLU + 1x128 once) at M = 8192;
+`--workload kv` the FP8 KV cache of one layer (scale recalibration and append
+of a 8192-token prefill, append of a 64-token decode step);
 `--workload decode` times the rollout forward of the same linears at M = 64;
 `--workload moe` the grouped (mixture-of-experts) layer of Qwen3-30B-A3B shape
 (hidden 2048, expert intermediate 768, 128 experts, top-8 of 8192 tokens with
@@ -55,11 +57,12 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="run 1 GiB device copies first (HBM counter calibration)")
     ap.add_argument("--events", type=int, default=1, help="per-kernel HIP events in the timed loop")
-    ap.add_argument("--workload", choices=("train", "decode", "moe", "fused"), default="train",
+    ap.add_argument("--workload", choices=("train", "decode", "moe", "fused", "kv"), default="train",
                     help="train: the M=8192 fwd+bwd step (the headline line); decode: the rollout "
                          "forward at M=64 over the same four linears; moe: the grouped expert "
                          "layer (Qwen3-30B-A3B shapes) fwd+bwd; fused: the fused RMSNorm/SwiGLU "
-                         "producers of the 1x128 inputs of one Llama-8B layer")
+                         "producers of the 1x128 inputs of one Llama-8B layer; kv: the FP8 KV cache "
+                         "(recalibration and append) of one Llama-8B layer")
     ap.add_argument("--fused-m", type=int, default=8192, help="tokens for --workload fused")
     ap.add_argument("--invariant", action="store_true",
                     help="decode: the batch-invariant forward (one K range, bit-identical to training)")
@@ -574,6 +577,105 @@ def fused_bench(args, torch, J):
     print(json.dumps(out), flush=True)
 
 
+KV_Q, KV_D, KV_T, KV_DECODE = 4096, 1024, 8192, 64
+
+
+def kv_bytes_calibrate(T, D):     # K and V read
+    return 2 * T * D * 2
+
+
+def kv_bytes_append(T, D):        # K and V read, slots read, codes written
+    return 2 * T * D * 2 + T * 8 + 2 * T * D
+
+
+def cpu_baseline_kv():
+    """The oracle (untuned) on the KV workload's prefill: all 8192 tokens
+    recalibrated and appended (a few seconds); GB/s of its bytes."""
+    from oracle import kv_cache as KV
+    from fp8_blockwise_quantized_amd import inputs
+    T = KV_T
+    y = inputs.normal_bf16((T, KV_Q + 2 * KV_D), 1.3, seed=0, tensor_id=inputs.ID_X)
+    k, v = y[:, KV_Q:KV_Q + KV_D], y[:, KV_Q + KV_D:]
+    cache = np.zeros((T, KV_D), np.uint8)
+    t0 = time.perf_counter()
+    (sk, rk), (sv, rv) = KV.kv_calibrate(k, v)
+    KV.kv_append(cache, k, np.arange(T), rk)
+    KV.kv_append(cache, v, np.arange(T), rv)
+    dt = time.perf_counter() - t0
+    nbytes = kv_bytes_calibrate(T, KV_D) + kv_bytes_append(T, KV_D)
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"the whole prefill, {T} tokens (D={KV_D}): recalibration and append of K and V "
+                      f"(NumPy, one thread); "
+                      f"host cpu_count={os.cpu_count()}"}
+
+
+def kv_bench(args, torch, J):
+    """FP8 KV cache of one Llama-3.1-8B layer (8 KV heads x 128): after a
+    weight update, recalibrate the K and V scales on a 8192-token prefill and
+    append it; then append one 64-token decode step.  value = algorithmic
+    bytes of recalibration + prefill append / their time."""
+    from fp8_blockwise_quantized_amd import inputs
+    log("building the KV-cache inputs")
+    y = torch.from_numpy(inputs.normal_bf16((KV_T, KV_Q + 2 * KV_D), 1.3, seed=0,
+                                            tensor_id=inputs.ID_X)).to(torch.bfloat16).cuda()
+    k, v = y[:, KV_Q:KV_Q + KV_D], y[:, KV_Q + KV_D:]
+    yd = y[:KV_DECODE]
+    kd, vd = yd[:, KV_Q:KV_Q + KV_D], yd[:, KV_Q + KV_D:]
+    rows = KV_T + 4096
+    kc = torch.zeros((rows, KV_D), dtype=torch.uint8, device="cuda")
+    vc = torch.zeros((rows, KV_D), dtype=torch.uint8, device="cuda")
+    slots = torch.randperm(KV_T, device="cuda", generator=torch.Generator(device="cuda").manual_seed(0))
+    slots_d = torch.arange(KV_T, KV_T + KV_DECODE, dtype=torch.int64, device="cuda")
+    sc = torch.empty(6, dtype=torch.float32, device="cuda")
+    plan = [("kv_calibrate", kv_bytes_calibrate(KV_T, KV_D), lambda: J.jet_kv_calibrate(k, v, kv_scales=sc)),
+            ("kv_append_prefill", kv_bytes_append(KV_T, KV_D), lambda: J.jet_kv_append(k, v, slots, sc, kc, vc)),
+            ("kv_append_decode", kv_bytes_append(KV_DECODE, KV_D),
+             lambda: J.jet_kv_append(kd, vd, slots_d, sc, kc, vc))]
+    E = torch.cuda.Event
+    for _ in range(args.warmup):
+        for _, _, fn in plan:
+            fn()
+    torch.cuda.synchronize()
+    log(f"{args.warmup} warm-up steps, then {args.steps} timed steps")
+    per = [[[E(enable_timing=True), E(enable_timing=True)] for _ in plan] for _ in range(args.steps)]
+    t0, t1 = E(enable_timing=True), E(enable_timing=True)
+    t0.record()
+    for st in range(args.steps):
+        for i, (_, _, fn) in enumerate(plan):
+            per[st][i][0].record()
+            fn()
+            per[st][i][1].record()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    kernels = {}
+    for i, (kind, b, _) in enumerate(plan):
+        us = sum(per[st][i][0].elapsed_time(per[st][i][1]) for st in range(args.steps)) / args.steps * 1e3
+        kernels[kind] = {"avg_us": round(us, 2), "bytes": b, "gbs": round(b / (us * 1e-6) / 1e9, 1),
+                         "frac_hbm_peak": round(b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    main_bytes = kernels["kv_calibrate"]["bytes"] + kernels["kv_append_prefill"]["bytes"]
+    main_us = kernels["kv_calibrate"]["avg_us"] + kernels["kv_append_prefill"]["avg_us"]
+    dom = "kv_append_prefill"
+    out = {
+        "metric": "FP8 KV-cache recalibration + append GB/s, Llama-8B layer (8 KV heads x 128)",
+        "value": round(main_bytes / (main_us * 1e-6) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"Llama-3.1-8B layer KV cache: per-tensor scale recalibration on a {KV_T}-token "
+                               f"prefill and its append (K and V column slices of the QKV output, D={KV_D}), "
+                               f"then a {KV_DECODE}-token decode append", "T": KV_T,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["gbs"], "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": kernels[dom]["frac_hbm_peak"], "traffic": None,
+                     "bytes_per_launch": kernels[dom]["bytes"]},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on its bounded sample")
+        out["cpu_baseline"] = cpu_baseline_kv()
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -591,6 +693,9 @@ def main():
         return
     if args.workload == "fused":
         fused_bench(args, torch, J)
+        return
+    if args.workload == "kv":
+        kv_bench(args, torch, J)
         return
     if args.copy_probe:
         copy_probe(torch)

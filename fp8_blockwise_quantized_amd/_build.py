@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libjetfp8.so")
-SOURCES = ["abi.hip", "quant.hip", "fused.hip", "gemm.hip"]
+SOURCES = ["abi.hip", "quant.hip", "fused.hip", "kvcache.hip", "gemm.hip"]
 ARCH = "gfx950"
 
 # No fast-math: the quantizers need IEEE division and FP32 denormals.

@@ -115,6 +115,45 @@ int jet_swiglu_quant_1x128(const void* gu, int64_t M, int64_t I, int64_t ldgu, v
                     "swiglu_quant_1x128");
 }
 
+static int check_kv_rows(const char* name, const void* k, const void* v, int64_t T, int64_t D, int64_t ldk,
+                         int64_t ldv) {
+  if (T < 0 || D <= 0 || D % 8 || T > kMaxDim || D > kMaxDim)
+    return fail(JET_ERR_SHAPE, "%s: need T >= 0 and D > 0 a multiple of 8 (T=%lld D=%lld)", name,
+                (long long)T, (long long)D);
+  if (T > 0 && (!k || !v)) return fail(JET_ERR_NULL, "%s: null pointer", name);
+  if (ldk < D || ldv < D) return fail(JET_ERR_SHAPE, "%s: row stride < D", name);
+  if (T > 0 && (!aligned(k, 16) || !aligned(v, 16) || ldk % 8 || ldv % 8))
+    return fail(JET_ERR_ALIGN, "%s: k, v need 16-byte alignment and row strides %% 8", name);
+  return JET_OK;
+}
+
+int jet_kv_calibrate(const void* k, const void* v, int64_t T, int64_t D, int64_t ldk, int64_t ldv,
+                     float* kv_scales, void* stream) {
+  g_last_error[0] = 0;
+  if (int st = check_kv_rows("kv_calibrate", k, v, T, D, ldk, ldv)) return st;
+  if (!kv_scales) return fail(JET_ERR_NULL, "kv_calibrate: null pointer");
+  if (!aligned(kv_scales, 4)) return fail(JET_ERR_ALIGN, "kv_calibrate: kv_scales needs 4-byte alignment");
+  return hip_status(jet::launch_kv_calibrate(static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                                             T, D, ldk, ldv, kv_scales, as_stream(stream)),
+                    "kv_calibrate");
+}
+
+int jet_kv_append(const void* k, const void* v, int64_t T, int64_t D, int64_t ldk, int64_t ldv,
+                  const int64_t* slots, const float* kv_scales, uint8_t* k_cache, uint8_t* v_cache,
+                  int64_t ldc, int64_t rows, void* stream) {
+  g_last_error[0] = 0;
+  if (int st = check_kv_rows("kv_append", k, v, T, D, ldk, ldv)) return st;
+  if (rows < 0 || ldc < D) return fail(JET_ERR_SHAPE, "kv_append: need rows >= 0 and ldc >= D");
+  if (T == 0 || rows == 0) return JET_OK;
+  if (!slots || !kv_scales || !k_cache || !v_cache) return fail(JET_ERR_NULL, "kv_append: null pointer");
+  if (!aligned(slots, 8) || !aligned(kv_scales, 4) || !aligned(k_cache, 8) || !aligned(v_cache, 8) || ldc % 8)
+    return fail(JET_ERR_ALIGN, "kv_append: slots and caches need 8-byte alignment, ldc %% 8");
+  return hip_status(jet::launch_kv_append(static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), T, D,
+                                          ldk, ldv, slots, kv_scales, k_cache, v_cache, ldc, rows,
+                                          as_stream(stream)),
+                    "kv_append");
+}
+
 int jet_quant_act_128x1_T(const void* src, int src_dtype, const float* src_s, int64_t M, int64_t K,
                           int64_t ldsrc, uint8_t* qT, int64_t ldqT, float* sT, void* stream) {
   g_last_error[0] = 0;

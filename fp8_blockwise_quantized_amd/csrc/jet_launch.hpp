@@ -53,6 +53,13 @@ hipError_t launch_rmsnorm_quant_1x128(const uint16_t* x, const uint16_t* gamma, 
                                       int64_t ldq, float* s, hipStream_t st);
 hipError_t launch_swiglu_quant_1x128(const uint16_t* gu, int64_t M, int64_t I, int64_t ldgu, uint16_t* h,
                                      int64_t ldh, uint8_t* q, int64_t ldq, float* s, hipStream_t st);
+// FP8 KV cache: per-tensor scales (scales[0..3] = s_k, r_k, s_v, r_v; scales[4..5]
+// the two amax words) and the quantize-and-append of token rows to cache rows.
+hipError_t launch_kv_calibrate(const uint16_t* k, const uint16_t* v, int64_t T, int64_t D, int64_t ldk,
+                               int64_t ldv, float* scales, hipStream_t st);
+hipError_t launch_kv_append(const uint16_t* k, const uint16_t* v, int64_t T, int64_t D, int64_t ldk,
+                            int64_t ldv, const int64_t* slots, const float* scales, uint8_t* kc, uint8_t* vc,
+                            int64_t ldc, int64_t rows, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs& a, int mode, int out, bool accum, bool fuseq,
                        hipStream_t st);
 // Small-M forward (M <= kSkinnyMaxM): one kernel when the K steps are not

@@ -33,6 +33,8 @@ SIGNATURES = {
     "jet_quant_act_1x128_128x1_T": [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _i32, _p],
     "jet_quant_weight_128x128": [_p, _i64, _i64, _i64, _p, _p, _p, _p],
     "jet_rmsnorm_quant_1x128": [_p, _p, _i64, _i64, _i64, _f32, _p, _i64, _p, _i64, _p, _p],
+    "jet_kv_calibrate": [_p, _p, _i64, _i64, _i64, _i64, _p, _p],
+    "jet_kv_append": [_p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _i64, _i64, _p],
     "jet_swiglu_quant_1x128": [_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _p],
     "jet_fp8_linear_fwd": [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _p, _p, _p, _sz, _p],
     "jet_fp8_linear_fwd_batch_invariant": [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _p, _p, _p],
@@ -137,6 +139,42 @@ def jet_quant_act_1x128(x, q=None, s=None, stream=None):
     _check("jet_quant_act_1x128", _lib.jet_quant_act_1x128(
         _ptr(x), M, K, x.stride(0), _ptr(q), q.stride(0), _ptr(s), _stream(stream)))
     return q, s
+
+
+def jet_kv_calibrate(k, v, kv_scales=None, stream=None):
+    """Per-tensor FP8 KV-cache scales from the BF16 K and V rows [T, D] of a
+    calibration batch.  Returns kv_scales float32 [6]: s_k, r_k, s_v, r_v
+    (then two working words)."""
+    _rowmajor(k, "k")
+    _rowmajor(v, "v")
+    if k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise TypeError("k and v must be bfloat16")
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    T, D = k.shape
+    kv_scales = kv_scales if kv_scales is not None else _empty((6,), torch.float32, k)
+    _check("jet_kv_calibrate", _lib.jet_kv_calibrate(
+        _ptr(k), _ptr(v), T, D, k.stride(0), v.stride(0), _ptr(kv_scales), _stream(stream)))
+    return kv_scales
+
+
+def jet_kv_append(k, v, slots, kv_scales, k_cache, v_cache, stream=None):
+    """Quantize the BF16 K and V rows [T, D] with the stored multipliers and
+    write them to cache rows slots[t] (int64 [T]; outside [0, rows) skipped)."""
+    _rowmajor(k, "k")
+    _rowmajor(v, "v")
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    if slots.dtype != torch.int64 or slots.dim() != 1 or not slots.is_contiguous() or slots.numel() != k.shape[0]:
+        raise TypeError("slots must be a contiguous int64 tensor [T]")
+    k_cache, v_cache = _codes(k_cache), _codes(v_cache)
+    _rowmajor(k_cache, "k_cache")
+    if k_cache.shape != v_cache.shape or k_cache.stride(0) != v_cache.stride(0):
+        raise ValueError("k_cache and v_cache must have the same shape and row stride")
+    T, D = k.shape
+    _check("jet_kv_append", _lib.jet_kv_append(
+        _ptr(k), _ptr(v), T, D, k.stride(0), v.stride(0), _ptr(slots), _ptr(kv_scales), _ptr(k_cache),
+        _ptr(v_cache), k_cache.stride(0), k_cache.shape[0], _stream(stream)))
 
 
 def jet_rmsnorm_quant_1x128(x, gamma, eps, y=None, return_y=False, q=None, s=None, stream=None):

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define JET_ABI_VERSION 5
+#define JET_ABI_VERSION 6
 
 typedef enum {
   JET_OK = 0,
@@ -99,6 +99,44 @@ int jet_quant_act_1x128(const void* x, int64_t M, int64_t K, int64_t ldx,
 int jet_quant_act_128x1_T(const void* src, int src_dtype, const float* src_s,
                           int64_t M, int64_t K, int64_t ldsrc,
                           uint8_t* qT, int64_t ldqT, float* sT, void* stream);
+
+/*
+ * FP8 KV cache of the rollout, step 1: recalibrate the scales after a weight
+ * update (66260.cn FP8-RL item, KV-cache paragraph: KV-cache scale factors
+ * calibrated dynamically and re-adjusted after each model update; nmedialink
+ * NeMo-RL repost: FP8 in the KV cache).  One FP32 scale per tensor (the
+ * pages give no granularity): from the K and V rows of a calibration batch,
+ *   amax_c = max(max|x|, 2^-96), s = amax_c / 448, r = 448 / amax_c
+ * (the quantizers' scale rule).
+ *
+ *   k, v      : BF16 [T, D] (D = KV heads x head dim), row strides ldk, ldv
+ *               elements (>= D, % 8) -- e.g. column slices of the QKV output
+ *   kv_scales : FP32 device array of 6: [0] s_k, [1] r_k, [2] s_v, [3] r_v
+ *               (s dequantizes, r quantizes); [4], [5] working space
+ *   T >= 0 (T == 0: the floor scale), D > 0, D % 8 == 0; k, v 16-byte aligned,
+ *   kv_scales 4-byte aligned.  Three kernel launches, no memset.
+ */
+int jet_kv_calibrate(const void* k, const void* v, int64_t T, int64_t D,
+                     int64_t ldk, int64_t ldv, float* kv_scales, void* stream);
+
+/*
+ * FP8 KV cache, step 2: quantize T new tokens' K and V rows with the stored
+ * multipliers (codes = E4M3 of x * r, round to nearest even, saturating at
+ * +-448: values beyond the calibration batch's range saturate) and write
+ * them to the cache rows named by slots (a paged cache's block * block_size +
+ * offset).
+ *
+ *   k, v, T, D, ldk, ldv : as jet_kv_calibrate
+ *   slots     : int64 device array [T]; a slot outside [0, rows) writes nothing
+ *               (-1 marks a padding token)
+ *   kv_scales : as written by jet_kv_calibrate
+ *   k_cache, v_cache : E4M3 [rows, D], row stride ldc bytes (ldc >= D, % 8)
+ *   slots and caches 8-byte aligned.  Rows not named by a slot are unchanged.
+ */
+int jet_kv_append(const void* k, const void* v, int64_t T, int64_t D,
+                  int64_t ldk, int64_t ldv, const int64_t* slots, const float* kv_scales,
+                  uint8_t* k_cache, uint8_t* v_cache, int64_t ldc, int64_t rows,
+                  void* stream);
 
 /*
  * Fused producer: RMSNorm + 1x128 quantization.  The input of the QKV and

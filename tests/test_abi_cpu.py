@@ -48,7 +48,7 @@ def test_binding_covers_header(J):
 
 
 def test_version_and_status_strings(J):
-    assert J.jet_abi_version() == 5
+    assert J.jet_abi_version() == 6
     assert J.jet_status_string(J.JET_ERR_SHAPE) == "JET_ERR_SHAPE"
     assert J.jet_status_string(99) == "JET_ERR_UNKNOWN"
 
@@ -85,6 +85,30 @@ def test_quantizer_validation(J):
     assert Q2(None, 0, 128, 128, None, 128, None, None, 0, None, 0, None) == J.JET_OK    # empty: no-op
     assert L.jet_quant_weight_128x128(P16, 100, 128, 128, P16, P16, None, None) == J.JET_ERR_SHAPE
     assert L.jet_quant_weight_128x128(P16, 128, 128, 128, P16, P16, P17, None) == J.JET_ERR_ALIGN
+
+
+def test_kv_cache_validation(J):
+    L = J._lib
+    cal, app = L.jet_kv_calibrate, L.jet_kv_append
+    assert cal(P16, P16, 4, 100, 128, 128, P16, None) == J.JET_ERR_SHAPE       # D % 8
+    assert cal(P16, P16, -1, 128, 128, 128, P16, None) == J.JET_ERR_SHAPE
+    assert cal(P16, P16, 4, 128, 64, 128, P16, None) == J.JET_ERR_SHAPE        # ldk < D
+    assert cal(None, P16, 4, 128, 128, 128, P16, None) == J.JET_ERR_NULL
+    assert cal(P16, P16, 4, 128, 128, 128, None, None) == J.JET_ERR_NULL
+    assert cal(P17, P16, 4, 128, 128, 128, P16, None) == J.JET_ERR_ALIGN
+    assert cal(P16, P16, 4, 128, 132, 128, P16, None) == J.JET_ERR_ALIGN      # ldk % 8
+    assert cal(P16, P16, 4, 128, 128, 128, P17, None) == J.JET_ERR_ALIGN
+    assert app(P16, P16, 4, 128, 128, 128, P16, P16, P16, P16, 64, 10, None) == J.JET_ERR_SHAPE   # ldc < D
+    assert app(P16, P16, 4, 128, 128, 128, P16, P16, P16, P16, 128, -1, None) == J.JET_ERR_SHAPE
+    assert app(P16, P16, 0, 128, 128, 128, None, None, None, None, 128, 10, None) == J.JET_OK
+    assert app(P16, P16, 4, 128, 128, 128, P16, P16, P16, P16, 128, 0, None) == J.JET_OK
+    assert app(P16, P16, 4, 128, 128, 128, None, P16, P16, P16, 128, 10, None) == J.JET_ERR_NULL
+    assert app(P16, P16, 4, 128, 128, 128, P16, P16, P16, None, 128, 10, None) == J.JET_ERR_NULL
+    P12 = ctypes.c_void_p(4108)                                                 # 4-byte aligned only
+    assert app(P16, P16, 4, 128, 128, 128, P12, P16, P16, P16, 128, 10, None) == J.JET_ERR_ALIGN
+    assert app(P16, P16, 4, 128, 128, 128, P16, P16, P12, P16, 128, 10, None) == J.JET_ERR_ALIGN
+    assert app(P16, P16, 4, 128, 128, 128, P16, P16, P16, P16, 132, 10, None) == J.JET_ERR_ALIGN
+    assert "kv_append" in J.jet_last_error()
 
 
 def test_batch_invariant_forward_validation(J):
