@@ -154,7 +154,7 @@ def _quantize_with(x32: np.ndarray, r32: np.ndarray) -> np.ndarray:
 # Quantizers
 # ---------------------------------------------------------------------------
 
-def quant_1x128(x) -> tuple[np.ndarray, np.ndarray]:
+def quant_1x128(x, scale_rule=None) -> tuple[np.ndarray, np.ndarray]:
     """1x128 per-group quantization of an activation or output gradient.
 
     [JET-DE] Quantisierungsschema (activations 1x128); [NV-RL] table (input
@@ -162,20 +162,22 @@ def quant_1x128(x) -> tuple[np.ndarray, np.ndarray]:
 
     x : [R, C] float32 holding BF16 values, C a multiple of 128.
     returns codes [R, C] uint8 and scales [C/128, R] float32, the scale of
-    (row m, columns 128j..128j+127) at [j, m].
+    (row m, columns 128j..128j+127) at [j, m].  scale_rule (default
+    scale_pair, reading R2) maps group maxima to (s, r).
     """
+    scale_rule = scale_pair if scale_rule is None else scale_rule
     x = np.asarray(x, dtype=np.float32)
     R, C = x.shape
     if C % GROUP:
         raise ValueError("quant_1x128: columns must be a multiple of 128")
     groups = x.reshape(R, C // GROUP, GROUP)
     amax = np.max(np.abs(groups), axis=2) if R else np.zeros((0, C // GROUP), np.float32)
-    s, r = scale_pair(amax)                              # [R, C/128]
+    s, r = scale_rule(amax)                              # [R, C/128]
     codes = _quantize_with(groups, np.broadcast_to(r[:, :, None], groups.shape))
     return codes.reshape(R, C), np.ascontiguousarray(s.T)
 
 
-def quant_128x128(w) -> tuple[np.ndarray, np.ndarray]:
+def quant_128x128(w, scale_rule=None) -> tuple[np.ndarray, np.ndarray]:
     """128x128 per-block quantization of a (BF16 master) weight.
 
     [JET-DE] Quantisierungsschema (weights 128x128); [NV-RL] table;
@@ -184,19 +186,21 @@ def quant_128x128(w) -> tuple[np.ndarray, np.ndarray]:
     w : [N, K] float32 holding BF16 values, N and K multiples of 128.
     returns codes [N, K] uint8 and scales [N/128, K/128] float32.
     The transposed codes used by the data-gradient GEMM are codes.T.
+    scale_rule as for quant_1x128.
     """
+    scale_rule = scale_pair if scale_rule is None else scale_rule
     w = np.asarray(w, dtype=np.float32)
     N, K = w.shape
     if N % GROUP or K % GROUP:
         raise ValueError("quant_128x128: both dims must be multiples of 128")
     blocks = w.reshape(N // GROUP, GROUP, K // GROUP, GROUP)
     amax = np.max(np.abs(blocks), axis=(1, 3))          # [N/128, K/128]
-    s, r = scale_pair(amax)
+    s, r = scale_rule(amax)
     codes = _quantize_with(blocks, np.broadcast_to(r[:, None, :, None], blocks.shape))
     return codes.reshape(N, K), s
 
 
-def quant_128x1_T(a) -> tuple[np.ndarray, np.ndarray]:
+def quant_128x1_T(a, scale_rule=None) -> tuple[np.ndarray, np.ndarray]:
     """128x1 per-group quantization along the row (token) axis, written transposed.
 
     [JET-DE] Quantisierungsschema (128x1 grouping for WGrad); [JET-ZH] 五
@@ -205,7 +209,9 @@ def quant_128x1_T(a) -> tuple[np.ndarray, np.ndarray]:
     a : [M, C] float32.  Groups are rows 128g..min(128g+127, M-1) of one
     column.  returns codesT [C, Mp] uint8 with Mp = ceil(M/128)*128 (columns
     M..Mp-1 hold zero codes) and scales [ceil(M/128), C] float32.
+    scale_rule as for quant_1x128.
     """
+    scale_rule = scale_pair if scale_rule is None else scale_rule
     a = np.asarray(a, dtype=np.float32)
     M, C = a.shape
     G = -(-M // GROUP)
@@ -215,7 +221,7 @@ def quant_128x1_T(a) -> tuple[np.ndarray, np.ndarray]:
     for g in range(G):
         rows = a[g * GROUP: min((g + 1) * GROUP, M)]        # valid rows only (R5)
         amax = np.max(np.abs(rows), axis=0)                 # per column
-        s, r = scale_pair(amax)
+        s, r = scale_rule(amax)
         scales[g] = s
         q = _quantize_with(rows, np.broadcast_to(r[None, :], rows.shape))
         codesT[:, g * GROUP: g * GROUP + rows.shape[0]] = q.T
@@ -230,13 +236,13 @@ def dequant_1x128_fl32(codes, scales) -> np.ndarray:
     return (vals * s_full).astype(np.float32)
 
 
-def requant_128x1_T_from_1x128(codes, scales) -> tuple[np.ndarray, np.ndarray]:
+def requant_128x1_T_from_1x128(codes, scales, scale_rule=None) -> tuple[np.ndarray, np.ndarray]:
     """Re-quantize saved 1x128 FP8 activations into transposed 128x1 groups.
 
     [JET-ZH] 五: activations quantized 1x128 in forward are re-quantized
     128x1 for backward; [JET-DE]: activations saved for backward are FP8.
     """
-    return quant_128x1_T(dequant_1x128_fl32(codes, scales))
+    return quant_128x1_T(dequant_1x128_fl32(codes, scales), scale_rule)
 
 
 # ---------------------------------------------------------------------------
