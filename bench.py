@@ -64,6 +64,8 @@ def parse():
                          "producers of the 1x128 inputs of one Llama-8B layer; kv: the FP8 KV cache "
                          "(recalibration and append) of one Llama-8B layer")
     ap.add_argument("--fused-m", type=int, default=8192, help="tokens for --workload fused")
+    ap.add_argument("--pow2", action="store_true",
+                    help="train: the power-of-two-scale variant (E8M0 scales applied by the MFMA)")
     ap.add_argument("--invariant", action="store_true",
                     help="decode: the batch-invariant forward (one K range, bit-identical to training)")
     ap.add_argument("--quant", choices=("both", "separate"), default="both",
@@ -208,11 +210,13 @@ class Layer:
             return M * N + M * N // 128 * 4 + w + M * K * 2
         return (N + K) * Mp + Mp // 128 * (N + K) * 4 + N * K * 4
 
-    def ops(self, J, separate=False):
+    def ops(self, J, separate=False, pow2=False):
         """(kernel kind, algorithmic work, unit, callable) in path order."""
         M, N, K = self.M, self.N, self.K
         if separate:
             return self.ops_separate(J)
+        if pow2:
+            return self.ops_pow2(J)
         return [
             ("quant_w128x128", q_bytes_w(N, K), "B",
              lambda: J.jet_quant_weight_128x128(self.w, q=self.wq, s=self.ws, qT=self.wqT)),
@@ -231,6 +235,27 @@ class Layer:
              lambda: J.jet_fp8_linear_wgrad(self.dyqT, self.dysT, self.xqT, self.xsT, M, dw=self.dw)),
         ]
 
+
+    def ops_pow2(self, J):
+        """The same step with power-of-two scales (E8M0, applied by the MFMA)."""
+        M = self.M
+        return [
+            ("quant_w128x128", q_bytes_w(self.N, self.K), "B",
+             lambda: J.jet_quant_weight_128x128_pow2(self.w, q=self.wq, s=self.ws, qT=self.wqT)),
+            ("quant_1x128_128x1_T_requant", q_bytes_both(M, self.K), "B",
+             lambda: J.jet_quant_act_1x128_128x1_T_pow2(self.x, True, q=self.xq, s=self.xs,
+                                                        qT=self.xqT, sT=self.xsT)),
+            ("gemm_fwd", self.flops, "F",
+             lambda: J.jet_fp8_linear_fwd_pow2(self.xq, self.xs, self.wq, self.ws, y=self.y,
+                                               fuse_quant=True, yq=self.yq, ys=self.ys)),
+            ("quant_1x128_128x1_T_bf16", q_bytes_both(M, self.N), "B",
+             lambda: J.jet_quant_act_1x128_128x1_T_pow2(self.dy, False, q=self.dyq, s=self.dys,
+                                                        qT=self.dyqT, sT=self.dysT)),
+            ("gemm_dgrad", self.flops, "F",
+             lambda: J.jet_fp8_linear_dgrad_pow2(self.dyq, self.dys, self.wqT, self.ws, dx=self.dx)),
+            ("gemm_wgrad", self.flops, "F",
+             lambda: J.jet_fp8_linear_wgrad_pow2(self.dyqT, self.dysT, self.xqT, self.xsT, M, dw=self.dw)),
+        ]
 
     def ops_separate(self, J):
         """The same step with the separate 1x128 and 128x1 quantizers."""
@@ -267,13 +292,15 @@ def copy_probe(torch):
     del a, b
 
 
-def cpu_baseline():
+def cpu_baseline(pow2=False):
     """The oracle (untuned) on a bounded sample of the workload: the QKV
     linear (4096 -> 6144) with its full weight and all 8192 tokens (one of
     the four layers), through every step of the path; scaled to TFLOP/s of
-    the sample's GEMMs."""
+    the sample's GEMMs.  pow2: with the power-of-two scale rule."""
     from oracle import jet_oracle as O
+    from oracle import pow2_scales as P
     from fp8_blockwise_quantized_amd import inputs
+    rule = P.scale_pair_pow2 if pow2 else None
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -284,14 +311,14 @@ def cpu_baseline():
     w = inputs.normal_bf16((N, K), 0.02, seed=0, tensor_id=inputs.ID_W)
     dy = inputs.normal_bf16((Ms, N), 1e-3, seed=0, tensor_id=inputs.ID_DY)
     t0 = time.perf_counter()
-    wq, ws = O.quant_128x128(w)
-    xq, xs = O.quant_1x128(x)
+    wq, ws = O.quant_128x128(w, rule)
+    xq, xs = O.quant_1x128(x, rule)
     y = O.bf16_rne(O.fl32(O.gemm_fwd(xq, xs, wq, ws)))
-    O.quant_1x128(y)
-    dyq, dys = O.quant_1x128(dy)
+    O.quant_1x128(y, rule)
+    dyq, dys = O.quant_1x128(dy, rule)
     O.gemm_dgrad(dyq, dys, wq, ws)
-    dyqT, dysT = O.quant_128x1_T(dy)
-    xqT, xsT = O.requant_128x1_T_from_1x128(xq, xs)
+    dyqT, dysT = O.quant_128x1_T(dy, rule)
+    xqT, xsT = O.requant_128x1_T_from_1x128(xq, xs, rule)
     O.gemm_wgrad(dyqT, dysT, xqT, xsT, Ms)
     dt = time.perf_counter() - t0
     flops = 3 * 2.0 * Ms * N * K
@@ -708,7 +735,7 @@ def main():
     else:
         layers = [Layer(J, torch, n, N, K, M_TOKENS, seed=0) for (n, N, K) in LAYERS]
         plan = [(l.name, kind, work, unit, fn) for l in layers
-                for (kind, work, unit, fn) in l.ops(J, separate=args.quant == "separate")]
+                for (kind, work, unit, fn) in l.ops(J, separate=args.quant == "separate", pow2=args.pow2)]
     torch.cuda.synchronize()
 
     def step(evs=None):
@@ -773,7 +800,9 @@ def main():
         flops = a["work"] / a["launches"]
         nbytes = sum(l.gemm_bytes(dom) for l in layers) / len(layers)
         intensity = flops / nbytes
-        common = {"kernel": dom, "traffic": counters_for(dom, MOE_COUNTERS if moe else COUNTERS),
+        common = {"kernel": dom,
+                  "traffic": counters_for(dom + ("_pow2" if args.pow2 and not moe else ""),
+                                          MOE_COUNTERS if moe else COUNTERS),
                   "flops_per_launch": flops, "bytes_per_launch": nbytes,
                   "intensity_flop_per_byte": round(intensity, 1)}
         if intensity >= PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
@@ -802,7 +831,9 @@ def main():
                               "gate+up 4096->28672, down 14336->4096), training batch M=8192 tokens, "
                               "fwd + dgrad + wgrad with every quantizer and the BF16-master weight "
                               "re-quantization per step",
-                  "M": M_TOKENS, "activation_quantizers": args.quant, "parallelism": "none (1 GPU)"}
+                  "M": M_TOKENS, "activation_quantizers": args.quant,
+                  "scales": "power of two (E8M0, applied by the MFMA)" if args.pow2 else "FP32 amax/448",
+                  "parallelism": "none (1 GPU)"}
     out = {
         "metric": metric, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
@@ -816,7 +847,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("timing the oracle on its bounded sample")
-        out["cpu_baseline"] = cpu_baseline_moe() if moe else cpu_baseline()
+        out["cpu_baseline"] = cpu_baseline_moe() if moe else cpu_baseline(pow2=args.pow2)
     print(json.dumps(out), flush=True)
 
 

@@ -55,20 +55,30 @@ const char* jet_status_string(int status) {
 
 const char* jet_last_error(void) { return g_last_error; }
 
-int jet_quant_act_1x128(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,
-                        float* s, void* stream) {
+static int quant_1x128(const char* name, bool p2, const void* x, int64_t M, int64_t K, int64_t ldx,
+                       uint8_t* q, int64_t ldq, float* s, void* stream) {
   g_last_error[0] = 0;
   if (M < 0 || K < 0 || K % kG || M > kMaxDim || K > kMaxDim)
-    return fail(JET_ERR_SHAPE, "quant_act_1x128: need M >= 0 and K a multiple of 128 (M=%lld K=%lld)",
+    return fail(JET_ERR_SHAPE, "%s: need M >= 0 and K a multiple of 128 (M=%lld K=%lld)", name,
                 (long long)M, (long long)K);
   if (M == 0 || K == 0) return JET_OK;
-  if (!x || !q || !s) return fail(JET_ERR_NULL, "quant_act_1x128: null pointer");
-  if (ldx < K || ldq < K) return fail(JET_ERR_SHAPE, "quant_act_1x128: leading dimension < K");
+  if (!x || !q || !s) return fail(JET_ERR_NULL, "%s: null pointer", name);
+  if (ldx < K || ldq < K) return fail(JET_ERR_SHAPE, "%s: leading dimension < K", name);
   if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4) || ldx % 8 || ldq % 16)
-    return fail(JET_ERR_ALIGN, "quant_act_1x128: x, q need 16-byte alignment, ldx %% 8, ldq %% 16");
+    return fail(JET_ERR_ALIGN, "%s: x, q need 16-byte alignment, ldx %% 8, ldq %% 16", name);
   return hip_status(jet::launch_quant_1x128(static_cast<const uint16_t*>(x), M, K, ldx, q, ldq, s,
-                                            as_stream(stream)),
-                    "quant_act_1x128");
+                                            as_stream(stream), p2),
+                    name);
+}
+
+int jet_quant_act_1x128(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,
+                        float* s, void* stream) {
+  return quant_1x128("quant_act_1x128", false, x, M, K, ldx, q, ldq, s, stream);
+}
+
+int jet_quant_act_1x128_pow2(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,
+                             float* s, void* stream) {
+  return quant_1x128("quant_act_1x128_pow2", true, x, M, K, ldx, q, ldq, s, stream);
 }
 
 int jet_rmsnorm_quant_1x128(const void* x, const void* gamma, int64_t M, int64_t H, int64_t ldx,
@@ -154,67 +164,103 @@ int jet_kv_append(const void* k, const void* v, int64_t T, int64_t D, int64_t ld
                     "kv_append");
 }
 
-int jet_quant_act_128x1_T(const void* src, int src_dtype, const float* src_s, int64_t M, int64_t K,
-                          int64_t ldsrc, uint8_t* qT, int64_t ldqT, float* sT, void* stream) {
+static int quant_128x1_T(const char* name, bool p2, const void* src, int src_dtype, const float* src_s,
+                         int64_t M, int64_t K, int64_t ldsrc, uint8_t* qT, int64_t ldqT, float* sT,
+                         void* stream) {
   g_last_error[0] = 0;
   if (src_dtype != JET_BF16 && src_dtype != JET_E4M3)
-    return fail(JET_ERR_DTYPE, "quant_act_128x1_T: src_dtype must be JET_BF16 or JET_E4M3");
+    return fail(JET_ERR_DTYPE, "%s: src_dtype must be JET_BF16 or JET_E4M3", name);
   if (M < 0 || K < 0 || K % kG || M > kMaxDim || K > kMaxDim)
-    return fail(JET_ERR_SHAPE, "quant_act_128x1_T: need M >= 0 and K a multiple of 128");
+    return fail(JET_ERR_SHAPE, "%s: need M >= 0 and K a multiple of 128", name);
   if (M == 0 || K == 0) return JET_OK;
   const bool fp8 = src_dtype == JET_E4M3;
   if (!src || !qT || !sT || (fp8 && !src_s))
-    return fail(JET_ERR_NULL, "quant_act_128x1_T: null pointer");
+    return fail(JET_ERR_NULL, "%s: null pointer", name);
   const int64_t Mp = (M + kG - 1) / kG * kG;
-  if (Mp / kG > 65535) return fail(JET_ERR_SHAPE, "quant_act_128x1_T: ceil(M/128) must be <= 65535");
+  if (Mp / kG > 65535) return fail(JET_ERR_SHAPE, "%s: ceil(M/128) must be <= 65535", name);
   if (ldsrc < K || ldqT < Mp)
-    return fail(JET_ERR_SHAPE, "quant_act_128x1_T: ldsrc < K or ldqT < ceil(M/128)*128");
+    return fail(JET_ERR_SHAPE, "%s: ldsrc < K or ldqT < ceil(M/128)*128", name);
   const int64_t ld_bytes = fp8 ? ldsrc : 2 * ldsrc;
   if (!aligned(src, 16) || !aligned(qT, 16) || !aligned(sT, 16) || ld_bytes % 16 || ldqT % 16 ||
       (fp8 && !aligned(src_s, 4)))
-    return fail(JET_ERR_ALIGN, "quant_act_128x1_T: src, qT, sT need 16-byte alignment; row strides 16 bytes");
+    return fail(JET_ERR_ALIGN, "%s: src, qT, sT need 16-byte alignment; row strides 16 bytes", name);
   return hip_status(jet::launch_quant_128x1_T(src, fp8, src_s, M, K, ldsrc, qT, ldqT, sT,
-                                              as_stream(stream)),
-                    "quant_act_128x1_T");
+                                              as_stream(stream), p2),
+                    name);
+}
+
+int jet_quant_act_128x1_T(const void* src, int src_dtype, const float* src_s, int64_t M, int64_t K,
+                          int64_t ldsrc, uint8_t* qT, int64_t ldqT, float* sT, void* stream) {
+  return quant_128x1_T("quant_act_128x1_T", false, src, src_dtype, src_s, M, K, ldsrc, qT, ldqT, sT, stream);
+}
+
+int jet_quant_act_128x1_T_pow2(const void* src, int src_dtype, const float* src_s, int64_t M, int64_t K,
+                               int64_t ldsrc, uint8_t* qT, int64_t ldqT, float* sT, void* stream) {
+  return quant_128x1_T("quant_act_128x1_T_pow2", true, src, src_dtype, src_s, M, K, ldsrc, qT, ldqT, sT,
+                       stream);
+}
+
+static int quant_1x128_128x1_T(const char* name, bool p2, const void* x, int64_t M, int64_t K, int64_t ldx,
+                               uint8_t* q, int64_t ldq, float* s, uint8_t* qT, int64_t ldqT, float* sT,
+                               int requant, void* stream) {
+  g_last_error[0] = 0;
+  if (requant != 0 && requant != 1)
+    return fail(JET_ERR_DTYPE, "%s: requant must be 0 or 1", name);
+  if (M < 0 || K < 0 || K % kG || M > kMaxDim || K > kMaxDim)
+    return fail(JET_ERR_SHAPE, "%s: need M >= 0 and K a multiple of 128", name);
+  if (M == 0 || K == 0) return JET_OK;
+  if (!x || !q || !s || !qT || !sT) return fail(JET_ERR_NULL, "%s: null pointer", name);
+  const int64_t Mp = (M + kG - 1) / kG * kG;
+  if (Mp / kG > 65535)
+    return fail(JET_ERR_SHAPE, "%s: ceil(M/128) must be <= 65535", name);
+  if (ldx < K || ldq < K || ldqT < Mp)
+    return fail(JET_ERR_SHAPE, "%s: ldx < K, ldq < K or ldqT < ceil(M/128)*128", name);
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(qT, 16) || !aligned(sT, 16) || !aligned(s, 4) ||
+      ldx % 8 || ldq % 16 || ldqT % 16)
+    return fail(JET_ERR_ALIGN,
+                "%s: x, q, qT, sT need 16-byte alignment, ldx %% 8, ldq %% 16, ldqT %% 16", name);
+  return hip_status(jet::launch_quant_1x128_128x1_T(static_cast<const uint16_t*>(x), M, K, ldx, q, ldq,
+                                                    s, qT, ldqT, sT, requant == 1, as_stream(stream), p2),
+                    name);
 }
 
 int jet_quant_act_1x128_128x1_T(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
                                 int64_t ldq, float* s, uint8_t* qT, int64_t ldqT, float* sT,
                                 int requant, void* stream) {
+  return quant_1x128_128x1_T("quant_act_1x128_128x1_T", false, x, M, K, ldx, q, ldq, s, qT, ldqT, sT, requant,
+                             stream);
+}
+
+int jet_quant_act_1x128_128x1_T_pow2(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                                     int64_t ldq, float* s, uint8_t* qT, int64_t ldqT, float* sT,
+                                     int requant, void* stream) {
+  return quant_1x128_128x1_T("quant_act_1x128_128x1_T_pow2", true, x, M, K, ldx, q, ldq, s, qT, ldqT, sT,
+                             requant, stream);
+}
+
+static int quant_weight(const char* name, bool p2, const void* w, int64_t N, int64_t K, int64_t ldw,
+                        uint8_t* q, float* s, uint8_t* qT, void* stream) {
   g_last_error[0] = 0;
-  if (requant != 0 && requant != 1)
-    return fail(JET_ERR_DTYPE, "quant_act_1x128_128x1_T: requant must be 0 or 1");
-  if (M < 0 || K < 0 || K % kG || M > kMaxDim || K > kMaxDim)
-    return fail(JET_ERR_SHAPE, "quant_act_1x128_128x1_T: need M >= 0 and K a multiple of 128");
-  if (M == 0 || K == 0) return JET_OK;
-  if (!x || !q || !s || !qT || !sT) return fail(JET_ERR_NULL, "quant_act_1x128_128x1_T: null pointer");
-  const int64_t Mp = (M + kG - 1) / kG * kG;
-  if (Mp / kG > 65535)
-    return fail(JET_ERR_SHAPE, "quant_act_1x128_128x1_T: ceil(M/128) must be <= 65535");
-  if (ldx < K || ldq < K || ldqT < Mp)
-    return fail(JET_ERR_SHAPE, "quant_act_1x128_128x1_T: ldx < K, ldq < K or ldqT < ceil(M/128)*128");
-  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(qT, 16) || !aligned(sT, 16) || !aligned(s, 4) ||
-      ldx % 8 || ldq % 16 || ldqT % 16)
-    return fail(JET_ERR_ALIGN,
-                "quant_act_1x128_128x1_T: x, q, qT, sT need 16-byte alignment, ldx %% 8, ldq %% 16, ldqT %% 16");
-  return hip_status(jet::launch_quant_1x128_128x1_T(static_cast<const uint16_t*>(x), M, K, ldx, q, ldq,
-                                                    s, qT, ldqT, sT, requant == 1, as_stream(stream)),
-                    "quant_act_1x128_128x1_T");
+  if (N < 0 || K < 0 || N % kG || K % kG || N > kMaxDim || K > kMaxDim)
+    return fail(JET_ERR_SHAPE, "%s: N and K must be multiples of 128", name);
+  if (N == 0 || K == 0) return JET_OK;
+  if (!w || !q || !s) return fail(JET_ERR_NULL, "%s: null pointer", name);
+  if (ldw < K) return fail(JET_ERR_SHAPE, "%s: ldw < K", name);
+  if (!aligned(w, 16) || !aligned(q, 16) || !aligned(s, 4) || ldw % 8 || (qT && !aligned(qT, 16)))
+    return fail(JET_ERR_ALIGN, "%s: w, q, qT need 16-byte alignment, ldw %% 8", name);
+  return hip_status(jet::launch_quant_128x128(static_cast<const uint16_t*>(w), N, K, ldw, q, s, qT,
+                                              as_stream(stream), p2),
+                    name);
 }
 
 int jet_quant_weight_128x128(const void* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q, float* s,
                              uint8_t* qT, void* stream) {
-  g_last_error[0] = 0;
-  if (N < 0 || K < 0 || N % kG || K % kG || N > kMaxDim || K > kMaxDim)
-    return fail(JET_ERR_SHAPE, "quant_weight_128x128: N and K must be multiples of 128");
-  if (N == 0 || K == 0) return JET_OK;
-  if (!w || !q || !s) return fail(JET_ERR_NULL, "quant_weight_128x128: null pointer");
-  if (ldw < K) return fail(JET_ERR_SHAPE, "quant_weight_128x128: ldw < K");
-  if (!aligned(w, 16) || !aligned(q, 16) || !aligned(s, 4) || ldw % 8 || (qT && !aligned(qT, 16)))
-    return fail(JET_ERR_ALIGN, "quant_weight_128x128: w, q, qT need 16-byte alignment, ldw %% 8");
-  return hip_status(jet::launch_quant_128x128(static_cast<const uint16_t*>(w), N, K, ldw, q, s, qT,
-                                              as_stream(stream)),
-                    "quant_weight_128x128");
+  return quant_weight("quant_weight_128x128", false, w, N, K, ldw, q, s, qT, stream);
+}
+
+int jet_quant_weight_128x128_pow2(const void* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q, float* s,
+                                  uint8_t* qT, void* stream) {
+  return quant_weight("quant_weight_128x128_pow2", true, w, N, K, ldw, q, s, qT, stream);
 }
 
 size_t jet_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {
@@ -241,12 +287,13 @@ static int check_gemm_common(const char* name, int64_t M, int64_t N, int64_t K, 
 }
 
 // The forward; invariant: one K range at every M (no workspace), so each
-// output element does not depend on M.
+// output element does not depend on M.  p2: power-of-two scales applied by the
+// MFMA (the tiled kernel at every M; no workspace).
 static int linear_fwd(const char* name, const uint8_t* xq, const float* xs, const uint8_t* wq,
                       const float* ws, int64_t M, int64_t N, int64_t K, void* y, int y_dtype, uint8_t* yq,
-                      float* ys, void* workspace, size_t ws_bytes, void* stream, bool invariant) {
+                      float* ys, void* workspace, size_t ws_bytes, void* stream, bool invariant, bool p2 = false) {
   g_last_error[0] = 0;
-  const size_t need = invariant ? 0 : jet_workspace_bytes(JET_OP_FWD, M, N, K);
+  const size_t need = (invariant || p2) ? 0 : jet_workspace_bytes(JET_OP_FWD, M, N, K);
   if (int st = check_gemm_common(name, M, N, K, need, ws_bytes, workspace)) return st;
   if (y_dtype != JET_BF16 && y_dtype != JET_F32)
     return fail(JET_ERR_DTYPE, "%s: y_dtype must be JET_BF16 or JET_F32", name);
@@ -267,9 +314,9 @@ static int linear_fwd(const char* name, const uint8_t* xq, const float* xs, cons
   a.C = y; a.ldc = N; a.Cq = yq; a.Cs = ys; a.ldcs = M;
   a.M = (int)M; a.N = (int)N; a.Kc = (int)K;
   const int out = y_dtype == JET_BF16 ? jet::kOutBf16 : jet::kOutF32;
-  if (M <= jet::kSkinnyMaxM)   // rollout decode: weight-streaming (split-K through the workspace)
+  if (M <= jet::kSkinnyMaxM && !p2)   // rollout decode: weight-streaming (split-K through the workspace)
     return hip_status(jet::launch_gemm_skinny(a, out, fuse, workspace, as_stream(stream), invariant), name);
-  return hip_status(jet::launch_gemm(a, jet::kRowBlock, out, false, fuse, as_stream(stream)), name);
+  return hip_status(jet::launch_gemm(a, jet::kRowBlock, out, false, fuse, as_stream(stream), p2), name);
 }
 
 int jet_fp8_linear_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
@@ -286,19 +333,25 @@ int jet_fp8_linear_fwd_batch_invariant(const uint8_t* xq, const float* xs, const
                     0, stream, true);
 }
 
-int jet_fp8_linear_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* wqT, const float* ws,
-                         int64_t M, int64_t N, int64_t K, void* dx, int dx_dtype, void* workspace,
-                         size_t ws_bytes, void* stream) {
+int jet_fp8_linear_fwd_pow2(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
+                            int64_t M, int64_t N, int64_t K, void* y, int y_dtype, uint8_t* yq, float* ys,
+                            void* stream) {
+  return linear_fwd("fp8_linear_fwd_pow2", xq, xs, wq, ws, M, N, K, y, y_dtype, yq, ys, nullptr, 0, stream,
+                    false, true);
+}
+
+static int linear_dgrad(const char* name, bool p2, const uint8_t* dyq, const float* dys, const uint8_t* wqT,
+                        const float* ws, int64_t M, int64_t N, int64_t K, void* dx, int dx_dtype, void* workspace,
+                        size_t ws_bytes, void* stream) {
   g_last_error[0] = 0;
-  if (int st = check_gemm_common("fp8_linear_dgrad", M, N, K, jet_workspace_bytes(JET_OP_DGRAD, M, N, K),
-                                 ws_bytes, workspace))
+  if (int st = check_gemm_common(name, M, N, K, jet_workspace_bytes(JET_OP_DGRAD, M, N, K), ws_bytes, workspace))
     return st;
   if (dx_dtype != JET_BF16 && dx_dtype != JET_F32)
-    return fail(JET_ERR_DTYPE, "fp8_linear_dgrad: dx_dtype must be JET_BF16 or JET_F32");
+    return fail(JET_ERR_DTYPE, "%s: dx_dtype must be JET_BF16 or JET_F32", name);
   if (M == 0 || K == 0) return JET_OK;
-  if (!dyq || !dys || !wqT || !ws || !dx) return fail(JET_ERR_NULL, "fp8_linear_dgrad: null pointer");
+  if (!dyq || !dys || !wqT || !ws || !dx) return fail(JET_ERR_NULL, "%s: null pointer", name);
   if (!aligned(dyq, 16) || !aligned(wqT, 16) || !aligned(dx, 16) || !aligned(dys, 4) || !aligned(ws, 4))
-    return fail(JET_ERR_ALIGN, "fp8_linear_dgrad: operands and output need 16-byte alignment");
+    return fail(JET_ERR_ALIGN, "%s: operands and output need 16-byte alignment", name);
   jet::GemmArgs a{};
   a.A = dyq; a.lda = N;
   a.B = wqT; a.ldb = N;
@@ -307,30 +360,42 @@ int jet_fp8_linear_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* wq
   a.C = dx; a.ldc = K;
   a.M = (int)M; a.N = (int)K; a.Kc = (int)N;
   return hip_status(jet::launch_gemm(a, jet::kRowBlock, dx_dtype == JET_BF16 ? jet::kOutBf16 : jet::kOutF32,
-                                     false, false, as_stream(stream)),
-                    "fp8_linear_dgrad");
+                                     false, false, as_stream(stream), p2),
+                    name);
 }
 
-int jet_fp8_linear_wgrad(const uint8_t* dyqT, const float* dysT, const uint8_t* xqT, const float* xsT,
-                         int64_t M, int64_t N, int64_t K, void* dw, int dw_dtype, int accumulate,
-                         void* workspace, size_t ws_bytes, void* stream) {
+int jet_fp8_linear_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* wqT, const float* ws,
+                         int64_t M, int64_t N, int64_t K, void* dx, int dx_dtype, void* workspace,
+                         size_t ws_bytes, void* stream) {
+  return linear_dgrad("fp8_linear_dgrad", false, dyq, dys, wqT, ws, M, N, K, dx, dx_dtype, workspace, ws_bytes,
+                      stream);
+}
+
+int jet_fp8_linear_dgrad_pow2(const uint8_t* dyq, const float* dys, const uint8_t* wqT, const float* ws,
+                              int64_t M, int64_t N, int64_t K, void* dx, int dx_dtype, void* stream) {
+  return linear_dgrad("fp8_linear_dgrad_pow2", true, dyq, dys, wqT, ws, M, N, K, dx, dx_dtype, nullptr, 0,
+                      stream);
+}
+
+static int linear_wgrad(const char* name, bool p2, const uint8_t* dyqT, const float* dysT, const uint8_t* xqT,
+                        const float* xsT, int64_t M, int64_t N, int64_t K, void* dw, int dw_dtype, int accumulate,
+                        void* workspace, size_t ws_bytes, void* stream) {
   g_last_error[0] = 0;
-  if (int st = check_gemm_common("fp8_linear_wgrad", M, N, K, jet_workspace_bytes(JET_OP_WGRAD, M, N, K),
-                                 ws_bytes, workspace))
+  if (int st = check_gemm_common(name, M, N, K, jet_workspace_bytes(JET_OP_WGRAD, M, N, K), ws_bytes, workspace))
     return st;
   if (dw_dtype != JET_F32 && dw_dtype != JET_BF16)
-    return fail(JET_ERR_DTYPE, "fp8_linear_wgrad: dw_dtype must be JET_F32 or JET_BF16");
+    return fail(JET_ERR_DTYPE, "%s: dw_dtype must be JET_F32 or JET_BF16", name);
   if (accumulate && dw_dtype != JET_F32)
-    return fail(JET_ERR_DTYPE, "fp8_linear_wgrad: accumulate needs dw_dtype JET_F32");
+    return fail(JET_ERR_DTYPE, "%s: accumulate needs dw_dtype JET_F32", name);
   if (N == 0 || K == 0) return JET_OK;
-  if (!dw) return fail(JET_ERR_NULL, "fp8_linear_wgrad: null pointer");
-  if (M > 0 && (!dyqT || !dysT || !xqT || !xsT)) return fail(JET_ERR_NULL, "fp8_linear_wgrad: null pointer");
+  if (!dw) return fail(JET_ERR_NULL, "%s: null pointer", name);
+  if (M > 0 && (!dyqT || !dysT || !xqT || !xsT)) return fail(JET_ERR_NULL, "%s: null pointer", name);
   const int64_t Mp = (M + kG - 1) / kG * kG;
   if (Mp > kMaxLd)
-    return fail(JET_ERR_SHAPE, "fp8_linear_wgrad: M must be <= 2^24 (row stride of the transposed operands)");
+    return fail(JET_ERR_SHAPE, "%s: M must be <= 2^24 (row stride of the transposed operands)", name);
   if (!aligned(dw, 16) || (M > 0 && (!aligned(dyqT, 16) || !aligned(xqT, 16) || !aligned(dysT, 4) ||
                                      !aligned(xsT, 4))))
-    return fail(JET_ERR_ALIGN, "fp8_linear_wgrad: operands and output need 16-byte alignment");
+    return fail(JET_ERR_ALIGN, "%s: operands and output need 16-byte alignment", name);
   jet::GemmArgs a{};
   a.A = dyqT; a.lda = Mp;
   a.B = xqT; a.ldb = Mp;
@@ -339,8 +404,22 @@ int jet_fp8_linear_wgrad(const uint8_t* dyqT, const float* dysT, const uint8_t* 
   a.C = dw; a.ldc = K;
   a.M = (int)N; a.N = (int)K; a.Kc = (int)Mp;
   return hip_status(jet::launch_gemm(a, jet::kRowCol, dw_dtype == JET_BF16 ? jet::kOutBf16 : jet::kOutF32,
-                                     accumulate != 0, false, as_stream(stream)),
-                    "fp8_linear_wgrad");
+                                     accumulate != 0, false, as_stream(stream), p2),
+                    name);
+}
+
+int jet_fp8_linear_wgrad(const uint8_t* dyqT, const float* dysT, const uint8_t* xqT, const float* xsT,
+                         int64_t M, int64_t N, int64_t K, void* dw, int dw_dtype, int accumulate,
+                         void* workspace, size_t ws_bytes, void* stream) {
+  return linear_wgrad("fp8_linear_wgrad", false, dyqT, dysT, xqT, xsT, M, N, K, dw, dw_dtype, accumulate,
+                      workspace, ws_bytes, stream);
+}
+
+int jet_fp8_linear_wgrad_pow2(const uint8_t* dyqT, const float* dysT, const uint8_t* xqT, const float* xsT,
+                              int64_t M, int64_t N, int64_t K, void* dw, int dw_dtype, int accumulate,
+                              void* stream) {
+  return linear_wgrad("fp8_linear_wgrad_pow2", true, dyqT, dysT, xqT, xsT, M, N, K, dw, dw_dtype, accumulate,
+                      nullptr, 0, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -16,6 +16,13 @@
 // with no power-of-two restriction, and the MFMA never sums more than 128
 // products (it adds them internally at reduced precision).
 //
+// Power-of-two variant (P2): when every group scale is a power of two (the
+// pow2 quantizers), each scale is the MFMA's own E8M0 operand scale (lane
+// l's byte scales row l % 16 of its slab, the same byte on all four lane
+// groups since a scale covers the whole 128-K step), and each step's MFMA
+// accumulates straight into the FP32 accumulator, which it adds at full FP32
+// precision: no per-step partial, no fold, no scale products.
+//
 // Structure (the tile shape, wave layout, stage count and LDS layout are the
 // compile-time parameters of GemmCfg):
 //   * WMW x WNW wavefronts, each owning TM x TN 16x16 sub-tiles; block tile
@@ -182,6 +189,16 @@ __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
 }
 
+// c + (2^(ea-127) a) . (2^(eb-127) b): per-lane E8M0 operand scales (byte 0 of
+// ea / eb; lane l's byte scales row l % 16 of its operand), the sum added to c
+// at full FP32 precision.
+__device__ __forceinline__ v4f mfma_fp8_e8m0(const v8i& a, const v8i& b, const v4f& c, int ea, int eb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, ea, 0, eb);
+}
+
+// E8M0 byte of a positive power-of-two FP32 scale: its biased exponent field.
+__device__ __forceinline__ int e8m0_of(float s) { return (int)(__float_as_uint(s) >> 23); }
+
 // Block index -> output tile.  Workgroups are dealt round-robin to the 8 XCDs;
 // renumber so each XCD receives a contiguous range of tiles (shared operand
 // panels stay in that XCD's L2), then walk tiles in groups of kGroupM tile-rows.
@@ -210,7 +227,7 @@ __device__ __forceinline__ int xcd_slot() {
   return (g % kXcds == 0) ? (b % kXcds) * (g / kXcds) + b / kXcds : b;
 }
 
-template <class CFG, int MODE, int OUT, bool ACCUM, bool FUSEQ, int GRP>
+template <class CFG, int MODE, int OUT, bool ACCUM, bool FUSEQ, int GRP, bool P2>
 __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa) {
   constexpr int TM = CFG::TM, TN = CFG::TN, BM = CFG::BM, BN = CFG::BN;
   constexpr bool FRAG = CFG::FRAG;
@@ -435,7 +452,14 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
       rsc[4 * q + 0] = r4.x; rsc[4 * q + 1] = r4.y; rsc[4 * q + 2] = r4.z; rsc[4 * q + 3] = r4.w;
     }
     float cb[TN][4];
-    if (MODE == kRowCol) {
+    int eb[TN], ea[TM];   // P2: E8M0 scales of the lane's B row (column of C) and A row
+    if constexpr (P2) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        eb[j] = e8m0_of(MODE == kRowCol ? Sc[wn * TN * 16 + 16 * j + lrow] : Sc[(wn * TN * 16) / 128]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) ea[i] = e8m0_of(rsc[i]);
+    } else if (MODE == kRowCol) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const float4 c4 = *reinterpret_cast<const float4*>(Sc + wn * TN * 16 + 16 * j + 4 * kg);
@@ -450,7 +474,7 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
     v4f part[LAG];
 #pragma unroll
     for (int n = 0; n < NM + LAG; ++n) {
-      if (n >= LAG) {
+      if (!P2 && n >= LAG) {
         const int ii = ORD.i[n - LAG], jj = ORD.j[n - LAG];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -460,7 +484,8 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
       }
       if (n < NM) {
         const int i = ORD.i[n], j = ORD.j[n];
-        part[n % LAG] = mfma_fp8(bf[j], af[i % R]);
+        if constexpr (P2) acc[i][j] = mfma_fp8_e8m0(bf[j], af[i % R], acc[i][j], eb[j], ea[i]);
+        else part[n % LAG] = mfma_fp8(bf[j], af[i % R]);
         if (n == 0) {
           // after the first MFMA: the next step's scale DMAs, the remaining
           // B fragments
@@ -548,7 +573,7 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
         am = max_abs_bf16x2(am, v.z);
         am = max_abs_bf16x2(am, v.w);
         am = row16_max_u16x2(am);
-        const ScalePair sp = scale_pair(fold_bf16x2(am));
+        const ScalePair sp = scale_rule<P2>(fold_bf16x2(am));
         const uint32_t q0 = e4m3x4(bf16_lo(v.x) * sp.r, bf16_hi(v.x) * sp.r,
                                    bf16_lo(v.y) * sp.r, bf16_hi(v.y) * sp.r);
         const uint32_t q1 = e4m3x4(bf16_lo(v.z) * sp.r, bf16_hi(v.z) * sp.r,
@@ -563,7 +588,7 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
   }
 }
 
-template <class CFG, int MODE, int OUT, bool ACCUM, bool FUSEQ, int GRP = kGrpNone>
+template <class CFG, int MODE, int OUT, bool ACCUM, bool FUSEQ, int GRP = kGrpNone, bool P2 = false>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
   const int64_t nbm = (a.M + CFG::BM - 1) / CFG::BM;
   const int64_t nbn = (a.N + CFG::BN - 1) / CFG::BN;
@@ -575,7 +600,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
   if (GRP != kGrpNone) blocks = (blocks + 7) / 8 * 8;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_gemm_fp8<CFG, MODE, OUT, ACCUM, FUSEQ, GRP>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((k_gemm_fp8<CFG, MODE, OUT, ACCUM, FUSEQ, GRP, P2>), dim3((unsigned)blocks),
                      dim3(CFG::THREADS), 0, st, a);
   return hipGetLastError();
 }
@@ -587,16 +612,16 @@ using CfgMain = GemmCfg<2, 4, 8, 4, 2, false>;
 // wave of workgroups.
 using CfgSmall = GemmCfg<2, 2, 4, 4, 2, false, 2>;
 
-template <class CFG, int GRP = kGrpNone>
+template <class CFG, int GRP = kGrpNone, bool P2 = false>
 hipError_t dispatch(const GemmArgs& a, int mode, int out, bool accum, bool fuseq, hipStream_t st) {
   if (mode == kRowBlock) {
-    if (fuseq) return launch_cfg<CFG, kRowBlock, kOutBf16, false, true, GRP>(a, st);
-    if (out == kOutBf16) return launch_cfg<CFG, kRowBlock, kOutBf16, false, false, GRP>(a, st);
-    return launch_cfg<CFG, kRowBlock, kOutF32, false, false, GRP>(a, st);
+    if (fuseq) return launch_cfg<CFG, kRowBlock, kOutBf16, false, true, GRP, P2>(a, st);
+    if (out == kOutBf16) return launch_cfg<CFG, kRowBlock, kOutBf16, false, false, GRP, P2>(a, st);
+    return launch_cfg<CFG, kRowBlock, kOutF32, false, false, GRP, P2>(a, st);
   }
-  if (out == kOutBf16) return launch_cfg<CFG, kRowCol, kOutBf16, false, false, GRP>(a, st);
-  if (accum) return launch_cfg<CFG, kRowCol, kOutF32, true, false, GRP>(a, st);
-  return launch_cfg<CFG, kRowCol, kOutF32, false, false, GRP>(a, st);
+  if (out == kOutBf16) return launch_cfg<CFG, kRowCol, kOutBf16, false, false, GRP, P2>(a, st);
+  if (accum) return launch_cfg<CFG, kRowCol, kOutF32, true, false, GRP, P2>(a, st);
+  return launch_cfg<CFG, kRowCol, kOutF32, false, false, GRP, P2>(a, st);
 }
 
 // Compute units of the current device (cached per device).
@@ -614,7 +639,7 @@ static int cu_count() {
 }
 
 hipError_t launch_gemm(const GemmArgs& a, int mode, int out, bool accum, bool fuseq,
-                       hipStream_t st) {
+                       hipStream_t st, bool p2) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
   // The big tile keeps the most work per byte staged; use it unless its last
   // wave of workgroups would leave more than a tenth of the CUs idle.
@@ -622,7 +647,12 @@ hipError_t launch_gemm(const GemmArgs& a, int mode, int out, bool accum, bool fu
                         (int64_t)((a.N + CfgMain::BN - 1) / CfgMain::BN);
   const int64_t cus = cu_count();
   const int64_t slots = (tiles + cus - 1) / cus * cus;
-  if (tiles * 10 >= slots * 9) return dispatch<CfgMain>(a, mode, out, accum, fuseq, st);
+  const bool big = tiles * 10 >= slots * 9;
+  if (p2) {
+    if (big) return dispatch<CfgMain, kGrpNone, true>(a, mode, out, accum, fuseq, st);
+    return dispatch<CfgSmall, kGrpNone, true>(a, mode, out, accum, fuseq, st);
+  }
+  if (big) return dispatch<CfgMain>(a, mode, out, accum, fuseq, st);
   return dispatch<CfgSmall>(a, mode, out, accum, fuseq, st);
 }
 

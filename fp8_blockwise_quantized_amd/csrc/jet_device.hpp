@@ -93,6 +93,23 @@ __device__ __forceinline__ ScalePair scale_pair(float amax) {
   return ScalePair{a / kE4M3Max, kE4M3Max / a};
 }
 
+// Power-of-two scale (the variant for the MFMA's E8M0 operand scales):
+// s = 2^e with e the smallest integer for which 448 * 2^e >= a, r = 2^-e.
+// a = (1 + f/2^23) * 2^E is a normal FP32 number (a >= 2^-96) and
+// 448 = 1.75 * 2^8, so e = E - 8 when f <= 0.75 * 2^23 and E - 7 otherwise;
+// -104 <= e <= 120 for finite amax, so both s and r are normal and exact.
+__device__ __forceinline__ ScalePair scale_pair_pow2(float amax) {
+  const uint32_t b = __float_as_uint(fmaxf(amax, kAmaxFloor));
+  const int e = (int)(b >> 23) - 127 - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  return ScalePair{__uint_as_float((uint32_t)(127 + e) << 23), __uint_as_float((uint32_t)(127 - e) << 23)};
+}
+
+template <bool P2>
+__device__ __forceinline__ ScalePair scale_rule(float amax) {
+  if constexpr (P2) return scale_pair_pow2(amax);
+  else return scale_pair(amax);
+}
+
 // ---------------------------------------------------------------------------
 // E4M3 conversion.  v_cvt_pk_fp8_f32 on gfx950 converts to OCP E4M3 with
 // round-to-nearest-even; the packed byte order is (a, b) into bytes 0/1 of the

@@ -34,18 +34,20 @@ struct GemmArgs {
   int kcap;
 };
 
+// p2: power-of-two scales (scale_pair_pow2) instead of amax / 448.
 hipError_t launch_quant_1x128(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
-                              int64_t ldq, float* s, hipStream_t st);
+                              int64_t ldq, float* s, hipStream_t st, bool p2 = false);
 hipError_t launch_quant_128x128(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
-                                float* s, uint8_t* qT, hipStream_t st);
+                                float* s, uint8_t* qT, hipStream_t st, bool p2 = false);
 hipError_t launch_quant_128x1_T(const void* src, bool fp8src, const float* src_s, int64_t M,
                                 int64_t K, int64_t ldsrc, uint8_t* qT, int64_t ldqT, float* sT,
-                                hipStream_t st);
+                                hipStream_t st, bool p2 = false);
 // 1x128 (q, s) and 128x1 transposed (qT, sT) of one BF16 activation in one read;
 // requant: the 128x1 groups quantize the dequantized 1x128 values.
 hipError_t launch_quant_1x128_128x1_T(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                       uint8_t* q, int64_t ldq, float* s, uint8_t* qT,
-                                      int64_t ldqT, float* sT, bool requant, hipStream_t st);
+                                      int64_t ldqT, float* sT, bool requant, hipStream_t st,
+                                      bool p2 = false);
 // Fused producers of the 1x128 input: RMSNorm (H <= 8192) and SwiGLU; y / h
 // (the BF16 tensor) may be null.
 hipError_t launch_rmsnorm_quant_1x128(const uint16_t* x, const uint16_t* gamma, int64_t M, int64_t H,
@@ -60,8 +62,11 @@ hipError_t launch_kv_calibrate(const uint16_t* k, const uint16_t* v, int64_t T, 
 hipError_t launch_kv_append(const uint16_t* k, const uint16_t* v, int64_t T, int64_t D, int64_t ldk,
                             int64_t ldv, const int64_t* slots, const float* scales, uint8_t* kc, uint8_t* vc,
                             int64_t ldc, int64_t rows, hipStream_t st);
+// p2: every scale is a power of two and is applied by the MFMA itself (E8M0
+// operand scales), accumulating across K steps inside the MFMA; the fused
+// 1x128 quantization of the output then uses power-of-two scales too.
 hipError_t launch_gemm(const GemmArgs& a, int mode, int out, bool accum, bool fuseq,
-                       hipStream_t st);
+                       hipStream_t st, bool p2 = false);
 // Small-M forward (M <= kSkinnyMaxM): one kernel when the K steps are not
 // split; otherwise split-K partial sums in the caller's workspace
 // (skinny_workspace_bytes) and a deterministic finishing pass.

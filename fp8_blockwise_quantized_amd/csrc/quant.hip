@@ -34,6 +34,7 @@ namespace jet {
 // block strides over the units by the grid size; consecutive units continue
 // along the rows.
 // ---------------------------------------------------------------------------
+template <bool P2>
 __global__ __launch_bounds__(256) void k_quant_1x128(const uint16_t* __restrict__ x, int64_t M,
                                                      int64_t K, int64_t ldx,
                                                      uint8_t* __restrict__ q, int64_t ldq,
@@ -62,7 +63,7 @@ __global__ __launch_bounds__(256) void k_quant_1x128(const uint16_t* __restrict_
       am = max_abs_bf16x2(am, v[p].z);
       am = max_abs_bf16x2(am, v[p].w);
       am = row16_max_u16x2(am);
-      const ScalePair sp = scale_pair(fold_bf16x2(am));
+      const ScalePair sp = scale_rule<P2>(fold_bf16x2(am));
       const uint32_t c0 = e4m3x4(bf16_lo(v[p].x) * sp.r, bf16_hi(v[p].x) * sp.r,
                                  bf16_lo(v[p].y) * sp.r, bf16_hi(v[p].y) * sp.r);
       const uint32_t c1 = e4m3x4(bf16_lo(v[p].z) * sp.r, bf16_hi(v[p].z) * sp.r,
@@ -80,13 +81,15 @@ __global__ __launch_bounds__(256) void k_quant_1x128(const uint16_t* __restrict_
 }
 
 hipError_t launch_quant_1x128(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
-                              int64_t ldq, float* s, hipStream_t st) {
+                              int64_t ldq, float* s, hipStream_t st, bool p2) {
   if (M == 0 || K == 0) return hipSuccess;
   constexpr int64_t kMaxBlocks = 2048;
   const int64_t units = ((M + 31) / 32) * ((K / kGroup + 3) / 4);
   const int64_t blocks = std::min<int64_t>(units, kMaxBlocks);
-  hipLaunchKernelGGL(k_quant_1x128, dim3((unsigned)blocks), dim3(256), 0, st, x, M, K, ldx, q, ldq,
-                     s);
+  if (p2)
+    hipLaunchKernelGGL(k_quant_1x128<true>, dim3((unsigned)blocks), dim3(256), 0, st, x, M, K, ldx, q, ldq, s);
+  else
+    hipLaunchKernelGGL(k_quant_1x128<false>, dim3((unsigned)blocks), dim3(256), 0, st, x, M, K, ldx, q, ldq, s);
   return hipGetLastError();
 }
 
@@ -102,6 +105,7 @@ __device__ __forceinline__ int tT_off(int k, int b) {
   return (k ^ ((k >> 3) & 1)) * kGroup + (b ^ (((k >> 3) & 7) << 4));
 }
 
+template <bool P2>
 __global__ __launch_bounds__(256) void k_quant_128x128(const uint16_t* __restrict__ w, int64_t N,
                                                        int64_t K, int64_t ldw,
                                                        uint8_t* __restrict__ q,
@@ -131,7 +135,7 @@ __global__ __launch_bounds__(256) void k_quant_128x128(const uint16_t* __restric
   am = red[0];
 #pragma unroll
   for (int i = 1; i < 16; ++i) am = max_abs_bf16x2(am, red[i]);
-  const ScalePair sp = scale_pair(fold_bf16x2(am));
+  const ScalePair sp = scale_rule<P2>(fold_bf16x2(am));
   if (threadIdx.x == 0) s[nb * (K / kGroup) + kb] = sp.s;
 
   float f[8][8];
@@ -172,10 +176,13 @@ __global__ __launch_bounds__(256) void k_quant_128x128(const uint16_t* __restric
 }
 
 hipError_t launch_quant_128x128(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
-                                float* s, uint8_t* qT, hipStream_t st) {
+                                float* s, uint8_t* qT, hipStream_t st, bool p2) {
   if (N == 0 || K == 0) return hipSuccess;
   dim3 grid((unsigned)(K / kGroup), (unsigned)(N / kGroup));
-  hipLaunchKernelGGL(k_quant_128x128, grid, dim3(256), 0, st, w, N, K, ldw, q, s, qT);
+  if (p2)
+    hipLaunchKernelGGL(k_quant_128x128<true>, grid, dim3(256), 0, st, w, N, K, ldw, q, s, qT);
+  else
+    hipLaunchKernelGGL(k_quant_128x128<false>, grid, dim3(256), 0, st, w, N, K, ldw, q, s, qT);
   return hipGetLastError();
 }
 
@@ -199,7 +206,7 @@ hipError_t launch_quant_128x128(const uint16_t* w, int64_t N, int64_t K, int64_t
 // separate quantizers bit for bit.  Rows at or past M are zeros: they have no
 // 1x128 output and encode to zero codes in the transposed padding columns.
 // ---------------------------------------------------------------------------
-template <bool REQUANT, int RG>
+template <bool REQUANT, int RG, bool P2>
 __global__ __launch_bounds__(256 * RG) void k_quant_1x128_128x1_T(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, uint8_t* __restrict__ q,
     int64_t ldq, float* __restrict__ s, uint8_t* __restrict__ qT, int64_t ldqT,
@@ -238,7 +245,7 @@ __global__ __launch_bounds__(256 * RG) void k_quant_1x128_128x1_T(
   uint32_t mine = amr[0];
 #pragma unroll
   for (int i = 1; i < 8; ++i) mine = ((c & 7) == i) ? amr[i] : mine;
-  const ScalePair own = scale_pair(fold_bf16x2(mine));
+  const ScalePair own = scale_rule<P2>(fold_bf16x2(mine));
   if (c < 8 && m0 + c < M) s[kb * M + m0 + c] = own.s;
   float rr[8], rs[8];
   row_bcast8(own.r, rr);
@@ -317,7 +324,7 @@ __global__ __launch_bounds__(256 * RG) void k_quant_1x128_128x1_T(
       for (int w = 1; w < 4; ++w) u = max_abs_bf16x2(u, cred[4 * cg + w][cc][jj >> 1]);
       amax = __uint_as_float(((jj & 1) ? (u >> 16) : (u & 0xFFFFu)) << 16);
     }
-    const ScalePair sp = scale_pair(amax);
+    const ScalePair sp = scale_rule<P2>(amax);
     colR[cg][col] = sp.r;
     const int64_t gg = (int64_t)blockIdx.y * RG + cg;
     if (gg < G) sT[gg * K + kb * kGroup + col] = sp.s;
@@ -361,17 +368,20 @@ __global__ __launch_bounds__(256 * RG) void k_quant_1x128_128x1_T(
 
 hipError_t launch_quant_1x128_128x1_T(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                       uint8_t* q, int64_t ldq, float* s, uint8_t* qT,
-                                      int64_t ldqT, float* sT, bool requant, hipStream_t st) {
+                                      int64_t ldqT, float* sT, bool requant, hipStream_t st, bool p2) {
   if (M == 0 || K == 0) return hipSuccess;
   constexpr int RG = 2;   // two row groups per block: 256-byte runs in every qT row
   const int64_t G = (M + kGroup - 1) / kGroup;
   dim3 grid((unsigned)(K / kGroup), (unsigned)((G + RG - 1) / RG));
-  if (requant)
-    hipLaunchKernelGGL((k_quant_1x128_128x1_T<true, RG>), grid, dim3(256 * RG), 0, st, x, M, K, ldx,
-                       q, ldq, s, qT, ldqT, sT);
-  else
-    hipLaunchKernelGGL((k_quant_1x128_128x1_T<false, RG>), grid, dim3(256 * RG), 0, st, x, M, K, ldx,
-                       q, ldq, s, qT, ldqT, sT);
+#define JET_Q11T(rq_, p2_)                                                                       \
+  hipLaunchKernelGGL((k_quant_1x128_128x1_T<rq_, RG, p2_>), grid, dim3(256 * RG), 0, st, x, M, K, \
+                     ldx, q, ldq, s, qT, ldqT, sT)
+  if (requant) {
+    if (p2) JET_Q11T(true, true); else JET_Q11T(true, false);
+  } else {
+    if (p2) JET_Q11T(false, true); else JET_Q11T(false, false);
+  }
+#undef JET_Q11T
   return hipGetLastError();
 }
 
@@ -397,7 +407,7 @@ hipError_t launch_quant_1x128_128x1_T(const uint16_t* x, int64_t M, int64_t K, i
 // (segment e owns slots first_e .. first_e + ceil(len_e/128) - 1), which is
 // also its output column block: the padded layout of the grouped WGrad.
 // ---------------------------------------------------------------------------
-template <bool FP8SRC, bool GROUPED>
+template <bool FP8SRC, bool GROUPED, bool P2>
 __global__ __launch_bounds__(256) void k_quant_128x1_T(const void* __restrict__ src,
                                                        const float* __restrict__ src_s,
                                                        int64_t M, int64_t K, int64_t ldsrc,
@@ -478,7 +488,7 @@ __global__ __launch_bounds__(256) void k_quant_128x1_T(const void* __restrict__ 
 #pragma unroll
   for (int jj = 0; jj < CW; ++jj) {
     const uint32_t other = __float_as_uint(red[wave ^ 1][lane & 7][jj]);
-    const ScalePair sp = scale_pair(__uint_as_float(max(am[jj], other)));
+    const ScalePair sp = scale_rule<P2>(__uint_as_float(max(am[jj], other)));
     rr[jj] = sp.r;
     ss[jj] = sp.s;
   }
@@ -498,18 +508,18 @@ __global__ __launch_bounds__(256) void k_quant_128x1_T(const void* __restrict__ 
   }
 }
 
-template <bool GROUPED>
+template <bool GROUPED, bool P2>
 static hipError_t launch_128x1_T(const void* src, bool fp8src, const float* src_s, int64_t M,
                                  int64_t K, int64_t ldsrc, const int32_t* seg, int E,
                                  unsigned groups, uint8_t* qT, int64_t ldqT, float* sT,
                                  hipStream_t st) {
   if (fp8src) {
     dim3 grid((unsigned)((K + 255) / 256), groups);
-    hipLaunchKernelGGL((k_quant_128x1_T<true, GROUPED>), grid, dim3(256), 0, st, src, src_s, M, K,
+    hipLaunchKernelGGL((k_quant_128x1_T<true, GROUPED, P2>), grid, dim3(256), 0, st, src, src_s, M, K,
                        ldsrc, seg, E, qT, ldqT, sT);
   } else {
     dim3 grid((unsigned)(K / kGroup), groups);
-    hipLaunchKernelGGL((k_quant_128x1_T<false, GROUPED>), grid, dim3(256), 0, st, src, src_s, M,
+    hipLaunchKernelGGL((k_quant_128x1_T<false, GROUPED, P2>), grid, dim3(256), 0, st, src, src_s, M,
                        K, ldsrc, seg, E, qT, ldqT, sT);
   }
   return hipGetLastError();
@@ -517,11 +527,13 @@ static hipError_t launch_128x1_T(const void* src, bool fp8src, const float* src_
 
 hipError_t launch_quant_128x1_T(const void* src, bool fp8src, const float* src_s, int64_t M,
                                 int64_t K, int64_t ldsrc, uint8_t* qT, int64_t ldqT, float* sT,
-                                hipStream_t st) {
+                                hipStream_t st, bool p2) {
   if (M == 0 || K == 0) return hipSuccess;
   const unsigned groups = (unsigned)((M + kGroup - 1) / kGroup);
-  return launch_128x1_T<false>(src, fp8src, src_s, M, K, ldsrc, nullptr, 0, groups, qT, ldqT, sT,
-                               st);
+  if (p2)
+    return launch_128x1_T<false, true>(src, fp8src, src_s, M, K, ldsrc, nullptr, 0, groups, qT, ldqT, sT, st);
+  return launch_128x1_T<false, false>(src, fp8src, src_s, M, K, ldsrc, nullptr, 0, groups, qT, ldqT, sT,
+                                      st);
 }
 
 hipError_t launch_quant_128x1_T_grouped(const void* src, bool fp8src, const float* src_s,
@@ -531,7 +543,7 @@ hipError_t launch_quant_128x1_T_grouped(const void* src, bool fp8src, const floa
   if (M == 0 || K == 0) return hipSuccess;
   // at most ceil(M/128) + E groups over all segments
   const unsigned slots = (unsigned)((M + kGroup - 1) / kGroup + E);
-  return launch_128x1_T<true>(src, fp8src, src_s, M, K, ldsrc, seg, E, slots, qT, ldqT, sT, st);
+  return launch_128x1_T<true, false>(src, fp8src, src_s, M, K, ldsrc, seg, E, slots, qT, ldqT, sT, st);
 }
 
 }  // namespace jet

@@ -46,6 +46,13 @@ SIGNATURES = {
     "jet_fp8_grouped_dgrad": [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p, _i32, _p, _sz, _p],
     "jet_fp8_grouped_wgrad": [_p, _p, _p, _p, _i64, _p, _i64, _i64, _i64, _i64, _p, _i32, _i32, _p,
                               _sz, _p],
+    "jet_quant_act_1x128_pow2": [_p, _i64, _i64, _i64, _p, _i64, _p, _p],
+    "jet_quant_act_128x1_T_pow2": [_p, _i32, _p, _i64, _i64, _i64, _p, _i64, _p, _p],
+    "jet_quant_act_1x128_128x1_T_pow2": [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _i32, _p],
+    "jet_quant_weight_128x128_pow2": [_p, _i64, _i64, _i64, _p, _p, _p, _p],
+    "jet_fp8_linear_fwd_pow2": [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _p, _p, _p],
+    "jet_fp8_linear_dgrad_pow2": [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _p],
+    "jet_fp8_linear_wgrad_pow2": [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _i32, _p],
 }
 _RESTYPES = {"jet_status_string": ctypes.c_char_p, "jet_last_error": ctypes.c_char_p,
              "jet_workspace_bytes": _sz}
@@ -129,6 +136,15 @@ def jet_workspace_bytes(op: int, M: int, N: int, K: int) -> int:
 
 def jet_quant_act_1x128(x, q=None, s=None, stream=None):
     """x BF16 [M, K] -> (q uint8 [M, K], s float32 [K/128, M])."""
+    return _quant_1x128("jet_quant_act_1x128", x, q, s, stream)
+
+
+def jet_quant_act_1x128_pow2(x, q=None, s=None, stream=None):
+    """As jet_quant_act_1x128 with power-of-two scales."""
+    return _quant_1x128("jet_quant_act_1x128_pow2", x, q, s, stream)
+
+
+def _quant_1x128(name, x, q, s, stream):
     _rowmajor(x, "x")
     if x.dtype != torch.bfloat16:
         raise TypeError("x must be bfloat16")
@@ -136,7 +152,7 @@ def jet_quant_act_1x128(x, q=None, s=None, stream=None):
     q = _codes(q) if q is not None else _empty((M, K), torch.uint8, x)
     s = s if s is not None else _empty((K // 128, M), torch.float32, x)
     _rowmajor(q, "q")
-    _check("jet_quant_act_1x128", _lib.jet_quant_act_1x128(
+    _check(name, getattr(_lib, name)(
         _ptr(x), M, K, x.stride(0), _ptr(q), q.stride(0), _ptr(s), _stream(stream)))
     return q, s
 
@@ -232,6 +248,15 @@ def jet_quant_act_128x1_T(src, src_s=None, qT=None, sT=None, stream=None):
     src_s [K/128, M].  Returns (qT uint8 [K, Mp], sT float32 [Mp/128, K]),
     Mp = ceil(M/128)*128.
     """
+    return _quant_128x1_T("jet_quant_act_128x1_T", src, src_s, qT, sT, stream)
+
+
+def jet_quant_act_128x1_T_pow2(src, src_s=None, qT=None, sT=None, stream=None):
+    """As jet_quant_act_128x1_T with power-of-two scales."""
+    return _quant_128x1_T("jet_quant_act_128x1_T_pow2", src, src_s, qT, sT, stream)
+
+
+def _quant_128x1_T(name, src, src_s, qT, sT, stream):
     _rowmajor(src, "src")
     M, K = src.shape
     if src_s is None:
@@ -245,7 +270,7 @@ def jet_quant_act_128x1_T(src, src_s=None, qT=None, sT=None, stream=None):
     qT = _codes(qT) if qT is not None else _empty((K, Mp), torch.uint8, src)
     sT = sT if sT is not None else _empty((Mp // 128, K), torch.float32, src)
     _rowmajor(qT, "qT")
-    _check("jet_quant_act_128x1_T", _lib.jet_quant_act_128x1_T(
+    _check(name, getattr(_lib, name)(
         _ptr(src), dt, _ptr(src_s), M, K, src.stride(0), _ptr(qT), qT.stride(0), _ptr(sT),
         _stream(stream)))
     return qT, sT
@@ -259,6 +284,15 @@ def jet_quant_act_1x128_128x1_T(x, requant, q=None, s=None, qT=None, sT=None, st
     jet_quant_act_128x1_T(x) (requant False) or jet_quant_act_128x1_T(q, s)
     (requant True).
     """
+    return _quant_1x128_128x1_T("jet_quant_act_1x128_128x1_T", x, requant, q, s, qT, sT, stream)
+
+
+def jet_quant_act_1x128_128x1_T_pow2(x, requant, q=None, s=None, qT=None, sT=None, stream=None):
+    """As jet_quant_act_1x128_128x1_T with power-of-two scales."""
+    return _quant_1x128_128x1_T("jet_quant_act_1x128_128x1_T_pow2", x, requant, q, s, qT, sT, stream)
+
+
+def _quant_1x128_128x1_T(name, x, requant, q, s, qT, sT, stream):
     _rowmajor(x, "x")
     if x.dtype != torch.bfloat16:
         raise TypeError("x must be bfloat16")
@@ -270,7 +304,7 @@ def jet_quant_act_1x128_128x1_T(x, requant, q=None, s=None, qT=None, sT=None, st
     sT = sT if sT is not None else _empty((Mp // 128, K), torch.float32, x)
     _rowmajor(q, "q")
     _rowmajor(qT, "qT")
-    _check("jet_quant_act_1x128_128x1_T", _lib.jet_quant_act_1x128_128x1_T(
+    _check(name, getattr(_lib, name)(
         _ptr(x), M, K, x.stride(0), _ptr(q), q.stride(0), _ptr(s), _ptr(qT), qT.stride(0),
         _ptr(sT), 1 if requant else 0, _stream(stream)))
     return q, s, qT, sT
@@ -278,6 +312,15 @@ def jet_quant_act_1x128_128x1_T(x, requant, q=None, s=None, qT=None, sT=None, st
 
 def jet_quant_weight_128x128(w, q=None, s=None, qT=None, transposed=True, stream=None):
     """w BF16 [N, K] -> (q uint8 [N, K], s float32 [N/128, K/128], qT uint8 [K, N] or None)."""
+    return _quant_weight("jet_quant_weight_128x128", w, q, s, qT, transposed, stream)
+
+
+def jet_quant_weight_128x128_pow2(w, q=None, s=None, qT=None, transposed=True, stream=None):
+    """As jet_quant_weight_128x128 with power-of-two scales."""
+    return _quant_weight("jet_quant_weight_128x128_pow2", w, q, s, qT, transposed, stream)
+
+
+def _quant_weight(name, w, q, s, qT, transposed, stream):
     _rowmajor(w, "w")
     if w.dtype != torch.bfloat16:
         raise TypeError("w must be bfloat16")
@@ -287,7 +330,7 @@ def jet_quant_weight_128x128(w, q=None, s=None, qT=None, transposed=True, stream
     if transposed and qT is None:
         qT = _empty((K, N), torch.uint8, w)
     qT = _codes(qT)
-    _check("jet_quant_weight_128x128", _lib.jet_quant_weight_128x128(
+    _check(name, getattr(_lib, name)(
         _ptr(w), N, K, w.stride(0), _ptr(q), _ptr(s), _ptr(qT), _stream(stream)))
     return q, s, qT
 
@@ -362,6 +405,46 @@ def jet_fp8_linear_wgrad(dyqT, dysT, xqT, xsT, M, dw=None, out_dtype=torch.float
         _ptr(dyqT), _ptr(dysT), _ptr(xqT), _ptr(xsT), M, N, K, _ptr(dw), _dtype_code(dw.dtype),
         1 if accumulate else 0, _ptr(workspace), 0 if workspace is None else workspace.numel(),
         _stream(stream)))
+    return dw
+
+
+def jet_fp8_linear_fwd_pow2(xq, xs, wq, ws, y=None, out_dtype=torch.bfloat16, fuse_quant=False,
+                            yq=None, ys=None, stream=None):
+    """Forward on power-of-two-scaled operands (scales applied by the MFMA).
+    Returns y, or (y, yq, ys) with the power-of-two 1x128 quantization of Y."""
+    xq, wq = _codes(xq), _codes(wq)
+    M, K = xq.shape
+    N = wq.shape[0]
+    y = y if y is not None else _empty((M, N), out_dtype, xq)
+    if fuse_quant:
+        yq = _codes(yq) if yq is not None else _empty((M, N), torch.uint8, xq)
+        ys = ys if ys is not None else _empty((N // 128, M), torch.float32, xq)
+    _check("jet_fp8_linear_fwd_pow2", _lib.jet_fp8_linear_fwd_pow2(
+        _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), M, N, K, _ptr(y), _dtype_code(y.dtype), _ptr(yq), _ptr(ys),
+        _stream(stream)))
+    return (y, yq, ys) if fuse_quant else y
+
+
+def jet_fp8_linear_dgrad_pow2(dyq, dys, wqT, ws, dx=None, out_dtype=torch.bfloat16, stream=None):
+    """DGrad on power-of-two-scaled operands; wqT the transposed weight codes [K, N]."""
+    dyq, wqT = _codes(dyq), _codes(wqT)
+    M, N = dyq.shape
+    K = wqT.shape[0]
+    dx = dx if dx is not None else _empty((M, K), out_dtype, dyq)
+    _check("jet_fp8_linear_dgrad_pow2", _lib.jet_fp8_linear_dgrad_pow2(
+        _ptr(dyq), _ptr(dys), _ptr(wqT), _ptr(ws), M, N, K, _ptr(dx), _dtype_code(dx.dtype), _stream(stream)))
+    return dx
+
+
+def jet_fp8_linear_wgrad_pow2(dyqT, dysT, xqT, xsT, M, dw=None, out_dtype=torch.float32, accumulate=False,
+                              stream=None):
+    """WGrad on power-of-two-scaled 128x1 operands ([N, Mp], [K, Mp])."""
+    dyqT, xqT = _codes(dyqT), _codes(xqT)
+    N, K = dyqT.shape[0], xqT.shape[0]
+    dw = dw if dw is not None else _empty((N, K), out_dtype, dyqT)
+    _check("jet_fp8_linear_wgrad_pow2", _lib.jet_fp8_linear_wgrad_pow2(
+        _ptr(dyqT), _ptr(dysT), _ptr(xqT), _ptr(xsT), M, N, K, _ptr(dw), _dtype_code(dw.dtype),
+        1 if accumulate else 0, _stream(stream)))
     return dw
 
 

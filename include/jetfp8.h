@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define JET_ABI_VERSION 6
+#define JET_ABI_VERSION 7
 
 typedef enum {
   JET_OK = 0,
@@ -401,6 +401,52 @@ int jet_fp8_grouped_wgrad(const uint8_t* dyqT, const float* dysT,
                           int64_t M, int64_t N, int64_t K,
                           void* dw, int dw_dtype, int accumulate,
                           void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Power-of-two-scale variant.  Not on the pages: their group scale is the FP32
+ * value amax/448 (explainer "Quantisierungsschema"; 163.com section 七: scales
+ * follow the data).  gfx950's block-scaled MFMA takes its operand scales as
+ * 8-bit powers of two (E8M0, 2^(b-127)); with power-of-two group scales the
+ * GEMMs hand each scale to the MFMA and accumulate across the 128-wide K steps
+ * inside it, so no FP32 rescaling runs per step.  Scale of a group:
+ *     amax_c = max(amax, 2^-96),  s = 2^e with e the smallest integer for
+ *     which 448 * 2^e >= amax_c,  code = E4M3(x * 2^-e)
+ * (-104 <= e <= 120 for finite data; nothing saturates and the group maximum encodes within
+ * (224, 448]).  The scales are stored as FP32 values, in the layouts of the
+ * FP32-scale entry points, so the two sets of quantizers and GEMMs take the
+ * same buffers; but the _pow2 GEMMs read only the exponent field of each
+ * scale (a scale that is not a power of two is taken as the power of two
+ * below it), so feed them the _pow2 quantizers' output.  Each _pow2 entry point
+ * takes the arguments, layouts and limits of its FP32-scale twin and reports
+ * the same errors; the GEMMs take no workspace.  The forward at M <= 128 runs
+ * the tiled kernel (no weight-streaming split), so it is batch-invariant at
+ * every M.
+ */
+int jet_quant_act_1x128_pow2(const void* x, int64_t M, int64_t K, int64_t ldx,
+                             uint8_t* q, int64_t ldq, float* s, void* stream);
+int jet_quant_act_128x1_T_pow2(const void* src, int src_dtype, const float* src_s,
+                               int64_t M, int64_t K, int64_t ldsrc,
+                               uint8_t* qT, int64_t ldqT, float* sT, void* stream);
+int jet_quant_act_1x128_128x1_T_pow2(const void* x, int64_t M, int64_t K, int64_t ldx,
+                                     uint8_t* q, int64_t ldq, float* s,
+                                     uint8_t* qT, int64_t ldqT, float* sT,
+                                     int requant, void* stream);
+int jet_quant_weight_128x128_pow2(const void* w, int64_t N, int64_t K, int64_t ldw,
+                                  uint8_t* q, float* s, uint8_t* qT, void* stream);
+/* yq, ys (optional): the power-of-two 1x128 quantization of the BF16 Y. */
+int jet_fp8_linear_fwd_pow2(const uint8_t* xq, const float* xs,
+                            const uint8_t* wq, const float* ws,
+                            int64_t M, int64_t N, int64_t K,
+                            void* y, int y_dtype, uint8_t* yq, float* ys,
+                            void* stream);
+int jet_fp8_linear_dgrad_pow2(const uint8_t* dyq, const float* dys,
+                              const uint8_t* wqT, const float* ws,
+                              int64_t M, int64_t N, int64_t K,
+                              void* dx, int dx_dtype, void* stream);
+int jet_fp8_linear_wgrad_pow2(const uint8_t* dyqT, const float* dysT,
+                              const uint8_t* xqT, const float* xsT,
+                              int64_t M, int64_t N, int64_t K,
+                              void* dw, int dw_dtype, int accumulate, void* stream);
 
 #ifdef __cplusplus
 }

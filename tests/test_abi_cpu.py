@@ -48,7 +48,7 @@ def test_binding_covers_header(J):
 
 
 def test_version_and_status_strings(J):
-    assert J.jet_abi_version() == 6
+    assert J.jet_abi_version() == 7
     assert J.jet_status_string(J.JET_ERR_SHAPE) == "JET_ERR_SHAPE"
     assert J.jet_status_string(99) == "JET_ERR_UNKNOWN"
 
@@ -232,3 +232,39 @@ def test_grouped_validation(J):
                                    None) == J.JET_ERR_DTYPE
     assert L.jet_fp8_grouped_fwd(None, None, None, None, P16, 2, 0, 128, 128, None, J.JET_BF16, None,
                                  None, None, 0, None) == J.JET_OK          # no rows: no-op
+
+
+def test_pow2_entry_points_validate_like_their_twins(J):
+    """The power-of-two-scale entry points share their twins' checks (and name
+    themselves in the error text); the GEMMs take no workspace."""
+    L = J._lib
+    assert L.jet_quant_act_1x128_pow2(P16, 4, 100, 128, P16, 128, P16, None) == J.JET_ERR_SHAPE
+    assert "quant_act_1x128_pow2" in J.jet_last_error()
+    assert L.jet_quant_act_1x128_pow2(P17, 4, 128, 128, P16, 128, P16, None) == J.JET_ERR_ALIGN
+    assert L.jet_quant_act_1x128_pow2(None, 0, 128, 128, None, 128, None, None) == J.JET_OK
+    assert L.jet_quant_act_128x1_T_pow2(P16, 7, None, 4, 128, 128, P16, 128, P16, None) == J.JET_ERR_DTYPE
+    assert L.jet_quant_act_128x1_T_pow2(P16, J.JET_E4M3, None, 4, 128, 128, P16, 128, P16,
+                                        None) == J.JET_ERR_NULL
+    Q2 = L.jet_quant_act_1x128_128x1_T_pow2
+    assert Q2(P16, 4, 128, 128, P16, 128, P16, P16, 128, P16, 2, None) == J.JET_ERR_DTYPE
+    assert Q2(P16, 200, 128, 128, P16, 128, P16, P16, 200, P16, 0, None) == J.JET_ERR_SHAPE
+    assert "128x1_T_pow2" in J.jet_last_error()
+    assert L.jet_quant_weight_128x128_pow2(P16, 100, 128, 128, P16, P16, None, None) == J.JET_ERR_SHAPE
+    assert L.jet_quant_weight_128x128_pow2(P16, 128, 128, 128, P16, P16, P17, None) == J.JET_ERR_ALIGN
+    a = (P16, P16, P16, P16)
+    f = L.jet_fp8_linear_fwd_pow2
+    assert f(*a, 64, 100, 128, P16, J.JET_BF16, None, None, None) == J.JET_ERR_SHAPE
+    assert "fwd_pow2" in J.jet_last_error()
+    assert f(*a, 64, 128, 128, P16, J.JET_F32, P16, P16, None) == J.JET_ERR_DTYPE
+    assert f(*a, 64, 128, 128, P16, J.JET_BF16, None, P16, None) == J.JET_ERR_NULL
+    assert f(*a, 64, 128, (1 << 24) + 128, P16, J.JET_BF16, None, None, None) == J.JET_ERR_SHAPE
+    assert f(*a, 0, 128, 128, P16, J.JET_BF16, None, None, None) == J.JET_OK
+    d = L.jet_fp8_linear_dgrad_pow2
+    assert d(*a, 64, 128, 96, P16, J.JET_BF16, None) == J.JET_ERR_SHAPE
+    assert d(*a, 64, 128, 128, P16, 9, None) == J.JET_ERR_DTYPE
+    assert d(P16, P16, P17, P16, 64, 128, 128, P16, J.JET_BF16, None) == J.JET_ERR_ALIGN
+    w = L.jet_fp8_linear_wgrad_pow2
+    assert w(*a, 64, 128, 128, P16, J.JET_BF16, 1, None) == J.JET_ERR_DTYPE
+    assert w(*a, 64, 128, 128, None, J.JET_F32, 0, None) == J.JET_ERR_NULL
+    assert w(*a, (1 << 24) + 128, 128, 128, P16, J.JET_F32, 0, None) == J.JET_ERR_SHAPE
+    assert "wgrad_pow2" in J.jet_last_error()
