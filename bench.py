@@ -65,7 +65,7 @@ def parse():
                          "(recalibration and append) of one Llama-8B layer")
     ap.add_argument("--fused-m", type=int, default=8192, help="tokens for --workload fused")
     ap.add_argument("--pow2", action="store_true",
-                    help="train: the power-of-two-scale variant (E8M0 scales applied by the MFMA)")
+                    help="train, moe: the power-of-two-scale variant (E8M0 scales applied by the MFMA)")
     ap.add_argument("--invariant", action="store_true",
                     help="decode: the batch-invariant forward (one K range, bit-identical to training)")
     ap.add_argument("--quant", choices=("both", "separate"), default="both",
@@ -143,30 +143,32 @@ class MoELayer:
             return M * N + M * N // 128 * 4 + w + M * K * 2
         return (N + K) * P + P // 128 * (N + K) * 4 + E * N * K * 4
 
-    def ops(self, J):
+    def ops(self, J, pow2=False):
         M, N, K, E, P = self.M, self.N, self.K, self.E, self.P
         wq3 = self.wq.view(E, N, K)
         ws3 = self.ws.view(E, N // 128, K // 128)
+        sfx = "_pow2" if pow2 else ""
+        f = lambda name: getattr(J, name + sfx)
         return [
             ("quant_w128x128", q_bytes_w(E * N, K), "B",
-             lambda: J.jet_quant_weight_128x128(self.w, q=self.wq, s=self.ws, qT=self.wqT)),
+             lambda: f("jet_quant_weight_128x128")(self.w, q=self.wq, s=self.ws, qT=self.wqT)),
             ("quant_1x128", q_bytes_1x128(M, K), "B",
-             lambda: J.jet_quant_act_1x128(self.x, q=self.xq, s=self.xs)),
+             lambda: f("jet_quant_act_1x128")(self.x, q=self.xq, s=self.xs)),
             ("quant_128x1_T_grouped_fp8", q_bytes_128x1_grouped(M, K, P, True), "B",
-             lambda: J.jet_quant_act_128x1_T_grouped(self.xq, self.seg, src_s=self.xs,
-                                                     qT=self.xqT, sT=self.xsT)),
+             lambda: f("jet_quant_act_128x1_T_grouped")(self.xq, self.seg, src_s=self.xs,
+                                                        qT=self.xqT, sT=self.xsT)),
             ("grouped_fwd", self.flops, "F",
-             lambda: J.jet_fp8_grouped_fwd(self.xq, self.xs, wq3, ws3, self.seg, y=self.y,
-                                           fuse_quant=True, yq=self.yq, ys=self.ys)),
+             lambda: f("jet_fp8_grouped_fwd")(self.xq, self.xs, wq3, ws3, self.seg, y=self.y,
+                                              fuse_quant=True, yq=self.yq, ys=self.ys)),
             ("quant_1x128", q_bytes_1x128(M, N), "B",
-             lambda: J.jet_quant_act_1x128(self.dy, q=self.dyq, s=self.dys)),
+             lambda: f("jet_quant_act_1x128")(self.dy, q=self.dyq, s=self.dys)),
             ("grouped_dgrad", self.flops, "F",
-             lambda: J.jet_fp8_grouped_dgrad(self.dyq, self.dys, self.wqT, ws3, self.seg, dx=self.dx)),
+             lambda: f("jet_fp8_grouped_dgrad")(self.dyq, self.dys, self.wqT, ws3, self.seg, dx=self.dx)),
             ("quant_128x1_T_grouped_bf16", q_bytes_128x1_grouped(M, N, P, False), "B",
-             lambda: J.jet_quant_act_128x1_T_grouped(self.dy, self.seg, qT=self.dyqT, sT=self.dysT)),
+             lambda: f("jet_quant_act_128x1_T_grouped")(self.dy, self.seg, qT=self.dyqT, sT=self.dysT)),
             ("grouped_wgrad", self.flops, "F",
-             lambda: J.jet_fp8_grouped_wgrad(self.dyqT, self.dysT, self.xqT, self.xsT, self.seg, M,
-                                             dw=self.dw)),
+             lambda: f("jet_fp8_grouped_wgrad")(self.dyqT, self.dysT, self.xqT, self.xsT, self.seg, M,
+                                                dw=self.dw)),
         ]
 
 
@@ -731,7 +733,7 @@ def main():
     if moe:
         seg = moe_routing()
         layers = [MoELayer(J, torch, n, N, K, seg, seed=0) for (n, N, K) in MOE_LAYERS]
-        plan = [(l.name, kind, work, unit, fn) for l in layers for (kind, work, unit, fn) in l.ops(J)]
+        plan = [(l.name, kind, work, unit, fn) for l in layers for (kind, work, unit, fn) in l.ops(J, pow2=args.pow2)]
     else:
         layers = [Layer(J, torch, n, N, K, M_TOKENS, seed=0) for (n, N, K) in LAYERS]
         plan = [(l.name, kind, work, unit, fn) for l in layers
@@ -801,7 +803,7 @@ def main():
         nbytes = sum(l.gemm_bytes(dom) for l in layers) / len(layers)
         intensity = flops / nbytes
         common = {"kernel": dom,
-                  "traffic": counters_for(dom + ("_pow2" if args.pow2 and not moe else ""),
+                  "traffic": counters_for(dom + ("_pow2" if args.pow2 else ""),
                                           MOE_COUNTERS if moe else COUNTERS),
                   "flops_per_launch": flops, "bytes_per_launch": nbytes,
                   "intensity_flop_per_byte": round(intensity, 1)}
@@ -824,6 +826,7 @@ def main():
                               f"dgrad + wgrad with every quantizer and the weight re-quantization per step",
                   "routed_rows": int(seg[-1]), "experts": MOE_EXPERTS,
                   "largest_segment": int(np.diff(seg).max()), "smallest_segment": int(np.diff(seg).min()),
+                  "scales": "power of two (E8M0, applied by the MFMA)" if args.pow2 else "FP32 amax/448",
                   "parallelism": "none (1 GPU)"}
     else:
         metric = METRIC

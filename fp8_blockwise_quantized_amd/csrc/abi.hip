@@ -437,50 +437,65 @@ static int check_grouped_common(const char* name, const int32_t* seg_off, int64_
   return JET_OK;
 }
 
-int jet_quant_act_128x1_T_grouped(const void* src, int src_dtype, const float* src_s, int64_t M,
-                                  int64_t K, int64_t ldsrc, const int32_t* seg_off, int64_t E,
-                                  uint8_t* qT, int64_t ldqT, float* sT, void* stream) {
+static int quant_128x1_T_grouped(const char* name, bool p2, const void* src, int src_dtype,
+                                 const float* src_s, int64_t M, int64_t K, int64_t ldsrc,
+                                 const int32_t* seg_off, int64_t E, uint8_t* qT, int64_t ldqT, float* sT,
+                                 void* stream) {
   g_last_error[0] = 0;
   if (src_dtype != JET_BF16 && src_dtype != JET_E4M3)
-    return fail(JET_ERR_DTYPE, "quant_act_128x1_T_grouped: src_dtype must be JET_BF16 or JET_E4M3");
-  if (int st = check_grouped_common("quant_act_128x1_T_grouped", seg_off, E, M)) return st;
+    return fail(JET_ERR_DTYPE, "%s: src_dtype must be JET_BF16 or JET_E4M3", name);
+  if (int st = check_grouped_common(name, seg_off, E, M)) return st;
   if (K < 0 || K % kG || K > kMaxDim)
-    return fail(JET_ERR_SHAPE, "quant_act_128x1_T_grouped: K must be a multiple of 128");
+    return fail(JET_ERR_SHAPE, "%s: K must be a multiple of 128", name);
   if (M == 0 || K == 0) return JET_OK;
   if ((M + kG - 1) / kG + E > 65535)
-    return fail(JET_ERR_SHAPE, "quant_act_128x1_T_grouped: ceil(M/128) + E must be <= 65535");
+    return fail(JET_ERR_SHAPE, "%s: ceil(M/128) + E must be <= 65535", name);
   const bool fp8 = src_dtype == JET_E4M3;
   if (!src || !qT || !sT || (fp8 && !src_s))
-    return fail(JET_ERR_NULL, "quant_act_128x1_T_grouped: null pointer");
+    return fail(JET_ERR_NULL, "%s: null pointer", name);
   if (ldsrc < K || ldqT < grouped_cols(M, E))
-    return fail(JET_ERR_SHAPE, "quant_act_128x1_T_grouped: ldsrc < K or ldqT < 128*(ceil(M/128)+E)");
+    return fail(JET_ERR_SHAPE, "%s: ldsrc < K or ldqT < 128*(ceil(M/128)+E)", name);
   const int64_t ld_bytes = fp8 ? ldsrc : 2 * ldsrc;
   if (!aligned(src, 16) || !aligned(qT, 16) || !aligned(sT, 16) || ld_bytes % 16 || ldqT % 16 ||
       (fp8 && !aligned(src_s, 4)))
-    return fail(JET_ERR_ALIGN, "quant_act_128x1_T_grouped: src, qT, sT need 16-byte alignment; row strides 16 bytes");
+    return fail(JET_ERR_ALIGN, "%s: src, qT, sT need 16-byte alignment; row strides 16 bytes", name);
   return hip_status(jet::launch_quant_128x1_T_grouped(src, fp8, src_s, M, K, ldsrc, seg_off, (int)E,
-                                                      qT, ldqT, sT, as_stream(stream)),
-                    "quant_act_128x1_T_grouped");
+                                                      qT, ldqT, sT, as_stream(stream), p2),
+                    name);
 }
 
-int jet_fp8_grouped_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
-                        const int32_t* seg_off, int64_t E, int64_t M, int64_t N, int64_t K, void* y,
-                        int y_dtype, uint8_t* yq, float* ys, void* workspace, size_t ws_bytes,
-                        void* stream) {
+int jet_quant_act_128x1_T_grouped(const void* src, int src_dtype, const float* src_s, int64_t M,
+                                  int64_t K, int64_t ldsrc, const int32_t* seg_off, int64_t E,
+                                  uint8_t* qT, int64_t ldqT, float* sT, void* stream) {
+  return quant_128x1_T_grouped("quant_act_128x1_T_grouped", false, src, src_dtype, src_s, M, K, ldsrc, seg_off, E,
+                               qT, ldqT, sT, stream);
+}
+
+int jet_quant_act_128x1_T_grouped_pow2(const void* src, int src_dtype, const float* src_s, int64_t M,
+                                       int64_t K, int64_t ldsrc, const int32_t* seg_off, int64_t E,
+                                       uint8_t* qT, int64_t ldqT, float* sT, void* stream) {
+  return quant_128x1_T_grouped("quant_act_128x1_T_grouped_pow2", true, src, src_dtype, src_s, M, K, ldsrc,
+                               seg_off, E, qT, ldqT, sT, stream);
+}
+
+static int grouped_fwd(const char* name, bool p2, const uint8_t* xq, const float* xs, const uint8_t* wq,
+                       const float* ws, const int32_t* seg_off, int64_t E, int64_t M, int64_t N, int64_t K,
+                       void* y, int y_dtype, uint8_t* yq, float* ys, void* workspace, size_t ws_bytes,
+                       void* stream) {
   g_last_error[0] = 0;
-  if (int st = check_grouped_common("fp8_grouped_fwd", seg_off, E, M)) return st;
-  if (int st = check_gemm_common("fp8_grouped_fwd", M, N, K, 0, ws_bytes, workspace)) return st;
+  if (int st = check_grouped_common(name, seg_off, E, M)) return st;
+  if (int st = check_gemm_common(name, M, N, K, 0, ws_bytes, workspace)) return st;
   if (y_dtype != JET_BF16 && y_dtype != JET_F32)
-    return fail(JET_ERR_DTYPE, "fp8_grouped_fwd: y_dtype must be JET_BF16 or JET_F32");
+    return fail(JET_ERR_DTYPE, "%s: y_dtype must be JET_BF16 or JET_F32", name);
   const bool fuse = yq || ys;
-  if (fuse && (!yq || !ys)) return fail(JET_ERR_NULL, "fp8_grouped_fwd: yq and ys go together");
+  if (fuse && (!yq || !ys)) return fail(JET_ERR_NULL, "%s: yq and ys go together", name);
   if (fuse && y_dtype != JET_BF16)
-    return fail(JET_ERR_DTYPE, "fp8_grouped_fwd: the fused 1x128 output needs y_dtype JET_BF16");
+    return fail(JET_ERR_DTYPE, "%s: the fused 1x128 output needs y_dtype JET_BF16", name);
   if (M == 0 || N == 0) return JET_OK;
-  if (!xq || !xs || !wq || !ws || !y) return fail(JET_ERR_NULL, "fp8_grouped_fwd: null pointer");
+  if (!xq || !xs || !wq || !ws || !y) return fail(JET_ERR_NULL, "%s: null pointer", name);
   if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(y, 16) || !aligned(xs, 4) || !aligned(ws, 4) ||
       (fuse && (!aligned(yq, 16) || !aligned(ys, 4))))
-    return fail(JET_ERR_ALIGN, "fp8_grouped_fwd: operands and outputs need 16-byte alignment");
+    return fail(JET_ERR_ALIGN, "%s: operands and outputs need 16-byte alignment", name);
   jet::GemmArgs a{};
   a.A = xq; a.lda = K;
   a.B = wq; a.ldb = K; a.bE = N * K;
@@ -491,23 +506,38 @@ int jet_fp8_grouped_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, c
   a.seg = seg_off; a.E = (int)E; a.seg_rows = (int)M;
   return hip_status(jet::launch_gemm_grouped(a, jet::kGrpRows, jet::kRowBlock,
                                              y_dtype == JET_BF16 ? jet::kOutBf16 : jet::kOutF32,
-                                             false, fuse, as_stream(stream)),
-                    "fp8_grouped_fwd");
+                                             false, fuse, as_stream(stream), p2),
+                    name);
 }
 
-int jet_fp8_grouped_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* wqT, const float* ws,
-                          const int32_t* seg_off, int64_t E, int64_t M, int64_t N, int64_t K,
-                          void* dx, int dx_dtype, void* workspace, size_t ws_bytes, void* stream) {
+int jet_fp8_grouped_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
+                        const int32_t* seg_off, int64_t E, int64_t M, int64_t N, int64_t K, void* y,
+                        int y_dtype, uint8_t* yq, float* ys, void* workspace, size_t ws_bytes,
+                        void* stream) {
+  return grouped_fwd("fp8_grouped_fwd", false, xq, xs, wq, ws, seg_off, E, M, N, K, y, y_dtype, yq, ys,
+                     workspace, ws_bytes, stream);
+}
+
+int jet_fp8_grouped_fwd_pow2(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
+                             const int32_t* seg_off, int64_t E, int64_t M, int64_t N, int64_t K, void* y,
+                             int y_dtype, uint8_t* yq, float* ys, void* stream) {
+  return grouped_fwd("fp8_grouped_fwd_pow2", true, xq, xs, wq, ws, seg_off, E, M, N, K, y, y_dtype, yq, ys,
+                     nullptr, 0, stream);
+}
+
+static int grouped_dgrad(const char* name, bool p2, const uint8_t* dyq, const float* dys, const uint8_t* wqT,
+                         const float* ws, const int32_t* seg_off, int64_t E, int64_t M, int64_t N, int64_t K,
+                         void* dx, int dx_dtype, void* workspace, size_t ws_bytes, void* stream) {
   g_last_error[0] = 0;
-  if (int st = check_grouped_common("fp8_grouped_dgrad", seg_off, E, M)) return st;
-  if (int st = check_gemm_common("fp8_grouped_dgrad", M, N, K, 0, ws_bytes, workspace)) return st;
+  if (int st = check_grouped_common(name, seg_off, E, M)) return st;
+  if (int st = check_gemm_common(name, M, N, K, 0, ws_bytes, workspace)) return st;
   if (dx_dtype != JET_BF16 && dx_dtype != JET_F32)
-    return fail(JET_ERR_DTYPE, "fp8_grouped_dgrad: dx_dtype must be JET_BF16 or JET_F32");
+    return fail(JET_ERR_DTYPE, "%s: dx_dtype must be JET_BF16 or JET_F32", name);
   if (M == 0 || K == 0) return JET_OK;
-  if (E * N > kMaxLd) return fail(JET_ERR_SHAPE, "fp8_grouped_dgrad: E*N must be <= 2^24 (row stride of wqT)");
-  if (!dyq || !dys || !wqT || !ws || !dx) return fail(JET_ERR_NULL, "fp8_grouped_dgrad: null pointer");
+  if (E * N > kMaxLd) return fail(JET_ERR_SHAPE, "%s: E*N must be <= 2^24 (row stride of wqT)", name);
+  if (!dyq || !dys || !wqT || !ws || !dx) return fail(JET_ERR_NULL, "%s: null pointer", name);
   if (!aligned(dyq, 16) || !aligned(wqT, 16) || !aligned(dx, 16) || !aligned(dys, 4) || !aligned(ws, 4))
-    return fail(JET_ERR_ALIGN, "fp8_grouped_dgrad: operands and output need 16-byte alignment");
+    return fail(JET_ERR_ALIGN, "%s: operands and output need 16-byte alignment", name);
   jet::GemmArgs a{};
   a.A = dyq; a.lda = N;
   a.B = wqT; a.ldb = E * N; a.bE = N;
@@ -518,30 +548,44 @@ int jet_fp8_grouped_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* w
   a.seg = seg_off; a.E = (int)E; a.seg_rows = (int)M;
   return hip_status(jet::launch_gemm_grouped(a, jet::kGrpRows, jet::kRowBlock,
                                              dx_dtype == JET_BF16 ? jet::kOutBf16 : jet::kOutF32,
-                                             false, false, as_stream(stream)),
-                    "fp8_grouped_dgrad");
+                                             false, false, as_stream(stream), p2),
+                    name);
 }
 
-int jet_fp8_grouped_wgrad(const uint8_t* dyqT, const float* dysT, const uint8_t* xqT,
-                          const float* xsT, int64_t ldT, const int32_t* seg_off, int64_t E,
-                          int64_t M, int64_t N, int64_t K, void* dw, int dw_dtype, int accumulate,
-                          void* workspace, size_t ws_bytes, void* stream) {
+int jet_fp8_grouped_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* wqT, const float* ws,
+                          const int32_t* seg_off, int64_t E, int64_t M, int64_t N, int64_t K,
+                          void* dx, int dx_dtype, void* workspace, size_t ws_bytes, void* stream) {
+  return grouped_dgrad("fp8_grouped_dgrad", false, dyq, dys, wqT, ws, seg_off, E, M, N, K, dx, dx_dtype,
+                       workspace, ws_bytes, stream);
+}
+
+int jet_fp8_grouped_dgrad_pow2(const uint8_t* dyq, const float* dys, const uint8_t* wqT, const float* ws,
+                               const int32_t* seg_off, int64_t E, int64_t M, int64_t N, int64_t K,
+                               void* dx, int dx_dtype, void* stream) {
+  return grouped_dgrad("fp8_grouped_dgrad_pow2", true, dyq, dys, wqT, ws, seg_off, E, M, N, K, dx, dx_dtype,
+                       nullptr, 0, stream);
+}
+
+static int grouped_wgrad(const char* name, bool p2, const uint8_t* dyqT, const float* dysT, const uint8_t* xqT,
+                         const float* xsT, int64_t ldT, const int32_t* seg_off, int64_t E, int64_t M, int64_t N,
+                         int64_t K, void* dw, int dw_dtype, int accumulate, void* workspace, size_t ws_bytes,
+                         void* stream) {
   g_last_error[0] = 0;
-  if (int st = check_grouped_common("fp8_grouped_wgrad", seg_off, E, M)) return st;
-  if (int st = check_gemm_common("fp8_grouped_wgrad", M, N, K, 0, ws_bytes, workspace)) return st;
+  if (int st = check_grouped_common(name, seg_off, E, M)) return st;
+  if (int st = check_gemm_common(name, M, N, K, 0, ws_bytes, workspace)) return st;
   if (dw_dtype != JET_F32 && dw_dtype != JET_BF16)
-    return fail(JET_ERR_DTYPE, "fp8_grouped_wgrad: dw_dtype must be JET_F32 or JET_BF16");
+    return fail(JET_ERR_DTYPE, "%s: dw_dtype must be JET_F32 or JET_BF16", name);
   if (accumulate && dw_dtype != JET_F32)
-    return fail(JET_ERR_DTYPE, "fp8_grouped_wgrad: accumulate needs dw_dtype JET_F32");
+    return fail(JET_ERR_DTYPE, "%s: accumulate needs dw_dtype JET_F32", name);
   if (N == 0 || K == 0) return JET_OK;
-  if (!dw) return fail(JET_ERR_NULL, "fp8_grouped_wgrad: null pointer");
+  if (!dw) return fail(JET_ERR_NULL, "%s: null pointer", name);
   if (M > 0 && (!dyqT || !dysT || !xqT || !xsT))
-    return fail(JET_ERR_NULL, "fp8_grouped_wgrad: null pointer");
+    return fail(JET_ERR_NULL, "%s: null pointer", name);
   if (ldT < grouped_cols(M, E) || ldT > kMaxLd || ldT % 16)
-    return fail(JET_ERR_SHAPE, "fp8_grouped_wgrad: need 128*(ceil(M/128)+E) <= ldT <= 2^24, ldT %% 16");
+    return fail(JET_ERR_SHAPE, "%s: need 128*(ceil(M/128)+E) <= ldT <= 2^24, ldT %% 16", name);
   if (!aligned(dw, 16) || (M > 0 && (!aligned(dyqT, 16) || !aligned(xqT, 16) || !aligned(dysT, 4) ||
                                      !aligned(xsT, 4))))
-    return fail(JET_ERR_ALIGN, "fp8_grouped_wgrad: operands and output need 16-byte alignment");
+    return fail(JET_ERR_ALIGN, "%s: operands and output need 16-byte alignment", name);
   jet::GemmArgs a{};
   a.A = dyqT; a.lda = ldT;
   a.B = xqT; a.ldb = ldT;
@@ -552,8 +596,24 @@ int jet_fp8_grouped_wgrad(const uint8_t* dyqT, const float* dysT, const uint8_t*
   a.seg = seg_off; a.E = (int)E; a.seg_rows = (int)M; a.kcap = (int)(ldT / kG * kG);
   return hip_status(jet::launch_gemm_grouped(a, jet::kGrpContraction, jet::kRowCol,
                                              dw_dtype == JET_BF16 ? jet::kOutBf16 : jet::kOutF32,
-                                             accumulate != 0, false, as_stream(stream)),
-                    "fp8_grouped_wgrad");
+                                             accumulate != 0, false, as_stream(stream), p2),
+                    name);
+}
+
+int jet_fp8_grouped_wgrad(const uint8_t* dyqT, const float* dysT, const uint8_t* xqT,
+                          const float* xsT, int64_t ldT, const int32_t* seg_off, int64_t E,
+                          int64_t M, int64_t N, int64_t K, void* dw, int dw_dtype, int accumulate,
+                          void* workspace, size_t ws_bytes, void* stream) {
+  return grouped_wgrad("fp8_grouped_wgrad", false, dyqT, dysT, xqT, xsT, ldT, seg_off, E, M, N, K, dw, dw_dtype,
+                       accumulate, workspace, ws_bytes, stream);
+}
+
+int jet_fp8_grouped_wgrad_pow2(const uint8_t* dyqT, const float* dysT, const uint8_t* xqT,
+                               const float* xsT, int64_t ldT, const int32_t* seg_off, int64_t E,
+                               int64_t M, int64_t N, int64_t K, void* dw, int dw_dtype, int accumulate,
+                               void* stream) {
+  return grouped_wgrad("fp8_grouped_wgrad_pow2", true, dyqT, dysT, xqT, xsT, ldT, seg_off, E, M, N, K, dw,
+                       dw_dtype, accumulate, nullptr, 0, stream);
 }
 
 }  // extern "C"

@@ -992,15 +992,17 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, int out, bool fuseq, void* work
 // expert layers (128 experts, segments of 72..7380 rows) it is 3-10 % faster
 // than the 128 x 128 tile despite the larger ragged remainder per segment.
 hipError_t launch_gemm_grouped(const GemmArgs& a, int grp, int mode, int out, bool accum,
-                               bool fuseq, hipStream_t st) {
+                               bool fuseq, hipStream_t st, bool p2) {
   if (a.N == 0 || a.E == 0) return hipSuccess;
   if (grp == kGrpRows) {
     if (a.seg_rows == 0) return hipSuccess;
     if (mode != kRowBlock || accum) return hipErrorInvalidValue;
+    if (p2) return dispatch<CfgMain, kGrpRows, true>(a, mode, out, false, fuseq, st);
     return dispatch<CfgMain, kGrpRows>(a, mode, out, false, fuseq, st);
   }
   if (grp == kGrpContraction) {
     if (a.M == 0 || mode != kRowCol || fuseq) return hipErrorInvalidValue;
+    if (p2) return dispatch<CfgMain, kGrpContraction, true>(a, mode, out, accum, false, st);
     return dispatch<CfgMain, kGrpContraction>(a, mode, out, accum, false, st);
   }
   return hipErrorInvalidValue;

@@ -78,10 +78,10 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, int out, bool fuseq, void* work
                               bool unsplit = false);
 // Grouped GEMMs: grp = kGrpRows (forward, dgrad) or kGrpContraction (wgrad).
 hipError_t launch_gemm_grouped(const GemmArgs& a, int grp, int mode, int out, bool accum,
-                               bool fuseq, hipStream_t st);
+                               bool fuseq, hipStream_t st, bool p2 = false);
 hipError_t launch_quant_128x1_T_grouped(const void* src, bool fp8src, const float* src_s,
                                         int64_t M, int64_t K, int64_t ldsrc, const int32_t* seg,
                                         int E, uint8_t* qT, int64_t ldqT, float* sT,
-                                        hipStream_t st);
+                                        hipStream_t st, bool p2 = false);
 
 }  // namespace jet

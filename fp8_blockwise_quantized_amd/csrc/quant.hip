@@ -539,10 +539,11 @@ hipError_t launch_quant_128x1_T(const void* src, bool fp8src, const float* src_s
 hipError_t launch_quant_128x1_T_grouped(const void* src, bool fp8src, const float* src_s,
                                         int64_t M, int64_t K, int64_t ldsrc, const int32_t* seg,
                                         int E, uint8_t* qT, int64_t ldqT, float* sT,
-                                        hipStream_t st) {
+                                        hipStream_t st, bool p2) {
   if (M == 0 || K == 0) return hipSuccess;
   // at most ceil(M/128) + E groups over all segments
   const unsigned slots = (unsigned)((M + kGroup - 1) / kGroup + E);
+  if (p2) return launch_128x1_T<true, true>(src, fp8src, src_s, M, K, ldsrc, seg, E, slots, qT, ldqT, sT, st);
   return launch_128x1_T<true, false>(src, fp8src, src_s, M, K, ldsrc, seg, E, slots, qT, ldqT, sT, st);
 }
 

@@ -53,6 +53,10 @@ SIGNATURES = {
     "jet_fp8_linear_fwd_pow2": [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _p, _p, _p],
     "jet_fp8_linear_dgrad_pow2": [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _p],
     "jet_fp8_linear_wgrad_pow2": [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _i32, _p],
+    "jet_quant_act_128x1_T_grouped_pow2": [_p, _i32, _p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _p],
+    "jet_fp8_grouped_fwd_pow2": [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p, _i32, _p, _p, _p],
+    "jet_fp8_grouped_dgrad_pow2": [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p, _i32, _p],
+    "jet_fp8_grouped_wgrad_pow2": [_p, _p, _p, _p, _i64, _p, _i64, _i64, _i64, _i64, _p, _i32, _i32, _p],
 }
 _RESTYPES = {"jet_status_string": ctypes.c_char_p, "jet_last_error": ctypes.c_char_p,
              "jet_workspace_bytes": _sz}
@@ -465,6 +469,15 @@ def _seg(seg_off):
 def jet_quant_act_128x1_T_grouped(src, seg_off, src_s=None, qT=None, sT=None, stream=None):
     """Grouped 128x1 transposed quantization.  Returns (qT uint8 [K, P], sT float32 [P/128, K]),
     P = grouped_columns(M, E); columns past the padded total are left as allocated."""
+    return _quant_128x1_T_grouped("jet_quant_act_128x1_T_grouped", src, seg_off, src_s, qT, sT, stream)
+
+
+def jet_quant_act_128x1_T_grouped_pow2(src, seg_off, src_s=None, qT=None, sT=None, stream=None):
+    """As jet_quant_act_128x1_T_grouped with power-of-two scales."""
+    return _quant_128x1_T_grouped("jet_quant_act_128x1_T_grouped_pow2", src, seg_off, src_s, qT, sT, stream)
+
+
+def _quant_128x1_T_grouped(name, src, seg_off, src_s, qT, sT, stream):
     _rowmajor(src, "src")
     seg_off, E = _seg(seg_off)
     M, K = src.shape
@@ -479,7 +492,7 @@ def jet_quant_act_128x1_T_grouped(src, seg_off, src_s=None, qT=None, sT=None, st
     qT = _codes(qT) if qT is not None else _empty((K, P), torch.uint8, src)
     sT = sT if sT is not None else _empty((qT.stride(0) // 128, K), torch.float32, src)
     _rowmajor(qT, "qT")
-    _check("jet_quant_act_128x1_T_grouped", _lib.jet_quant_act_128x1_T_grouped(
+    _check(name, getattr(_lib, name)(
         _ptr(src), dt, _ptr(src_s), M, K, src.stride(0), _ptr(seg_off), E, _ptr(qT), qT.stride(0),
         _ptr(sT), _stream(stream)))
     return qT, sT
@@ -534,4 +547,49 @@ def jet_fp8_grouped_wgrad(dyqT, dysT, xqT, xsT, seg_off, M, dw=None, out_dtype=t
         _ptr(dyqT), _ptr(dysT), _ptr(xqT), _ptr(xsT), dyqT.stride(0), _ptr(seg_off), E, M, N, K,
         _ptr(dw), _dtype_code(dw.dtype), 1 if accumulate else 0, _ptr(workspace),
         0 if workspace is None else workspace.numel(), _stream(stream)))
+    return dw
+
+
+def jet_fp8_grouped_fwd_pow2(xq, xs, wq, ws, seg_off, y=None, out_dtype=torch.bfloat16,
+                             fuse_quant=False, yq=None, ys=None, stream=None):
+    """jet_fp8_grouped_fwd on power-of-two-scaled operands (scales applied by the MFMA)."""
+    xq, wq = _codes(xq), _codes(wq)
+    seg_off, E = _seg(seg_off)
+    M, K = xq.shape
+    N = wq.shape[1]
+    y = y if y is not None else _empty((M, N), out_dtype, xq)
+    if fuse_quant:
+        yq = _codes(yq) if yq is not None else _empty((M, N), torch.uint8, xq)
+        ys = ys if ys is not None else _empty((N // 128, M), torch.float32, xq)
+    _check("jet_fp8_grouped_fwd_pow2", _lib.jet_fp8_grouped_fwd_pow2(
+        _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(seg_off), E, M, N, K, _ptr(y),
+        _dtype_code(y.dtype), _ptr(yq), _ptr(ys), _stream(stream)))
+    return (y, yq, ys) if fuse_quant else y
+
+
+def jet_fp8_grouped_dgrad_pow2(dyq, dys, wqT, ws, seg_off, dx=None, out_dtype=torch.bfloat16, stream=None):
+    """jet_fp8_grouped_dgrad on power-of-two-scaled operands."""
+    dyq, wqT = _codes(dyq), _codes(wqT)
+    seg_off, E = _seg(seg_off)
+    M, N = dyq.shape
+    K = wqT.shape[0]
+    dx = dx if dx is not None else _empty((M, K), out_dtype, dyq)
+    _check("jet_fp8_grouped_dgrad_pow2", _lib.jet_fp8_grouped_dgrad_pow2(
+        _ptr(dyq), _ptr(dys), _ptr(wqT), _ptr(ws), _ptr(seg_off), E, M, N, K, _ptr(dx),
+        _dtype_code(dx.dtype), _stream(stream)))
+    return dx
+
+
+def jet_fp8_grouped_wgrad_pow2(dyqT, dysT, xqT, xsT, seg_off, M, dw=None, out_dtype=torch.float32,
+                               accumulate=False, stream=None):
+    """jet_fp8_grouped_wgrad on power-of-two-scaled operands."""
+    dyqT, xqT = _codes(dyqT), _codes(xqT)
+    seg_off, E = _seg(seg_off)
+    N, K = dyqT.shape[0], xqT.shape[0]
+    if dyqT.stride(0) != xqT.stride(0):
+        raise ValueError("dyqT and xqT need the same row stride")
+    dw = dw if dw is not None else _empty((E, N, K), out_dtype, dyqT)
+    _check("jet_fp8_grouped_wgrad_pow2", _lib.jet_fp8_grouped_wgrad_pow2(
+        _ptr(dyqT), _ptr(dysT), _ptr(xqT), _ptr(xsT), dyqT.stride(0), _ptr(seg_off), E, M, N, K,
+        _ptr(dw), _dtype_code(dw.dtype), 1 if accumulate else 0, _stream(stream)))
     return dw

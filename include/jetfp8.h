@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define JET_ABI_VERSION 7
+#define JET_ABI_VERSION 8
 
 typedef enum {
   JET_OK = 0,
@@ -447,6 +447,28 @@ int jet_fp8_linear_wgrad_pow2(const uint8_t* dyqT, const float* dysT,
                               const uint8_t* xqT, const float* xsT,
                               int64_t M, int64_t N, int64_t K,
                               void* dw, int dw_dtype, int accumulate, void* stream);
+/* The grouped (mixture-of-experts) layer with power-of-two scales: the 1x128
+ * and 128x128 quantizers are the dense _pow2 ones (as for the FP32-scale
+ * grouped layer); these four are the twins of the grouped entry points. */
+int jet_quant_act_128x1_T_grouped_pow2(const void* src, int src_dtype, const float* src_s,
+                                       int64_t M, int64_t K, int64_t ldsrc,
+                                       const int32_t* seg_off, int64_t E,
+                                       uint8_t* qT, int64_t ldqT, float* sT, void* stream);
+int jet_fp8_grouped_fwd_pow2(const uint8_t* xq, const float* xs,
+                             const uint8_t* wq, const float* ws,
+                             const int32_t* seg_off, int64_t E,
+                             int64_t M, int64_t N, int64_t K,
+                             void* y, int y_dtype, uint8_t* yq, float* ys, void* stream);
+int jet_fp8_grouped_dgrad_pow2(const uint8_t* dyq, const float* dys,
+                               const uint8_t* wqT, const float* ws,
+                               const int32_t* seg_off, int64_t E,
+                               int64_t M, int64_t N, int64_t K,
+                               void* dx, int dx_dtype, void* stream);
+int jet_fp8_grouped_wgrad_pow2(const uint8_t* dyqT, const float* dysT,
+                               const uint8_t* xqT, const float* xsT, int64_t ldT,
+                               const int32_t* seg_off, int64_t E,
+                               int64_t M, int64_t N, int64_t K,
+                               void* dw, int dw_dtype, int accumulate, void* stream);
 
 #ifdef __cplusplus
 }

@@ -307,12 +307,13 @@ def segment_columns(seg_off) -> np.ndarray:
     return col
 
 
-def quant_128x1_T_grouped(a, seg_off) -> tuple[np.ndarray, np.ndarray]:
+def quant_128x1_T_grouped(a, seg_off, scale_rule=None) -> tuple[np.ndarray, np.ndarray]:
     """128x1 transposed quantization with groups restarting at each segment.
 
     a : [M, C] float32, seg_off : [E+1].  returns codesT [C, P] and scales
     [P/128, C], P = segment_columns(seg_off)[E]; segment e occupies columns
-    col[e] .. col[e+1]-1 (its own quant_128x1_T output).
+    col[e] .. col[e+1]-1 (its own quant_128x1_T output).  scale_rule as for
+    quant_1x128.
     """
     a = np.asarray(a, dtype=np.float32)
     col = segment_columns(seg_off)
@@ -323,15 +324,15 @@ def quant_128x1_T_grouped(a, seg_off) -> tuple[np.ndarray, np.ndarray]:
         lo, hi = int(seg_off[e]), int(seg_off[e + 1])
         if hi == lo:
             continue
-        qT, sT = quant_128x1_T(a[lo:hi])
+        qT, sT = quant_128x1_T(a[lo:hi], scale_rule)
         codesT[:, col[e]:col[e + 1]] = qT
         scales[col[e] // GROUP: col[e + 1] // GROUP] = sT
     return codesT, scales
 
 
-def requant_128x1_T_grouped_from_1x128(codes, scales, seg_off) -> tuple[np.ndarray, np.ndarray]:
+def requant_128x1_T_grouped_from_1x128(codes, scales, seg_off, scale_rule=None) -> tuple[np.ndarray, np.ndarray]:
     """Grouped form of requant_128x1_T_from_1x128 (readings R4, R7)."""
-    return quant_128x1_T_grouped(dequant_1x128_fl32(codes, scales), seg_off)
+    return quant_128x1_T_grouped(dequant_1x128_fl32(codes, scales), seg_off, scale_rule)
 
 
 def gemm_grouped_fwd(xq, xs, wq, ws, seg_off) -> np.ndarray:

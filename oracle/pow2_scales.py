@@ -21,7 +21,8 @@ R19 All other steps as in jet_oracle: codes enc(fl32(x * r)) (R3; x * r is
     exact here unless it falls below FP32's subnormal range), the weight's
     128x128 blocks, the 128x1 re-quantization of the activations from their
     dequantized 1x128 values (R4; with power-of-two scales the dequantization
-    is exact), the zero-padded token tail (R5), and the GEMM reference (R6):
+    is exact), the zero-padded token tail (R5), the expert segments of the
+    grouped layer (R7), and the GEMM reference (R6):
     the float64 product of the exactly dequantized operands, so jet_oracle's
     GEMM functions apply unchanged.  The forward's fused output quantization
     is quant_1x128_pow2 of the BF16 output.
@@ -83,3 +84,14 @@ def quant_128x1_T_pow2(a):
 def requant_128x1_T_from_1x128_pow2(codes, scales):
     """R18-R19: the saved 1x128 activation re-quantized as 128x1 (transposed)."""
     return J.requant_128x1_T_from_1x128(codes, scales, scale_rule=scale_pair_pow2)
+
+
+def quant_128x1_T_grouped_pow2(a, seg_off):
+    """R18-R19 with R7: 128x1 groups restarting at each expert segment,
+    in the padded transposed layout."""
+    return J.quant_128x1_T_grouped(a, seg_off, scale_rule=scale_pair_pow2)
+
+
+def requant_128x1_T_grouped_from_1x128_pow2(codes, scales, seg_off):
+    """R18-R19 with R7: the grouped 128x1 re-quantization of the 1x128 activation."""
+    return J.requant_128x1_T_grouped_from_1x128(codes, scales, seg_off, scale_rule=scale_pair_pow2)

@@ -48,7 +48,7 @@ def test_binding_covers_header(J):
 
 
 def test_version_and_status_strings(J):
-    assert J.jet_abi_version() == 7
+    assert J.jet_abi_version() == 8
     assert J.jet_status_string(J.JET_ERR_SHAPE) == "JET_ERR_SHAPE"
     assert J.jet_status_string(99) == "JET_ERR_UNKNOWN"
 
@@ -268,3 +268,24 @@ def test_pow2_entry_points_validate_like_their_twins(J):
     assert w(*a, 64, 128, 128, None, J.JET_F32, 0, None) == J.JET_ERR_NULL
     assert w(*a, (1 << 24) + 128, 128, 128, P16, J.JET_F32, 0, None) == J.JET_ERR_SHAPE
     assert "wgrad_pow2" in J.jet_last_error()
+
+
+def test_grouped_pow2_entry_points_validate(J):
+    L = J._lib
+    seg = P16
+    assert L.jet_quant_act_128x1_T_grouped_pow2(P16, 7, None, 4, 128, 128, seg, 2, P16, 512, P16,
+                                                None) == J.JET_ERR_DTYPE
+    assert "grouped_pow2" in J.jet_last_error()
+    assert L.jet_quant_act_128x1_T_grouped_pow2(P16, J.JET_BF16, None, 4, 100, 128, seg, 2, P16, 512, P16,
+                                                None) == J.JET_ERR_SHAPE
+    a = (P16, P16, P16, P16)
+    assert L.jet_fp8_grouped_fwd_pow2(*a, None, 2, 64, 128, 128, P16, J.JET_BF16, None, None,
+                                      None) == J.JET_ERR_NULL
+    assert L.jet_fp8_grouped_fwd_pow2(*a, seg, 2, 64, 100, 128, P16, J.JET_BF16, None, None,
+                                      None) == J.JET_ERR_SHAPE
+    assert "grouped_fwd_pow2" in J.jet_last_error()
+    assert L.jet_fp8_grouped_dgrad_pow2(*a, seg, 2, 64, 128, 128, P16, 9, None) == J.JET_ERR_DTYPE
+    assert L.jet_fp8_grouped_wgrad_pow2(*a, 128, seg, 2, 64, 128, 128, P16, J.JET_BF16, 1,
+                                        None) == J.JET_ERR_DTYPE
+    assert L.jet_fp8_grouped_wgrad_pow2(*a, 100, seg, 2, 64, 128, 128, P16, J.JET_F32, 0,
+                                        None) == J.JET_ERR_SHAPE

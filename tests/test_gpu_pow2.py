@@ -287,3 +287,98 @@ def test_training_shapes_sampled(gpu_lib, name):
     a = O.dequant_128x1_T(host(dyqT[nidx]), host(dysT[:, nidx]), M)
     b = O.dequant_128x1_T(host(xqT), host(xsT), M)
     check_f32_output(host(dw[nidx]), a @ b.T, oracle_absprod(a, b), f"pow2 wgrad {name}")
+
+
+# --- grouped (mixture-of-experts) layer --------------------------------------
+
+LENS = [5, 0, 200, 128, 1, 130, 0, 257]
+
+
+def test_grouped_all_steps(gpu_lib):
+    """Every step of the grouped layer with power-of-two scales: the dense
+    _pow2 1x128 and stacked 128x128 quantizers, the grouped 128x1 quantizer
+    (bit-exact on the padded layout), the grouped GEMMs per expert to the
+    GEMM tolerance, the fused codes by composition, empty experts' dW zero."""
+    J = gpu_lib
+    seg = np.concatenate([[0], np.cumsum(LENS)]).astype(np.int32)
+    E, N, K = len(LENS), 256, 384
+    M = int(seg[-1])
+    x = inputs.activations_with_outliers(M, K, seed=31)
+    w = inputs.normal_bf16((E, N, K), 0.02, seed=31, tensor_id=inputs.ID_W)
+    dy = inputs.normal_bf16((M, N), 1e-3, seed=31, tensor_id=inputs.ID_DY)
+    segd = torch.from_numpy(seg).cuda()
+    xq, xs = J.jet_quant_act_1x128_pow2(dev_bf16(x))
+    dyq, dys = J.jet_quant_act_1x128_pow2(dev_bf16(dy))
+    wq, ws, wqT = J.jet_quant_weight_128x128_pow2(dev_bf16(w.reshape(E * N, K)))
+    dyqT, dysT = J.jet_quant_act_128x1_T_grouped_pow2(dev_bf16(dy), segd)
+    xqT, xsT = J.jet_quant_act_128x1_T_grouped_pow2(xq, segd, src_s=xs)
+    y16, yq, ys = J.jet_fp8_grouped_fwd_pow2(xq, xs, wq.view(E, N, K), ws.view(E, N // 128, K // 128), segd,
+                                             fuse_quant=True)
+    dx16 = J.jet_fp8_grouped_dgrad_pow2(dyq, dys, wqT, ws.view(E, N // 128, K // 128), segd)
+    dw32 = J.jet_fp8_grouped_wgrad_pow2(dyqT, dysT, xqT, xsT, segd, M)
+    torch.cuda.synchronize()
+    rxq, rxs = P.quant_1x128_pow2(x)
+    rdq, rds = P.quant_1x128_pow2(dy)
+    assert_bits_equal(host(xq), rxq, "grouped x codes")
+    assert_bits_equal(host(dys), rds, "grouped dy scales")
+    rdqT, rdsT = P.quant_128x1_T_grouped_pow2(dy, seg)
+    rxqT, rxsT = P.requant_128x1_T_grouped_from_1x128_pow2(rxq, rxs, seg)
+    Pc = rdqT.shape[1]
+    assert_bits_equal(host(dyqT)[:, :Pc], rdqT, "grouped dyqT")
+    assert_bits_equal(host(dysT)[:Pc // 128], rdsT, "grouped dysT")
+    assert_bits_equal(host(xqT)[:, :Pc], rxqT, "grouped xqT")
+    assert_bits_equal(host(xsT)[:Pc // 128], rxsT, "grouped xsT")
+    hwq, hws = host(wq).reshape(E, N, K), host(ws).reshape(E, N // 128, K // 128)
+    y16h, dx16h, dw32h, yqh, ysh = host(y16), host(dx16), host(dw32), host(yq), host(ys)
+    col = O.segment_columns(seg)
+    for e in range(E):
+        lo, hi = int(seg[e]), int(seg[e + 1])
+        tag = f"pow2 expert {e} rows {lo}:{hi}"
+        if hi == lo:
+            assert not dw32h[e].any(), f"empty {tag}: dW must be zero"
+            continue
+        owq, ows = P.quant_128x128_pow2(w[e])
+        assert_bits_equal(hwq[e], owq, f"w codes {tag}")
+        assert_bits_equal(hws[e], ows, f"w scales {tag}")
+        qo, so = P.quant_1x128_pow2(y16h[lo:hi])
+        assert_bits_equal(yqh[lo:hi], qo, f"fused codes {tag}")
+        assert_bits_equal(ysh[:, lo:hi], so, f"fused scales {tag}")
+        a_x = O.dequant_1x128(rxq[lo:hi], rxs[:, lo:hi])
+        a_dy = O.dequant_1x128(rdq[lo:hi], rds[:, lo:hi])
+        b_w = O.dequant_128x128(owq, ows)
+        check_bf16_output(y16h[lo:hi], a_x @ b_w.T, oracle_absprod(a_x, b_w), f"fwd {tag}")
+        check_bf16_output(dx16h[lo:hi], a_dy @ b_w, oracle_absprod(a_dy, b_w.T), f"dgrad {tag}")
+        c0, c1 = int(col[e]), int(col[e + 1])
+        a_dyT = O.dequant_128x1_T(rdqT[:, c0:c1], rdsT[c0 // 128:c1 // 128], hi - lo)
+        a_xT = O.dequant_128x1_T(rxqT[:, c0:c1], rxsT[c0 // 128:c1 // 128], hi - lo)
+        check_f32_output(dw32h[e], a_dyT @ a_xT.T, oracle_absprod(a_dyT, a_xT), f"wgrad {tag}")
+
+
+def test_grouped_single_expert_equals_dense(gpu_lib):
+    """E = 1: the grouped _pow2 GEMMs give the dense _pow2 results bit for
+    bit (every output element's MFMA chain is the same in either kernel)."""
+    J = gpu_lib
+    M, N, K = 300, 256, 256
+    x = inputs.activations_with_outliers(M, K, seed=3)
+    w = inputs.normal_bf16((N, K), 0.02, seed=3, tensor_id=inputs.ID_W)
+    dy = inputs.normal_bf16((M, N), 1e-3, seed=3, tensor_id=inputs.ID_DY)
+    seg = torch.tensor([0, M], dtype=torch.int32, device="cuda")
+    xq, xs = J.jet_quant_act_1x128_pow2(dev_bf16(x))
+    dyq, dys = J.jet_quant_act_1x128_pow2(dev_bf16(dy))
+    wq, ws, wqT = J.jet_quant_weight_128x128_pow2(dev_bf16(w))
+    dyqT_g, dysT_g = J.jet_quant_act_128x1_T_grouped_pow2(dev_bf16(dy), seg)
+    xqT_g, xsT_g = J.jet_quant_act_128x1_T_grouped_pow2(xq, seg, src_s=xs)
+    y_g = J.jet_fp8_grouped_fwd_pow2(xq, xs, wq[None], ws[None], seg, out_dtype=torch.float32)
+    y_d = J.jet_fp8_linear_fwd_pow2(xq, xs, wq, ws, out_dtype=torch.float32)
+    dx_g = J.jet_fp8_grouped_dgrad_pow2(dyq, dys, wqT, ws[None], seg, out_dtype=torch.float32)
+    dx_d = J.jet_fp8_linear_dgrad_pow2(dyq, dys, wqT, ws, out_dtype=torch.float32)
+    dw_g = J.jet_fp8_grouped_wgrad_pow2(dyqT_g, dysT_g, xqT_g, xsT_g, seg, M)
+    dyqT, dysT = J.jet_quant_act_128x1_T_pow2(dev_bf16(dy))
+    xqT, xsT = J.jet_quant_act_128x1_T_pow2(xq, src_s=xs)
+    dw_d = J.jet_fp8_linear_wgrad_pow2(dyqT, dysT, xqT, xsT, M)
+    torch.cuda.synchronize()
+    Mp = dyqT.shape[1]
+    assert torch.equal(dyqT_g[:, :Mp], dyqT) and torch.equal(xsT_g[:Mp // 128], xsT)
+    assert_bits_equal(host(y_g), host(y_d), "grouped vs dense fwd")
+    assert_bits_equal(host(dx_g), host(dx_d), "grouped vs dense dgrad")
+    assert_bits_equal(host(dw_g)[0], host(dw_d), "grouped vs dense wgrad")

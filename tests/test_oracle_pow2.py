@@ -163,3 +163,25 @@ def test_planted_multiplier_mistake_is_caught(monkeypatch):
     monkeypatch.setattr(P, "scale_pair_pow2", _pair_r_is_s)
     with pytest.raises(AssertionError):
         test_hand_codes_1x128_and_128x128()
+
+
+def test_grouped_restarts_per_segment():
+    """R7 with R18: the grouped 128x1 groups restart at every expert segment,
+    each segment's columns equal to its own power-of-two 128x1 quantization."""
+    lens = [5, 0, 200, 128, 1, 130]
+    seg = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    a = inputs.activations_with_outliers(int(seg[-1]), 256, seed=9)
+    qT, sT = P.quant_128x1_T_grouped_pow2(a, seg)
+    col = J.segment_columns(seg)
+    for e in range(len(lens)):
+        lo, hi = int(seg[e]), int(seg[e + 1])
+        if hi == lo:
+            assert col[e] == col[e + 1]
+            continue
+        q1, s1 = P.quant_128x1_T_pow2(a[lo:hi])
+        assert np.array_equal(qT[:, col[e]:col[e + 1]], q1)
+        assert np.array_equal(sT[col[e] // 128:col[e + 1] // 128], s1)
+    P.e8m0(sT)
+    xq, xs = P.quant_1x128_pow2(a)
+    rq, rs = P.requant_128x1_T_grouped_from_1x128_pow2(xq, xs, seg)
+    assert np.array_equal(rq, P.quant_128x1_T_grouped_pow2(J.dequant_1x128(xq, xs).astype(np.float32), seg)[0])
