@@ -65,7 +65,7 @@ def parse():
                          "(recalibration and append) of one Llama-8B layer")
     ap.add_argument("--fused-m", type=int, default=8192, help="tokens for --workload fused")
     ap.add_argument("--pow2", action="store_true",
-                    help="train, moe: the power-of-two-scale variant (E8M0 scales applied by the MFMA)")
+                    help="train, moe, decode: the power-of-two-scale variant (E8M0 scales applied by the MFMA)")
     ap.add_argument("--invariant", action="store_true",
                     help="decode: the batch-invariant forward (one K range, bit-identical to training)")
     ap.add_argument("--quant", choices=("both", "separate"), default="both",
@@ -409,15 +409,22 @@ def decode_bench(args, torch, J):
         for (name, N, K) in LAYERS:
             x = bf(inputs.activations_with_outliers(M, K, seed=c))
             w = bf(inputs.normal_bf16((N, K), 0.02, seed=c, tensor_id=inputs.ID_W))
-            xq, xs = J.jet_quant_act_1x128(x)
-            wq, ws, _ = J.jet_quant_weight_128x128(w, transposed=False)
+            if args.pow2:
+                xq, xs = J.jet_quant_act_1x128_pow2(x)
+                wq, ws, _ = J.jet_quant_weight_128x128_pow2(w, transposed=False)
+            else:
+                xq, xs = J.jet_quant_act_1x128(x)
+                wq, ws, _ = J.jet_quant_weight_128x128(w, transposed=False)
             del x, w
             y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
             yq = torch.empty(M, N, dtype=torch.uint8, device="cuda")
             ys = torch.empty(N // 128, M, dtype=torch.float32, device="cuda")
             wsp = torch.empty(max(J.jet_workspace_bytes(J.JET_OP_FWD, M, N, K), 16), dtype=torch.uint8,
                               device="cuda")
-            if args.invariant:
+            if args.pow2:
+                fn = (lambda xq=xq, xs=xs, wq=wq, ws=ws, y=y, yq=yq, ys=ys:
+                      J.jet_fp8_linear_fwd_pow2(xq, xs, wq, ws, y=y, fuse_quant=True, yq=yq, ys=ys))
+            elif args.invariant:
                 fn = (lambda xq=xq, xs=xs, wq=wq, ws=ws, y=y, yq=yq, ys=ys:
                       J.jet_fp8_linear_fwd_batch_invariant(xq, xs, wq, ws, y=y, fuse_quant=True, yq=yq, ys=ys))
             else:
@@ -469,7 +476,8 @@ def decode_bench(args, torch, J):
         "config": {"workload": "Llama-3.1-8B decoder linears (QKV, O, gate+up, down) at rollout decode "
                                "batch M=64, forward with the fused 1x128 output, weights cycled over "
                                f"{DECODE_COPIES} copies", "M": M, "parallelism": "none (1 GPU)",
-                   "forward": "batch-invariant (one K range)" if args.invariant else "split-K"},
+                   "forward": ("power-of-two scales (E8M0, applied by the MFMA), one K range" if args.pow2
+                               else "batch-invariant (one K range)" if args.invariant else "split-K")},
         "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
         "roofline": None if dom is None else {
             "bound": "hbm", "kernel": dom, "achieved": kernels[dom]["weight_gbs"], "peak": PEAK_HBM_GBS,

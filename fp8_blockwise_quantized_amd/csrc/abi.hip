@@ -288,7 +288,7 @@ static int check_gemm_common(const char* name, int64_t M, int64_t N, int64_t K, 
 
 // The forward; invariant: one K range at every M (no workspace), so each
 // output element does not depend on M.  p2: power-of-two scales applied by the
-// MFMA (the tiled kernel at every M; no workspace).
+// MFMA, one K range at every M (no workspace; batch-invariant as well).
 static int linear_fwd(const char* name, const uint8_t* xq, const float* xs, const uint8_t* wq,
                       const float* ws, int64_t M, int64_t N, int64_t K, void* y, int y_dtype, uint8_t* yq,
                       float* ys, void* workspace, size_t ws_bytes, void* stream, bool invariant, bool p2 = false) {
@@ -314,8 +314,8 @@ static int linear_fwd(const char* name, const uint8_t* xq, const float* xs, cons
   a.C = y; a.ldc = N; a.Cq = yq; a.Cs = ys; a.ldcs = M;
   a.M = (int)M; a.N = (int)N; a.Kc = (int)K;
   const int out = y_dtype == JET_BF16 ? jet::kOutBf16 : jet::kOutF32;
-  if (M <= jet::kSkinnyMaxM && !p2)   // rollout decode: weight-streaming (split-K through the workspace)
-    return hip_status(jet::launch_gemm_skinny(a, out, fuse, workspace, as_stream(stream), invariant), name);
+  if (M <= jet::kSkinnyMaxM)   // rollout decode: weight-streaming (split-K through the workspace)
+    return hip_status(jet::launch_gemm_skinny(a, out, fuse, workspace, as_stream(stream), invariant, p2), name);
   return hip_status(jet::launch_gemm(a, jet::kRowBlock, out, false, fuse, as_stream(stream), p2), name);
 }
 

@@ -699,7 +699,7 @@ struct SkinnyCfg {
   static_assert(LDS <= 160 * 1024, "LDS");
 };
 
-template <int MT, int NST, int WS, int OUT, bool FUSEQ>
+template <int MT, int NST, int WS, int OUT, bool FUSEQ, bool P2 = false>
 __global__ __launch_bounds__(256) void k_gemm_fp8_skinny(GemmArgs p, float* __restrict__ part,
                                                          int splits) {
   using C = SkinnyCfg<MT, NST, WS>;
@@ -788,6 +788,23 @@ __global__ __launch_bounds__(256) void k_gemm_fp8_skinny(GemmArgs p, float* __re
       sx[4 * q] = r4.x; sx[4 * q + 1] = r4.y; sx[4 * q + 2] = r4.z; sx[4 * q + 3] = r4.w;
     }
     const float swb = Sc[64 * C::NSX + lane];
+    if constexpr (P2) {
+      // power-of-two scales as the MFMA's E8M0 operand scales, accumulated in
+      // place: per element the same MFMA chain as k_gemm_fp8<..., P2>
+      int ea[MT];
+#pragma unroll
+      for (int i = 0; i < MT; ++i) ea[i] = e8m0_of(sx[i]);
+      const int eb = e8m0_of(swb);
+#pragma unroll
+      for (int j = 0; j < WS; ++j) {
+        const v8i bfr = frag32<false>(Ws, wave * WS + j, lane);
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+          acc[j][i] = mfma_fp8_e8m0(bfr, frag32<false>(Xs, i, lane), acc[j][i], eb, ea[i]);
+      }
+      st = (st + 1 == NST) ? 0 : st + 1;
+      continue;
+    }
 #pragma unroll
     for (int j = 0; j < WS; ++j) {
       const v8i bfr = frag32<false>(Ws, wave * WS + j, lane);
@@ -865,7 +882,7 @@ __global__ __launch_bounds__(256) void k_gemm_fp8_skinny(GemmArgs p, float* __re
       am = max_abs_bf16x2(am, w.z);
       am = max_abs_bf16x2(am, w.w);
       am = row16_max_u16x2(am);
-      const ScalePair sp = scale_pair(fold_bf16x2(am));
+      const ScalePair sp = scale_rule<P2>(fold_bf16x2(am));
       const uint32_t q0 = e4m3x4(bf16_lo(w.x) * sp.r, bf16_hi(w.x) * sp.r, bf16_lo(w.y) * sp.r, bf16_hi(w.y) * sp.r);
       const uint32_t q1 = e4m3x4(bf16_lo(w.z) * sp.r, bf16_hi(w.z) * sp.r, bf16_lo(w.w) * sp.r, bf16_hi(w.w) * sp.r);
       if (ok) {
@@ -956,9 +973,10 @@ size_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return S == 1 ? 0 : (size_t)S * (size_t)M * (size_t)N * sizeof(float);
 }
 
-template <int MT, int NST, int WS, int OUT, bool FUSEQ>
+template <int MT, int NST, int WS, int OUT, bool FUSEQ, bool P2 = false>
 static hipError_t launch_skinny_mt(const GemmArgs& a, float* part, int S, hipStream_t st) {
-  hipLaunchKernelGGL((k_gemm_fp8_skinny<MT, NST, WS, OUT, FUSEQ>),
+  if (P2 && S != 1) return hipErrorInvalidValue;   // the power-of-two path runs one K range
+  hipLaunchKernelGGL((k_gemm_fp8_skinny<MT, NST, WS, OUT, FUSEQ, P2>),
                      dim3((unsigned)(a.N / (64 * WS)), (unsigned)S), dim3(256), 0, st, a, part, S);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
@@ -967,18 +985,22 @@ static hipError_t launch_skinny_mt(const GemmArgs& a, float* part, int S, hipStr
   return hipGetLastError();
 }
 
-template <int MT, int NST>
+template <int MT, int NST, bool P2 = false>
 static hipError_t launch_skinny_out(const GemmArgs& a, int out, bool fuseq, float* part, int S,
                                     hipStream_t st) {
-  if (out == kOutF32) return launch_skinny_mt<MT, NST, kSkWS, kOutF32, false>(a, part, S, st);
-  if (fuseq) return launch_skinny_mt<MT, NST, kSkWS, kOutBf16, true>(a, part, S, st);
-  return launch_skinny_mt<MT, NST, kSkWS, kOutBf16, false>(a, part, S, st);
+  if (out == kOutF32) return launch_skinny_mt<MT, NST, kSkWS, kOutF32, false, P2>(a, part, S, st);
+  if (fuseq) return launch_skinny_mt<MT, NST, kSkWS, kOutBf16, true, P2>(a, part, S, st);
+  return launch_skinny_mt<MT, NST, kSkWS, kOutBf16, false, P2>(a, part, S, st);
 }
 
 hipError_t launch_gemm_skinny(const GemmArgs& a, int out, bool fuseq, void* workspace, hipStream_t st,
-                              bool unsplit) {
+                              bool unsplit, bool p2) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
   if (a.M > kSkinnyMaxM || a.Kc <= 0 || a.N % (64 * kSkWS)) return hipErrorInvalidValue;
+  if (p2) {   // one K range: the chain of k_gemm_fp8<..., P2> (no workspace)
+    if (a.M <= 64) return launch_skinny_out<4, kSkNST, true>(a, out, fuseq, nullptr, 1, st);
+    return launch_skinny_out<8, 4, true>(a, out, fuseq, nullptr, 1, st);
+  }
   // unsplit: every output element is the same chain of per-step FMAs, in K
   // order, as in k_gemm_fp8 (bit-identical to the large-M forward)
   const int S = unsplit ? 1 : skinny_splits(a.M, a.N, a.Kc);

@@ -74,8 +74,10 @@ constexpr int64_t kSkinnyMaxM = 128;
 int skinny_splits(int64_t M, int64_t N, int64_t K);
 size_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K);
 // unsplit: one K range (no workspace), bit-identical to launch_gemm's forward.
+// p2: power-of-two scales applied by the MFMA, one K range (bit-identical to
+// launch_gemm's p2 forward).
 hipError_t launch_gemm_skinny(const GemmArgs& a, int out, bool fuseq, void* workspace, hipStream_t st,
-                              bool unsplit = false);
+                              bool unsplit = false, bool p2 = false);
 // Grouped GEMMs: grp = kGrpRows (forward, dgrad) or kGrpContraction (wgrad).
 hipError_t launch_gemm_grouped(const GemmArgs& a, int grp, int mode, int out, bool accum,
                                bool fuseq, hipStream_t st, bool p2 = false);

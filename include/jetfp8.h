@@ -418,9 +418,10 @@ int jet_fp8_grouped_wgrad(const uint8_t* dyqT, const float* dysT,
  * scale (a scale that is not a power of two is taken as the power of two
  * below it), so feed them the _pow2 quantizers' output.  Each _pow2 entry point
  * takes the arguments, layouts and limits of its FP32-scale twin and reports
- * the same errors; the GEMMs take no workspace.  The forward at M <= 128 runs
- * the tiled kernel (no weight-streaming split), so it is batch-invariant at
- * every M.
+ * the same errors; the GEMMs take no workspace.  The forward at M <= 128
+ * streams the weight with one K range, each output element the same chain of
+ * MFMAs as in the tiled kernel used for larger M, so it is batch-invariant
+ * at every M.
  */
 int jet_quant_act_1x128_pow2(const void* x, int64_t M, int64_t K, int64_t ldx,
                              uint8_t* q, int64_t ldq, float* s, void* stream);

@@ -382,3 +382,41 @@ def test_grouped_single_expert_equals_dense(gpu_lib):
     assert_bits_equal(host(y_g), host(y_d), "grouped vs dense fwd")
     assert_bits_equal(host(dx_g), host(dx_d), "grouped vs dense dgrad")
     assert_bits_equal(host(dw_g)[0], host(dw_d), "grouped vs dense wgrad")
+
+
+DECODE = {"qkv": (6144, 4096), "o": (4096, 4096), "gate_up": (28672, 4096), "down": (4096, 14336)}
+
+
+@pytest.mark.parametrize("name", list(DECODE))
+def test_decode_rows_equal_training_rows(gpu_lib, name):
+    """Rollout decode on the Llama-8B layers: rows computed at M = 1, 64 and
+    100 (the weight-streaming kernel, one K range) equal the same rows of a
+    2048-row batch (the tiled kernel) bit for bit, in BF16, in the fused codes
+    and scales, and in FP32; the M = 64 rows meet the GEMM rule against the
+    oracle on sampled columns."""
+    J = gpu_lib
+    N, K = DECODE[name]
+    x = inputs.activations_with_outliers(2048, K, seed=5)
+    w = inputs.normal_bf16((N, K), 0.02, seed=5, tensor_id=inputs.ID_W)
+    xq, xs = J.jet_quant_act_1x128_pow2(dev_bf16(x))
+    wq, ws, _ = J.jet_quant_weight_128x128_pow2(dev_bf16(w), transposed=False)
+    y, yq, ys = J.jet_fp8_linear_fwd_pow2(xq, xs, wq, ws, fuse_quant=True)
+    y32 = J.jet_fp8_linear_fwd_pow2(xq, xs, wq, ws, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for lo, m in ((7, 1), (100, 64), (1000, 100)):
+        sx, ss = xq[lo:lo + m].contiguous(), xs[:, lo:lo + m].contiguous()
+        yd, yqd, ysd = J.jet_fp8_linear_fwd_pow2(sx, ss, wq, ws, fuse_quant=True)
+        y32d = J.jet_fp8_linear_fwd_pow2(sx, ss, wq, ws, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        tag = f"{name} rows {lo}:{lo + m}"
+        assert torch.equal(yd, y[lo:lo + m]), f"BF16 {tag}"
+        assert torch.equal(yqd, yq[lo:lo + m]) and torch.equal(ysd, ys[:, lo:lo + m]), f"fused {tag}"
+        assert_bits_equal(host(y32d), host(y32[lo:lo + m]), f"FP32 {tag}")
+    rng = np.random.default_rng(N)
+    cols = np.sort(rng.choice(N, 256, replace=False))
+    q1, s1 = P.quant_1x128_pow2(x[100:164])
+    assert_bits_equal(host(xq[100:164]), q1, "decode x codes")
+    wq_h, ws_h = host(wq), host(ws)
+    b = O.e4m3_decode(wq_h[cols]) * np.repeat(ws_h[cols // 128], 128, axis=1)
+    a = O.dequant_1x128(q1, s1)
+    check_f32_output(host(y32[100:164])[:, cols], a @ b.T, oracle_absprod(a, b), f"decode fwd {name}")
