@@ -81,48 +81,66 @@ int jet_quant_act_1x128_pow2(const void* x, int64_t M, int64_t K, int64_t ldx, u
   return quant_1x128("quant_act_1x128_pow2", true, x, M, K, ldx, q, ldq, s, stream);
 }
 
-int jet_rmsnorm_quant_1x128(const void* x, const void* gamma, int64_t M, int64_t H, int64_t ldx,
-                            float eps, void* y, int64_t ldy, uint8_t* q, int64_t ldq, float* s,
-                            void* stream) {
+static int rmsnorm_quant(const char* name, bool p2, const void* x, const void* gamma, int64_t M, int64_t H,
+                         int64_t ldx, float eps, void* y, int64_t ldy, uint8_t* q, int64_t ldq, float* s,
+                         void* stream) {
   g_last_error[0] = 0;
   if (M < 0 || H <= 0 || H % kG || H > 8192 || M > kMaxDim)
-    return fail(JET_ERR_SHAPE, "rmsnorm_quant_1x128: need M >= 0 and 0 < H <= 8192, H %% 128 == 0 "
-                               "(M=%lld H=%lld)", (long long)M, (long long)H);
-  if (!(eps >= 0.0f) || eps > 3.0e38f)
-    return fail(JET_ERR_SHAPE, "rmsnorm_quant_1x128: eps must be finite and >= 0");
+    return fail(JET_ERR_SHAPE, "%s: need M >= 0 and 0 < H <= 8192, H %% 128 == 0 (M=%lld H=%lld)", name,
+                (long long)M, (long long)H);
+  if (!(eps >= 0.0f) || eps > 3.0e38f) return fail(JET_ERR_SHAPE, "%s: eps must be finite and >= 0", name);
   if (M == 0) return JET_OK;
-  if (!x || !gamma || !q || !s) return fail(JET_ERR_NULL, "rmsnorm_quant_1x128: null pointer");
-  if (ldx < H || ldq < H || (y && ldy < H))
-    return fail(JET_ERR_SHAPE, "rmsnorm_quant_1x128: leading dimension < H");
+  if (!x || !gamma || !q || !s) return fail(JET_ERR_NULL, "%s: null pointer", name);
+  if (ldx < H || ldq < H || (y && ldy < H)) return fail(JET_ERR_SHAPE, "%s: leading dimension < H", name);
   if (!aligned(x, 16) || !aligned(gamma, 16) || !aligned(q, 16) || !aligned(s, 4) || ldx % 8 ||
       ldq % 16 || (y && (!aligned(y, 16) || ldy % 8)))
-    return fail(JET_ERR_ALIGN, "rmsnorm_quant_1x128: x, gamma, y, q need 16-byte alignment, "
-                               "ldx %% 8, ldy %% 8, ldq %% 16");
+    return fail(JET_ERR_ALIGN, "%s: x, gamma, y, q need 16-byte alignment, ldx %% 8, ldy %% 8, ldq %% 16", name);
   return hip_status(jet::launch_rmsnorm_quant_1x128(static_cast<const uint16_t*>(x),
                                                     static_cast<const uint16_t*>(gamma), M, H, ldx, eps,
                                                     static_cast<uint16_t*>(y), ldy, q, ldq, s,
-                                                    as_stream(stream)),
-                    "rmsnorm_quant_1x128");
+                                                    as_stream(stream), p2),
+                    name);
+}
+
+int jet_rmsnorm_quant_1x128(const void* x, const void* gamma, int64_t M, int64_t H, int64_t ldx,
+                            float eps, void* y, int64_t ldy, uint8_t* q, int64_t ldq, float* s,
+                            void* stream) {
+  return rmsnorm_quant("rmsnorm_quant_1x128", false, x, gamma, M, H, ldx, eps, y, ldy, q, ldq, s, stream);
+}
+
+int jet_rmsnorm_quant_1x128_pow2(const void* x, const void* gamma, int64_t M, int64_t H, int64_t ldx,
+                                 float eps, void* y, int64_t ldy, uint8_t* q, int64_t ldq, float* s,
+                                 void* stream) {
+  return rmsnorm_quant("rmsnorm_quant_1x128_pow2", true, x, gamma, M, H, ldx, eps, y, ldy, q, ldq, s, stream);
+}
+
+static int swiglu_quant(const char* name, bool p2, const void* gu, int64_t M, int64_t I, int64_t ldgu,
+                        void* h, int64_t ldh, uint8_t* q, int64_t ldq, float* s, void* stream) {
+  g_last_error[0] = 0;
+  if (M < 0 || I < 0 || I % kG || M > kMaxDim || I > kMaxDim)
+    return fail(JET_ERR_SHAPE, "%s: need M >= 0 and I a multiple of 128 (M=%lld I=%lld)", name, (long long)M,
+                (long long)I);
+  if (M == 0 || I == 0) return JET_OK;
+  if (!gu || !q || !s) return fail(JET_ERR_NULL, "%s: null pointer", name);
+  if (ldgu < 2 * I || ldq < I || (h && ldh < I))
+    return fail(JET_ERR_SHAPE, "%s: need ldgu >= 2*I, ldq >= I, ldh >= I", name);
+  if (!aligned(gu, 16) || !aligned(q, 16) || !aligned(s, 4) || ldgu % 8 || ldq % 16 ||
+      (h && (!aligned(h, 16) || ldh % 8)))
+    return fail(JET_ERR_ALIGN, "%s: gu, h, q need 16-byte alignment, ldgu %% 8, ldh %% 8, ldq %% 16", name);
+  return hip_status(jet::launch_swiglu_quant_1x128(static_cast<const uint16_t*>(gu), M, I, ldgu,
+                                                   static_cast<uint16_t*>(h), ldh, q, ldq, s,
+                                                   as_stream(stream), p2),
+                    name);
 }
 
 int jet_swiglu_quant_1x128(const void* gu, int64_t M, int64_t I, int64_t ldgu, void* h, int64_t ldh,
                            uint8_t* q, int64_t ldq, float* s, void* stream) {
-  g_last_error[0] = 0;
-  if (M < 0 || I < 0 || I % kG || M > kMaxDim || I > kMaxDim)
-    return fail(JET_ERR_SHAPE, "swiglu_quant_1x128: need M >= 0 and I a multiple of 128 (M=%lld I=%lld)",
-                (long long)M, (long long)I);
-  if (M == 0 || I == 0) return JET_OK;
-  if (!gu || !q || !s) return fail(JET_ERR_NULL, "swiglu_quant_1x128: null pointer");
-  if (ldgu < 2 * I || ldq < I || (h && ldh < I))
-    return fail(JET_ERR_SHAPE, "swiglu_quant_1x128: need ldgu >= 2*I, ldq >= I, ldh >= I");
-  if (!aligned(gu, 16) || !aligned(q, 16) || !aligned(s, 4) || ldgu % 8 || ldq % 16 ||
-      (h && (!aligned(h, 16) || ldh % 8)))
-    return fail(JET_ERR_ALIGN, "swiglu_quant_1x128: gu, h, q need 16-byte alignment, ldgu %% 8, "
-                               "ldh %% 8, ldq %% 16");
-  return hip_status(jet::launch_swiglu_quant_1x128(static_cast<const uint16_t*>(gu), M, I, ldgu,
-                                                   static_cast<uint16_t*>(h), ldh, q, ldq, s,
-                                                   as_stream(stream)),
-                    "swiglu_quant_1x128");
+  return swiglu_quant("swiglu_quant_1x128", false, gu, M, I, ldgu, h, ldh, q, ldq, s, stream);
+}
+
+int jet_swiglu_quant_1x128_pow2(const void* gu, int64_t M, int64_t I, int64_t ldgu, void* h, int64_t ldh,
+                                uint8_t* q, int64_t ldq, float* s, void* stream) {
+  return swiglu_quant("swiglu_quant_1x128_pow2", true, gu, M, I, ldgu, h, ldh, q, ldq, s, stream);
 }
 
 static int check_kv_rows(const char* name, const void* k, const void* v, int64_t T, int64_t D, int64_t ldk,

@@ -42,13 +42,14 @@ struct Codes8 {
   uint32_t c0, c1;
   float s;
 };
+template <bool P2>
 __device__ __forceinline__ Codes8 quant_row16(const uint32_t w[4]) {
   uint32_t am = max_abs_bf16x2(0u, w[0]);
   am = max_abs_bf16x2(am, w[1]);
   am = max_abs_bf16x2(am, w[2]);
   am = max_abs_bf16x2(am, w[3]);
   am = row16_max_u16x2(am);
-  const ScalePair sp = scale_pair(fold_bf16x2(am));
+  const ScalePair sp = scale_rule<P2>(fold_bf16x2(am));
   Codes8 c;
   c.c0 = e4m3x4(bf16_lo(w[0]) * sp.r, bf16_hi(w[0]) * sp.r, bf16_lo(w[1]) * sp.r, bf16_hi(w[1]) * sp.r);
   c.c1 = e4m3x4(bf16_lo(w[2]) * sp.r, bf16_hi(w[2]) * sp.r, bf16_lo(w[3]) * sp.r, bf16_hi(w[3]) * sp.r);
@@ -70,7 +71,7 @@ constexpr int kRmsMaxChunks = 16;                  // H <= 8192
 constexpr int kRmsRowsPerBlock = 8;                // = wavefronts per block
 
 // CH: 512-column chunks held in registers (H <= 512*CH)
-template <int CH>
+template <int CH, bool P2>
 __global__ __launch_bounds__(64 * kRmsRowsPerBlock) void k_rmsnorm_quant_1x128(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma, int64_t M, int64_t H,
     int64_t ldx, float eps, uint16_t* __restrict__ y, int64_t ldy, uint8_t* __restrict__ q,
@@ -128,7 +129,7 @@ __global__ __launch_bounds__(64 * kRmsRowsPerBlock) void k_rmsnorm_quant_1x128(
         const uint32_t hi = bf16_rne((bf16_hi(xw[k]) * r) * bf16_hi(gw[k]));
         yw[k] = lo | (hi << 16);
       }
-      const Codes8 cd = quant_row16(yw);
+      const Codes8 cd = quant_row16<P2>(yw);
       if (ok) {
         store_stream8(q + m * ldq + col, cd.c0, cd.c1);
         if (y) store_stream16(y + m * ldy + col, make_uint4(yw[0], yw[1], yw[2], yw[3]));
@@ -147,19 +148,25 @@ __global__ __launch_bounds__(64 * kRmsRowsPerBlock) void k_rmsnorm_quant_1x128(
 
 hipError_t launch_rmsnorm_quant_1x128(const uint16_t* x, const uint16_t* gamma, int64_t M, int64_t H,
                                       int64_t ldx, float eps, uint16_t* y, int64_t ldy, uint8_t* q,
-                                      int64_t ldq, float* s, hipStream_t st) {
+                                      int64_t ldq, float* s, hipStream_t st, bool p2) {
   if (M == 0) return hipSuccess;
   if (H <= 0 || H % kGroup || H > 512 * kRmsMaxChunks) return hipErrorInvalidValue;
   const int64_t blocks = (M + kRmsRowsPerBlock - 1) / kRmsRowsPerBlock;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)blocks), block(64 * kRmsRowsPerBlock);
-  if (H <= 2048)
-    hipLaunchKernelGGL(k_rmsnorm_quant_1x128<4>, grid, block, 0, st, x, gamma, M, H, ldx, eps, y, ldy, q, ldq, s);
-  else if (H <= 4096)
-    hipLaunchKernelGGL(k_rmsnorm_quant_1x128<8>, grid, block, 0, st, x, gamma, M, H, ldx, eps, y, ldy, q, ldq, s);
-  else
-    hipLaunchKernelGGL(k_rmsnorm_quant_1x128<16>, grid, block, 0, st, x, gamma, M, H, ldx, eps, y, ldy, q, ldq,
-                       s);
+#define JET_RMS(ch_)                                                                                  \
+  do {                                                                                                \
+    if (p2)                                                                                           \
+      hipLaunchKernelGGL((k_rmsnorm_quant_1x128<ch_, true>), grid, block, 0, st, x, gamma, M, H, ldx, \
+                         eps, y, ldy, q, ldq, s);                                                     \
+    else                                                                                              \
+      hipLaunchKernelGGL((k_rmsnorm_quant_1x128<ch_, false>), grid, block, 0, st, x, gamma, M, H, ldx, \
+                         eps, y, ldy, q, ldq, s);                                                     \
+  } while (0)
+  if (H <= 2048) JET_RMS(4);
+  else if (H <= 4096) JET_RMS(8);
+  else JET_RMS(16);
+#undef JET_RMS
   return hipGetLastError();
 }
 
@@ -184,6 +191,7 @@ __device__ __forceinline__ float swiglu1(float g, float u) {
   return (g * sg) * u;
 }
 
+template <bool P2>
 __global__ __launch_bounds__(256) void k_swiglu_quant_1x128(
     const uint16_t* __restrict__ gu, int64_t M, int64_t I, int64_t ldgu, uint16_t* __restrict__ h,
     int64_t ldh, uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s) {
@@ -220,7 +228,7 @@ __global__ __launch_bounds__(256) void k_swiglu_quant_1x128(
         const uint32_t hi = bf16_rne(swiglu1(bf16_hi(gw[k]), bf16_hi(uw[k])));
         hw[k] = lo | (hi << 16);
       }
-      const Codes8 cd = quant_row16(hw);
+      const Codes8 cd = quant_row16<P2>(hw);
       if (m < M && j < G) {
         store_stream8(q + m * ldq + j * kGroup + lane16 * 8, cd.c0, cd.c1);
         if (h) store_stream16(h + m * ldh + j * kGroup + lane16 * 8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
@@ -237,14 +245,18 @@ __global__ __launch_bounds__(256) void k_swiglu_quant_1x128(
 }
 
 hipError_t launch_swiglu_quant_1x128(const uint16_t* gu, int64_t M, int64_t I, int64_t ldgu, uint16_t* h,
-                                     int64_t ldh, uint8_t* q, int64_t ldq, float* s, hipStream_t st) {
+                                     int64_t ldh, uint8_t* q, int64_t ldq, float* s, hipStream_t st, bool p2) {
   if (M == 0 || I == 0) return hipSuccess;
   if (I % kGroup) return hipErrorInvalidValue;
   constexpr int64_t kMaxBlocks = 2048;
   const int64_t units = ((M + 31) / 32) * ((I / kGroup + 3) / 4);
   const int64_t blocks = std::min<int64_t>(units, kMaxBlocks);
-  hipLaunchKernelGGL(k_swiglu_quant_1x128, dim3((unsigned)blocks), dim3(256), 0, st, gu, M, I, ldgu, h,
-                     ldh, q, ldq, s);
+  if (p2)
+    hipLaunchKernelGGL(k_swiglu_quant_1x128<true>, dim3((unsigned)blocks), dim3(256), 0, st, gu, M, I, ldgu, h,
+                       ldh, q, ldq, s);
+  else
+    hipLaunchKernelGGL(k_swiglu_quant_1x128<false>, dim3((unsigned)blocks), dim3(256), 0, st, gu, M, I, ldgu, h,
+                       ldh, q, ldq, s);
   return hipGetLastError();
 }
 

@@ -52,9 +52,9 @@ hipError_t launch_quant_1x128_128x1_T(const uint16_t* x, int64_t M, int64_t K, i
 // (the BF16 tensor) may be null.
 hipError_t launch_rmsnorm_quant_1x128(const uint16_t* x, const uint16_t* gamma, int64_t M, int64_t H,
                                       int64_t ldx, float eps, uint16_t* y, int64_t ldy, uint8_t* q,
-                                      int64_t ldq, float* s, hipStream_t st);
+                                      int64_t ldq, float* s, hipStream_t st, bool p2 = false);
 hipError_t launch_swiglu_quant_1x128(const uint16_t* gu, int64_t M, int64_t I, int64_t ldgu, uint16_t* h,
-                                     int64_t ldh, uint8_t* q, int64_t ldq, float* s, hipStream_t st);
+                                     int64_t ldh, uint8_t* q, int64_t ldq, float* s, hipStream_t st, bool p2 = false);
 // FP8 KV cache: per-tensor scales (scales[0..3] = s_k, r_k, s_v, r_v; scales[4..5]
 // the two amax words) and the quantize-and-append of token rows to cache rows.
 hipError_t launch_kv_calibrate(const uint16_t* k, const uint16_t* v, int64_t T, int64_t D, int64_t ldk,

@@ -53,6 +53,8 @@ SIGNATURES = {
     "jet_fp8_linear_fwd_pow2": [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _p, _p, _p],
     "jet_fp8_linear_dgrad_pow2": [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _p],
     "jet_fp8_linear_wgrad_pow2": [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _i32, _p],
+    "jet_rmsnorm_quant_1x128_pow2": [_p, _p, _i64, _i64, _i64, _f32, _p, _i64, _p, _i64, _p, _p],
+    "jet_swiglu_quant_1x128_pow2": [_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _p],
     "jet_quant_act_128x1_T_grouped_pow2": [_p, _i32, _p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _p],
     "jet_fp8_grouped_fwd_pow2": [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p, _i32, _p, _p, _p],
     "jet_fp8_grouped_dgrad_pow2": [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p, _i32, _p],
@@ -201,6 +203,15 @@ def jet_rmsnorm_quant_1x128(x, gamma, eps, y=None, return_y=False, q=None, s=Non
     """RMSNorm of each row of x BF16 [M, H] with weight gamma BF16 [H], fused
     with its 1x128 quantization.  Returns (q uint8 [M, H], s float32 [H/128, M]),
     or (y, q, s) with the BF16 RMSNorm output y when return_y (or y given)."""
+    return _rmsnorm_quant("jet_rmsnorm_quant_1x128", x, gamma, eps, y, return_y, q, s, stream)
+
+
+def jet_rmsnorm_quant_1x128_pow2(x, gamma, eps, y=None, return_y=False, q=None, s=None, stream=None):
+    """As jet_rmsnorm_quant_1x128 with power-of-two scales."""
+    return _rmsnorm_quant("jet_rmsnorm_quant_1x128_pow2", x, gamma, eps, y, return_y, q, s, stream)
+
+
+def _rmsnorm_quant(name, x, gamma, eps, y, return_y, q, s, stream):
     _rowmajor(x, "x")
     if x.dtype != torch.bfloat16 or gamma.dtype != torch.bfloat16:
         raise TypeError("x and gamma must be bfloat16")
@@ -216,7 +227,7 @@ def jet_rmsnorm_quant_1x128(x, gamma, eps, y=None, return_y=False, q=None, s=Non
     q = _codes(q) if q is not None else _empty((M, H), torch.uint8, x)
     s = s if s is not None else _empty((H // 128, M), torch.float32, x)
     _rowmajor(q, "q")
-    _check("jet_rmsnorm_quant_1x128", _lib.jet_rmsnorm_quant_1x128(
+    _check(name, getattr(_lib, name)(
         _ptr(x), _ptr(gamma), M, H, x.stride(0), float(eps), _ptr(y), 0 if y is None else y.stride(0),
         _ptr(q), q.stride(0), _ptr(s), _stream(stream)))
     return (y, q, s) if y is not None else (q, s)
@@ -227,6 +238,15 @@ def jet_swiglu_quant_1x128(gu, inter=None, h=None, return_h=False, q=None, s=Non
     0..I-1, up = I..2I-1), fused with its 1x128 quantization.  Returns
     (q uint8 [M, I], s float32 [I/128, M]), or (h, q, s) with the BF16 h when
     return_h (or h given)."""
+    return _swiglu_quant("jet_swiglu_quant_1x128", gu, inter, h, return_h, q, s, stream)
+
+
+def jet_swiglu_quant_1x128_pow2(gu, inter=None, h=None, return_h=False, q=None, s=None, stream=None):
+    """As jet_swiglu_quant_1x128 with power-of-two scales."""
+    return _swiglu_quant("jet_swiglu_quant_1x128_pow2", gu, inter, h, return_h, q, s, stream)
+
+
+def _swiglu_quant(name, gu, inter, h, return_h, q, s, stream):
     _rowmajor(gu, "gu")
     if gu.dtype != torch.bfloat16:
         raise TypeError("gu must be bfloat16")
@@ -239,7 +259,7 @@ def jet_swiglu_quant_1x128(gu, inter=None, h=None, return_h=False, q=None, s=Non
     q = _codes(q) if q is not None else _empty((M, I), torch.uint8, gu)
     s = s if s is not None else _empty((I // 128, M), torch.float32, gu)
     _rowmajor(q, "q")
-    _check("jet_swiglu_quant_1x128", _lib.jet_swiglu_quant_1x128(
+    _check(name, getattr(_lib, name)(
         _ptr(gu), M, I, gu.stride(0), _ptr(h), 0 if h is None else h.stride(0), _ptr(q), q.stride(0),
         _ptr(s), _stream(stream)))
     return (h, q, s) if h is not None else (q, s)

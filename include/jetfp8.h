@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define JET_ABI_VERSION 8
+#define JET_ABI_VERSION 9
 
 typedef enum {
   JET_OK = 0,
@@ -448,6 +448,13 @@ int jet_fp8_linear_wgrad_pow2(const uint8_t* dyqT, const float* dysT,
                               const uint8_t* xqT, const float* xsT,
                               int64_t M, int64_t N, int64_t K,
                               void* dw, int dw_dtype, int accumulate, void* stream);
+/* The fused producers of the 1x128 input with power-of-two scales. */
+int jet_rmsnorm_quant_1x128_pow2(const void* x, const void* gamma, int64_t M, int64_t H,
+                                 int64_t ldx, float eps, void* y, int64_t ldy,
+                                 uint8_t* q, int64_t ldq, float* s, void* stream);
+int jet_swiglu_quant_1x128_pow2(const void* gu, int64_t M, int64_t I, int64_t ldgu,
+                                void* h, int64_t ldh, uint8_t* q, int64_t ldq, float* s,
+                                void* stream);
 /* The grouped (mixture-of-experts) layer with power-of-two scales: the 1x128
  * and 128x128 quantizers are the dense _pow2 ones (as for the FP32-scale
  * grouped layer); these four are the twins of the grouped entry points. */

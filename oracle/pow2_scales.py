@@ -95,3 +95,21 @@ def quant_128x1_T_grouped_pow2(a, seg_off):
 def requant_128x1_T_grouped_from_1x128_pow2(codes, scales, seg_off):
     """R18-R19 with R7: the grouped 128x1 re-quantization of the 1x128 activation."""
     return J.requant_128x1_T_grouped_from_1x128(codes, scales, seg_off, scale_rule=scale_pair_pow2)
+
+
+def rmsnorm_quant_1x128_pow2(x, gamma, eps: float):
+    """R12 + R14 with R18: the BF16 RMSNorm output and its power-of-two 1x128
+    quantization."""
+    from oracle.fused_producers import rmsnorm_bf16
+    y = rmsnorm_bf16(x, gamma, eps)
+    q, s = quant_1x128_pow2(y)
+    return y, q, s
+
+
+def swiglu_quant_1x128_pow2(gu, inter: int):
+    """R13 + R14 with R18: the BF16 SwiGLU output and its power-of-two 1x128
+    quantization."""
+    from oracle.fused_producers import swiglu_bf16
+    h = swiglu_bf16(gu, inter)
+    q, s = quant_1x128_pow2(h)
+    return h, q, s

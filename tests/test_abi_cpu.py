@@ -48,7 +48,7 @@ def test_binding_covers_header(J):
 
 
 def test_version_and_status_strings(J):
-    assert J.jet_abi_version() == 8
+    assert J.jet_abi_version() == 9
     assert J.jet_status_string(J.JET_ERR_SHAPE) == "JET_ERR_SHAPE"
     assert J.jet_status_string(99) == "JET_ERR_UNKNOWN"
 
@@ -289,3 +289,18 @@ def test_grouped_pow2_entry_points_validate(J):
                                         None) == J.JET_ERR_DTYPE
     assert L.jet_fp8_grouped_wgrad_pow2(*a, 100, seg, 2, 64, 128, 128, P16, J.JET_F32, 0,
                                         None) == J.JET_ERR_SHAPE
+
+
+def test_fused_pow2_entry_points_validate(J):
+    L = J._lib
+    assert L.jet_rmsnorm_quant_1x128_pow2(P16, P16, 4, 100, 128, 1e-5, None, 0, P16, 128, P16,
+                                          None) == J.JET_ERR_SHAPE
+    assert "rmsnorm_quant_1x128_pow2" in J.jet_last_error()
+    assert L.jet_rmsnorm_quant_1x128_pow2(P16, P16, 4, 128, 128, -1.0, None, 0, P16, 128, P16,
+                                          None) == J.JET_ERR_SHAPE
+    assert L.jet_rmsnorm_quant_1x128_pow2(P16, None, 4, 128, 128, 1e-5, None, 0, P16, 128, P16,
+                                          None) == J.JET_ERR_NULL
+    assert L.jet_swiglu_quant_1x128_pow2(P16, 4, 100, 256, None, 0, P16, 128, P16, None) == J.JET_ERR_SHAPE
+    assert "swiglu_quant_1x128_pow2" in J.jet_last_error()
+    assert L.jet_swiglu_quant_1x128_pow2(P16, 4, 128, 128, None, 0, P16, 128, P16, None) == J.JET_ERR_SHAPE
+    assert L.jet_swiglu_quant_1x128_pow2(P17, 4, 128, 256, None, 0, P16, 128, P16, None) == J.JET_ERR_ALIGN

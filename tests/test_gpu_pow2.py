@@ -420,3 +420,44 @@ def test_decode_rows_equal_training_rows(gpu_lib, name):
     b = O.e4m3_decode(wq_h[cols]) * np.repeat(ws_h[cols // 128], 128, axis=1)
     a = O.dequant_1x128(q1, s1)
     check_f32_output(host(y32[100:164])[:, cols], a @ b.T, oracle_absprod(a, b), f"decode fwd {name}")
+
+
+# --- fused producers of the 1x128 input ---------------------------------------
+
+@pytest.mark.parametrize("M,H", [(1, 128), (37, 640), (100, 4096), (64, 8192)])
+def test_rmsnorm_quant_pow2(gpu_lib, M, H):
+    """The BF16 RMSNorm output is bit-identical to the FP32-scale producer's
+    (only the scale rule differs) and its codes and scales are the oracle's
+    power-of-two 1x128 quantization of it."""
+    from oracle import fused_producers as F
+    J = gpu_lib
+    x = inputs.activations_with_outliers(M, H, seed=H)
+    gam = O.bf16_rne(inputs.normal_bf16((H,), 0.1, seed=H, tensor_id=inputs.ID_W) + np.float32(1.0))
+    xd, gd = dev_bf16(x), dev_bf16(gam)
+    y2, q2, s2 = J.jet_rmsnorm_quant_1x128_pow2(xd, gd, 1e-5, return_y=True)
+    y1, _, _ = J.jet_rmsnorm_quant_1x128(xd, gd, 1e-5, return_y=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y2, y1), "BF16 output differs from the FP32-scale producer's"
+    ref_y = F.rmsnorm_bf16(x, gam, 1e-5)
+    assert np.all(np.abs(host(y2).astype(np.float64) - ref_y) <= np.maximum(F.bf16_ulp(ref_y), 2.0 ** -126))
+    rq, rs = P.quant_1x128_pow2(host(y2))
+    assert_bits_equal(host(q2), rq, f"rmsnorm pow2 codes M={M} H={H}")
+    assert_bits_equal(host(s2), rs, f"rmsnorm pow2 scales M={M} H={H}")
+    P.e8m0(host(s2))
+
+
+@pytest.mark.parametrize("M,I", [(1, 128), (37, 384), (100, 14336)])
+def test_swiglu_quant_pow2(gpu_lib, M, I):
+    from oracle import fused_producers as F
+    J = gpu_lib
+    gu = inputs.normal_bf16((M, 2 * I), 2.0, seed=I, tensor_id=inputs.ID_X)
+    gd = dev_bf16(gu)
+    h2, q2, s2 = J.jet_swiglu_quant_1x128_pow2(gd, return_h=True)
+    h1, _, _ = J.jet_swiglu_quant_1x128(gd, return_h=True)
+    torch.cuda.synchronize()
+    assert torch.equal(h2, h1), "BF16 output differs from the FP32-scale producer's"
+    ref_h = F.swiglu_bf16(gu, I)
+    assert np.all(np.abs(host(h2).astype(np.float64) - ref_h) <= np.maximum(F.bf16_ulp(ref_h), 2.0 ** -126))
+    rq, rs = P.quant_1x128_pow2(host(h2))
+    assert_bits_equal(host(q2), rq, f"swiglu pow2 codes M={M} I={I}")
+    assert_bits_equal(host(s2), rs, f"swiglu pow2 scales M={M} I={I}")

@@ -185,3 +185,21 @@ def test_grouped_restarts_per_segment():
     xq, xs = P.quant_1x128_pow2(a)
     rq, rs = P.requant_128x1_T_grouped_from_1x128_pow2(xq, xs, seg)
     assert np.array_equal(rq, P.quant_128x1_T_grouped_pow2(J.dequant_1x128(xq, xs).astype(np.float32), seg)[0])
+
+
+def test_fused_producers_compose():
+    """R14 with R18: the fused producers' FP8 output is the power-of-two 1x128
+    quantization of their BF16 output (hand case: RMSNorm of [3, 4, 0...] with
+    gamma 1 has its maximum 4/sqrt(25/128) = 9.0509... in BF16 9.0625, so
+    e = -5 (448 * 2^-6 = 7 < 9.0625 <= 14) and the code of 9.0625 * 32 = 290
+    is 288 = 0x79)."""
+    from oracle import fused_producers as F
+    x = np.zeros((1, 128), np.float32)
+    x[0, :2] = [3.0, 4.0]
+    y, q, s = P.rmsnorm_quant_1x128_pow2(x, np.ones(128, np.float32), 0.0)
+    assert y[0, 1] == np.float32(9.0625) and s[0, 0] == np.float32(2.0 ** -5)
+    assert q[0, 1] == 0x79
+    gu = inputs.normal_bf16((3, 256), 2.0, seed=1, tensor_id=inputs.ID_X)
+    h, hq, hs = P.swiglu_quant_1x128_pow2(gu, 128)
+    assert np.array_equal(h, F.swiglu_bf16(gu, 128))
+    assert all(np.array_equal(a, b) for a, b in zip((hq, hs), P.quant_1x128_pow2(h)))
