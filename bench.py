@@ -19,7 +19,7 @@ of a 8192-token prefill, append of a 64-token decode step);
 (hidden 2048, expert intermediate 768, 128 experts, top-8 of 8192 tokens with
 Zipf(1.1) expert load), fwd + dgrad + wgrad with every quantizer.
 
-Prints ONE JSON line.  --gpus above 1 is refused: this build runs on one GPU.
+Prints ONE JSON line.  --gpus above 1 is refused: the benchmark measures one GPU.
 """
 from __future__ import annotations
 
@@ -716,7 +716,7 @@ def kv_bench(args, torch, J):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported: this build runs on exactly one GPU "
+        print(f"bench.py: --gpus {args.gpus} is not supported: the benchmark measures exactly one GPU "
               f"(the path shards by tokens; a multi-GPU run is not part of it).", file=sys.stderr)
         sys.exit(2)
     import torch
