@@ -58,7 +58,9 @@ def parse():
                     help="train: skip timing hipBLASLt BF16 GEMMs on the same shapes (context only)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run 1 GiB device copies first (HBM counter calibration)")
-    ap.add_argument("--events", type=int, default=1, help="per-kernel HIP events in the timed loop")
+    ap.add_argument("--events", type=int, default=1,
+                    help="1: after the timed steps, as many steps again with HIP events around every "
+                         "launch (per-kernel times); 0: skip that pass")
     ap.add_argument("--workload", choices=("train", "decode", "moe", "fused", "kv"), default="train",
                     help="train: the M=8192 fwd+bwd step (the headline line); decode: the rollout "
                          "forward at M=64 over the same four linears; moe: the grouped expert "
@@ -605,10 +607,14 @@ def fused_bench(args, torch, J):
     t0, t1 = E(enable_timing=True), E(enable_timing=True)
     t0.record()
     for st in range(args.steps):
-        step(per[st] if args.events else None)
+        step()
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
+    if args.events:     # per-kernel times from a second pass with events
+        for st in range(args.steps):
+            step(per[st])
+        torch.cuda.synchronize()
     u0, u1 = E(enable_timing=True), E(enable_timing=True)
     u0.record()
     for _ in range(args.steps):
@@ -803,15 +809,24 @@ def main():
     torch.cuda.synchronize()
 
     E = torch.cuda.Event
+    # The timed steps run without per-launch events: recording two events
+    # around each of the step's launches adds about 3 % to the step.  The
+    # per-kernel breakdown (and the roofline) comes from a second pass of the
+    # same number of steps with an event pair around every launch.
     per = [[[E(enable_timing=True), E(enable_timing=True)] for _ in plan] for _ in range(args.steps)]
     t_start, t_end = E(enable_timing=True), E(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
     for s in range(args.steps):
-        step(per[s] if args.events else None)
+        step()
     t_end.record()
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
+    if args.events:
+        log(f"{args.steps} steps with an event pair around every launch (per-kernel times)")
+        for s in range(args.steps):
+            step(per[s])
+        torch.cuda.synchronize()
 
     # per-kernel-kind aggregates over the timed region
     agg = {}
