@@ -500,3 +500,42 @@ def test_batch_invariant_forward_matches_training_batch(gpu_lib, name):
         report.append(f"M={M}: split-K differs in {int((diff > 0).sum())}/{diff.numel()} elements, "
                       f"max {float(diff.max()):.2e}")
     print(f"{name}: " + "; ".join(report))
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_empty_batch_every_entry_point(gpu_lib, pow2):
+    """M = 0 tokens (an empty rollout or micro-batch): every quantizer and GEMM
+    entry point returns JET_OK with empty outputs and launches nothing; the
+    library then still serves an ordinary call."""
+    J, sfx = gpu_lib, ("_pow2" if pow2 else "")
+    f = lambda name: getattr(J, name + sfx)
+    N, K = 256, 384
+    x, w, dy = layer_inputs(3, N, K, 21)
+    wq, ws, wqT = f("jet_quant_weight_128x128")(dev_bf16(w))
+    x0 = torch.empty((0, K), dtype=torch.bfloat16, device="cuda")
+    dy0 = torch.empty((0, N), dtype=torch.bfloat16, device="cuda")
+    xq, xs = f("jet_quant_act_1x128")(x0)
+    assert xq.shape == (0, K) and xs.shape == (K // 128, 0)
+    for requant in (False, True):
+        q, s, qT, sT = f("jet_quant_act_1x128_128x1_T")(x0, requant)
+        assert q.shape == (0, K) and qT.shape == (K, 0) and sT.shape == (0, K)
+    qT, sT = f("jet_quant_act_128x1_T")(x0)
+    assert qT.shape == (K, 0) and sT.shape == (0, K)
+    qT, sT = f("jet_quant_act_128x1_T")(xq, src_s=xs)
+    assert qT.shape == (K, 0)
+    y, yq, ys = f("jet_fp8_linear_fwd")(xq, xs, wq, ws, fuse_quant=True)
+    assert y.shape == (0, N) and yq.shape == (0, N) and ys.shape == (N // 128, 0)
+    assert f("jet_fp8_linear_fwd")(xq, xs, wq, ws, out_dtype=torch.float32).shape == (0, N)
+    if not pow2:
+        assert J.jet_fp8_linear_fwd_batch_invariant(xq, xs, wq, ws).shape == (0, N)
+    dyq, dys = f("jet_quant_act_1x128")(dy0)
+    assert f("jet_fp8_linear_dgrad")(dyq, dys, wqT, ws).shape == (0, K)
+    torch.cuda.synchronize()
+    # ordinary calls afterwards: no error was left behind
+    if pow2:
+        xq3, xs3 = f("jet_quant_act_1x128")(dev_bf16(x))
+        y3 = f("jet_fp8_linear_fwd")(xq3, xs3, wq, ws)
+        torch.cuda.synchronize()
+        assert y3.shape == (3, N) and torch.isfinite(y3.float()).all()
+    else:
+        quantize_all(J, x, w, dy)   # asserts bit-exact codes and scales
