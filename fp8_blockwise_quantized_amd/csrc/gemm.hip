@@ -659,9 +659,10 @@ hipError_t launch_gemm(const GemmArgs& a, int mode, int out, bool accum, bool fu
 // ---------------------------------------------------------------------------
 // Small-M forward (rollout decode, M <= 128): Y = Xq . Wq^T streams the whole
 // weight once for a handful of rows, so it is bound by HBM bandwidth and needs
-// many weight bytes in flight.  The output is cut into 64*WS-column blocks
-// and the K steps into S contiguous ranges; a workgroup (4 wavefronts) computes
-// the FP32 sum of one (block, range) through an NST-stage ring of direct
+// many weight bytes in flight.  The output is cut into 64*WS-column blocks,
+// the K steps into S contiguous ranges and (with one range) the rows into
+// groups of MT*16; a workgroup (4 wavefronts) computes the FP32 sum of one
+// (block, range, row group) through an NST-stage ring of direct
 // global->LDS loads (NST-1 steps of prefetch).  With S = 1 it writes Y (BF16
 // or FP32) and, for BF16, the fused 1x128 quantization of Y itself.  With
 // S > 1 it writes its partial sum to the caller's workspace P[S][M][N] and
@@ -689,7 +690,7 @@ struct SkinnyCfg {
   static constexpr int STAGE = XT + WT + 1024;
   static constexpr int XBLK = XT / 1024, WBLK = WT / 1024;
   static constexpr int BPW = (XBLK + WBLK) / 4;        // tile DMAs per wavefront and stage
-  static constexpr int NSX = MT / 4;                   // scale slots holding X row scales
+  static constexpr int NSX = (MT + 3) / 4;             // scale slots holding X row scales
   static constexpr int LOADS = BPW + 1;
   static constexpr int LDS = NST * STAGE;
   static constexpr int TP = BN + 4;                    // FP32 output tile pitch (floats)
@@ -708,6 +709,21 @@ __global__ __launch_bounds__(256) void k_gemm_fp8_skinny(GemmArgs p, float* __re
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lrow = lane & 15, kg = lane >> 4;
   const int n0 = blockIdx.x * C::BN;
+  // Row group blockIdx.z: rows MT*16*z .. of X and of the outputs (one K
+  // range only; a split launch has a single row group).
+  if (blockIdx.z > 0) {
+    const int row0 = (int)blockIdx.z * MT * 16;
+    if (row0 >= p.M) return;
+    p.A += (int64_t)row0 * p.lda;
+    p.sA += row0;
+    p.C = static_cast<uint8_t*>(p.C) + (int64_t)row0 * p.ldc * (OUT == kOutF32 ? 4 : 2);
+    if (FUSEQ) {
+      p.Cq += (int64_t)row0 * p.ldc;
+      p.Cs += row0;
+    }
+    p.M -= row0;
+  }
+  if (p.M > MT * 16) p.M = MT * 16;
   const int sidx = blockIdx.y;
   const int KB = p.Kc / 128;
   const int kb0 = (int)((int64_t)KB * sidx / splits), kb1 = (int)((int64_t)KB * (sidx + 1) / splits);
@@ -782,10 +798,17 @@ __global__ __launch_bounds__(256) void k_gemm_fp8_skinny(GemmArgs p, float* __re
     // the stage step k-1 used is free: refill it with step k + D
     if (k + D < nsteps) issue((st + D) % NST, kb0 + k + D);
     float sx[MT];
+    if constexpr (MT >= 4) {
 #pragma unroll
-    for (int q = 0; q < MT / 4; ++q) {
-      const float4 r4 = *reinterpret_cast<const float4*>(Sc + 64 * q + 4 * lrow);
-      sx[4 * q] = r4.x; sx[4 * q + 1] = r4.y; sx[4 * q + 2] = r4.z; sx[4 * q + 3] = r4.w;
+      for (int q = 0; q < MT / 4; ++q) {
+        const float4 r4 = *reinterpret_cast<const float4*>(Sc + 64 * q + 4 * lrow);
+        sx[4 * q] = r4.x; sx[4 * q + 1] = r4.y; sx[4 * q + 2] = r4.z; sx[4 * q + 3] = r4.w;
+      }
+    } else {
+      // slot 0 holds rows t*16 + lrow at 4*lrow + t; rows past MT*16 are unused
+      const float4 r4 = *reinterpret_cast<const float4*>(Sc + 4 * lrow);
+      sx[0] = r4.x;
+      if constexpr (MT > 1) sx[1] = r4.y;
     }
     const float swb = Sc[64 * C::NSX + lane];
     if constexpr (P2) {
@@ -954,6 +977,7 @@ __global__ __launch_bounds__(256) void k_skinny_finish(GemmArgs p, const float* 
 constexpr int kSkWS = 2;        // W slabs per wavefront: 128 output columns per workgroup
 constexpr int kSkNST = 6;       // ring stages for M <= 64 (4 for M <= 128)
 constexpr int kSkTarget = 128;  // workgroups aimed at over all column blocks and K ranges
+constexpr int kSkRowSplitBlocks = 64;   // one K range below this many column blocks: 32-row groups
 
 // K-step ranges of the small-M forward: about kSkTarget workgroups in total,
 // at least one K step per range, at most 16 ranges.
@@ -976,8 +1000,12 @@ size_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 template <int MT, int NST, int WS, int OUT, bool FUSEQ, bool P2 = false>
 static hipError_t launch_skinny_mt(const GemmArgs& a, float* part, int S, hipStream_t st) {
   if (P2 && S != 1) return hipErrorInvalidValue;   // the power-of-two path runs one K range
+  // row groups of MT*16 rows (a split launch covers all rows in one group)
+  const int R = (a.M + MT * 16 - 1) / (MT * 16);
+  if (S > 1 && R != 1) return hipErrorInvalidValue;
   hipLaunchKernelGGL((k_gemm_fp8_skinny<MT, NST, WS, OUT, FUSEQ, P2>),
-                     dim3((unsigned)(a.N / (64 * WS)), (unsigned)S), dim3(256), 0, st, a, part, S);
+                     dim3((unsigned)(a.N / (64 * WS)), (unsigned)S, (unsigned)R), dim3(256), 0, st, a,
+                     part, S);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   const dim3 g((unsigned)(a.N / 128), (unsigned)((a.M + 15) / 16));
@@ -997,7 +1025,13 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, int out, bool fuseq, void* work
                               bool unsplit, bool p2) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
   if (a.M > kSkinnyMaxM || a.Kc <= 0 || a.N % (64 * kSkWS)) return hipErrorInvalidValue;
+  // One K range with few column blocks: 32-row groups, each its own
+  // workgroup, so the weight streams through up to four times as many CUs.
+  // A row's MFMA operands, lanes and chain are those of the 64-row
+  // workgroup, so its outputs are the same bits.
+  const bool rows32 = a.N / (64 * kSkWS) < kSkRowSplitBlocks;
   if (p2) {   // one K range: the chain of k_gemm_fp8<..., P2> (no workspace)
+    if (rows32) return launch_skinny_out<2, kSkNST, true>(a, out, fuseq, nullptr, 1, st);
     if (a.M <= 64) return launch_skinny_out<4, kSkNST, true>(a, out, fuseq, nullptr, 1, st);
     return launch_skinny_out<8, 4, true>(a, out, fuseq, nullptr, 1, st);
   }
@@ -1006,6 +1040,7 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, int out, bool fuseq, void* work
   const int S = unsplit ? 1 : skinny_splits(a.M, a.N, a.Kc);
   if (S > 1 && workspace == nullptr) return hipErrorInvalidValue;
   float* part = static_cast<float*>(workspace);
+  if (S == 1 && rows32) return launch_skinny_out<2, kSkNST>(a, out, fuseq, part, 1, st);
   if (a.M <= 64) return launch_skinny_out<4, kSkNST>(a, out, fuseq, part, S, st);
   return launch_skinny_out<8, 4>(a, out, fuseq, part, S, st);
 }
