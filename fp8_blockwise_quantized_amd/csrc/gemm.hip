@@ -678,9 +678,10 @@ hipError_t launch_gemm(const GemmArgs& a, int mode, int out, bool accum, bool fu
 //
 // Stage layout: the X tile (MT*16 rows x 128 bytes, swizzled rows), the W
 // tile (64 rows x 128 bytes), then four 256-byte scale slots, one DMA per
-// wavefront: slots q < MT/4 hold X row scales (float 4r + t of slot q is row
-// (4q + t)*16 + r, so lane r reads its rows i*16 + r, i < MT, as MT/4 16-byte
-// loads); the other slots hold 64 copies of the W block scale.
+// wavefront: slots q < ceil(MT/4) hold X row scales (float 4r + t of slot q
+// is row (4q + t)*16 + r, so lane r reads its rows i*16 + r, i < MT, as
+// ceil(MT/4) 16-byte loads); the other slots hold 64 copies of the W block
+// scale.
 // Wavefront w multiplies W slab w (output columns 16w..16w+15 of the block)
 // with the MT X slabs.
 template <int MT, int NST, int WS>
@@ -689,12 +690,13 @@ struct SkinnyCfg {
   static constexpr int XT = MT * 16 * 128, WT = BN * 128;
   static constexpr int STAGE = XT + WT + 1024;
   static constexpr int XBLK = XT / 1024, WBLK = WT / 1024;
-  static constexpr int BPW = (XBLK + WBLK) / 4;        // tile DMAs per wavefront and stage
+  static constexpr int BPW = (XBLK + WBLK + 3) / 4;    // tile DMAs per wavefront and stage (slots
+                                                       // past the last block repeat it)
   static constexpr int NSX = (MT + 3) / 4;             // scale slots holding X row scales
   static constexpr int LOADS = BPW + 1;
   static constexpr int LDS = NST * STAGE;
   static constexpr int TP = BN + 4;                    // FP32 output tile pitch (floats)
-  static_assert((XBLK + WBLK) % 4 == 0 && NSX >= 1 && NSX < 4, "DMA split");
+  static_assert(NSX >= 1 && NSX < 4, "scale slots");
   static_assert(BN == 128, "one 1x128 output group and one weight block scale per workgroup");
   static_assert(MT * 16 * TP * 4 <= LDS, "output tile fits the stage ring");
   static_assert(LDS <= 160 * 1024, "LDS");
@@ -739,7 +741,8 @@ __global__ __launch_bounds__(256) void k_gemm_fp8_skinny(GemmArgs p, float* __re
   bool isx[C::BPW];
 #pragma unroll
   for (int t = 0; t < C::BPW; ++t) {
-    const int gb = wave * C::BPW + t;
+    // a repeated block writes the same bytes to the same LDS slot again
+    const int gb = min(wave * C::BPW + t, C::XBLK + C::WBLK - 1);
     int row; uint32_t col;
     if (gb < C::XBLK) {
       dma_src<false>(gb, lane, row, col);
@@ -977,7 +980,7 @@ __global__ __launch_bounds__(256) void k_skinny_finish(GemmArgs p, const float* 
 constexpr int kSkWS = 2;        // W slabs per wavefront: 128 output columns per workgroup
 constexpr int kSkNST = 6;       // ring stages for M <= 64 (4 for M <= 128)
 constexpr int kSkTarget = 128;  // workgroups aimed at over all column blocks and K ranges
-constexpr int kSkRowSplitBlocks = 64;   // one K range below this many column blocks: 32-row groups
+constexpr int kSkRowSplitBlocks = 64;   // one K range below this many column blocks: 16-row groups
 
 // K-step ranges of the small-M forward: about kSkTarget workgroups in total,
 // at least one K step per range, at most 16 ranges.
@@ -1025,13 +1028,17 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, int out, bool fuseq, void* work
                               bool unsplit, bool p2) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
   if (a.M > kSkinnyMaxM || a.Kc <= 0 || a.N % (64 * kSkWS)) return hipErrorInvalidValue;
-  // One K range with few column blocks: 32-row groups, each its own
-  // workgroup, so the weight streams through up to four times as many CUs.
-  // A row's MFMA operands, lanes and chain are those of the 64-row
-  // workgroup, so its outputs are the same bits.
-  const bool rows32 = a.N / (64 * kSkWS) < kSkRowSplitBlocks;
+  // One K range with few column blocks: each 16-row slab of X is a
+  // workgroup of its own.  A workgroup's rate of streaming its weight
+  // column is bound by its step (fewer rows, less work per step) and more
+  // of them run at once; the workgroups of one column block share an XCD
+  // (the block index differs by multiples of the column-block count, a
+  // multiple of 8 on every Llama/Qwen shape), so its weight bytes come from
+  // that XCD's L2 after the first.  A row's MFMA operands, lanes and chain
+  // are those of the 64-row workgroup, so its outputs are the same bits.
+  const bool rows16 = a.N / (64 * kSkWS) < kSkRowSplitBlocks;
   if (p2) {   // one K range: the chain of k_gemm_fp8<..., P2> (no workspace)
-    if (rows32) return launch_skinny_out<2, kSkNST, true>(a, out, fuseq, nullptr, 1, st);
+    if (rows16) return launch_skinny_out<1, kSkNST, true>(a, out, fuseq, nullptr, 1, st);
     if (a.M <= 64) return launch_skinny_out<4, kSkNST, true>(a, out, fuseq, nullptr, 1, st);
     return launch_skinny_out<8, 4, true>(a, out, fuseq, nullptr, 1, st);
   }
@@ -1040,7 +1047,7 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, int out, bool fuseq, void* work
   const int S = unsplit ? 1 : skinny_splits(a.M, a.N, a.Kc);
   if (S > 1 && workspace == nullptr) return hipErrorInvalidValue;
   float* part = static_cast<float*>(workspace);
-  if (S == 1 && rows32) return launch_skinny_out<2, kSkNST>(a, out, fuseq, part, 1, st);
+  if (S == 1 && rows16) return launch_skinny_out<1, kSkNST>(a, out, fuseq, part, 1, st);
   if (a.M <= 64) return launch_skinny_out<4, kSkNST>(a, out, fuseq, part, S, st);
   return launch_skinny_out<8, 4>(a, out, fuseq, part, S, st);
 }
