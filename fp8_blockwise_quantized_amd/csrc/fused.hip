@@ -63,9 +63,11 @@ __device__ __forceinline__ Codes8 quant_row16(const uint32_t w[4]) {
 // RMSNorm + 1x128.  One wavefront per row; lane l holds columns 512c + 8l ..
 // +7 of every 512-column chunk c (16-byte loads, each instruction a whole
 // 1 KiB of the row), so the 16 lanes of a DPP row hold one 128-column group.
-// The row and gamma are loaded together (one memory latency per row).  A
-// block of kRmsRowsPerBlock wavefronts takes as many consecutive rows; its
-// scales are staged in LDS and written as runs of consecutive rows per group.
+// Each wavefront issues its row's loads first; the block then stages gamma
+// in LDS once (one 16-byte load per thread and chunk) for all its rows,
+// instead of every wavefront loading and holding its own copy.  A block of
+// kRmsRowsPerBlock wavefronts takes as many consecutive rows; its scales are
+// staged in LDS and written as runs of consecutive rows per group.
 // ---------------------------------------------------------------------------
 constexpr int kRmsMaxChunks = 16;                  // H <= 8192
 constexpr int kRmsRowsPerBlock = 8;                // = wavefronts per block
@@ -77,6 +79,7 @@ __global__ __launch_bounds__(64 * kRmsRowsPerBlock) void k_rmsnorm_quant_1x128(
     int64_t ldx, float eps, uint16_t* __restrict__ y, int64_t ldy, uint8_t* __restrict__ q,
     int64_t ldq, float* __restrict__ s) {
   __shared__ float stg[CH * 4][kRmsRowsPerBlock];
+  __shared__ uint4 gsh[CH * 64];                  // gamma, 8 BF16 per entry
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nb = (int)gridDim.x, b = (int)blockIdx.x;
   // consecutive blocks on one XCD (blocks are dealt round-robin to the 8 XCDs),
@@ -89,19 +92,17 @@ __global__ __launch_bounds__(64 * kRmsRowsPerBlock) void k_rmsnorm_quant_1x128(
 
   const int rr = wave;
   const int64_t m = m0 + rr;
-  if (m < M) {
-    const uint16_t* xr = x + m * ldx;
-    uint4 v[CH], gv[CH];
+  uint4 v[CH];
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      v[c] = make_uint4(0u, 0u, 0u, 0u);
-      gv[c] = v[c];
-      const int64_t col = 512 * c + 8 * lane;
-      if (c < chunks && col < H) {
-        v[c] = load_stream16(xr + col);
-        gv[c] = *reinterpret_cast<const uint4*>(gamma + col);
-      }
-    }
+  for (int c = 0; c < CH; ++c) {
+    v[c] = make_uint4(0u, 0u, 0u, 0u);
+    const int64_t col = 512 * c + 8 * lane;
+    if (m < M && c < chunks && col < H) v[c] = load_stream16(x + m * ldx + col);
+  }
+  for (int i = threadIdx.x; i < (int)(H / 8); i += 64 * kRmsRowsPerBlock)
+    gsh[i] = *reinterpret_cast<const uint4*>(gamma + 8 * (int64_t)i);
+  __syncthreads();
+  if (m < M) {
     float ss = 0.0f;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
@@ -121,7 +122,8 @@ __global__ __launch_bounds__(64 * kRmsRowsPerBlock) void k_rmsnorm_quant_1x128(
       const int64_t col = 512 * c + 8 * lane;
       const bool ok = col < H;                     // uniform per DPP row (H % 128 == 0)
       const uint32_t xw[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
-      const uint32_t gw[4] = {gv[c].x, gv[c].y, gv[c].z, gv[c].w};
+      const uint4 g4 = gsh[ok ? 64 * c + lane : 0];
+      const uint32_t gw[4] = {g4.x, g4.y, g4.z, g4.w};
       uint32_t yw[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
