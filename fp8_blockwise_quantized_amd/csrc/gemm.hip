@@ -641,13 +641,15 @@ static int cu_count() {
 hipError_t launch_gemm(const GemmArgs& a, int mode, int out, bool accum, bool fuseq,
                        hipStream_t st, bool p2) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
-  // The big tile keeps the most work per byte staged; use it unless its last
-  // wave of workgroups would leave more than a tenth of the CUs idle.
+  // The big tile keeps the most work per byte staged; use it unless its
+  // grid fills less than 85 % of its waves of workgroups (the small tile
+  // runs at about 85 % of the big tile's rate, so below that the idle CUs of
+  // the big tile's last wave cost more).
   const int64_t tiles = (int64_t)((a.M + CfgMain::BM - 1) / CfgMain::BM) *
                         (int64_t)((a.N + CfgMain::BN - 1) / CfgMain::BN);
   const int64_t cus = cu_count();
   const int64_t slots = (tiles + cus - 1) / cus * cus;
-  const bool big = tiles * 10 >= slots * 9;
+  const bool big = tiles * 100 >= slots * 85;
   if (p2) {
     if (big) return dispatch<CfgMain, kGrpNone, true>(a, mode, out, accum, fuseq, st);
     return dispatch<CfgSmall, kGrpNone, true>(a, mode, out, accum, fuseq, st);
