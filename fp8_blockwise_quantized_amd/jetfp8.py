@@ -123,6 +123,61 @@ def _empty(shape, dtype, like):
     return torch.empty(shape, dtype=dtype, device=like.device)
 
 
+def _dense(t, name, shape, dtypes):
+    """The GEMM entry points take dense operands (no leading dimensions): t
+    must be a contiguous tensor of exactly `shape` with a dtype in `dtypes`."""
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must have dtype {' or '.join(str(d) for d in dtypes)}, not {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (dense row-major)")
+    return t
+
+
+def _mult128(name, v):
+    if v % 128:
+        raise ValueError(f"{name} must be a multiple of 128 (got {v})")
+
+
+def _codes_out(q, name, rows, cols, like, min_ld=None):
+    """A row-major E4M3 output [rows, cols] (row stride >= min_ld, default cols)."""
+    q = _codes(q) if q is not None else _empty((rows, cols), torch.uint8, like)
+    _rowmajor(q, name)
+    if q.shape[0] != rows or q.shape[1] < cols or (min_ld is None and q.shape[1] != cols):
+        raise ValueError(f"{name} must have {rows} rows of {cols} codes, not shape {tuple(q.shape)}")
+    if rows > 1 and q.stride(0) < (cols if min_ld is None else min_ld):
+        raise ValueError(f"{name} row stride {q.stride(0)} is too small")
+    return q
+
+
+def _scales_out(s, name, shape, like):
+    s = s if s is not None else _empty(shape, torch.float32, like)
+    return _dense(s, name, shape, _F32)
+
+
+def _workspace(workspace, need, like, stream):
+    """The caller's workspace (checked) or, when it needs one and gave none, a
+    new one that the caching allocator keeps from other work until `stream`
+    has finished with it."""
+    if workspace is None:
+        if not need:
+            return None
+        workspace = _empty((need,), torch.uint8, like)
+        if stream is not None:
+            workspace.record_stream(stream)
+        return workspace
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must hold at least {need} bytes")
+    return workspace
+
+
+def _ws_bytes(workspace):
+    return 0 if workspace is None else workspace.numel() * workspace.element_size()
+
+
 # ---------------------------------------------------------------------------
 def jet_abi_version() -> int:
     return _lib.jet_abi_version()
@@ -155,9 +210,9 @@ def _quant_1x128(name, x, q, s, stream):
     if x.dtype != torch.bfloat16:
         raise TypeError("x must be bfloat16")
     M, K = x.shape
-    q = _codes(q) if q is not None else _empty((M, K), torch.uint8, x)
-    s = s if s is not None else _empty((K // 128, M), torch.float32, x)
-    _rowmajor(q, "q")
+    _mult128("K", K)
+    q = _codes_out(q, "q", M, K, x)
+    s = _scales_out(s, "s", (K // 128, M), x)
     _check(name, getattr(_lib, name)(
         _ptr(x), M, K, x.stride(0), _ptr(q), q.stride(0), _ptr(s), _stream(stream)))
     return q, s
@@ -174,7 +229,7 @@ def jet_kv_calibrate(k, v, kv_scales=None, stream=None):
     if k.shape != v.shape:
         raise ValueError("k and v must have the same shape")
     T, D = k.shape
-    kv_scales = kv_scales if kv_scales is not None else _empty((6,), torch.float32, k)
+    kv_scales = _scales_out(kv_scales, "kv_scales", (6,), k)
     _check("jet_kv_calibrate", _lib.jet_kv_calibrate(
         _ptr(k), _ptr(v), T, D, k.stride(0), v.stride(0), _ptr(kv_scales), _stream(stream)))
     return kv_scales
@@ -194,6 +249,9 @@ def jet_kv_append(k, v, slots, kv_scales, k_cache, v_cache, stream=None):
     if k_cache.shape != v_cache.shape or k_cache.stride(0) != v_cache.stride(0):
         raise ValueError("k_cache and v_cache must have the same shape and row stride")
     T, D = k.shape
+    _dense(kv_scales, "kv_scales", (6,), _F32)
+    if k_cache.shape[1] < D:
+        raise ValueError("k_cache rows must hold D codes")
     _check("jet_kv_append", _lib.jet_kv_append(
         _ptr(k), _ptr(v), T, D, k.stride(0), v.stride(0), _ptr(slots), _ptr(kv_scales), _ptr(k_cache),
         _ptr(v_cache), k_cache.stride(0), k_cache.shape[0], _stream(stream)))
@@ -220,13 +278,15 @@ def _rmsnorm_quant(name, x, gamma, eps, y, return_y, q, s, stream):
     M, H = x.shape
     if gamma.numel() != H:
         raise ValueError("gamma must have H elements")
+    _mult128("H", H)
     if y is None and return_y:
         y = _empty((M, H), torch.bfloat16, x)
     if y is not None:
         _rowmajor(y, "y")
-    q = _codes(q) if q is not None else _empty((M, H), torch.uint8, x)
-    s = s if s is not None else _empty((H // 128, M), torch.float32, x)
-    _rowmajor(q, "q")
+        if tuple(y.shape) != (M, H) or y.dtype != torch.bfloat16:
+            raise ValueError(f"y must be a bfloat16 tensor of shape {(M, H)}")
+    q = _codes_out(q, "q", M, H, x)
+    s = _scales_out(s, "s", (H // 128, M), x)
     _check(name, getattr(_lib, name)(
         _ptr(x), _ptr(gamma), M, H, x.stride(0), float(eps), _ptr(y), 0 if y is None else y.stride(0),
         _ptr(q), q.stride(0), _ptr(s), _stream(stream)))
@@ -252,13 +312,17 @@ def _swiglu_quant(name, gu, inter, h, return_h, q, s, stream):
         raise TypeError("gu must be bfloat16")
     M = gu.shape[0]
     I = gu.shape[1] // 2 if inter is None else int(inter)
+    _mult128("I", I)
+    if gu.shape[1] < 2 * I:
+        raise ValueError(f"gu must hold 2*I = {2 * I} columns")
     if h is None and return_h:
         h = _empty((M, I), torch.bfloat16, gu)
     if h is not None:
         _rowmajor(h, "h")
-    q = _codes(q) if q is not None else _empty((M, I), torch.uint8, gu)
-    s = s if s is not None else _empty((I // 128, M), torch.float32, gu)
-    _rowmajor(q, "q")
+        if tuple(h.shape) != (M, I) or h.dtype != torch.bfloat16:
+            raise ValueError(f"h must be a bfloat16 tensor of shape {(M, I)}")
+    q = _codes_out(q, "q", M, I, gu)
+    s = _scales_out(s, "s", (I // 128, M), gu)
     _check(name, getattr(_lib, name)(
         _ptr(gu), M, I, gu.stride(0), _ptr(h), 0 if h is None else h.stride(0), _ptr(q), q.stride(0),
         _ptr(s), _stream(stream)))
@@ -283,17 +347,18 @@ def jet_quant_act_128x1_T_pow2(src, src_s=None, qT=None, sT=None, stream=None):
 def _quant_128x1_T(name, src, src_s, qT, sT, stream):
     _rowmajor(src, "src")
     M, K = src.shape
+    _mult128("K", K)
     if src_s is None:
         if src.dtype != torch.bfloat16:
             raise TypeError("src must be bfloat16 when src_s is None")
         dt = JET_BF16
     else:
         src = _codes(src)
+        _dense(src_s, "src_s", (K // 128, M), _F32)
         dt = JET_E4M3
     Mp = -(-M // 128) * 128
-    qT = _codes(qT) if qT is not None else _empty((K, Mp), torch.uint8, src)
-    sT = sT if sT is not None else _empty((Mp // 128, K), torch.float32, src)
-    _rowmajor(qT, "qT")
+    qT = _codes_out(qT, "qT", K, Mp, src, min_ld=Mp)
+    sT = _scales_out(sT, "sT", (Mp // 128, K), src)
     _check(name, getattr(_lib, name)(
         _ptr(src), dt, _ptr(src_s), M, K, src.stride(0), _ptr(qT), qT.stride(0), _ptr(sT),
         _stream(stream)))
@@ -321,13 +386,12 @@ def _quant_1x128_128x1_T(name, x, requant, q, s, qT, sT, stream):
     if x.dtype != torch.bfloat16:
         raise TypeError("x must be bfloat16")
     M, K = x.shape
+    _mult128("K", K)
     Mp = -(-M // 128) * 128
-    q = _codes(q) if q is not None else _empty((M, K), torch.uint8, x)
-    s = s if s is not None else _empty((K // 128, M), torch.float32, x)
-    qT = _codes(qT) if qT is not None else _empty((K, Mp), torch.uint8, x)
-    sT = sT if sT is not None else _empty((Mp // 128, K), torch.float32, x)
-    _rowmajor(q, "q")
-    _rowmajor(qT, "qT")
+    q = _codes_out(q, "q", M, K, x)
+    s = _scales_out(s, "s", (K // 128, M), x)
+    qT = _codes_out(qT, "qT", K, Mp, x, min_ld=Mp)
+    sT = _scales_out(sT, "sT", (Mp // 128, K), x)
     _check(name, getattr(_lib, name)(
         _ptr(x), M, K, x.stride(0), _ptr(q), q.stride(0), _ptr(s), _ptr(qT), qT.stride(0),
         _ptr(sT), 1 if requant else 0, _stream(stream)))
@@ -349,11 +413,15 @@ def _quant_weight(name, w, q, s, qT, transposed, stream):
     if w.dtype != torch.bfloat16:
         raise TypeError("w must be bfloat16")
     N, K = w.shape
-    q = _codes(q) if q is not None else _empty((N, K), torch.uint8, w)
-    s = s if s is not None else _empty((N // 128, K // 128), torch.float32, w)
+    _mult128("N", N)
+    _mult128("K", K)
+    # the weight codes are dense (the entry point takes no leading dimension for them)
+    q = _dense(_codes(q) if q is not None else _empty((N, K), torch.uint8, w), "q", (N, K), _U8)
+    s = _scales_out(s, "s", (N // 128, K // 128), w)
     if transposed and qT is None:
         qT = _empty((K, N), torch.uint8, w)
-    qT = _codes(qT)
+    if qT is not None:
+        qT = _dense(_codes(qT), "qT", (K, N), _U8)
     _check(name, getattr(_lib, name)(
         _ptr(w), N, K, w.stride(0), _ptr(q), _ptr(s), _ptr(qT), _stream(stream)))
     return q, s, qT
@@ -363,23 +431,93 @@ def _dtype_code(dt):
     return {torch.bfloat16: JET_BF16, torch.float32: JET_F32}[dt]
 
 
+_U8, _F32, _OUT = (torch.uint8,), (torch.float32,), (torch.bfloat16, torch.float32)
+
+
+def _operands(a, b, name_a, name_b):
+    """Codes of the two FP8 GEMM operands: 2-D, dense, sizes multiples of 128
+    where the layout needs it.  Returns them as uint8 views."""
+    a, b = _codes(a), _codes(b)
+    for t, n in ((a, name_a), (b, name_b)):
+        if t.dim() != 2:
+            raise ValueError(f"{n} must be a 2-D tensor")
+    return a, b
+
+
+def _out(t, name, shape, dtype, like, dtypes=_OUT):
+    t = t if t is not None else _empty(shape, dtype, like)
+    return _dense(t, name, shape, dtypes)
+
+
+def _fused_out(fuse_quant, y, yq, ys, M, N, like):
+    if not fuse_quant:
+        if yq is not None or ys is not None:
+            raise ValueError("yq and ys are outputs of the fused quantization (fuse_quant=True)")
+        return None, None
+    if y.dtype != torch.bfloat16:
+        raise TypeError("the fused 1x128 output quantizes a bfloat16 y")
+    yq = _dense(_codes(yq) if yq is not None else _empty((M, N), torch.uint8, like), "yq", (M, N), _U8)
+    ys = _out(ys, "ys", (N // 128, M), torch.float32, like, _F32)
+    return yq, ys
+
+
+def _fwd_args(xq, xs, wq, ws, y, out_dtype, fuse_quant, yq, ys):
+    xq, wq = _operands(xq, wq, "xq", "wq")
+    M, K = xq.shape
+    N = wq.shape[0]
+    _mult128("K", K)
+    _mult128("N", N)
+    _dense(xq, "xq", (M, K), _U8)
+    _dense(wq, "wq", (N, K), _U8)
+    _dense(xs, "xs", (K // 128, M), _F32)
+    _dense(ws, "ws", (N // 128, K // 128), _F32)
+    y = _out(y, "y", (M, N), out_dtype, xq)
+    yq, ys = _fused_out(fuse_quant, y, yq, ys, M, N, xq)
+    return xq, wq, M, N, K, y, yq, ys
+
+
+def _dgrad_args(dyq, dys, wqT, ws, dx, out_dtype):
+    dyq, wqT = _operands(dyq, wqT, "dyq", "wqT")
+    M, N = dyq.shape
+    K = wqT.shape[0]
+    _mult128("K", K)
+    _mult128("N", N)
+    _dense(dyq, "dyq", (M, N), _U8)
+    _dense(wqT, "wqT", (K, N), _U8)
+    _dense(dys, "dys", (N // 128, M), _F32)
+    _dense(ws, "ws", (N // 128, K // 128), _F32)
+    dx = _out(dx, "dx", (M, K), out_dtype, dyq)
+    return dyq, wqT, M, N, K, dx
+
+
+def _wgrad_args(dyqT, dysT, xqT, xsT, M, dw, out_dtype, accumulate):
+    dyqT, xqT = _operands(dyqT, xqT, "dyqT", "xqT")
+    M = int(M)
+    if M < 0:
+        raise ValueError("M must be >= 0")
+    N, K = dyqT.shape[0], xqT.shape[0]
+    _mult128("K", K)
+    _mult128("N", N)
+    Mp = -(-M // 128) * 128
+    # the transposed operands hold exactly ceil(M/128)*128 token columns (their row stride)
+    _dense(dyqT, "dyqT", (N, Mp), _U8)
+    _dense(xqT, "xqT", (K, Mp), _U8)
+    _dense(dysT, "dysT", (Mp // 128, N), _F32)
+    _dense(xsT, "xsT", (Mp // 128, K), _F32)
+    dw = _out(dw, "dw", (N, K), out_dtype, dyqT)
+    if accumulate and dw.dtype != torch.float32:
+        raise TypeError("accumulate needs a float32 dw")
+    return dyqT, xqT, M, N, K, dw
+
+
 def jet_fp8_linear_fwd(xq, xs, wq, ws, y=None, out_dtype=torch.bfloat16, fuse_quant=False,
                        yq=None, ys=None, workspace=None, stream=None):
     """Y = deq(xq) . deq(wq)^T.  Returns y, or (y, yq, ys) with fuse_quant."""
-    xq, wq = _codes(xq), _codes(wq)
-    M, K = xq.shape
-    N = wq.shape[0]
-    y = y if y is not None else _empty((M, N), out_dtype, xq)
-    if fuse_quant:
-        yq = _codes(yq) if yq is not None else _empty((M, N), torch.uint8, xq)
-        ys = ys if ys is not None else _empty((N // 128, M), torch.float32, xq)
-    need = jet_workspace_bytes(JET_OP_FWD, M, N, K)
-    if workspace is None and need:
-        workspace = _empty((need,), torch.uint8, xq)
+    xq, wq, M, N, K, y, yq, ys = _fwd_args(xq, xs, wq, ws, y, out_dtype, fuse_quant, yq, ys)
+    workspace = _workspace(workspace, jet_workspace_bytes(JET_OP_FWD, M, N, K), xq, stream)
     _check("jet_fp8_linear_fwd", _lib.jet_fp8_linear_fwd(
         _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), M, N, K, _ptr(y), _dtype_code(y.dtype),
-        _ptr(yq), _ptr(ys), _ptr(workspace), 0 if workspace is None else workspace.numel(),
-        _stream(stream)))
+        _ptr(yq), _ptr(ys), _ptr(workspace), _ws_bytes(workspace), _stream(stream)))
     return (y, yq, ys) if fuse_quant else y
 
 
@@ -387,13 +525,7 @@ def jet_fp8_linear_fwd_batch_invariant(xq, xs, wq, ws, y=None, out_dtype=torch.b
                                        yq=None, ys=None, stream=None):
     """As jet_fp8_linear_fwd, with each output row bit-identical at every M
     (no workspace)."""
-    xq, wq = _codes(xq), _codes(wq)
-    M, K = xq.shape
-    N = wq.shape[0]
-    y = y if y is not None else _empty((M, N), out_dtype, xq)
-    if fuse_quant:
-        yq = _codes(yq) if yq is not None else _empty((M, N), torch.uint8, xq)
-        ys = ys if ys is not None else _empty((N // 128, M), torch.float32, xq)
+    xq, wq, M, N, K, y, yq, ys = _fwd_args(xq, xs, wq, ws, y, out_dtype, fuse_quant, yq, ys)
     _check("jet_fp8_linear_fwd_batch_invariant", _lib.jet_fp8_linear_fwd_batch_invariant(
         _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), M, N, K, _ptr(y), _dtype_code(y.dtype), _ptr(yq), _ptr(ys),
         _stream(stream)))
@@ -403,32 +535,23 @@ def jet_fp8_linear_fwd_batch_invariant(xq, xs, wq, ws, y=None, out_dtype=torch.b
 def jet_fp8_linear_dgrad(dyq, dys, wqT, ws, dx=None, out_dtype=torch.bfloat16, workspace=None,
                          stream=None):
     """dX = deq(dyq) . deq(W); wqT is the transposed weight codes [K, N]."""
-    dyq, wqT = _codes(dyq), _codes(wqT)
-    M, N = dyq.shape
-    K = wqT.shape[0]
-    dx = dx if dx is not None else _empty((M, K), out_dtype, dyq)
-    need = jet_workspace_bytes(JET_OP_DGRAD, M, N, K)
-    if workspace is None and need:
-        workspace = _empty((need,), torch.uint8, dyq)
+    dyq, wqT, M, N, K, dx = _dgrad_args(dyq, dys, wqT, ws, dx, out_dtype)
+    workspace = _workspace(workspace, jet_workspace_bytes(JET_OP_DGRAD, M, N, K), dyq, stream)
     _check("jet_fp8_linear_dgrad", _lib.jet_fp8_linear_dgrad(
         _ptr(dyq), _ptr(dys), _ptr(wqT), _ptr(ws), M, N, K, _ptr(dx), _dtype_code(dx.dtype),
-        _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream)))
+        _ptr(workspace), _ws_bytes(workspace), _stream(stream)))
     return dx
 
 
 def jet_fp8_linear_wgrad(dyqT, dysT, xqT, xsT, M, dw=None, out_dtype=torch.float32,
                          accumulate=False, workspace=None, stream=None):
-    """dW (+)= deq(dyqT) . deq(xqT)^T over the M tokens (operands [N, Mp], [K, Mp])."""
-    dyqT, xqT = _codes(dyqT), _codes(xqT)
-    N, K = dyqT.shape[0], xqT.shape[0]
-    dw = dw if dw is not None else _empty((N, K), out_dtype, dyqT)
-    need = jet_workspace_bytes(JET_OP_WGRAD, M, N, K)
-    if workspace is None and need:
-        workspace = _empty((need,), torch.uint8, dyqT)
+    """dW (+)= deq(dyqT) . deq(xqT)^T over the M tokens (operands [N, Mp], [K, Mp],
+    Mp = ceil(M/128)*128)."""
+    dyqT, xqT, M, N, K, dw = _wgrad_args(dyqT, dysT, xqT, xsT, M, dw, out_dtype, accumulate)
+    workspace = _workspace(workspace, jet_workspace_bytes(JET_OP_WGRAD, M, N, K), dyqT, stream)
     _check("jet_fp8_linear_wgrad", _lib.jet_fp8_linear_wgrad(
         _ptr(dyqT), _ptr(dysT), _ptr(xqT), _ptr(xsT), M, N, K, _ptr(dw), _dtype_code(dw.dtype),
-        1 if accumulate else 0, _ptr(workspace), 0 if workspace is None else workspace.numel(),
-        _stream(stream)))
+        1 if accumulate else 0, _ptr(workspace), _ws_bytes(workspace), _stream(stream)))
     return dw
 
 
@@ -436,13 +559,7 @@ def jet_fp8_linear_fwd_pow2(xq, xs, wq, ws, y=None, out_dtype=torch.bfloat16, fu
                             yq=None, ys=None, stream=None):
     """Forward on power-of-two-scaled operands (scales applied by the MFMA).
     Returns y, or (y, yq, ys) with the power-of-two 1x128 quantization of Y."""
-    xq, wq = _codes(xq), _codes(wq)
-    M, K = xq.shape
-    N = wq.shape[0]
-    y = y if y is not None else _empty((M, N), out_dtype, xq)
-    if fuse_quant:
-        yq = _codes(yq) if yq is not None else _empty((M, N), torch.uint8, xq)
-        ys = ys if ys is not None else _empty((N // 128, M), torch.float32, xq)
+    xq, wq, M, N, K, y, yq, ys = _fwd_args(xq, xs, wq, ws, y, out_dtype, fuse_quant, yq, ys)
     _check("jet_fp8_linear_fwd_pow2", _lib.jet_fp8_linear_fwd_pow2(
         _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), M, N, K, _ptr(y), _dtype_code(y.dtype), _ptr(yq), _ptr(ys),
         _stream(stream)))
@@ -451,10 +568,7 @@ def jet_fp8_linear_fwd_pow2(xq, xs, wq, ws, y=None, out_dtype=torch.bfloat16, fu
 
 def jet_fp8_linear_dgrad_pow2(dyq, dys, wqT, ws, dx=None, out_dtype=torch.bfloat16, stream=None):
     """DGrad on power-of-two-scaled operands; wqT the transposed weight codes [K, N]."""
-    dyq, wqT = _codes(dyq), _codes(wqT)
-    M, N = dyq.shape
-    K = wqT.shape[0]
-    dx = dx if dx is not None else _empty((M, K), out_dtype, dyq)
+    dyq, wqT, M, N, K, dx = _dgrad_args(dyq, dys, wqT, ws, dx, out_dtype)
     _check("jet_fp8_linear_dgrad_pow2", _lib.jet_fp8_linear_dgrad_pow2(
         _ptr(dyq), _ptr(dys), _ptr(wqT), _ptr(ws), M, N, K, _ptr(dx), _dtype_code(dx.dtype), _stream(stream)))
     return dx
@@ -463,9 +577,7 @@ def jet_fp8_linear_dgrad_pow2(dyq, dys, wqT, ws, dx=None, out_dtype=torch.bfloat
 def jet_fp8_linear_wgrad_pow2(dyqT, dysT, xqT, xsT, M, dw=None, out_dtype=torch.float32, accumulate=False,
                               stream=None):
     """WGrad on power-of-two-scaled 128x1 operands ([N, Mp], [K, Mp])."""
-    dyqT, xqT = _codes(dyqT), _codes(xqT)
-    N, K = dyqT.shape[0], xqT.shape[0]
-    dw = dw if dw is not None else _empty((N, K), out_dtype, dyqT)
+    dyqT, xqT, M, N, K, dw = _wgrad_args(dyqT, dysT, xqT, xsT, M, dw, out_dtype, accumulate)
     _check("jet_fp8_linear_wgrad_pow2", _lib.jet_fp8_linear_wgrad_pow2(
         _ptr(dyqT), _ptr(dysT), _ptr(xqT), _ptr(xsT), M, N, K, _ptr(dw), _dtype_code(dw.dtype),
         1 if accumulate else 0, _stream(stream)))
@@ -501,86 +613,124 @@ def _quant_128x1_T_grouped(name, src, seg_off, src_s, qT, sT, stream):
     _rowmajor(src, "src")
     seg_off, E = _seg(seg_off)
     M, K = src.shape
+    _mult128("K", K)
     if src_s is None:
         if src.dtype != torch.bfloat16:
             raise TypeError("src must be bfloat16 when src_s is None")
         dt = JET_BF16
     else:
         src = _codes(src)
+        _dense(src_s, "src_s", (K // 128, M), _F32)
         dt = JET_E4M3
     P = grouped_columns(M, E)
-    qT = _codes(qT) if qT is not None else _empty((K, P), torch.uint8, src)
-    sT = sT if sT is not None else _empty((qT.stride(0) // 128, K), torch.float32, src)
-    _rowmajor(qT, "qT")
+    qT = _codes_out(qT, "qT", K, P, src, min_ld=P)
+    if K > 1 and qT.stride(0) % 128:
+        raise ValueError("qT's row stride must be a multiple of 128")
+    ld = qT.stride(0) if K > 1 else qT.shape[1]
+    sT = _scales_out(sT, "sT", (ld // 128, K), src)
     _check(name, getattr(_lib, name)(
         _ptr(src), dt, _ptr(src_s), M, K, src.stride(0), _ptr(seg_off), E, _ptr(qT), qT.stride(0),
         _ptr(sT), _stream(stream)))
     return qT, sT
 
 
+def _grouped_fwd_args(xq, xs, wq, ws, seg_off, y, out_dtype, fuse_quant, yq, ys):
+    seg_off, E = _seg(seg_off)
+    xq, wq = _codes(xq), _codes(wq)
+    if xq.dim() != 2 or wq.dim() != 3:
+        raise ValueError("xq must be 2-D [M, K] and wq 3-D [E, N, K]")
+    M, K = xq.shape
+    N = wq.shape[1]
+    _mult128("K", K)
+    _mult128("N", N)
+    _dense(xq, "xq", (M, K), _U8)
+    _dense(wq, "wq", (E, N, K), _U8)
+    _dense(xs, "xs", (K // 128, M), _F32)
+    _dense(ws, "ws", (E, N // 128, K // 128), _F32)
+    y = _out(y, "y", (M, N), out_dtype, xq)
+    yq, ys = _fused_out(fuse_quant, y, yq, ys, M, N, xq)
+    return seg_off, E, xq, wq, M, N, K, y, yq, ys
+
+
+def _grouped_dgrad_args(dyq, dys, wqT, ws, seg_off, dx, out_dtype):
+    seg_off, E = _seg(seg_off)
+    dyq, wqT = _operands(dyq, wqT, "dyq", "wqT")
+    M, N = dyq.shape
+    K = wqT.shape[0]
+    _mult128("K", K)
+    _mult128("N", N)
+    _dense(dyq, "dyq", (M, N), _U8)
+    _dense(wqT, "wqT", (K, E * N), _U8)
+    _dense(dys, "dys", (N // 128, M), _F32)
+    _dense(ws, "ws", (E, N // 128, K // 128), _F32)
+    dx = _out(dx, "dx", (M, K), out_dtype, dyq)
+    return seg_off, E, dyq, wqT, M, N, K, dx
+
+
+def _grouped_wgrad_args(dyqT, dysT, xqT, xsT, seg_off, M, dw, out_dtype, accumulate):
+    seg_off, E = _seg(seg_off)
+    dyqT, xqT = _operands(dyqT, xqT, "dyqT", "xqT")
+    M = int(M)
+    if M < 0:
+        raise ValueError("M must be >= 0")
+    N, K = dyqT.shape[0], xqT.shape[0]
+    _mult128("K", K)
+    _mult128("N", N)
+    _rowmajor(dyqT, "dyqT")
+    _rowmajor(xqT, "xqT")
+    ldT = dyqT.stride(0)
+    if xqT.stride(0) != ldT:
+        raise ValueError("dyqT and xqT need the same row stride")
+    if ldT % 128 or ldT < grouped_columns(M, E) or dyqT.shape[1] > ldT or xqT.shape[1] > ldT:
+        raise ValueError(f"the grouped transposed operands need a row stride that is a multiple of 128 "
+                         f"and >= {grouped_columns(M, E)} (got {ldT})")
+    _dense(dysT, "dysT", (ldT // 128, N), _F32)
+    _dense(xsT, "xsT", (ldT // 128, K), _F32)
+    dw = _out(dw, "dw", (E, N, K), out_dtype, dyqT)
+    if accumulate and dw.dtype != torch.float32:
+        raise TypeError("accumulate needs a float32 dw")
+    return seg_off, E, dyqT, xqT, ldT, M, N, K, dw
+
+
 def jet_fp8_grouped_fwd(xq, xs, wq, ws, seg_off, y=None, out_dtype=torch.bfloat16,
                         fuse_quant=False, yq=None, ys=None, workspace=None, stream=None):
     """Y rows of expert e = deq(xq_e) . deq(wq[e])^T; wq [E, N, K], ws [E, N/128, K/128]."""
-    xq, wq = _codes(xq), _codes(wq)
-    seg_off, E = _seg(seg_off)
-    M, K = xq.shape
-    N = wq.shape[1]
-    y = y if y is not None else _empty((M, N), out_dtype, xq)
-    if fuse_quant:
-        yq = _codes(yq) if yq is not None else _empty((M, N), torch.uint8, xq)
-        ys = ys if ys is not None else _empty((N // 128, M), torch.float32, xq)
-    # the grouped GEMMs take no workspace (a caller's buffer is passed through)
+    seg_off, E, xq, wq, M, N, K, y, yq, ys = _grouped_fwd_args(xq, xs, wq, ws, seg_off, y, out_dtype,
+                                                               fuse_quant, yq, ys)
+    # the grouped GEMMs need no workspace (a caller's buffer is passed through)
     _check("jet_fp8_grouped_fwd", _lib.jet_fp8_grouped_fwd(
         _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(seg_off), E, M, N, K, _ptr(y),
-        _dtype_code(y.dtype), _ptr(yq), _ptr(ys), _ptr(workspace),
-        0 if workspace is None else workspace.numel(), _stream(stream)))
+        _dtype_code(y.dtype), _ptr(yq), _ptr(ys), _ptr(workspace), _ws_bytes(workspace), _stream(stream)))
     return (y, yq, ys) if fuse_quant else y
 
 
 def jet_fp8_grouped_dgrad(dyq, dys, wqT, ws, seg_off, dx=None, out_dtype=torch.bfloat16,
                           workspace=None, stream=None):
     """dX rows of expert e = deq(dyq_e) . deq(W_e); wqT [K, E*N] (stacked transposed codes)."""
-    dyq, wqT = _codes(dyq), _codes(wqT)
-    seg_off, E = _seg(seg_off)
-    M, N = dyq.shape
-    K = wqT.shape[0]
-    dx = dx if dx is not None else _empty((M, K), out_dtype, dyq)
-    # the grouped GEMMs take no workspace (a caller's buffer is passed through)
+    seg_off, E, dyq, wqT, M, N, K, dx = _grouped_dgrad_args(dyq, dys, wqT, ws, seg_off, dx, out_dtype)
     _check("jet_fp8_grouped_dgrad", _lib.jet_fp8_grouped_dgrad(
         _ptr(dyq), _ptr(dys), _ptr(wqT), _ptr(ws), _ptr(seg_off), E, M, N, K, _ptr(dx),
-        _dtype_code(dx.dtype), _ptr(workspace), 0 if workspace is None else workspace.numel(),
-        _stream(stream)))
+        _dtype_code(dx.dtype), _ptr(workspace), _ws_bytes(workspace), _stream(stream)))
     return dx
 
 
 def jet_fp8_grouped_wgrad(dyqT, dysT, xqT, xsT, seg_off, M, dw=None, out_dtype=torch.float32,
                           accumulate=False, workspace=None, stream=None):
     """dW_e (+)= deq(dyqT_e) . deq(xqT_e)^T; operands in the padded grouped layout [N, P], [K, P]."""
-    dyqT, xqT = _codes(dyqT), _codes(xqT)
-    seg_off, E = _seg(seg_off)
-    N, K = dyqT.shape[0], xqT.shape[0]
-    if dyqT.stride(0) != xqT.stride(0):
-        raise ValueError("dyqT and xqT need the same row stride")
-    dw = dw if dw is not None else _empty((E, N, K), out_dtype, dyqT)
-    # the grouped GEMMs take no workspace (a caller's buffer is passed through)
+    seg_off, E, dyqT, xqT, ldT, M, N, K, dw = _grouped_wgrad_args(dyqT, dysT, xqT, xsT, seg_off, M, dw,
+                                                                  out_dtype, accumulate)
     _check("jet_fp8_grouped_wgrad", _lib.jet_fp8_grouped_wgrad(
-        _ptr(dyqT), _ptr(dysT), _ptr(xqT), _ptr(xsT), dyqT.stride(0), _ptr(seg_off), E, M, N, K,
-        _ptr(dw), _dtype_code(dw.dtype), 1 if accumulate else 0, _ptr(workspace),
-        0 if workspace is None else workspace.numel(), _stream(stream)))
+        _ptr(dyqT), _ptr(dysT), _ptr(xqT), _ptr(xsT), ldT, _ptr(seg_off), E, M, N, K,
+        _ptr(dw), _dtype_code(dw.dtype), 1 if accumulate else 0, _ptr(workspace), _ws_bytes(workspace),
+        _stream(stream)))
     return dw
 
 
 def jet_fp8_grouped_fwd_pow2(xq, xs, wq, ws, seg_off, y=None, out_dtype=torch.bfloat16,
                              fuse_quant=False, yq=None, ys=None, stream=None):
     """jet_fp8_grouped_fwd on power-of-two-scaled operands (scales applied by the MFMA)."""
-    xq, wq = _codes(xq), _codes(wq)
-    seg_off, E = _seg(seg_off)
-    M, K = xq.shape
-    N = wq.shape[1]
-    y = y if y is not None else _empty((M, N), out_dtype, xq)
-    if fuse_quant:
-        yq = _codes(yq) if yq is not None else _empty((M, N), torch.uint8, xq)
-        ys = ys if ys is not None else _empty((N // 128, M), torch.float32, xq)
+    seg_off, E, xq, wq, M, N, K, y, yq, ys = _grouped_fwd_args(xq, xs, wq, ws, seg_off, y, out_dtype,
+                                                               fuse_quant, yq, ys)
     _check("jet_fp8_grouped_fwd_pow2", _lib.jet_fp8_grouped_fwd_pow2(
         _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(seg_off), E, M, N, K, _ptr(y),
         _dtype_code(y.dtype), _ptr(yq), _ptr(ys), _stream(stream)))
@@ -589,11 +739,7 @@ def jet_fp8_grouped_fwd_pow2(xq, xs, wq, ws, seg_off, y=None, out_dtype=torch.bf
 
 def jet_fp8_grouped_dgrad_pow2(dyq, dys, wqT, ws, seg_off, dx=None, out_dtype=torch.bfloat16, stream=None):
     """jet_fp8_grouped_dgrad on power-of-two-scaled operands."""
-    dyq, wqT = _codes(dyq), _codes(wqT)
-    seg_off, E = _seg(seg_off)
-    M, N = dyq.shape
-    K = wqT.shape[0]
-    dx = dx if dx is not None else _empty((M, K), out_dtype, dyq)
+    seg_off, E, dyq, wqT, M, N, K, dx = _grouped_dgrad_args(dyq, dys, wqT, ws, seg_off, dx, out_dtype)
     _check("jet_fp8_grouped_dgrad_pow2", _lib.jet_fp8_grouped_dgrad_pow2(
         _ptr(dyq), _ptr(dys), _ptr(wqT), _ptr(ws), _ptr(seg_off), E, M, N, K, _ptr(dx),
         _dtype_code(dx.dtype), _stream(stream)))
@@ -603,13 +749,9 @@ def jet_fp8_grouped_dgrad_pow2(dyq, dys, wqT, ws, seg_off, dx=None, out_dtype=to
 def jet_fp8_grouped_wgrad_pow2(dyqT, dysT, xqT, xsT, seg_off, M, dw=None, out_dtype=torch.float32,
                                accumulate=False, stream=None):
     """jet_fp8_grouped_wgrad on power-of-two-scaled operands."""
-    dyqT, xqT = _codes(dyqT), _codes(xqT)
-    seg_off, E = _seg(seg_off)
-    N, K = dyqT.shape[0], xqT.shape[0]
-    if dyqT.stride(0) != xqT.stride(0):
-        raise ValueError("dyqT and xqT need the same row stride")
-    dw = dw if dw is not None else _empty((E, N, K), out_dtype, dyqT)
+    seg_off, E, dyqT, xqT, ldT, M, N, K, dw = _grouped_wgrad_args(dyqT, dysT, xqT, xsT, seg_off, M, dw,
+                                                                  out_dtype, accumulate)
     _check("jet_fp8_grouped_wgrad_pow2", _lib.jet_fp8_grouped_wgrad_pow2(
-        _ptr(dyqT), _ptr(dysT), _ptr(xqT), _ptr(xsT), dyqT.stride(0), _ptr(seg_off), E, M, N, K,
+        _ptr(dyqT), _ptr(dysT), _ptr(xqT), _ptr(xsT), ldT, _ptr(seg_off), E, M, N, K,
         _ptr(dw), _dtype_code(dw.dtype), 1 if accumulate else 0, _stream(stream)))
     return dw

@@ -312,6 +312,34 @@ def test_small_m_graph_replay(gpu_lib):
         torch.cuda.synchronize()
 
 
+def test_forward_on_a_side_stream_with_its_own_workspace(gpu_lib):
+    """The binding allocates the split-K workspace itself when none is given;
+    on a side stream the result equals the current-stream call bit for bit."""
+    M, N, K = 64, 1024, 4096
+    assert gpu_lib.jet_workspace_bytes(gpu_lib.JET_OP_FWD, M, N, K) > 0
+    x, w, _ = layer_inputs(M, N, K, 12)
+    xq, xs = gpu_lib.jet_quant_act_1x128(dev_bf16(x))
+    wq, ws, _ = gpu_lib.jet_quant_weight_128x128(dev_bf16(w), transposed=False)
+    ref, refq, refs = gpu_lib.jet_fp8_linear_fwd(xq, xs, wq, ws, fuse_quant=True)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(3):
+        y = torch.empty_like(ref)
+        yq = torch.empty_like(refq)
+        ys = torch.empty_like(refs)
+        with torch.cuda.stream(side):
+            y.record_stream(side); yq.record_stream(side); ys.record_stream(side)
+        gpu_lib.jet_fp8_linear_fwd(xq, xs, wq, ws, y=y, fuse_quant=True, yq=yq, ys=ys, stream=side)
+        # work on the current stream that may reuse freed blocks meanwhile
+        junk = torch.empty(M * N * 16, dtype=torch.uint8, device="cuda").fill_(0xA5)
+        del junk
+        outs.append((y, yq, ys))
+    torch.cuda.synchronize()
+    for y, yq, ys in outs:
+        assert torch.equal(y, ref) and torch.equal(yq, refq) and torch.equal(ys, refs)
+
+
 def test_small_m_matches_exact_integer_case(gpu_lib):
     """Integer operands with +-7 anchors (every scale 2^-6): the split-K sums
     are exact, so the small-M forward equals the int64 matmul bit for bit."""
@@ -361,9 +389,10 @@ def test_decode_forward_llama_shapes(gpu_lib, name):
     del wsub
 
 
-@pytest.mark.parametrize("name", ["qkv", "down"])
+@pytest.mark.parametrize("name", list(LLAMA))
 def test_training_shapes_sampled(gpu_lib, name):
-    """Training M=8192: all three GEMMs at full size, checked on sampled rows."""
+    """Training M=8192, every Llama-3.1-8B linear: all three GEMMs at full
+    size with FP32 scales, checked on sampled rows."""
     N, K = LLAMA[name]
     M = 8192
     x, w, dy = layer_inputs(M, N, K, 0)
@@ -405,16 +434,18 @@ def test_training_shapes_sampled(gpu_lib, name):
 
 # --- Qwen-14B/32B shapes at M=16384 (sampled) ---------------------------------
 
-QWEN = {"qkv": (7168, 5120), "down_32b": (5120, 27648), "gate_up_14b": (34816, 5120)}
+# (N, K): hidden 5120; QKV with 40 query and 8 key/value heads of 128; the
+# fused gate+up projections of the 14B (intermediate 17408) and 32B (27648)
+# models and their down projections.
+QWEN = {"qkv": (7168, 5120), "o": (5120, 5120), "gate_up_14b": (34816, 5120),
+        "gate_up_32b": (55296, 5120), "down_14b": (5120, 17408), "down_32b": (5120, 27648)}
 
 
-@pytest.mark.parametrize("name", ["qkv", "down_32b"])
+@pytest.mark.parametrize("name", list(QWEN))
 def test_qwen_shapes_sampled(gpu_lib, name):
-    """Qwen-14B/32B-shaped linears (hidden 5120; QKV 5120->7168 with 40 query
-    and 8 key/value heads of 128; the 32B down projection 27648->5120) at
-    M=16384 training tokens: the step's quantizers (both activation groupings
-    from one read) and all three GEMMs at full size, checked on sampled rows
-    and columns against the oracle."""
+    """Every Qwen-14B/32B-shaped linear at M=16384 training tokens: the step's
+    quantizers (both activation groupings from one read) and all three GEMMs
+    at full size, checked on sampled rows and columns against the oracle."""
     N, K = QWEN[name]
     M = 16384
     x, w, dy = layer_inputs(M, N, K, 3)
