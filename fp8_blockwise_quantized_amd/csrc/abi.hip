@@ -4,6 +4,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "../../include/jetfp8.h"
 #include "jet_launch.hpp"
 
@@ -309,7 +311,8 @@ static int check_gemm_common(const char* name, int64_t M, int64_t N, int64_t K, 
 // MFMA, one K range at every M (no workspace; batch-invariant as well).
 static int linear_fwd(const char* name, const uint8_t* xq, const float* xs, const uint8_t* wq,
                       const float* ws, int64_t M, int64_t N, int64_t K, void* y, int y_dtype, uint8_t* yq,
-                      float* ys, void* workspace, size_t ws_bytes, void* stream, bool invariant, bool p2 = false) {
+                      float* ys, void* workspace, size_t ws_bytes, void* stream, bool invariant, bool p2 = false,
+                      bool validate_only = false) {
   g_last_error[0] = 0;
   const size_t need = (invariant || p2) ? 0 : jet_workspace_bytes(JET_OP_FWD, M, N, K);
   if (int st = check_gemm_common(name, M, N, K, need, ws_bytes, workspace)) return st;
@@ -324,6 +327,7 @@ static int linear_fwd(const char* name, const uint8_t* xq, const float* xs, cons
   if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(y, 16) || !aligned(xs, 4) || !aligned(ws, 4) ||
       (fuse && (!aligned(yq, 16) || !aligned(ys, 4))))
     return fail(JET_ERR_ALIGN, "%s: operands and outputs need 16-byte alignment", name);
+  if (validate_only) return JET_OK;
   jet::GemmArgs a{};
   a.A = xq; a.lda = K;
   a.B = wq; a.ldb = K;
@@ -341,6 +345,69 @@ int jet_fp8_linear_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, co
                        int64_t M, int64_t N, int64_t K, void* y, int y_dtype, uint8_t* yq, float* ys,
                        void* workspace, size_t ws_bytes, void* stream) {
   return linear_fwd("fp8_linear_fwd", xq, xs, wq, ws, M, N, K, y, y_dtype, yq, ys, workspace, ws_bytes,
+                    stream, false);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Device scratch of jet_fp8_linear_fwd_noalloc: the split-K partial sums of
+// the small-M forward live here instead of in a caller's workspace.  Every
+// GPU the library runs on holds its own copy of the array until the process
+// ends.  16 MiB covers every split the forward chooses (at most
+// S * M * N * 4 bytes with M <= 128 and S * N <= 128 * (N/128 + 128): below
+// 16.7 million bytes); the guard below still rejects a larger need.
+namespace {
+
+constexpr size_t kScratchBytes = size_t(16) << 20;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of this device's copy of `scratch`, looked up once per
+// device (with that device current) and kept.  In host code the array's name
+// is only a host-side stand-in, never a device address.
+int scratch_address(const char* name, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, name);
+  if (dev < 0 || dev >= kMaxDevices) return fail(JET_ERR_HIP, "%s: device %d out of range", name, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, name);
+    if (!p) return fail(JET_ERR_HIP, "%s: no device address for the scratch array", name);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return JET_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int jet_fp8_linear_fwd_noalloc(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
+                               int64_t M, int64_t N, int64_t K, void* y, int y_dtype, uint8_t* yq,
+                               float* ys, void* stream) {
+  static const char* const name = "fp8_linear_fwd_noalloc";
+  g_last_error[0] = 0;
+  const size_t need = jet_workspace_bytes(JET_OP_FWD, M, N, K);
+  if (need > kScratchBytes)
+    return fail(JET_ERR_WORKSPACE, "%s: this shape needs %zu bytes of scratch; the static scratch holds %zu",
+                name, need, kScratchBytes);
+  // every argument error before any HIP call; an empty output launches nothing
+  void* const fake = reinterpret_cast<void*>(uintptr_t(256));   // aligned stand-in, never dereferenced
+  if (int st = linear_fwd(name, xq, xs, wq, ws, M, N, K, y, y_dtype, yq, ys, need ? fake : nullptr,
+                          kScratchBytes, stream, false, false, true))
+    return st;
+  if (M == 0 || N == 0) return JET_OK;
+  void* sp = nullptr;
+  if (int st = scratch_address(name, &sp)) return st;
+  return linear_fwd(name, xq, xs, wq, ws, M, N, K, y, y_dtype, yq, ys, need ? sp : nullptr, kScratchBytes,
                     stream, false);
 }
 

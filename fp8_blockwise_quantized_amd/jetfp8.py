@@ -38,6 +38,7 @@ SIGNATURES = {
     "jet_swiglu_quant_1x128": [_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _p],
     "jet_fp8_linear_fwd": [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _p, _p, _p, _sz, _p],
     "jet_fp8_linear_fwd_batch_invariant": [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _p, _p, _p],
+    "jet_fp8_linear_fwd_noalloc": [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _p, _p, _p],
     "jet_fp8_linear_dgrad": [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _p, _sz, _p],
     "jet_fp8_linear_wgrad": [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _i32, _p, _sz, _p],
     "jet_workspace_bytes": [_i32, _i64, _i64, _i64],
@@ -527,6 +528,19 @@ def jet_fp8_linear_fwd_batch_invariant(xq, xs, wq, ws, y=None, out_dtype=torch.b
     (no workspace)."""
     xq, wq, M, N, K, y, yq, ys = _fwd_args(xq, xs, wq, ws, y, out_dtype, fuse_quant, yq, ys)
     _check("jet_fp8_linear_fwd_batch_invariant", _lib.jet_fp8_linear_fwd_batch_invariant(
+        _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), M, N, K, _ptr(y), _dtype_code(y.dtype), _ptr(yq), _ptr(ys),
+        _stream(stream)))
+    return (y, yq, ys) if fuse_quant else y
+
+
+def jet_fp8_linear_fwd_noalloc(xq, xs, wq, ws, y=None, out_dtype=torch.bfloat16, fuse_quant=False,
+                               yq=None, ys=None, stream=None):
+    """As jet_fp8_linear_fwd, with the split-K partial sums in the library's
+    static device scratch (the C call allocates nothing; pass y, and yq and
+    ys when fusing, to allocate nothing here either).  Calls that overlap on
+    one GPU race on the scratch."""
+    xq, wq, M, N, K, y, yq, ys = _fwd_args(xq, xs, wq, ws, y, out_dtype, fuse_quant, yq, ys)
+    _check("jet_fp8_linear_fwd_noalloc", _lib.jet_fp8_linear_fwd_noalloc(
         _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), M, N, K, _ptr(y), _dtype_code(y.dtype), _ptr(yq), _ptr(ys),
         _stream(stream)))
     return (y, yq, ys) if fuse_quant else y

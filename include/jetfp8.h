@@ -32,7 +32,10 @@
  *    round-to-nearest-even from the FP32 accumulator.
  *  - Identical inputs give bit-identical outputs (no atomics in reductions).
  *  - The library keeps no global mutable state other than the thread-local
- *    error string; calls from several host threads are safe.
+ *    error string, and, for jet_fp8_linear_fwd_noalloc only, its static
+ *    device scratch and the per-device table of that scratch's address
+ *    (filled once under a lock); calls from several host threads are safe,
+ *    except overlapping jet_fp8_linear_fwd_noalloc calls on one GPU.
  */
 #ifndef JETFP8_H
 #define JETFP8_H
@@ -44,7 +47,7 @@
 extern "C" {
 #endif
 
-#define JET_ABI_VERSION 9
+#define JET_ABI_VERSION 10
 
 typedef enum {
   JET_OK = 0,
@@ -280,6 +283,29 @@ int jet_fp8_linear_fwd_batch_invariant(const uint8_t* xq, const float* xs,
                                        int64_t M, int64_t N, int64_t K,
                                        void* y, int y_dtype, uint8_t* yq, float* ys,
                                        void* stream);
+
+/*
+ * jet_fp8_linear_fwd for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The split-K partial sums of the small-M forward (the only
+ * scratch of jet_fp8_linear_fwd) go to a static device array of 16 MiB that
+ * the library holds on every GPU it runs on until the process ends, instead
+ * of a caller's workspace; the call itself allocates and frees nothing.
+ * Arguments, layouts, results (bit for bit) and errors as jet_fp8_linear_fwd
+ * without the workspace; JET_ERR_WORKSPACE if jet_workspace_bytes(JET_OP_FWD,
+ * M, N, K) exceeds the array (no shape the forward accepts needs more than
+ * 16,646,144 bytes today).  The first call on a device looks up that
+ * device's copy of the array (hipGetSymbolAddress); JET_ERR_HIP if that
+ * fails.  All calls on one GPU share its array and nothing in it needs to
+ * start at zero (every partial sum is written before it is read), but calls
+ * that overlap in time on one GPU -- on different streams, or from several
+ * host threads -- race on it: serialise them.
+ */
+int jet_fp8_linear_fwd_noalloc(const uint8_t* xq, const float* xs,
+                               const uint8_t* wq, const float* ws,
+                               int64_t M, int64_t N, int64_t K,
+                               void* y, int y_dtype, uint8_t* yq, float* ys,
+                               void* stream);
 
 /*
  * Data-gradient GEMM  dX[m,k] = sum_n dYhat[m,n] * What[n,k].

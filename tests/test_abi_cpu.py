@@ -48,7 +48,7 @@ def test_binding_covers_header(J):
 
 
 def test_version_and_status_strings(J):
-    assert J.jet_abi_version() == 9
+    assert J.jet_abi_version() == 10
     assert J.jet_status_string(J.JET_ERR_SHAPE) == "JET_ERR_SHAPE"
     assert J.jet_status_string(99) == "JET_ERR_UNKNOWN"
 
@@ -123,6 +123,23 @@ def test_batch_invariant_forward_validation(J):
     assert f(P17, P16, P16, P16, 64, 128, 128, P16, J.JET_BF16, None, None, None) == J.JET_ERR_ALIGN
     assert f(*a, 0, 128, 128, P16, J.JET_BF16, None, None, None) == J.JET_OK
     assert "batch_invariant" in J.jet_last_error() or J.jet_last_error() == ""
+
+
+def test_noalloc_forward_validation(J):
+    """Argument errors are reported before the scratch is looked up (no HIP
+    call): the same rules as the forward, no workspace argument."""
+    L = J._lib
+    a = (P16, P16, P16, P16)
+    f = L.jet_fp8_linear_fwd_noalloc
+    assert f(*a, 64, 100, 128, P16, J.JET_BF16, None, None, None) == J.JET_ERR_SHAPE
+    assert f(*a, 64, 128, 128, P16, 7, None, None, None) == J.JET_ERR_DTYPE
+    assert f(*a, 64, 128, 128, P16, J.JET_F32, P16, P16, None) == J.JET_ERR_DTYPE
+    assert f(*a, 64, 128, 128, P16, J.JET_BF16, P16, None, None) == J.JET_ERR_NULL
+    assert f(None, P16, P16, P16, 64, 128, 1280, P16, J.JET_BF16, None, None, None) == J.JET_ERR_NULL
+    assert f(P17, P16, P16, P16, 64, 128, 1280, P16, J.JET_BF16, None, None, None) == J.JET_ERR_ALIGN
+    assert "noalloc" in J.jet_last_error()
+    assert f(*a, 0, 128, 128, P16, J.JET_BF16, None, None, None) == J.JET_OK   # empty: nothing launched
+    assert f(*a, 64, (1 << 24) + 128, 128, P16, J.JET_BF16, None, None, None) == J.JET_ERR_SHAPE
 
 
 def test_gemm_operand_stride_limit(J):
