@@ -17,7 +17,14 @@ of a 8192-token prefill, append of a 64-token decode step);
 `--workload decode` times the rollout forward of the same linears at M = 64;
 `--workload moe` the grouped (mixture-of-experts) layer of Qwen3-30B-A3B shape
 (hidden 2048, expert intermediate 768, 128 experts, top-8 of 8192 tokens with
-Zipf(1.1) expert load), fwd + dgrad + wgrad with every quantizer.
+Zipf(1.1) expert load), fwd + dgrad + wgrad with every quantizer;
+`--workload qwen` the train step over the six Qwen-14B/32B-shaped linears at
+M = 16384 tokens.
+
+Every line carries `measured_ceilings`: streaming rates for the quantizers'
+read/write mixes and the FP8 MFMA rate with and without the per-step FP32
+fold on this GPU (include/jetprobe.h), with the shader clock under that MFMA
+load, next to the published peaks the roofline fractions use.
 
 Prints ONE JSON line.  --gpus above 1 is refused: the benchmark measures one GPU.
 """
@@ -38,8 +45,15 @@ PEAK_FP8_TFLOPS = 5000.0       # MI355X dense OCP-FP8 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 LAYERS = [("qkv", 6144, 4096), ("o", 4096, 4096), ("gate_up", 28672, 4096), ("down", 4096, 14336)]
 M_TOKENS = 8192
+# Qwen-14B/32B (hidden 5120): QKV with 40 query and 8 key/value heads of 128,
+# O, the fused gate+up of the 14B (intermediate 17408) and 32B (27648)
+# models, and their down projections.
+QWEN_LAYERS = [("qkv", 7168, 5120), ("o", 5120, 5120), ("gate_up_14b", 34816, 5120),
+               ("gate_up_32b", 55296, 5120), ("down_14b", 5120, 17408), ("down_32b", 5120, 27648)]
+QWEN_TOKENS = 16384
 COUNTERS = os.path.join(ROOT, "profiles", "gemm_counters.json")
 MOE_COUNTERS = os.path.join(ROOT, "profiles", "moe_counters.json")
+QWEN_COUNTERS = os.path.join(ROOT, "profiles", "qwen_counters.json")
 GEMM_SRC = os.path.join(ROOT, "fp8_blockwise_quantized_amd", "csrc", "gemm.hip")
 
 
@@ -51,8 +65,10 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured ceilings (streaming and MFMA probes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16-context", action="store_true",
                     help="train: skip timing hipBLASLt BF16 GEMMs on the same shapes (context only)")
@@ -61,9 +77,10 @@ def parse():
     ap.add_argument("--events", type=int, default=1,
                     help="1: after the timed steps, as many steps again with HIP events around every "
                          "launch (per-kernel times); 0: skip that pass")
-    ap.add_argument("--workload", choices=("train", "decode", "moe", "fused", "kv"), default="train",
+    ap.add_argument("--workload", choices=("train", "qwen", "decode", "moe", "fused", "kv"), default="train",
                     help="train: the M=8192 fwd+bwd step (the headline line); decode: the rollout "
-                         "forward at M=64 over the same four linears; moe: the grouped expert "
+                         "forward at M=64 over the same four linears; qwen: the train step over the six "
+                         "Qwen-14B/32B linears at M=16384; moe: the grouped expert "
                          "layer (Qwen3-30B-A3B shapes) fwd+bwd; fused: the fused RMSNorm/SwiGLU "
                          "producers of the 1x128 inputs of one Llama-8B layer; kv: the FP8 KV cache "
                          "(recalibration and append) of one Llama-8B layer")
@@ -72,6 +89,8 @@ def parse():
                     help="train, moe, decode: the power-of-two-scale variant (E8M0 scales applied by the MFMA)")
     ap.add_argument("--invariant", action="store_true",
                     help="decode: the batch-invariant forward (one K range, bit-identical to training)")
+    ap.add_argument("--no-mismatch", action="store_true",
+                    help="decode: skip the token-mult-prob-error against the training forward")
     ap.add_argument("--quant", choices=("both", "separate"), default="both",
                     help="activation quantizers: one read for both groupings (default), or the "
                          "separate 1x128 and 128x1 kernels")
@@ -337,6 +356,109 @@ def copy_probe(torch):
     del a, b
 
 
+PROBE_LIB = os.path.join(ROOT, "fp8_blockwise_quantized_amd", "lib", "libjetprobe.so")
+
+
+def measured_ceilings(torch):
+    """Ceilings measured on this GPU with the probes of include/jetprobe.h:
+    streaming TB/s for the quantizers' read:write byte mixes over a 1 GiB
+    source (past the 256 MB MALL; best of 5), the FP8 MFMA rate with
+    register-resident operands, pure and with the per-step FP32 fold (best
+    of 3), and the shader clock the MFMA probe ran at."""
+    import ctypes
+    if not os.path.exists(PROBE_LIB):
+        raise RuntimeError(f"{PROBE_LIB} is not built; run `python -m fp8_blockwise_quantized_amd._build`")
+    L = ctypes.CDLL(PROBE_LIB)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.jet_probe_stream.argtypes = [vp, vp, i64, i32, i32, i32, vp]
+    L.jet_probe_mfma.argtypes = [vp, vp, vp, i32, i32, i32, vp]
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    E = torch.cuda.Event
+    cus = int(L.jet_probe_cu_count()) or 256
+
+    def timed(fn, reps):
+        best = None
+        for _ in range(reps):
+            t0, t1 = E(enable_timing=True), E(enable_timing=True)
+            t0.record()
+            fn()
+            t1.record()
+            torch.cuda.synchronize()
+            ms = t0.elapsed_time(t1)
+            best = ms if best is None else min(best, ms)
+        return best
+
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(0x3C)
+    dst = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    out = {}
+    for name, lb, sb in (("copy_16r_16w", 16, 16), ("quant_16r_8w", 16, 8), ("swiglu_32r_8w", 32, 8),
+                         ("read_16r", 16, 0)):
+        units = (1 << 30) // lb
+
+        def run(lb=lb, sb=sb, units=units):
+            rc = L.jet_probe_stream(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), units,
+                                    lb, sb, 4 * cus, st)
+            if rc:
+                raise RuntimeError(f"jet_probe_stream failed ({rc})")
+        run()
+        ms = timed(run, 5)
+        out[f"hbm_{name}_gbs"] = round(units * (lb + sb) / (ms * 1e-3) / 1e9, 1)
+    del src, dst
+    ops = torch.randint(-100, 100, (1025,), dtype=torch.int32, device="cuda")
+    ops[1024] = 3
+    res = torch.empty(cus * 512, dtype=torch.float32, device="cuda")
+    clk = torch.zeros(2, dtype=torch.int64, device="cuda")
+    iters = 1000
+    for fold in (0, 1):
+        def run(fold=fold):
+            rc = L.jet_probe_mfma(ctypes.c_void_p(ops.data_ptr()), ctypes.c_void_p(res.data_ptr()),
+                                  ctypes.c_void_p(clk.data_ptr()), iters, fold, cus, st)
+            if rc:
+                raise RuntimeError(f"jet_probe_mfma failed ({rc})")
+        run()
+        ms = timed(run, 3)
+        flops = cus * 8 * iters * 32 * 2.0 * 16 * 16 * 128
+        key = "mfma_fp8_fold" if fold else "mfma_fp8"
+        out[f"{key}_tflops"] = round(flops / (ms * 1e-3) / 1e12, 1)
+        c = clk.cpu().numpy()
+        khz = int(L.jet_probe_wall_clock_khz())
+        if c[1] > 0 and khz > 0:
+            out[f"{key}_sclk_mhz"] = round(float(c[0]) / float(c[1]) * khz / 1e3, 0)
+    out["what"] = ("best of 5 (streams, 1 GiB source) / 3 (MFMA: the GEMMs' 8x4-fragment wave tile in "
+                   "registers, one 8-wavefront block per CU) probe launches, with the shader clock wavefront 0 "
+                   "saw; published peaks: 8000 GB/s HBM, 5000 TFLOP/s dense FP8 at 2.4 GHz")
+    return out
+
+
+def host_threads():
+    """(host CPU count, BLAS threads NumPy runs with).  A cpu_baseline's
+    `cores` is the threads its oracle run used: the BLAS threads where float64
+    GEMMs dominate, 1 for the element-wise oracles; the host's CPU count is
+    reported beside it."""
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas = 1
+    return os.cpu_count() or 1, int(blas)
+
+
+def step_distribution(torch, step, n):
+    """Per-step times (one event pair per step, no per-launch events) over n
+    steps: median, min and max in ms."""
+    E = torch.cuda.Event
+    evs = [(E(enable_timing=True), E(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for i in range(n):
+        evs[i][0].record()
+        step(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in evs)
+    return {"steps": n, "median_ms": round(t[n // 2] if n % 2 else 0.5 * (t[n // 2 - 1] + t[n // 2]), 4),
+            "min_ms": round(t[0], 4), "max_ms": round(t[-1], 4)}
+
+
 def cpu_baseline(pow2=False):
     """The oracle (untuned) on a bounded sample of the workload: the QKV
     linear (4096 -> 6144) with its full weight and all 8192 tokens (one of
@@ -346,11 +468,7 @@ def cpu_baseline(pow2=False):
     from oracle import pow2_scales as P
     from fp8_blockwise_quantized_amd import inputs
     rule = P.scale_pair_pow2 if pow2 else None
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
+    cores, blas = host_threads()
     Ms, N, K = M_TOKENS, 6144, 4096
     x = inputs.activations_with_outliers(Ms, K, seed=0)
     w = inputs.normal_bf16((N, K), 0.02, seed=0, tensor_id=inputs.ID_W)
@@ -367,11 +485,43 @@ def cpu_baseline(pow2=False):
     O.gemm_wgrad(dyqT, dysT, xqT, xsT, Ms)
     dt = time.perf_counter() - t0
     flops = 3 * 2.0 * Ms * N * K
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "seconds": round(dt, 3),
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": blas, "host_cpu_count": cores,
+            "kind": "oracle", "seconds": round(dt, 3),
             "sample": f"QKV linear 4096->6144, full weight, {Ms} of {M_TOKENS} tokens, all path steps "
-                      f"(weight/act quantizers, fwd+fused quant, dgrad, 128x1 quantizers, wgrad); "
-                      f"host cpu_count={os.cpu_count()}"}
+                      f"(weight/act quantizers, fwd+fused quant, dgrad, 128x1 quantizers, wgrad); NumPy "
+                      f"element-wise steps on one thread, float64 BLAS on {blas}"}
+
+
+QWEN_SAMPLE_TOKENS = 4096
+
+
+def cpu_baseline_qwen():
+    """The oracle (untuned) on a bounded sample of the Qwen workload: the QKV
+    linear (5120 -> 7168) with its full weight and 4096 of the 16384 tokens,
+    through every step of the path; TFLOP/s of the sample's GEMMs."""
+    from oracle import jet_oracle as O
+    from fp8_blockwise_quantized_amd import inputs
+    cores, blas = host_threads()
+    Ms, (_, N, K) = QWEN_SAMPLE_TOKENS, QWEN_LAYERS[0]
+    x = inputs.activations_with_outliers(Ms, K, seed=0)
+    w = inputs.normal_bf16((N, K), 0.02, seed=0, tensor_id=inputs.ID_W)
+    dy = inputs.normal_bf16((Ms, N), 1e-3, seed=0, tensor_id=inputs.ID_DY)
+    t0 = time.perf_counter()
+    wq, ws = O.quant_128x128(w)
+    xq, xs = O.quant_1x128(x)
+    y = O.bf16_rne(O.fl32(O.gemm_fwd(xq, xs, wq, ws)))
+    O.quant_1x128(y)
+    dyq, dys = O.quant_1x128(dy)
+    O.gemm_dgrad(dyq, dys, wq, ws)
+    dyqT, dysT = O.quant_128x1_T(dy)
+    xqT, xsT = O.requant_128x1_T_from_1x128(xq, xs)
+    O.gemm_wgrad(dyqT, dysT, xqT, xsT, Ms)
+    dt = time.perf_counter() - t0
+    flops = 3 * 2.0 * Ms * N * K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": blas, "host_cpu_count": cores,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"QKV linear 5120->7168, full weight, {Ms} of {QWEN_TOKENS} tokens, all path steps; "
+                      f"NumPy element-wise steps on one thread, float64 BLAS on {blas}"}
 
 
 MOE_SAMPLE_EXPERTS = 16
@@ -385,11 +535,7 @@ def cpu_baseline_moe():
     TFLOP/s of the sample's GEMMs."""
     from oracle import jet_oracle as O
     from fp8_blockwise_quantized_amd import inputs
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
+    cores, blas = host_threads()
     seg_all = moe_routing()
     E = MOE_SAMPLE_EXPERTS
     seg = seg_all[:E + 1].astype(np.int32)
@@ -413,12 +559,12 @@ def cpu_baseline_moe():
     O.gemm_grouped_wgrad(dyqT, dysT, xqT, xsT, seg)
     dt = time.perf_counter() - t0
     flops = 3 * 2.0 * M * N * K
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "seconds": round(dt, 3),
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": blas, "host_cpu_count": cores,
+            "kind": "oracle", "seconds": round(dt, 3),
             "sample": f"gate+up expert layer 2048->1536, the first {E} of {MOE_EXPERTS} experts "
                       f"({M} of {int(seg_all[-1])} routed rows), full expert weights, all path steps "
                       f"(weight/act quantizers, grouped fwd+fused quant, dgrad, grouped 128x1 "
-                      f"quantizers, wgrad); host cpu_count={os.cpu_count()}"}
+                      f"quantizers, wgrad); NumPy element-wise steps on one thread, float64 BLAS on {blas}"}
 
 
 def counters_for(kernel: str, path: str = COUNTERS):
@@ -436,10 +582,100 @@ def counters_for(kernel: str, path: str = COUNTERS):
 
 
 DECODE_M = 64
+DECODE_COUNTERS = os.path.join(ROOT, "profiles", "decode_counters.json")
+
+
+def decode_traffic(kernel, args):
+    """HBM bytes per call of the decode forward `kernel` (fwd_<layer>: the
+    weight-streaming kernel plus its finishing pass) from the committed
+    counter summary, or None (absent, another forward variant, or taken on a
+    different gemm.hip)."""
+    variant = "pow2" if args.pow2 else "batch_invariant" if args.invariant else "split_k"
+    return counters_for(f"{kernel}_{variant}", DECODE_COUNTERS)
 DECODE_COPIES = 4      # weight copies cycled per step: 4 x 218 MB exceeds the 256 MB MALL
 
 
-def decode_bench(args, torch, J):
+MISMATCH_VOCAB, MISMATCH_ROW0 = 32768, 1000
+
+
+def token_mult_prob_error(logits_train, logits_infer, ids):
+    """The multiplicative probability error of the NeMo-RL FP8 page (section
+    on numerical divergence): the mean over the scored tokens of
+    exp(|log p_train - log p_infer|), each log-probability the log-softmax of
+    its row's logits at the token's id (float64 on the host)."""
+    def logp(z):
+        zmax = z.max(axis=1, keepdims=True)
+        return z[np.arange(z.shape[0]), ids] - (zmax[:, 0] + np.log(np.exp(z - zmax).sum(axis=1)))
+    return float(np.mean(np.exp(np.abs(logp(logits_train) - logp(logits_infer)))))
+
+
+def decode_mismatch(torch, J, pow2=False):
+    """Train/rollout mismatch of the rollout forward that the decode line
+    times, on synthetic logits: the Llama-3.1-8B down projection (14336 ->
+    4096) computed for 64 rows inside a training batch of 8192 rows (the tiled
+    forward) and as a 64-row rollout batch (split-K, batch-invariant, and
+    power-of-two forwards); each BF16 output projected to logits by a fixed
+    BF16 output projection (vocabulary 32768, N(0, 0.02^2)) in float64 on the
+    host, the token of each row sampled from the rollout's logits (seeded
+    Gumbel-max)."""
+    from fp8_blockwise_quantized_amd import inputs
+    N, K = 4096, 14336
+    bf = lambda a: torch.from_numpy(a).to(torch.bfloat16).cuda()
+    x = bf(inputs.activations_with_outliers(M_TOKENS, K, seed=21))
+    w = bf(inputs.normal_bf16((N, K), 0.02, seed=21, tensor_id=inputs.ID_W))
+    head = inputs.normal_bf16((MISMATCH_VOCAB, N), 0.02, seed=22, tensor_id=inputs.ID_W).astype(np.float64)
+    rows = slice(MISMATCH_ROW0, MISMATCH_ROW0 + DECODE_M)
+    logits = lambda y: y.float().cpu().numpy().astype(np.float64) @ head.T
+    out = {}
+    variants = ((("pow2", J.jet_quant_act_1x128_pow2, J.jet_quant_weight_128x128_pow2, J.jet_fp8_linear_fwd_pow2),)
+                if pow2 else
+                (("split_k", J.jet_quant_act_1x128, J.jet_quant_weight_128x128, J.jet_fp8_linear_fwd),
+                 ("batch_invariant", J.jet_quant_act_1x128, J.jet_quant_weight_128x128,
+                  J.jet_fp8_linear_fwd_batch_invariant)))
+    for name, qa, qw, fwd in variants:
+        xq, xs = qa(x)
+        wq, ws, _ = qw(w, transposed=False)
+        train_fwd = J.jet_fp8_linear_fwd_pow2 if pow2 else J.jet_fp8_linear_fwd
+        y_train = train_fwd(xq, xs, wq, ws)
+        y_roll = fwd(xq[rows].contiguous(), xs[:, rows].contiguous(), wq, ws)
+        torch.cuda.synchronize()
+        lr = logits(y_roll)
+        ids = np.argmax(lr + np.random.default_rng(23).gumbel(size=lr.shape), axis=1)
+        out[name] = token_mult_prob_error(logits(y_train[rows]), lr, ids)
+    return {"token_mult_prob_error": out,
+            "what": "rollout (M=64) vs training-batch (M=8192) forward of the same rows, Llama-3.1-8B down "
+                    "projection, synthetic logits (BF16 output projection, vocabulary 32768); 1 = identical; "
+                    "the page quotes 1.03-1.05 as the usual range"}
+
+
+def cpu_baseline_decode():
+    """The oracle (untuned) on the decode workload itself: the four linears'
+    forward at M = 64 (1x128 quantization of X, the float64 GEMM from the
+    dequantized operands, BF16 output and its fused 1x128 quantization), from
+    codes made once; GB/s of weight bytes streamed, as the line's value."""
+    from oracle import jet_oracle as O
+    from fp8_blockwise_quantized_amd import inputs
+    cores, blas = host_threads()
+    qs = []
+    for (name, N, K) in LAYERS:
+        x = inputs.activations_with_outliers(DECODE_M, K, seed=0)
+        w = inputs.normal_bf16((N, K), 0.02, seed=0, tensor_id=inputs.ID_W)
+        qs.append((x, O.quant_128x128(w)))
+    t0 = time.perf_counter()
+    for x, (wq, ws) in qs:
+        xq, xs = O.quant_1x128(x)
+        y = O.bf16_rne(O.fl32(O.gemm_fwd(xq, xs, wq, ws)))
+        O.quant_1x128(y)
+    dt = time.perf_counter() - t0
+    wbytes = sum(N * K + N * K // 16384 * 4 for (_, N, K) in LAYERS)
+    return {"value": wbytes / dt / 1e9, "unit": "GB/s", "cores": blas, "host_cpu_count": cores,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"the whole decode step: the four linears' forward at M={DECODE_M} with the fused "
+                      f"1x128 output (weights quantized beforehand, untimed); NumPy element-wise steps on "
+                      f"one thread, float64 BLAS on {blas}"}
+
+
+def decode_bench(args, torch, J, ceilings=None):
     """Rollout decode: forward of the four linears at M=64, one weight copy per
     step (cycling DECODE_COPIES copies, so weights stream from HBM), with the
     fused 1x128 output.  value = weight bytes streamed / time."""
@@ -497,6 +733,7 @@ def decode_bench(args, torch, J):
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
+    dist = step_distribution(torch, step, max(args.steps, 50))
     per = [[[E(enable_timing=True), E(enable_timing=True)] for _ in LAYERS] for _ in range(args.steps)]
     if args.events:
         for s in range(args.steps):
@@ -522,11 +759,20 @@ def decode_bench(args, torch, J):
                    "forward": ("power-of-two scales (E8M0, applied by the MFMA), one K range" if args.pow2
                                else "batch-invariant (one K range)" if args.invariant else "split-K")},
         "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+        "step_distribution": dist,
         "roofline": None if dom is None else {
             "bound": "hbm", "kernel": dom, "achieved": kernels[dom]["weight_gbs"], "peak": PEAK_HBM_GBS,
-            "unit": "GB/s", "frac": round(kernels[dom]["weight_gbs"] / PEAK_HBM_GBS, 4), "traffic": None},
+            "unit": "GB/s", "frac": round(kernels[dom]["weight_gbs"] / PEAK_HBM_GBS, 4),
+            "traffic": decode_traffic(dom, args)},
         "kernels": kernels,
+        "measured_ceilings": ceilings,
     }
+    if not args.no_mismatch:
+        log("token-mult-prob-error of the rollout forward against the training forward")
+        out["mismatch"] = decode_mismatch(torch, J, pow2=args.pow2)
+    if not args.no_cpu_baseline:
+        log("timing the oracle on its bounded sample")
+        out["cpu_baseline"] = cpu_baseline_decode()
     print(json.dumps(out), flush=True)
 
 
@@ -548,10 +794,11 @@ def cpu_baseline_fused():
     F.swiglu_quant_1x128(gu, FUSED_I)
     dt = time.perf_counter() - t0
     nbytes = fused_bytes_rms(rows, FUSED_H) + fused_bytes_swiglu(rows, FUSED_I)
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "seconds": round(dt, 3),
+    cores, blas = host_threads()
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "host_cpu_count": cores,
+            "kind": "oracle", "seconds": round(dt, 3),
             "sample": f"{rows} rows: RMSNorm+1x128 at H={FUSED_H} and SwiGLU+1x128 at I={FUSED_I} "
-                      f"(element-wise NumPy, one thread); host cpu_count={os.cpu_count()}"}
+                      f"(element-wise NumPy, one thread)"}
 
 
 def fused_bytes_rms(M, H):      # x and gamma in; codes and scales out
@@ -562,7 +809,7 @@ def fused_bytes_swiglu(M, I):   # gate and up in; codes and scales out
     return M * 2 * I * 2 + M * I + M * I // 128 * 4
 
 
-def fused_bench(args, torch, J):
+def fused_bench(args, torch, J, ceilings=None):
     """Fused producers of one Llama-3.1-8B layer's linear inputs at M tokens:
     RMSNorm + 1x128 for the attention and MLP inputs (H=4096), SwiGLU + 1x128
     for the down projection's input (I=14336).  value = algorithmic bytes /
@@ -651,6 +898,7 @@ def fused_bench(args, torch, J):
             "unit": "GB/s", "frac": round(kernels[dom]["gbs"] / PEAK_HBM_GBS, 4), "traffic": None,
             "bytes_per_launch": kernels[dom]["bytes"] // kernels[dom]["launches_per_step"]},
         "kernels": kernels,
+        "measured_ceilings": ceilings,
         "unfused_context": {"ms_per_step": round(ms_unfused, 4),
                             "what": "torch BF16 rms_norm / silu*mul, then jet_quant_act_1x128",
                             "speedup_of_fused": round(ms_unfused / ms, 2)},
@@ -687,13 +935,14 @@ def cpu_baseline_kv():
     KV.kv_append(cache, v, np.arange(T), rv)
     dt = time.perf_counter() - t0
     nbytes = kv_bytes_calibrate(T, KV_D) + kv_bytes_append(T, KV_D)
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle", "seconds": round(dt, 3),
+    cores, blas = host_threads()
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "host_cpu_count": cores,
+            "kind": "oracle", "seconds": round(dt, 3),
             "sample": f"the whole prefill, {T} tokens (D={KV_D}): recalibration and append of K and V "
-                      f"(NumPy, one thread); "
-                      f"host cpu_count={os.cpu_count()}"}
+                      f"(NumPy, one thread)"}
 
 
-def kv_bench(args, torch, J):
+def kv_bench(args, torch, J, ceilings=None):
     """FP8 KV cache of one Llama-3.1-8B layer (8 KV heads x 128): after a
     weight update, recalibrate the K and V scales on a 8192-token prefill and
     append it; then append one 64-token decode step.  value = algorithmic
@@ -753,6 +1002,7 @@ def kv_bench(args, torch, J):
                      "unit": "GB/s", "frac": kernels[dom]["frac_hbm_peak"], "traffic": None,
                      "bytes_per_launch": kernels[dom]["bytes"]},
         "kernels": kernels,
+        "measured_ceilings": ceilings,
     }
     if not args.no_cpu_baseline:
         log("timing the oracle on its bounded sample")
@@ -772,25 +1022,32 @@ def main():
         sys.exit(1)
     from fp8_blockwise_quantized_amd import jetfp8 as J
 
+    ceilings = None
+    if not args.no_ceilings:
+        log("measuring the ceilings (streaming and MFMA probes)")
+        ceilings = measured_ceilings(torch)
+        torch.cuda.empty_cache()
     if args.workload == "decode":
-        decode_bench(args, torch, J)
+        decode_bench(args, torch, J, ceilings)
         return
     if args.workload == "fused":
-        fused_bench(args, torch, J)
+        fused_bench(args, torch, J, ceilings)
         return
     if args.workload == "kv":
-        kv_bench(args, torch, J)
+        kv_bench(args, torch, J, ceilings)
         return
     if args.copy_probe:
         copy_probe(torch)
     moe = args.workload == "moe"
+    qwen = args.workload == "qwen"
     log(f"building the {args.workload} inputs")
     if moe:
         seg = moe_routing()
         layers = [MoELayer(J, torch, n, N, K, seg, seed=0) for (n, N, K) in MOE_LAYERS]
         plan = [(l.name, kind, work, unit, fn) for l in layers for (kind, work, unit, fn) in l.ops(J, pow2=args.pow2)]
     else:
-        layers = [Layer(J, torch, n, N, K, M_TOKENS, seed=0) for (n, N, K) in LAYERS]
+        shapes, tokens = (QWEN_LAYERS, QWEN_TOKENS) if qwen else (LAYERS, M_TOKENS)
+        layers = [Layer(J, torch, n, N, K, tokens, seed=0) for (n, N, K) in shapes]
         plan = [(l.name, kind, work, unit, fn) for l in layers
                 for (kind, work, unit, fn) in l.ops(J, separate=args.quant == "separate", pow2=args.pow2)]
     torch.cuda.synchronize()
@@ -822,6 +1079,8 @@ def main():
     t_end.record()
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
+    log(f"{max(args.steps, 50)} more steps with one event pair per step (median step time)")
+    dist = step_distribution(torch, lambda i: step(), max(args.steps, 50))
     if args.events:
         log(f"{args.steps} steps with an event pair around every launch (per-kernel times)")
         for s in range(args.steps):
@@ -868,7 +1127,7 @@ def main():
         intensity = flops / nbytes
         common = {"kernel": dom,
                   "traffic": counters_for(dom + ("_pow2" if args.pow2 else ""),
-                                          MOE_COUNTERS if moe else COUNTERS),
+                                          MOE_COUNTERS if moe else QWEN_COUNTERS if qwen else COUNTERS),
                   "flops_per_launch": flops, "bytes_per_launch": nbytes,
                   "intensity_flop_per_byte": round(intensity, 1)}
         if intensity >= PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
@@ -892,6 +1151,15 @@ def main():
                   "largest_segment": int(np.diff(seg).max()), "smallest_segment": int(np.diff(seg).min()),
                   "scales": "power of two (E8M0, applied by the MFMA)" if args.pow2 else "FP32 amax/448",
                   "parallelism": "none (1 GPU)"}
+    elif qwen:
+        metric = "FP8 linear fwd+bwd TFLOP/s (% FP8 MFMA peak) + quantizer GB/s, Qwen-14B/32B shapes"
+        config = {"workload": "Qwen-14B/32B-shaped linears (hidden 5120: QKV 5120->7168, O 5120->5120, "
+                              "gate+up 5120->34816 and 5120->55296, down 17408->5120 and 27648->5120), "
+                              f"training batch M={QWEN_TOKENS} tokens, fwd + dgrad + wgrad with every "
+                              "quantizer and the BF16-master weight re-quantization per step",
+                  "M": QWEN_TOKENS, "activation_quantizers": args.quant,
+                  "scales": "power of two (E8M0, applied by the MFMA)" if args.pow2 else "FP32 amax/448",
+                  "parallelism": "none (1 GPU)"}
     else:
         metric = METRIC
         config = {"workload": "Llama-3.1-8B decoder linears (QKV 4096->6144, O 4096->4096, "
@@ -908,9 +1176,11 @@ def main():
         "data": "synthetic",
         "config": config,
         "frac_fp8_peak_step": round(value / PEAK_FP8_TFLOPS, 4),
+        "step_distribution": dist,
         "quantizer_gbs_step": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1) if quant_ms else None,
         "roofline": roofline,
         "kernels": kernels,
+        "measured_ceilings": ceilings,
     }
     if not moe and not args.no_bf16_context:
         log("timing hipBLASLt BF16 GEMMs on the same shapes (context)")
@@ -918,7 +1188,8 @@ def main():
         out["bf16_context"] = bf16_context(torch, layers, ms_step, gemm_ms)
     if not args.no_cpu_baseline:
         log("timing the oracle on its bounded sample")
-        out["cpu_baseline"] = cpu_baseline_moe() if moe else cpu_baseline(pow2=args.pow2)
+        out["cpu_baseline"] = (cpu_baseline_moe() if moe else cpu_baseline_qwen() if qwen
+                               else cpu_baseline(pow2=args.pow2))
     print(json.dumps(out), flush=True)
 
 

@@ -16,6 +16,9 @@ CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libjetfp8.so")
 SOURCES = ["abi.hip", "quant.hip", "fused.hip", "kvcache.hip", "gemm.hip"]
+# Roofline probes used by the benchmark only (include/jetprobe.h): a library of their own.
+PROBE_LIB = os.path.join(LIBDIR, "libjetprobe.so")
+PROBE_SOURCES = ["probes.hip"]
 ARCH = "gfx950"
 
 # No fast-math: the quantizers need IEEE division and FP32 denormals.
@@ -40,8 +43,9 @@ def hipcc() -> str:
 def build(verbose: bool = False) -> str:
     os.makedirs(LIBDIR, exist_ok=True)
     # never leave a library built from older sources behind a failed build
-    if os.path.exists(LIB):
-        os.remove(LIB)
+    for lib in (LIB, PROBE_LIB):
+        if os.path.exists(lib):
+            os.remove(lib)
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
     cc = hipcc()
@@ -56,14 +60,15 @@ def build(verbose: bool = False) -> str:
             raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
         return obj
 
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    with ThreadPoolExecutor(max_workers=len(SOURCES) + len(PROBE_SOURCES)) as ex:
+        objs = list(ex.map(compile_one, SOURCES + PROBE_SOURCES))
+    for lib, lib_objs in ((LIB, objs[:len(SOURCES)]), (PROBE_LIB, objs[len(SOURCES):])):
+        tmp = lib + ".tmp"
+        cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *lib_objs]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+        os.replace(tmp, lib)
     return LIB
 
 

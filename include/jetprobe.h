@@ -1,0 +1,46 @@
+/*
+ * jetprobe.h -- roofline probes for gfx950 (libjetprobe.so).  Not part of the
+ * FP8 linear layer's ABI (jetfp8.h): these kernels measure the ceilings the
+ * layer's kernels are compared with -- streaming bandwidth for the
+ * quantizers' read/write mixes, the FP8 MFMA rate with and without the
+ * per-step FP32 fold of the GEMMs, and the shader clock under that load.
+ * All pointers are device pointers owned by the caller; every call only
+ * enqueues on `stream` (a hipStream_t) and returns 0, or non-zero for a bad
+ * argument (nothing launched) or a failed launch.
+ */
+#ifndef JETPROBE_H
+#define JETPROBE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* `units` units, each reading load_bytes (16 or 32) from `in` (16-byte
+ * aligned, units*load_bytes bytes) and writing store_bytes (16, 8, or 0 for a
+ * read-only pass) to `out` (units*store_bytes bytes); grid of `blocks`
+ * workgroups of 256 threads, non-temporal accesses. */
+int jet_probe_stream(const void* in, void* out, int64_t units, int load_bytes, int store_bytes, int blocks,
+                     void* stream);
+
+/* `blocks` workgroups of 8 wavefronts (one per CU: each holds 96 KB of LDS),
+ * each wavefront issuing iters x 32 v_mfma_scale_f32_16x16x128_f8f6f4 on
+ * register operands (8 A x 4 B fragments; 2*16*16*128 FLOP each).  fold != 0: each MFMA starts
+ * from zero and its result is folded into an FP32 accumulator with one FMA
+ * per element.  in: int32[1025] (operand bytes, then one word for the fold
+ * factor); out: float[blocks*512]; clocks: int64[2] receives the core cycles
+ * and wall-counter ticks wavefront 0 of block 0 spent in its loop. */
+int jet_probe_mfma(const int* in, float* out, long long* clocks, int iters, int fold, int blocks, void* stream);
+
+/* Rate of the wall counter read by jet_probe_mfma, kHz (0 on failure). */
+int jet_probe_wall_clock_khz(void);
+
+/* Compute units of the current device (0 on failure). */
+int jet_probe_cu_count(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

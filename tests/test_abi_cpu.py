@@ -43,6 +43,17 @@ def test_library_exports_every_declared_symbol(J):
     assert set(declared_functions()) <= exported
 
 
+def test_probe_library_exports_its_header():
+    """The roofline probes (include/jetprobe.h) are a library of their own,
+    loaded only by the benchmark."""
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "jetprobe.h")).read(), flags=re.S)
+    names = set(re.findall(r"\b(jet_probe_\w+)\s*\(", text))
+    assert {"jet_probe_stream", "jet_probe_mfma", "jet_probe_wall_clock_khz", "jet_probe_cu_count"} <= names
+    lib = os.path.join(ROOT, "fp8_blockwise_quantized_amd", "lib", "libjetprobe.so")
+    out = subprocess.run(["nm", "-D", "--defined-only", lib], capture_output=True, text=True).stdout
+    assert names <= set(re.findall(r"\bT (jet_probe_\w+)", out))
+
+
 def test_binding_covers_header(J):
     assert set(J.SIGNATURES) == set(declared_functions())
 
