@@ -354,9 +354,9 @@ int jet_fp8_linear_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, co
 // Device scratch of jet_fp8_linear_fwd_noalloc: the split-K partial sums of
 // the small-M forward live here instead of in a caller's workspace.  Every
 // GPU the library runs on holds its own copy of the array until the process
-// ends.  16 MiB covers every split the forward chooses (at most
-// S * M * N * 4 bytes with M <= 128 and S * N <= 128 * (N/128 + 128): below
-// 16.7 million bytes); the guard below still rejects a larger need.
+// ends.  16 MiB covers every split the forward chooses (S * M * N * 4 bytes
+// with M <= 128 and S ranges of N/128 column blocks, S * N/128 <= 256: at most
+// exactly 16 MiB); the guard below still rejects a larger need.
 namespace {
 
 constexpr size_t kScratchBytes = size_t(16) << 20;

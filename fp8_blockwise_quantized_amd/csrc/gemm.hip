@@ -199,21 +199,44 @@ __device__ __forceinline__ v4f mfma_fp8_e8m0(const v8i& a, const v8i& b, const v
 // E8M0 byte of a positive power-of-two FP32 scale: its biased exponent field.
 __device__ __forceinline__ int e8m0_of(float s) { return (int)(__float_as_uint(s) >> 23); }
 
-// Block index -> output tile.  Workgroups are dealt round-robin to the 8 XCDs;
-// renumber so each XCD receives a contiguous range of tiles (shared operand
-// panels stay in that XCD's L2), then walk tiles in groups of kGroupM tile-rows.
+// Block index -> output tile.  Workgroups are dealt round-robin to the 8 XCDs
+// (block b to XCD b % 8), each with its own L2.  When the tile grid splits
+// evenly, each XCD takes one block of a gy x gx split of it, the split that
+// minimises the operand panels the XCDs fetch (gx copies of A's rows, gy
+// copies of B's columns); a split into row blocks only (gy = 8), or no even
+// split, gives each XCD a contiguous range of the grid's walk instead.
+// Either way an XCD walks its part in groups of kGroupM tile-rows.
 __device__ __forceinline__ void tile_of_block(int nbm, int nbn, int& tm, int& tn) {
   constexpr int kXcds = 8, kGroupM = 4;
   const int total = nbm * nbn;
   int b = blockIdx.x;
-  if (total % kXcds == 0) b = (b % kXcds) * (total / kXcds) + b / kXcds;
-  const int per_group = kGroupM * nbn;
+  int gy = 0, gx = 0, cost = 0x7fffffff;
+  if (total % kXcds == 0) {
+#pragma unroll
+    for (int y = 1; y <= kXcds; y *= 2) {
+      const int x = kXcds / y;
+      const int c = x * nbm + y * nbn;
+      if (nbm % y == 0 && nbn % x == 0 && c < cost) { cost = c; gy = y; gx = x; }
+    }
+  }
+  int rows = nbm, cols = nbn, r0 = 0, c0 = 0;
+  if (gy > 0 && gy < kXcds) {
+    const int xcd = b % kXcds;
+    b /= kXcds;
+    rows = nbm / gy;
+    cols = nbn / gx;
+    r0 = (xcd / gx) * rows;
+    c0 = (xcd % gx) * cols;
+  } else if (total % kXcds == 0) {
+    b = (b % kXcds) * (total / kXcds) + b / kXcds;
+  }
+  const int per_group = kGroupM * cols;
   const int group = b / per_group;
   const int first_m = group * kGroupM;
-  const int gsz = min(nbm - first_m, kGroupM);
+  const int gsz = min(rows - first_m, kGroupM);
   const int in_group = b - group * per_group;
-  tm = first_m + in_group % gsz;
-  tn = in_group / gsz;
+  tm = r0 + first_m + in_group % gsz;
+  tn = c0 + in_group / gsz;
 }
 
 }  // namespace
@@ -976,20 +999,23 @@ __global__ __launch_bounds__(256) void k_skinny_finish(GemmArgs p, const float* 
   if (ok) *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.C) + (int64_t)m * p.ldc + n) = w;
 }
 
-// Small-M configuration (measured on the Llama-8B decode shapes: 4, 6 or 8
-// stages and 128..1024 target workgroups all land within 10 %; this one needs
-// the fewest ranges, so the least workspace).
+// Small-M configuration.  One workgroup of this kernel streams its weight
+// columns at about 35 GB/s (measured with weights cycled past the 256 MB
+// MALL), so HBM bandwidth needs every CU streaming: the K steps are split
+// into as many ranges as fit one wave of at most kSkFill workgroups (a
+// second, partial wave of workgroups measured slower: Llama-8B decode
+// QKV 6 ranges / 288 workgroups 19.1 us against 5 / 240 at 13.9 us).
 constexpr int kSkWS = 2;        // W slabs per wavefront: 128 output columns per workgroup
 constexpr int kSkNST = 6;       // ring stages for M <= 64 (4 for M <= 128)
-constexpr int kSkTarget = 128;  // workgroups aimed at over all column blocks and K ranges
+constexpr int kSkFill = 256;    // workgroups of one wave on MI355X (one per CU: the ring fills LDS)
 constexpr int kSkRowSplitBlocks = 64;   // one K range below this many column blocks: 16-row groups
 
-// K-step ranges of the small-M forward: about kSkTarget workgroups in total,
-// at least one K step per range, at most 16 ranges.
+// K-step ranges of the small-M forward: floor(kSkFill / column blocks), at
+// least one K step per range, at most 16 ranges.
 int skinny_splits(int64_t M, int64_t N, int64_t K) {
   (void)M;
   const int64_t blocks = N / (64 * kSkWS), kb = K / 128;
-  int64_t s = (kSkTarget + blocks - 1) / blocks;
+  int64_t s = blocks > 0 ? kSkFill / blocks : 1;
   if (s > 16) s = 16;
   if (s > kb) s = kb;
   return (int)(s < 1 ? 1 : s);

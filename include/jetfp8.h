@@ -294,7 +294,7 @@ int jet_fp8_linear_fwd_batch_invariant(const uint8_t* xq, const float* xs,
  * Arguments, layouts, results (bit for bit) and errors as jet_fp8_linear_fwd
  * without the workspace; JET_ERR_WORKSPACE if jet_workspace_bytes(JET_OP_FWD,
  * M, N, K) exceeds the array (no shape the forward accepts needs more than
- * 16,646,144 bytes today).  The first call on a device looks up that
+ * its 16,777,216 bytes).  The first call on a device looks up that
  * device's copy of the array (hipGetSymbolAddress); JET_ERR_HIP if that
  * fails.  All calls on one GPU share its array and nothing in it needs to
  * start at zero (every partial sum is written before it is read), but calls

@@ -210,8 +210,10 @@ def test_gemm_validation(J):
                                 None) == J.JET_ERR_ALIGN
     # small M (rollout decode) keeps split-K partial sums in the caller's workspace
     need = J.jet_workspace_bytes(J.JET_OP_FWD, 64, 4096, 4096)
-    assert need == 4 * 64 * 4096 * 4                    # 4 K ranges: 128 workgroups over 32 column blocks
+    assert need == 8 * 64 * 4096 * 4                    # 8 K ranges: 256 workgroups over 32 column blocks
     assert J.jet_workspace_bytes(J.JET_OP_FWD, 64, 28672, 4096) == 0   # 224 column blocks: no split
+    assert J.jet_workspace_bytes(J.JET_OP_FWD, 64, 6144, 4096) == 5 * 64 * 6144 * 4   # 5 ranges of 48 blocks
+    assert J.jet_workspace_bytes(J.JET_OP_FWD, 128, 4096, 4096) == 16 << 20   # the largest need
     assert J.jet_workspace_bytes(J.JET_OP_FWD, 128, 4096, 256) == 2 * 128 * 4096 * 4   # one range per K step
     assert J.jet_workspace_bytes(J.JET_OP_FWD, 1, 128, 4096) == 16 * 512   # at most 16 ranges
     assert L.jet_fp8_linear_fwd(*a, 64, 4096, 4096, P16, J.JET_BF16, None, None, P17, need,
