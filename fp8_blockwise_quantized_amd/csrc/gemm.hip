@@ -1006,7 +1006,13 @@ __global__ __launch_bounds__(256) void k_skinny_finish(GemmArgs p, const float* 
 // second, partial wave of workgroups measured slower: Llama-8B decode
 // QKV 6 ranges / 288 workgroups 19.1 us against 5 / 240 at 13.9 us).
 constexpr int kSkWS = 2;        // W slabs per wavefront: 128 output columns per workgroup
-constexpr int kSkNST = 6;       // ring stages for M <= 64 (4 for M <= 128)
+constexpr int kSkNST = 6;       // ring stages of the 16-row groups (one K range, few column blocks)
+// Ring stages of the 64-row workgroups (M <= 64; 4 for M <= 128): with every
+// CU streaming, three stages (two in flight, 48 KB of weights per CU) are
+// enough and deeper rings only lengthen the memory queues (Llama-8B decode
+// step, weights cycled past the MALL: 2 / 3 / 4 / 6 stages 84.5 / 72.1 /
+// 73.5 / 80.8 us).
+constexpr int kSkNST64 = 3;
 constexpr int kSkFill = 256;    // workgroups of one wave on MI355X (one per CU: the ring fills LDS)
 constexpr int kSkRowSplitBlocks = 64;   // one K range below this many column blocks: 16-row groups
 
@@ -1067,7 +1073,7 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, int out, bool fuseq, void* work
   const bool rows16 = a.N / (64 * kSkWS) < kSkRowSplitBlocks;
   if (p2) {   // one K range: the chain of k_gemm_fp8<..., P2> (no workspace)
     if (rows16) return launch_skinny_out<1, kSkNST, true>(a, out, fuseq, nullptr, 1, st);
-    if (a.M <= 64) return launch_skinny_out<4, kSkNST, true>(a, out, fuseq, nullptr, 1, st);
+    if (a.M <= 64) return launch_skinny_out<4, kSkNST64, true>(a, out, fuseq, nullptr, 1, st);
     return launch_skinny_out<8, 4, true>(a, out, fuseq, nullptr, 1, st);
   }
   // unsplit: every output element is the same chain of per-step FMAs, in K
@@ -1076,7 +1082,7 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, int out, bool fuseq, void* work
   if (S > 1 && workspace == nullptr) return hipErrorInvalidValue;
   float* part = static_cast<float*>(workspace);
   if (S == 1 && rows16) return launch_skinny_out<1, kSkNST>(a, out, fuseq, part, 1, st);
-  if (a.M <= 64) return launch_skinny_out<4, kSkNST>(a, out, fuseq, part, S, st);
+  if (a.M <= 64) return launch_skinny_out<4, kSkNST64>(a, out, fuseq, part, S, st);
   return launch_skinny_out<8, 4>(a, out, fuseq, part, S, st);
 }
 
