@@ -51,10 +51,12 @@ M_TOKENS = 8192
 QWEN_LAYERS = [("qkv", 7168, 5120), ("o", 5120, 5120), ("gate_up_14b", 34816, 5120),
                ("gate_up_32b", 55296, 5120), ("down_14b", 5120, 17408), ("down_32b", 5120, 27648)]
 QWEN_TOKENS = 16384
-COUNTERS = os.path.join(ROOT, "profiles", "gemm_counters.json")
-MOE_COUNTERS = os.path.join(ROOT, "profiles", "moe_counters.json")
-QWEN_COUNTERS = os.path.join(ROOT, "profiles", "qwen_counters.json")
-GEMM_SRC = os.path.join(ROOT, "fp8_blockwise_quantized_amd", "csrc", "gemm.hip")
+CSRC = os.path.join(ROOT, "fp8_blockwise_quantized_amd", "csrc")
+
+
+def counters_path(workload: str) -> str:
+    """The committed HBM counter summary of a workload (profile_summary.py hbm)."""
+    return os.path.join(ROOT, "profiles", f"counters_{workload}.json")
 
 
 def log(msg):
@@ -66,6 +68,9 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--median-steps", type=int, default=50,
+                    help="steps of the per-step distribution pass (at least --steps; 0 skips it, "
+                         "so a profiled run covers exactly the warm-up and timed steps)")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the measured ceilings (streaming and MFMA probes)")
@@ -345,6 +350,64 @@ def bf16_context(torch, layers, ms_step, fp8_gemm_ms, steps=10, warmup=3):
                      "(end-to-end, other hardware)"}
 
 
+def fp8_library_context(torch, layers, fp8_gemm_ms, steps=10, warmup=3):
+    """Context, not the product: the same twelve GEMMs as plain FP8 products
+    through torch._scaled_mm (hipBLASLt), E4M3 operands with one scale per
+    tensor (no per-block scaling, so no per-step fold), BF16 outputs, every
+    operand in the layout the library wants (transposes made before timing).
+    It shows what the vendor's FP8 GEMM reaches on these shapes on this GPU
+    without block scales."""
+    f8 = torch.float8_e4m3fn
+    one = torch.ones((), dtype=torch.float32, device="cuda")
+    ops, per = [], []
+    try:
+        for l in layers:
+            x8 = l.x.to(f8)
+            w8 = l.w.to(f8)
+            dy8 = l.dy.mul(1000.0).to(f8)
+            wT8 = w8.t().contiguous()
+            dyT8 = dy8.t().contiguous()
+            xT8 = x8.t().contiguous()
+            trip = [(lambda a=x8, b=w8: torch._scaled_mm(a, b.t(), one, one, out_dtype=torch.bfloat16)),
+                    (lambda a=dy8, b=wT8: torch._scaled_mm(a, b.t(), one, one, out_dtype=torch.bfloat16)),
+                    (lambda a=dyT8, b=xT8: torch._scaled_mm(a, b.t(), one, one, out_dtype=torch.bfloat16))]
+            ops += trip
+            per.append((l.name, trip, l.flops))
+        for _ in range(warmup):
+            for f in ops:
+                f()
+        torch.cuda.synchronize()
+    except Exception as e:   # a torch build without FP8 GEMMs for this GPU
+        return {"kind": "third-party: hipBLASLt FP8 via torch._scaled_mm", "error": str(e)[:200]}
+    E = torch.cuda.Event
+    t0, t1 = E(enable_timing=True), E(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        for f in ops:
+            f()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    layer_tflops = {}
+    for name, trip, fl in per:
+        a, b = E(enable_timing=True), E(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            for f in trip:
+                f()
+        b.record()
+        torch.cuda.synchronize()
+        layer_tflops[name] = round(3 * fl * steps / (a.elapsed_time(b) * 1e-3) / 1e12, 1)
+    flops = sum(3 * l.flops for l in layers)
+    del ops, per
+    torch.cuda.empty_cache()
+    return {"kind": "third-party: hipBLASLt FP8 GEMMs via torch._scaled_mm on the same shapes (fwd, dgrad, "
+                    "wgrad per linear; E4M3 operands with one scale per tensor, no block scaling; BF16 out)",
+            "ms_per_step": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "tflops_per_layer": layer_tflops,
+            "block_scaled_gemm_ratio": round(ms / fp8_gemm_ms, 3) if fp8_gemm_ms else None}
+
+
 def copy_probe(torch):
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -567,31 +630,37 @@ def cpu_baseline_moe():
                       f"quantizers, wgrad); NumPy element-wise steps on one thread, float64 BLAS on {blas}"}
 
 
-def counters_for(kernel: str, path: str = COUNTERS):
-    """HBM traffic per launch of `kernel` from the committed rocprofv3 counter
-    summary, or None if absent or taken on a different gemm.hip."""
+def counters_for(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the workload's committed
+    rocprofv3 FETCH_SIZE/WRITE_SIZE summary, or None if absent or taken on
+    other kernel sources than the ones built now."""
     try:
-        c = json.load(open(path))
+        c = json.load(open(counters_path(workload)))
     except (OSError, ValueError):
         return None
-    sha = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
-    if c.get("gemm_source_sha256") != sha:
+    shas = c.get("sources_sha256") or {}
+    if not shas:
         return None
+    for f, h in shas.items():
+        try:
+            if hashlib.sha256(open(os.path.join(CSRC, f), "rb").read()).hexdigest() != h:
+                return None
+        except OSError:
+            return None
     k = c.get("kernels", {}).get(kernel)
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
 DECODE_M = 64
-DECODE_COUNTERS = os.path.join(ROOT, "profiles", "decode_counters.json")
 
 
 def decode_traffic(kernel, args):
     """HBM bytes per call of the decode forward `kernel` (fwd_<layer>: the
     weight-streaming kernel plus its finishing pass) from the committed
-    counter summary, or None (absent, another forward variant, or taken on a
-    different gemm.hip)."""
-    variant = "pow2" if args.pow2 else "batch_invariant" if args.invariant else "split_k"
-    return counters_for(f"{kernel}_{variant}", DECODE_COUNTERS)
+    counter summary of the same forward variant, or None."""
+    variant, wl = (("pow2", "decode_pow2") if args.pow2 else ("batch_invariant", "decode_invariant")
+                   if args.invariant else ("split_k", "decode"))
+    return counters_for(f"{kernel}_{variant}", wl)
 DECODE_COPIES = 4      # weight copies cycled per step: 4 x 218 MB exceeds the 256 MB MALL
 
 
@@ -733,7 +802,7 @@ def decode_bench(args, torch, J, ceilings=None):
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
-    dist = step_distribution(torch, step, max(args.steps, 50))
+    dist = step_distribution(torch, step, max(args.steps, args.median_steps)) if args.median_steps else None
     per = [[[E(enable_timing=True), E(enable_timing=True)] for _ in LAYERS] for _ in range(args.steps)]
     if args.events:
         for s in range(args.steps):
@@ -895,7 +964,8 @@ def fused_bench(args, torch, J, ceilings=None):
                    "parallelism": "none (1 GPU)"},
         "roofline": None if dom is None else {
             "bound": "hbm", "kernel": dom, "achieved": kernels[dom]["gbs"], "peak": PEAK_HBM_GBS,
-            "unit": "GB/s", "frac": round(kernels[dom]["gbs"] / PEAK_HBM_GBS, 4), "traffic": None,
+            "unit": "GB/s", "frac": round(kernels[dom]["gbs"] / PEAK_HBM_GBS, 4),
+            "traffic": counters_for(dom, "fused"),
             "bytes_per_launch": kernels[dom]["bytes"] // kernels[dom]["launches_per_step"]},
         "kernels": kernels,
         "measured_ceilings": ceilings,
@@ -999,8 +1069,8 @@ def kv_bench(args, torch, J, ceilings=None):
                                f"then a {KV_DECODE}-token decode append", "T": KV_T,
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["gbs"], "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": kernels[dom]["frac_hbm_peak"], "traffic": None,
-                     "bytes_per_launch": kernels[dom]["bytes"]},
+                     "unit": "GB/s", "frac": kernels[dom]["frac_hbm_peak"],
+                     "traffic": counters_for(dom, "kv"), "bytes_per_launch": kernels[dom]["bytes"]},
         "kernels": kernels,
         "measured_ceilings": ceilings,
     }
@@ -1026,6 +1096,8 @@ def main():
     if not args.no_ceilings:
         log("measuring the ceilings (streaming and MFMA probes)")
         ceilings = measured_ceilings(torch)
+    if args.copy_probe:
+        copy_probe(torch)
         torch.cuda.empty_cache()
     if args.workload == "decode":
         decode_bench(args, torch, J, ceilings)
@@ -1036,8 +1108,6 @@ def main():
     if args.workload == "kv":
         kv_bench(args, torch, J, ceilings)
         return
-    if args.copy_probe:
-        copy_probe(torch)
     moe = args.workload == "moe"
     qwen = args.workload == "qwen"
     log(f"building the {args.workload} inputs")
@@ -1080,7 +1150,8 @@ def main():
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
     log(f"{max(args.steps, 50)} more steps with one event pair per step (median step time)")
-    dist = step_distribution(torch, lambda i: step(), max(args.steps, 50))
+    dist = (step_distribution(torch, lambda i: step(), max(args.steps, args.median_steps))
+            if args.median_steps else None)
     if args.events:
         log(f"{args.steps} steps with an event pair around every launch (per-kernel times)")
         for s in range(args.steps):
@@ -1126,8 +1197,8 @@ def main():
         nbytes = sum(l.gemm_bytes(dom) for l in layers) / len(layers)
         intensity = flops / nbytes
         common = {"kernel": dom,
-                  "traffic": counters_for(dom + ("_pow2" if args.pow2 else ""),
-                                          MOE_COUNTERS if moe else QWEN_COUNTERS if qwen else COUNTERS),
+                  "traffic": counters_for(dom + ("_pow2" if args.pow2 and not (moe or qwen) else ""),
+                                          "moe" if moe else "qwen" if qwen else "pow2" if args.pow2 else "train"),
                   "flops_per_launch": flops, "bytes_per_launch": nbytes,
                   "intensity_flop_per_byte": round(intensity, 1)}
         if intensity >= PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
@@ -1186,6 +1257,8 @@ def main():
         log("timing hipBLASLt BF16 GEMMs on the same shapes (context)")
         gemm_ms = sum(agg[k]["ms"] for k in gemm_kinds) / args.steps if args.events else None
         out["bf16_context"] = bf16_context(torch, layers, ms_step, gemm_ms)
+        log("timing hipBLASLt FP8 (tensor-wise scales) GEMMs on the same shapes (context)")
+        out["fp8_library_context"] = fp8_library_context(torch, layers, gemm_ms)
     if not args.no_cpu_baseline:
         log("timing the oracle on its bounded sample")
         out["cpu_baseline"] = (cpu_baseline_moe() if moe else cpu_baseline_qwen() if qwen
