@@ -722,7 +722,7 @@ struct SkinnyCfg {
   static constexpr int LDS = NST * STAGE;
   static constexpr int TP = BN + 4;                    // FP32 output tile pitch (floats)
   static_assert(NSX >= 1 && NSX < 4, "scale slots");
-  static_assert(BN == 128, "one 1x128 output group and one weight block scale per workgroup");
+  static_assert(BN == 128 || BN == 64, "one weight block scale per workgroup");
   static_assert(MT * 16 * TP * 4 <= LDS, "output tile fits the stage ring");
   static_assert(LDS <= 160 * 1024, "LDS");
 };
@@ -731,6 +731,7 @@ template <int MT, int NST, int WS, int OUT, bool FUSEQ, bool P2 = false>
 __global__ __launch_bounds__(256) void k_gemm_fp8_skinny(GemmArgs p, float* __restrict__ part,
                                                          int splits) {
   using C = SkinnyCfg<MT, NST, WS>;
+  static_assert(C::BN == 128 || !FUSEQ, "the fused 1x128 output needs whole 128-column groups");
   __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -905,10 +906,11 @@ __global__ __launch_bounds__(256) void k_gemm_fp8_skinny(GemmArgs p, float* __re
 
   // ---- outputs: 16 rows per pass, a DPP row of 16 lanes per row (8 columns
   // per lane, one 1x128 group per row) ----
-  const int c = tid & 15;
+  constexpr int LPR = C::BN / 8;                    // lanes per output row (8 columns each)
+  const int c = tid % LPR;
   const int n = n0 + 8 * c;
-  for (int m0r = 0; m0r < p.M; m0r += 16) {
-    const int m = m0r + (tid >> 4);
+  for (int m0r = 0; m0r < p.M; m0r += 256 / LPR) {
+    const int m = m0r + tid / LPR;
     const bool ok = m < p.M;
     const float* src = T + (ok ? m : p.M - 1) * C::TP + 8 * c;
     const float4 a = *reinterpret_cast<const float4*>(src);
@@ -1015,6 +1017,7 @@ constexpr int kSkNST = 6;       // ring stages of the 16-row groups (one K range
 constexpr int kSkNST64 = 3;
 constexpr int kSkFill = 256;    // workgroups of one wave on MI355X (one per CU: the ring fills LDS)
 constexpr int kSkRowSplitBlocks = 64;   // one K range below this many column blocks: 16-row groups
+constexpr int kSkLongK = 64;            // ... of 64 columns from this many K steps on
 
 // K-step ranges of the small-M forward: floor(kSkFill / column blocks), at
 // least one K step per range, at most 16 ranges.
@@ -1050,6 +1053,27 @@ static hipError_t launch_skinny_mt(const GemmArgs& a, float* part, int S, hipStr
   return hipGetLastError();
 }
 
+// One K range, 16-row groups, 64-column blocks: twice the workgroups of
+// 128-column blocks, each streaming half the weight column, for long
+// contractions (at least kSkLongK K steps), where the stream dominates.  A
+// fused 1x128 output then comes from the 1x128 quantizer run on the BF16 Y,
+// which is the fused epilogue's definition, so the bits are the same.
+// (Llama-8B decode, one K range, down projection 14336 -> 4096: 42.6 ->
+// 35.8 us; for QKV and O, 32 K steps, the extra launch costs more: 15.1 ->
+// 18.8 us.)
+template <bool P2>
+static hipError_t launch_skinny_rows16_64(const GemmArgs& a, int out, bool fuseq, hipStream_t st) {
+  const dim3 g((unsigned)(a.N / 64), 1u, (unsigned)((a.M + 15) / 16));
+  if (out == kOutF32) {
+    hipLaunchKernelGGL((k_gemm_fp8_skinny<1, kSkNST, 1, kOutF32, false, P2>), g, dim3(256), 0, st, a, nullptr, 1);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((k_gemm_fp8_skinny<1, kSkNST, 1, kOutBf16, false, P2>), g, dim3(256), 0, st, a, nullptr, 1);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !fuseq) return e;
+  return launch_quant_1x128(static_cast<const uint16_t*>(a.C), a.M, a.N, a.ldc, a.Cq, a.ldc, a.Cs, st, P2);
+}
+
 template <int MT, int NST, bool P2 = false>
 static hipError_t launch_skinny_out(const GemmArgs& a, int out, bool fuseq, float* part, int S,
                                     hipStream_t st) {
@@ -1072,6 +1096,7 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, int out, bool fuseq, void* work
   // are those of the 64-row workgroup, so its outputs are the same bits.
   const bool rows16 = a.N / (64 * kSkWS) < kSkRowSplitBlocks;
   if (p2) {   // one K range: the chain of k_gemm_fp8<..., P2> (no workspace)
+    if (rows16 && a.Kc / 128 >= kSkLongK) return launch_skinny_rows16_64<true>(a, out, fuseq, st);
     if (rows16) return launch_skinny_out<1, kSkNST, true>(a, out, fuseq, nullptr, 1, st);
     if (a.M <= 64) return launch_skinny_out<4, kSkNST64, true>(a, out, fuseq, nullptr, 1, st);
     return launch_skinny_out<8, 4, true>(a, out, fuseq, nullptr, 1, st);
@@ -1081,6 +1106,7 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, int out, bool fuseq, void* work
   const int S = unsplit ? 1 : skinny_splits(a.M, a.N, a.Kc);
   if (S > 1 && workspace == nullptr) return hipErrorInvalidValue;
   float* part = static_cast<float*>(workspace);
+  if (S == 1 && rows16 && a.Kc / 128 >= kSkLongK) return launch_skinny_rows16_64<false>(a, out, fuseq, st);
   if (S == 1 && rows16) return launch_skinny_out<1, kSkNST>(a, out, fuseq, part, 1, st);
   if (a.M <= 64) return launch_skinny_out<4, kSkNST64>(a, out, fuseq, part, S, st);
   return launch_skinny_out<8, 4>(a, out, fuseq, part, S, st);
