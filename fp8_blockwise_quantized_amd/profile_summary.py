@@ -63,9 +63,34 @@ def _csv(d: str, suffix: str) -> str:
     return sorted(hits)[0]
 
 
-def trace(d: str):
-    rows = list(csv.DictReader(open(_csv(d, "_kernel_stats.csv"))))
+def trace(d: str, by_grid: bool = False):
+    """Per kernel kind: calls, average, min, max and total duration.  With
+    by_grid, from the per-dispatch trace, one row per (kind, grid) so that
+    launches of one kernel on different shapes (decode layers) stay apart."""
     agg = collections.OrderedDict()
+    if by_grid:
+        rows = list(csv.DictReader(open(_csv(d, "_kernel_trace.csv"))))
+        for r in rows:
+            name = r["Kernel_Name"]
+            if "jet::" not in name:
+                continue
+            wg = int(r.get("Workgroup_Size_X") or 1) * int(r.get("Workgroup_Size_Y") or 1)
+            gx, gy, gz = (int(r.get(f"Grid_Size_{a}") or 1) for a in "XYZ")
+            grid = f"{gx // max(int(r.get('Workgroup_Size_X') or 1), 1)} x {gy} x {gz}"
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+            k = (kind(name), grid)
+            a = agg.setdefault(k, {"calls": 0, "total_ns": 0.0, "min": float("inf"), "max": 0.0})
+            a["calls"] += 1
+            a["total_ns"] += dur
+            a["min"] = min(a["min"], dur)
+            a["max"] = max(a["max"], dur)
+        out = ["| kernel kind | grid (workgroups) | calls | average us | min us | max us | total ms |",
+               "|---|---|---|---|---|---|---|"]
+        for (k, g), a in sorted(agg.items(), key=lambda kv: -kv[1]["total_ns"]):
+            out.append(f"| {k} | {g} | {a['calls']} | {a['total_ns'] / a['calls'] / 1e3:.2f} | "
+                       f"{a['min'] / 1e3:.2f} | {a['max'] / 1e3:.2f} | {a['total_ns'] / 1e6:.3f} |")
+        return out
+    rows = list(csv.DictReader(open(_csv(d, "_kernel_stats.csv"))))
     for r in rows:
         k = kind(r["Name"])
         a = agg.setdefault(k, {"calls": 0, "total_ns": 0.0, "min": float("inf"), "max": 0.0})
@@ -241,6 +266,7 @@ def main(argv=None):
     ap.add_argument("--title", default="")
     ap.add_argument("--cmd", action="append", default=[])
     ap.add_argument("--out", default="")
+    ap.add_argument("--by-grid", action="store_true", help="(trace) one row per kernel kind and grid")
     a = ap.parse_args(argv)
     lines = []
     if a.title:
@@ -252,7 +278,7 @@ def main(argv=None):
             raise SystemExit("hbm WORKLOAD FETCH_DIR WRITE_DIR --out JSON")
         lines += hbm(a.dir, a.more[0], a.more[1], a.out, a.cmd)
     else:
-        lines += trace(a.dir) if a.what == "trace" else counters(a.dir)
+        lines += trace(a.dir, a.by_grid) if a.what == "trace" else counters(a.dir)
     print("\n".join(lines))
 
 
