@@ -127,9 +127,7 @@ __global__ __launch_bounds__(64 * kRmsRowsPerBlock) void k_rmsnorm_quant_1x128(
       uint32_t yw[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const uint32_t lo = bf16_rne((bf16_lo(xw[k]) * r) * bf16_lo(gw[k]));
-        const uint32_t hi = bf16_rne((bf16_hi(xw[k]) * r) * bf16_hi(gw[k]));
-        yw[k] = lo | (hi << 16);
+        yw[k] = bf16x2_rne((bf16_lo(xw[k]) * r) * bf16_lo(gw[k]), (bf16_hi(xw[k]) * r) * bf16_hi(gw[k]));
       }
       const Codes8 cd = quant_row16<P2>(yw);
       if (ok) {
@@ -226,9 +224,7 @@ __global__ __launch_bounds__(256) void k_swiglu_quant_1x128(
       uint32_t hw[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const uint32_t lo = bf16_rne(swiglu1(bf16_lo(gw[k]), bf16_lo(uw[k])));
-        const uint32_t hi = bf16_rne(swiglu1(bf16_hi(gw[k]), bf16_hi(uw[k])));
-        hw[k] = lo | (hi << 16);
+        hw[k] = bf16x2_rne(swiglu1(bf16_lo(gw[k]), bf16_lo(uw[k])), swiglu1(bf16_hi(gw[k]), bf16_hi(uw[k])));
       }
       const Codes8 cd = quant_row16<P2>(hw);
       if (m < M && j < G) {

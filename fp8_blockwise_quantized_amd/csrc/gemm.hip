@@ -572,8 +572,8 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const uint32_t lo = bf16_rne(acc[i][j][0]) | (bf16_rne(acc[i][j][1]) << 16);
-        const uint32_t hi = bf16_rne(acc[i][j][2]) | (bf16_rne(acc[i][j][3]) << 16);
+        const uint32_t lo = bf16x2_rne(acc[i][j][0], acc[i][j][1]);
+        const uint32_t hi = bf16x2_rne(acc[i][j][2], acc[i][j][3]);
         *reinterpret_cast<uint2*>(t + (wm * TM * 16 + i * 16 + lrow) * CFG::EPI_PITCH +
                                   wn * TN * 16 + j * 16 + 4 * kg) = make_uint2(lo, hi);
       }
@@ -924,10 +924,10 @@ __global__ __launch_bounds__(256) void k_gemm_fp8_skinny(GemmArgs p, float* __re
       continue;
     }
     uint4 w;
-    w.x = bf16_rne(a.x) | (bf16_rne(a.y) << 16);
-    w.y = bf16_rne(a.z) | (bf16_rne(a.w) << 16);
-    w.z = bf16_rne(b.x) | (bf16_rne(b.y) << 16);
-    w.w = bf16_rne(b.z) | (bf16_rne(b.w) << 16);
+    w.x = bf16x2_rne(a.x, a.y);
+    w.y = bf16x2_rne(a.z, a.w);
+    w.z = bf16x2_rne(b.x, b.y);
+    w.w = bf16x2_rne(b.z, b.w);
     if (FUSEQ) {
       // 1x128 quantization of the BF16 output, as in the main kernel's epilogue
       uint32_t am = max_abs_bf16x2(0u, w.x);
@@ -979,10 +979,10 @@ __global__ __launch_bounds__(256) void k_skinny_finish(GemmArgs p, const float* 
     return;
   }
   uint4 w;
-  w.x = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
-  w.y = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
-  w.z = bf16_rne(v[4]) | (bf16_rne(v[5]) << 16);
-  w.w = bf16_rne(v[6]) | (bf16_rne(v[7]) << 16);
+  w.x = bf16x2_rne(v[0], v[1]);
+  w.y = bf16x2_rne(v[2], v[3]);
+  w.z = bf16x2_rne(v[4], v[5]);
+  w.w = bf16x2_rne(v[6], v[7]);
   if (FUSEQ) {
     // 1x128 quantization of the BF16 output, as in the main kernel's epilogue
     uint32_t am = max_abs_bf16x2(0u, w.x);

@@ -125,10 +125,15 @@ __device__ __forceinline__ float e4m3_at(uint32_t word) {
   return __builtin_amdgcn_cvt_f32_fp8((int)word, BYTE);
 }
 
-// BF16 bits of a finite FP32 value, round to nearest even.
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// BF16 bits of two FP32 values, round to nearest even, packed (lo in bits
+// 0..15): one v_cvt_pk_bf16_f32.  For every non-NaN input, denormals
+// included, it gives the bits of the integer rounding (u + 0x7FFF + bit 16
+// of u) >> 16; NaN stays NaN.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // ---------------------------------------------------------------------------
