@@ -117,7 +117,8 @@ int jet_quant_act_128x1_T(const void* src, int src_dtype, const float* src_s,
  *   kv_scales : FP32 device array of 6: [0] s_k, [1] r_k, [2] s_v, [3] r_v
  *               (s dequantizes, r quantizes); [4], [5] working space
  *   T >= 0 (T == 0: the floor scale), D > 0, D % 8 == 0; k, v 16-byte aligned,
- *   kv_scales 4-byte aligned.  Three kernel launches, no memset.
+ *   kv_scales 4-byte aligned.  Two kernel launches, no memset; during the
+ *   call kv_scales[0] also counts the workgroups that have finished.
  */
 int jet_kv_calibrate(const void* k, const void* v, int64_t T, int64_t D,
                      int64_t ldk, int64_t ldv, float* kv_scales, void* stream);

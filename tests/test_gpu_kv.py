@@ -92,3 +92,21 @@ def test_kv_full_prefill_llama8b(gpu_lib):
     assert scales_host(sc) == ((sk, rk), (sv, rv))
     assert_bits_equal(host(kc)[::-1], KV.kv_codes(y[:, q:q + d], rk), "K cache full prefill")
     assert_bits_equal(host(vc)[::-1], KV.kv_codes(y[:, q + d:], rv), "V cache full prefill")
+
+
+def test_kv_recalibration_reuses_the_scale_buffer(gpu_lib):
+    """Repeated recalibrations into one kv_scales buffer (one after each
+    weight update), 256 workgroups per tensor: each call's scales are the
+    oracle's for its own batch, whichever workgroup holds the maximum and
+    whatever the previous call left in the buffer."""
+    q, d, T = 4096, 1024, 8192
+    sc = torch.full((6,), 123.0, dtype=torch.float32, device="cuda")
+    for it, (row, col, val) in enumerate([(8191, 5, 9.0), (0, 1000, 0.5), (4100, 512, -300.0)]):
+        y = qkv_output(T, seed=20 + it)
+        y[row, q + col] = np.float32(val)               # an outlier in K
+        y[T - 1 - row, q + d + col] = np.float32(-val)  # and in V, in another workgroup's rows
+        yd = dev_bf16(y)
+        gpu_lib.jet_kv_calibrate(yd[:, q:q + d], yd[:, q + d:], kv_scales=sc)
+        torch.cuda.synchronize()
+        (sk, rk), (sv, rv) = KV.kv_calibrate(y[:, q:q + d], y[:, q + d:])
+        assert scales_host(sc) == ((sk, rk), (sv, rv)), f"recalibration {it}: scales differ"
