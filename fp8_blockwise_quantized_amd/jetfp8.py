@@ -15,7 +15,10 @@ import os
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libjetfp8.so")
+# JET_LIB_PATH names another build of the same library (the host-sanitized
+# build of the CPU validation tests); the default is the in-tree build.
+_LIB_PATH = os.environ.get("JET_LIB_PATH") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib",
+                                                          "libjetfp8.so")
 
 JET_OK, JET_ERR_NULL, JET_ERR_SHAPE, JET_ERR_ALIGN, JET_ERR_DTYPE, JET_ERR_WORKSPACE, JET_ERR_HIP = range(7)
 JET_BF16, JET_F32, JET_E4M3 = 1, 2, 3
