@@ -581,32 +581,69 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
     uint16_t* C = static_cast<uint16_t*>(p.C);
     constexpr int kLanesPerRow = BN / 8;                      // 16 bytes per lane
     constexpr int kRowsPerPass = CFG::THREADS / kLanesPerRow;
+    constexpr int NP = BM / kRowsPerPass;                     // passes over the tile
     const int c8 = tid % kLanesPerRow;
     const int n = n0 + 8 * c8;
-#pragma unroll 2
-    for (int pass = 0; pass < BM / kRowsPerPass; ++pass) {
-      const int row = tid / kLanesPerRow + kRowsPerPass * pass;
-      const int m = m0 + row;
-      const uint4 v = *reinterpret_cast<const uint4*>(t + row * CFG::EPI_PITCH + 8 * c8);
-      const bool ok = m < p.M && n < p.N;
-      if (FUSEQ) {
-        // 1x128 quantization of the BF16 output: 16 lanes (one DPP row) = one group
-        uint32_t am = max_abs_bf16x2(0u, v.x);
-        am = max_abs_bf16x2(am, v.y);
-        am = max_abs_bf16x2(am, v.z);
-        am = max_abs_bf16x2(am, v.w);
-        am = row16_max_u16x2(am);
-        const ScalePair sp = scale_rule<P2>(fold_bf16x2(am));
-        const uint32_t q0 = e4m3x4(bf16_lo(v.x) * sp.r, bf16_hi(v.x) * sp.r,
-                                   bf16_lo(v.y) * sp.r, bf16_hi(v.y) * sp.r);
-        const uint32_t q1 = e4m3x4(bf16_lo(v.z) * sp.r, bf16_hi(v.z) * sp.r,
-                                   bf16_lo(v.w) * sp.r, bf16_hi(v.w) * sp.r);
-        if (ok) {
-          *reinterpret_cast<uint2*>(p.Cq + (int64_t)m * p.ldc + n) = make_uint2(q0, q1);
-          if ((c8 & 15) == 0) p.Cs[(int64_t)(n / 128) * p.ldcs + m] = sp.s;
-        }
+    if constexpr (FUSEQ) {
+      // 1x128 quantization of the BF16 output: 16 lanes (one DPP row) hold
+      // one group per pass.  All passes' group maxima first; then each lane
+      // L of the wavefront takes the maximum of pass L/4, DPP row L%4, so one
+      // scale computation covers the wavefront's 4*NP groups; each pass then
+      // fetches its multiplier back and quantizes.
+      static_assert(4 * NP <= 64, "one group per lane");
+      uint4 v[NP];
+      float am[NP];
+#pragma unroll
+      for (int pass = 0; pass < NP; ++pass) {
+        const int row = tid / kLanesPerRow + kRowsPerPass * pass;
+        v[pass] = *reinterpret_cast<const uint4*>(t + row * CFG::EPI_PITCH + 8 * c8);
+        uint32_t a = max_abs_bf16x2(0u, v[pass].x);
+        a = max_abs_bf16x2(a, v[pass].y);
+        a = max_abs_bf16x2(a, v[pass].z);
+        a = max_abs_bf16x2(a, v[pass].w);
+        am[pass] = fold_bf16x2(row16_max_u16x2(a));
       }
-      if (ok) *reinterpret_cast<uint4*>(C + (int64_t)m * p.ldc + n) = v;
+      float a_all = 0.0f;
+#pragma unroll
+      for (int pass = 0; pass < NP; ++pass) {
+        const float x = __shfl(am[pass], 16 * (lane & 3), 64);
+        if ((lane >> 2) == pass) a_all = x;
+      }
+      const ScalePair sp = scale_rule<P2>(a_all);
+      {
+        // lane L writes the scale of its group (pass L/4, DPP row L%4)
+        const int pass = lane >> 2, tq = 64 * wave + 16 * (lane & 3);
+        const int m = m0 + tq / kLanesPerRow + kRowsPerPass * pass;
+        const int ng = n0 + 8 * (tq % kLanesPerRow);
+        if (pass < NP && m < p.M && ng < p.N) p.Cs[(int64_t)(ng / 128) * p.ldcs + m] = sp.s;
+      }
+      // row pointers advanced by kRowsPerPass rows per pass
+      const int mfirst = m0 + tid / kLanesPerRow;
+      const int64_t off0 = (int64_t)mfirst * p.ldc + n, step = (int64_t)kRowsPerPass * p.ldc;
+      uint8_t* cq = p.Cq + off0;
+      uint16_t* cy = C + off0;
+#pragma unroll
+      for (int pass = 0; pass < NP; ++pass) {
+        const float r = __shfl(sp.r, 4 * pass + (lane >> 4), 64);
+        const uint32_t q0 = e4m3x4(bf16_lo(v[pass].x) * r, bf16_hi(v[pass].x) * r,
+                                   bf16_lo(v[pass].y) * r, bf16_hi(v[pass].y) * r);
+        const uint32_t q1 = e4m3x4(bf16_lo(v[pass].z) * r, bf16_hi(v[pass].z) * r,
+                                   bf16_lo(v[pass].w) * r, bf16_hi(v[pass].w) * r);
+        if (mfirst + kRowsPerPass * pass < p.M && n < p.N) {
+          *reinterpret_cast<uint2*>(cq) = make_uint2(q0, q1);
+          *reinterpret_cast<uint4*>(cy) = v[pass];
+        }
+        cq += step;
+        cy += step;
+      }
+    } else {
+#pragma unroll 2
+      for (int pass = 0; pass < NP; ++pass) {
+        const int row = tid / kLanesPerRow + kRowsPerPass * pass;
+        const int m = m0 + row;
+        const uint4 v = *reinterpret_cast<const uint4*>(t + row * CFG::EPI_PITCH + 8 * c8);
+        if (m < p.M && n < p.N) *reinterpret_cast<uint4*>(C + (int64_t)m * p.ldc + n) = v;
+      }
     }
   }
 }
