@@ -36,27 +36,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// 1x128 quantization of 8 BF16 values (4 dwords) held by each lane of a
-// 16-lane DPP row (one group of 128): codes (two dwords) and the scale pair.
-struct Codes8 {
-  uint32_t c0, c1;
-  float s;
-};
-template <bool P2>
-__device__ __forceinline__ Codes8 quant_row16(const uint32_t w[4]) {
-  uint32_t am = max_abs_bf16x2(0u, w[0]);
-  am = max_abs_bf16x2(am, w[1]);
-  am = max_abs_bf16x2(am, w[2]);
-  am = max_abs_bf16x2(am, w[3]);
-  am = row16_max_u16x2(am);
-  const ScalePair sp = scale_rule<P2>(fold_bf16x2(am));
-  Codes8 c;
-  c.c0 = e4m3x4(bf16_lo(w[0]) * sp.r, bf16_hi(w[0]) * sp.r, bf16_lo(w[1]) * sp.r, bf16_hi(w[1]) * sp.r);
-  c.c1 = e4m3x4(bf16_lo(w[2]) * sp.r, bf16_hi(w[2]) * sp.r, bf16_lo(w[3]) * sp.r, bf16_hi(w[3]) * sp.r);
-  c.s = sp.s;
-  return c;
-}
-
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -116,11 +95,11 @@ __global__ __launch_bounds__(64 * kRmsRowsPerBlock) void k_rmsnorm_quant_1x128(
     }
     const float ms = wave_sum(ss) * inv_h;
     const float r = 1.0f / sqrtf(ms + eps);
+    uint4 yv[CH];
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      if (c >= chunks) continue;                   // uniform; keeps the loop fully unrolled
       const int64_t col = 512 * c + 8 * lane;
-      const bool ok = col < H;                     // uniform per DPP row (H % 128 == 0)
+      const bool ok = c < chunks && col < H;       // uniform per DPP row (H % 128 == 0)
       const uint32_t xw[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
       const uint4 g4 = gsh[ok ? 64 * c + lane : 0];
       const uint32_t gw[4] = {g4.x, g4.y, g4.z, g4.w};
@@ -129,12 +108,24 @@ __global__ __launch_bounds__(64 * kRmsRowsPerBlock) void k_rmsnorm_quant_1x128(
       for (int k = 0; k < 4; ++k) {
         yw[k] = bf16x2_rne((bf16_lo(xw[k]) * r) * bf16_lo(gw[k]), (bf16_hi(xw[k]) * r) * bf16_hi(gw[k]));
       }
-      const Codes8 cd = quant_row16<P2>(yw);
-      if (ok) {
-        store_stream8(q + m * ldq + col, cd.c0, cd.c1);
-        if (y) store_stream16(y + m * ldy + col, make_uint4(yw[0], yw[1], yw[2], yw[3]));
-        if ((lane & 15) == 0) stg[4 * c + (lane >> 4)][rr] = cd.s;
+      yv[c] = make_uint4(yw[0], yw[1], yw[2], yw[3]);
+    }
+    // 1x128 codes of every chunk (a DPP row holds one group per chunk), one
+    // scale computation for the row's 4*CH groups
+    uint2 qc[CH];
+    const float sc = quant_1x128_passes<CH, P2>(yv, qc);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int64_t col = 512 * c + 8 * lane;
+      if (c < chunks && col < H) {
+        store_stream8(q + m * ldq + col, qc[c].x, qc[c].y);
+        if (y) store_stream16(y + m * ldy + col, yv[c]);
       }
+    }
+    {
+      // lane L holds the scale of chunk L/4, DPP row L%4
+      const int c = lane >> 2, g = 4 * c + (lane & 3);
+      if (c < CH && c < chunks && 128 * (int64_t)g < H) stg[g][rr] = sc;
     }
   }
   __syncthreads();
@@ -215,10 +206,9 @@ __global__ __launch_bounds__(256) void k_swiglu_quant_1x128(
         vu[p] = load_stream16(row + I);
       }
     }
+    uint4 hv[8];
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
-      const int r = 16 * (p & 1) + dr, g = p >> 1;
-      const int64_t m = m0 + r, j = j0 + g;
       const uint32_t gw[4] = {vg[p].x, vg[p].y, vg[p].z, vg[p].w};
       const uint32_t uw[4] = {vu[p].x, vu[p].y, vu[p].z, vu[p].w};
       uint32_t hw[4];
@@ -226,12 +216,25 @@ __global__ __launch_bounds__(256) void k_swiglu_quant_1x128(
       for (int k = 0; k < 4; ++k) {
         hw[k] = bf16x2_rne(swiglu1(bf16_lo(gw[k]), bf16_lo(uw[k])), swiglu1(bf16_hi(gw[k]), bf16_hi(uw[k])));
       }
-      const Codes8 cd = quant_row16<P2>(hw);
+      hv[p] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    }
+    // codes of all 8 passes, one scale computation for the wavefront's 32 groups
+    uint2 qc[8];
+    const float sc = quant_1x128_passes<8, P2>(hv, qc);
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int r = 16 * (p & 1) + dr, g = p >> 1;
+      const int64_t m = m0 + r, j = j0 + g;
       if (m < M && j < G) {
-        store_stream8(q + m * ldq + j * kGroup + lane16 * 8, cd.c0, cd.c1);
-        if (h) store_stream16(h + m * ldh + j * kGroup + lane16 * 8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+        store_stream8(q + m * ldq + j * kGroup + lane16 * 8, qc[p].x, qc[p].y);
+        if (h) store_stream16(h + m * ldh + j * kGroup + lane16 * 8, hv[p]);
       }
-      if (lane16 == 0) stg[buf][g][r] = cd.s;
+    }
+    {
+      // lane L of wavefront w holds the scale of pass L/4, DPP row L%4: row
+      // 16*(pass&1) + 4w + L%4 of the unit, group pass/2
+      const int lane = threadIdx.x & 63, p = lane >> 2;
+      if (p < 8) stg[buf][p >> 1][16 * (p & 1) + 4 * (threadIdx.x >> 6) + (lane & 3)] = sc;
     }
     __syncthreads();
     if (threadIdx.x < 128) {

@@ -586,36 +586,21 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
     const int n = n0 + 8 * c8;
     if constexpr (FUSEQ) {
       // 1x128 quantization of the BF16 output: 16 lanes (one DPP row) hold
-      // one group per pass.  All passes' group maxima first; then each lane
-      // L of the wavefront takes the maximum of pass L/4, DPP row L%4, so one
-      // scale computation covers the wavefront's 4*NP groups; each pass then
-      // fetches its multiplier back and quantizes.
-      static_assert(4 * NP <= 64, "one group per lane");
+      // one group per pass; one scale computation per wavefront
+      // (quant_1x128_passes), lane L writing the scale of pass L/4, DPP row L%4.
       uint4 v[NP];
-      float am[NP];
+      uint2 qc[NP];
 #pragma unroll
       for (int pass = 0; pass < NP; ++pass) {
         const int row = tid / kLanesPerRow + kRowsPerPass * pass;
         v[pass] = *reinterpret_cast<const uint4*>(t + row * CFG::EPI_PITCH + 8 * c8);
-        uint32_t a = max_abs_bf16x2(0u, v[pass].x);
-        a = max_abs_bf16x2(a, v[pass].y);
-        a = max_abs_bf16x2(a, v[pass].z);
-        a = max_abs_bf16x2(a, v[pass].w);
-        am[pass] = fold_bf16x2(row16_max_u16x2(a));
       }
-      float a_all = 0.0f;
-#pragma unroll
-      for (int pass = 0; pass < NP; ++pass) {
-        const float x = __shfl(am[pass], 16 * (lane & 3), 64);
-        if ((lane >> 2) == pass) a_all = x;
-      }
-      const ScalePair sp = scale_rule<P2>(a_all);
+      const float sc = quant_1x128_passes<NP, P2>(v, qc);
       {
-        // lane L writes the scale of its group (pass L/4, DPP row L%4)
         const int pass = lane >> 2, tq = 64 * wave + 16 * (lane & 3);
         const int m = m0 + tq / kLanesPerRow + kRowsPerPass * pass;
         const int ng = n0 + 8 * (tq % kLanesPerRow);
-        if (pass < NP && m < p.M && ng < p.N) p.Cs[(int64_t)(ng / 128) * p.ldcs + m] = sp.s;
+        if (pass < NP && m < p.M && ng < p.N) p.Cs[(int64_t)(ng / 128) * p.ldcs + m] = sc;
       }
       // row pointers advanced by kRowsPerPass rows per pass
       const int mfirst = m0 + tid / kLanesPerRow;
@@ -624,13 +609,8 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
       uint16_t* cy = C + off0;
 #pragma unroll
       for (int pass = 0; pass < NP; ++pass) {
-        const float r = __shfl(sp.r, 4 * pass + (lane >> 4), 64);
-        const uint32_t q0 = e4m3x4(bf16_lo(v[pass].x) * r, bf16_hi(v[pass].x) * r,
-                                   bf16_lo(v[pass].y) * r, bf16_hi(v[pass].y) * r);
-        const uint32_t q1 = e4m3x4(bf16_lo(v[pass].z) * r, bf16_hi(v[pass].z) * r,
-                                   bf16_lo(v[pass].w) * r, bf16_hi(v[pass].w) * r);
         if (mfirst + kRowsPerPass * pass < p.M && n < p.N) {
-          *reinterpret_cast<uint2*>(cq) = make_uint2(q0, q1);
+          *reinterpret_cast<uint2*>(cq) = qc[pass];
           *reinterpret_cast<uint4*>(cy) = v[pass];
         }
         cq += step;

@@ -161,6 +161,45 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 // ---------------------------------------------------------------------------
+// 1x128 quantization of BF16 data laid out as NP passes per wavefront, each
+// 16-lane DPP row holding one 128-element group per pass (8 values, 4 dwords,
+// per lane).  The group maxima of every pass come first; lane L of the
+// wavefront then takes the maximum of pass L/4, DPP row L%4, so one scale
+// computation covers the wavefront's 4*NP groups, and each pass fetches its
+// multiplier back.  Same codes and scales as one scale computation per group.
+// Every lane of the wavefront must be active.  Returns the scale s of the
+// lane's group (pass lane/4, DPP row lane%4; meaningful for lane < 4*NP).
+// ---------------------------------------------------------------------------
+template <int NP, bool P2>
+__device__ __forceinline__ float quant_1x128_passes(const uint4 (&w)[NP], uint2 (&codes)[NP]) {
+  static_assert(NP >= 1 && 4 * NP <= 64, "one group per lane");
+  const int lane = threadIdx.x & 63;
+  float am[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    uint32_t a = max_abs_bf16x2(0u, w[p].x);
+    a = max_abs_bf16x2(a, w[p].y);
+    a = max_abs_bf16x2(a, w[p].z);
+    a = max_abs_bf16x2(a, w[p].w);
+    am[p] = fold_bf16x2(row16_max_u16x2(a));
+  }
+  float a_all = 0.0f;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const float x = __shfl(am[p], 16 * (lane & 3), 64);
+    if ((lane >> 2) == p) a_all = x;
+  }
+  const ScalePair sp = scale_rule<P2>(a_all);
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const float r = __shfl(sp.r, 4 * p + (lane >> 4), 64);
+    codes[p].x = e4m3x4(bf16_lo(w[p].x) * r, bf16_hi(w[p].x) * r, bf16_lo(w[p].y) * r, bf16_hi(w[p].y) * r);
+    codes[p].y = e4m3x4(bf16_lo(w[p].z) * r, bf16_hi(w[p].z) * r, bf16_lo(w[p].w) * r, bf16_hi(w[p].w) * r);
+  }
+  return sp.s;
+}
+
+// ---------------------------------------------------------------------------
 // Segments of a grouped (mixture-of-experts) problem.  seg[0..E] are the
 // device row offsets of the experts' segments; each bound is clamped to
 // [0, rows] and a segment's end to at least its start, so malformed offsets

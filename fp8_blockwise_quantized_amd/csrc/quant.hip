@@ -54,22 +54,19 @@ __global__ __launch_bounds__(256) void k_quant_1x128(const uint16_t* __restrict_
       v[p] = make_uint4(0u, 0u, 0u, 0u);
       if (m < M && j < G) v[p] = load_stream16(x + m * ldx + j * kGroup + lane16 * 8);
     }
+    // codes of all 8 passes, one scale computation for the wavefront's 32 groups
+    uint2 qc[8];
+    const float sc = quant_1x128_passes<8, P2>(v, qc);
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
-      const int r = 16 * (p & 1) + dr, g = p >> 1;
-      const int64_t m = m0 + r, j = j0 + g;
-      uint32_t am = max_abs_bf16x2(0u, v[p].x);
-      am = max_abs_bf16x2(am, v[p].y);
-      am = max_abs_bf16x2(am, v[p].z);
-      am = max_abs_bf16x2(am, v[p].w);
-      am = row16_max_u16x2(am);
-      const ScalePair sp = scale_rule<P2>(fold_bf16x2(am));
-      const uint32_t c0 = e4m3x4(bf16_lo(v[p].x) * sp.r, bf16_hi(v[p].x) * sp.r,
-                                 bf16_lo(v[p].y) * sp.r, bf16_hi(v[p].y) * sp.r);
-      const uint32_t c1 = e4m3x4(bf16_lo(v[p].z) * sp.r, bf16_hi(v[p].z) * sp.r,
-                                 bf16_lo(v[p].w) * sp.r, bf16_hi(v[p].w) * sp.r);
-      if (m < M && j < G) store_stream8(q + m * ldq + j * kGroup + lane16 * 8, c0, c1);
-      if (lane16 == 0) stg[buf][g][r] = sp.s;
+      const int64_t m = m0 + 16 * (p & 1) + dr, j = j0 + (p >> 1);
+      if (m < M && j < G) store_stream8(q + m * ldq + j * kGroup + lane16 * 8, qc[p].x, qc[p].y);
+    }
+    {
+      // lane L of wavefront w holds the scale of pass L/4, DPP row L%4: row
+      // 16*(pass&1) + 4w + L%4 of the unit, group pass/2
+      const int lane = threadIdx.x & 63, p = lane >> 2;
+      if (p < 8) stg[buf][p >> 1][16 * (p & 1) + 4 * (threadIdx.x >> 6) + (lane & 3)] = sc;
     }
     __syncthreads();
     if (threadIdx.x < 128) {
