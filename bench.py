@@ -487,6 +487,28 @@ def measured_ceilings(torch):
         khz = int(L.jet_probe_wall_clock_khz())
         if c[1] > 0 and khz > 0:
             out[f"{key}_sclk_mhz"] = round(float(c[0]) / float(c[1]) * khz / 1e3, 0)
+    # the GEMMs' K step on synthetic bytes, built up from its parts (one 8-wavefront block per CU)
+    L.jet_probe_gemm_step.argtypes = [vp, vp, i32, i32, i32, vp]
+    gsrc = torch.empty(cus * 262144, dtype=torch.uint8, device="cuda").fill_(0x3C)
+    gout = torch.empty(cus * 512, dtype=torch.float32, device="cuda")
+    steps = 512
+    step = {}
+    for name, parts in (("mfma", 0), ("lds", 1), ("pipe_l2", 3), ("fold", 4), ("pipe_l2_fold", 7),
+                        ("pipe_mall", 11), ("pipe_mall_fold", 15)):
+        def run(parts=parts):
+            rc = L.jet_probe_gemm_step(ctypes.c_void_p(gsrc.data_ptr()), ctypes.c_void_p(gout.data_ptr()), steps,
+                                       parts, cus, st)
+            if rc:
+                raise RuntimeError(f"jet_probe_gemm_step failed ({rc})")
+        run()
+        ms = timed(run, 3)
+        step[f"{name}_tflops"] = round(cus * 8 * steps * 32 * 2.0 * 16 * 16 * 128 / (ms * 1e-3) / 1e12, 1)
+    del gsrc, gout
+    step["what"] = ("the GEMMs' K step (8 wavefronts of 128 x 64, two 64 KiB LDS stages, 32 MFMAs per "
+                    "wavefront and step) on synthetic bytes: MFMA only; + the step's LDS fragment reads; + the "
+                    "pipeline (next stage's direct loads, their wait, one barrier); FP32 fold; with the loads "
+                    "hitting L2 or all missing it (MALL); best of 3")
+    out["gemm_step"] = step
     out["what"] = ("best of 5 (streams, 1 GiB source) / 3 (MFMA: the GEMMs' 8x4-fragment wave tile in "
                    "registers, one 8-wavefront block per CU) probe launches, with the shader clock wavefront 0 "
                    "saw; published peaks: 8000 GB/s HBM, 5000 TFLOP/s dense FP8 at 2.4 GHz")

@@ -18,6 +18,19 @@
 //    block 0 records the core cycle counter and the constant-rate wall
 //    counter over its loop; the fold's VALU work lowers the clock the chip
 //    sustains, so the host reports the clock of each pass.
+//  * k_gemm_step<PARTS>: the GEMMs' K-step on synthetic bytes, built up from
+//    its parts.  A block is the GEMM's 8 wavefronts (2 x 4, wave tile 128 x
+//    64 of a 256 x 256 tile) with two 64 KiB LDS stages (A and B, 256 rows x
+//    128 bytes each, the GEMM's row swizzle); a step is 32 MFMAs per
+//    wavefront on fragments held in registers, plus, by flag: the step's 12
+//    fragment reads from LDS (24 ds_read_b128), the next stage's direct
+//    global->LDS loads (8 per wavefront, 64 KiB per block) waited for at the
+//    next step's start and followed by one barrier, and the per-step FP32 fold
+//    (each MFMA from zero, folded three MFMAs later with one FMA per
+//    element).  The source is either a 128 KiB window shared by every 32nd
+//    block (the loads hit L2) or a 256 KiB window of the block's own that the
+//    steps cycle through (with 32 blocks per XCD, 8 MiB per XCD: every load
+//    misses L2 and comes from the MALL).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -109,6 +122,118 @@ __global__ __launch_bounds__(512) void k_mfma_rate(const int* __restrict__ in, f
   out[(int64_t)blockIdx.x * 512 + threadIdx.x] = t + (float)lds_hold[(threadIdx.x + 1) & 511];
 }
 
+enum { kStepLds = 1, kStepPipe = 2, kStepFold = 4, kStepMall = 8 };
+
+__device__ __forceinline__ uint32_t rfl(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// 64 lanes x 16 bytes from base + voff (per lane) to LDS [lds_addr, +1024).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void probe_dma16(uint32_t lds_addr, const uint8_t* base, uint32_t voff) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint64_t bs = (uint64_t)rfl((uint32_t)b) | ((uint64_t)rfl((uint32_t)(b >> 32)) << 32);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(rfl(lds_addr)), "v"(voff), "s"(reinterpret_cast<const void*>(bs)) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+typedef __attribute__((address_space(3))) uint8_t lds_byte;
+
+template <int PARTS>
+__global__ __launch_bounds__(512) void k_gemm_step(const uint8_t* __restrict__ src, float* __restrict__ out,
+                                                   int steps) {
+  constexpr int kStage = 65536;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave % 2, wn = wave / 2;
+  const int lrow = lane & 15, kg = lane >> 4;
+  for (int i = tid; i < 2 * kStage / 4; i += 512) reinterpret_cast<uint32_t*>(lds)[i] = (uint32_t)i * 2654435761u;
+  __syncthreads();
+  v8i af[8], bf[4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) af[i][e] = lane * 8 + e + i;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bf[j][e] = lane * 8 + e + 3 * j;
+  v4f acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(const lds_byte*)lds;
+  const uint8_t* base = src + ((PARTS & kStepMall) ? (int64_t)blockIdx.x * 262144 : (int64_t)(blockIdx.x % 32) * 131072);
+  const uint32_t voff = (uint32_t)((lane >> 3) * 128 + (lane & 7) * 16);
+  for (int kb = 0; kb < steps; ++kb) {
+    const int st = kb & 1;
+    if (PARTS & kStepPipe) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      // this wavefront's 8 KiB of the next stage
+      const int64_t off = (PARTS & kStepMall) ? (int64_t)((kb + 1) & 3) * kStage : (int64_t)((kb + 1) & 1) * kStage;
+      const uint32_t dst = lds0 + (uint32_t)((st ^ 1) * kStage + wave * 8192);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) probe_dma16(dst + t * 1024, base + off + wave * 8192 + t * 1024, voff);
+    }
+    const uint8_t* As = lds + st * kStage;
+    const uint8_t* Bs = As + kStage / 2;
+    v4f part[3];
+    const float c = (float)(lane + kb) * 1e-3f;
+#pragma unroll
+    for (int n = 0; n < 32 + 3; ++n) {
+      if ((PARTS & kStepFold) && n >= 3) {
+        const int ii = (n - 3) / 4, jj = (n - 3) % 4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[ii][jj][r] = fmaf(part[(n - 3) % 3][r], c, acc[ii][jj][r]);
+      }
+      if (n >= 32) continue;
+      const int i = n / 4, j = n % 4;
+      if (j == 0) {
+        if (PARTS & kStepLds) {
+          // rows i (and i + 1 ahead), all B fragments at the step's start
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int ia = (i == 0) ? q : (q == 0 ? -1 : i + 1);
+            if (ia < 0 || ia >= 8) continue;
+            const int row = (wm * 8 + ia) * 16 + lrow, f = (row & 7) ^ ((row >> 3) & 1);
+            const uint4 lo = *reinterpret_cast<const uint4*>(As + row * 128 + (((2 * kg) ^ f) << 4));
+            const uint4 hi = *reinterpret_cast<const uint4*>(As + row * 128 + (((2 * kg + 1) ^ f) << 4));
+            af[ia] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          }
+          if (i == 0) {
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb) {
+              const int row = (wn * 4 + jb) * 16 + lrow, f = (row & 7) ^ ((row >> 3) & 1);
+              const uint4 lo = *reinterpret_cast<const uint4*>(Bs + row * 128 + (((2 * kg) ^ f) << 4));
+              const uint4 hi = *reinterpret_cast<const uint4*>(Bs + row * 128 + (((2 * kg + 1) ^ f) << 4));
+              bf[jb] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            }
+          }
+        } else {
+          asm volatile("" : "+v"(af[i]));   // operands are not loop-invariant to the compiler
+        }
+      }
+      if (PARTS & kStepFold)
+        part[n % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[i], v4f{0.0f, 0.0f, 0.0f, 0.0f},
+                                                                       0, 0, 0, 0, 0, 0);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[i], acc[i][j], 0, 0, 0, 0, 0, 0);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  float t = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) t += acc[i][j][0] + acc[i][j][3];
+  // an LDS read keeps the 128 KiB allocation in every variant: one block per CU
+  out[(int64_t)blockIdx.x * 512 + tid] = t + (float)lds[(tid * 257) & (2 * kStage - 1)];
+}
+
 }  // namespace
 
 extern "C" {
@@ -135,6 +260,22 @@ int jet_probe_mfma(const int* in, float* out, long long* clocks, int iters, int 
     hipLaunchKernelGGL((k_mfma_rate<true>), dim3((unsigned)blocks), dim3(512), 0, st, in, out, clocks, iters);
   else
     hipLaunchKernelGGL((k_mfma_rate<false>), dim3((unsigned)blocks), dim3(512), 0, st, in, out, clocks, iters);
+  return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
+int jet_probe_gemm_step(const void* src, float* out, int steps, int parts, int blocks, void* stream) {
+  if (!src || !out || steps < 1 || blocks < 1 || parts < 0 || parts > 15) return 1;
+  if ((parts & kStepMall) && !(parts & kStepPipe)) return 1;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const uint8_t* s8 = static_cast<const uint8_t*>(src);
+  const dim3 g((unsigned)blocks), b(512);
+  switch (parts) {
+#define JET_STEP(P) \
+  case P: hipLaunchKernelGGL((k_gemm_step<P>), g, b, 0, st, s8, out, steps); break;
+    JET_STEP(0) JET_STEP(1) JET_STEP(3) JET_STEP(4) JET_STEP(7) JET_STEP(11) JET_STEP(15)
+#undef JET_STEP
+    default: return 2;
+  }
   return hipGetLastError() == hipSuccess ? 0 : 3;
 }
 

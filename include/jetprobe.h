@@ -33,6 +33,16 @@ int jet_probe_stream(const void* in, void* out, int64_t units, int load_bytes, i
  * and wall-counter ticks wavefront 0 of block 0 spent in its loop. */
 int jet_probe_mfma(const int* in, float* out, long long* clocks, int iters, int fold, int blocks, void* stream);
 
+/* The GEMMs' K-step on synthetic bytes (8 wavefronts of 128 x 64, 256 x 256
+ * block tile, two 64 KiB LDS stages, 32 MFMAs per wavefront and step), built
+ * up from parts: parts = 0 MFMA only; +1 the step's LDS fragment reads; +2 the
+ * pipeline (the next stage's direct global->LDS loads, the wait for them and
+ * one barrier per step; needs +1); +4 the per-step FP32 fold; +8 the loads
+ * miss L2 (each block cycles a 256 KiB window of its own; needs +2); parts in
+ * {0, 1, 3, 4, 7, 11, 15}.  src: device bytes, at least blocks * 262144 (with
+ * +8) or 32 * 131072; out: float[blocks * 512]; `steps` K steps per block. */
+int jet_probe_gemm_step(const void* src, float* out, int steps, int parts, int blocks, void* stream);
+
 /* Rate of the wall counter read by jet_probe_mfma, kHz (0 on failure). */
 int jet_probe_wall_clock_khz(void);
 
