@@ -493,7 +493,7 @@ def measured_ceilings(torch):
     gout = torch.empty(cus * 512, dtype=torch.float32, device="cuda")
     steps = 512
     step = {}
-    for name, parts in (("mfma", 0), ("lds", 1), ("pipe_l2", 3), ("fold", 4), ("pipe_l2_fold", 7),
+    for name, parts in (("mfma", 0), ("lds", 1), ("lds_a_only", 17), ("pipe_l2", 3), ("fold", 4), ("pipe_l2_fold", 7),
                         ("pipe_mall", 11), ("pipe_mall_fold", 15)):
         def run(parts=parts):
             rc = L.jet_probe_gemm_step(ctypes.c_void_p(gsrc.data_ptr()), ctypes.c_void_p(gout.data_ptr()), steps,
@@ -505,7 +505,8 @@ def measured_ceilings(torch):
         step[f"{name}_tflops"] = round(cus * 8 * steps * 32 * 2.0 * 16 * 16 * 128 / (ms * 1e-3) / 1e12, 1)
     del gsrc, gout
     step["what"] = ("the GEMMs' K step (8 wavefronts of 128 x 64, two 64 KiB LDS stages, 32 MFMAs per "
-                    "wavefront and step) on synthetic bytes: MFMA only; + the step's LDS fragment reads; + the "
+                    "wavefront and step) on synthetic bytes: MFMA only; + the step's LDS fragment reads (or the A "
+                    "fragments only); + the "
                     "pipeline (next stage's direct loads, their wait, one barrier); FP32 fold; with the loads "
                     "hitting L2 or all missing it (MALL); best of 3")
     out["gemm_step"] = step

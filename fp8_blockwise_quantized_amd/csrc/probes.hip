@@ -23,7 +23,7 @@
 //    64 of a 256 x 256 tile) with two 64 KiB LDS stages (A and B, 256 rows x
 //    128 bytes each, the GEMM's row swizzle); a step is 32 MFMAs per
 //    wavefront on fragments held in registers, plus, by flag: the step's 12
-//    fragment reads from LDS (24 ds_read_b128), the next stage's direct
+//    fragment reads from LDS (24 ds_read_b128; or only the 8 A fragments), the next stage's direct
 //    global->LDS loads (8 per wavefront, 64 KiB per block) waited for at the
 //    next step's start and followed by one barrier, and the per-step FP32 fold
 //    (each MFMA from zero, folded three MFMAs later with one FMA per
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(512) void k_mfma_rate(const int* __restrict__ in, f
   out[(int64_t)blockIdx.x * 512 + threadIdx.x] = t + (float)lds_hold[(threadIdx.x + 1) & 511];
 }
 
-enum { kStepLds = 1, kStepPipe = 2, kStepFold = 4, kStepMall = 8 };
+enum { kStepLds = 1, kStepPipe = 2, kStepFold = 4, kStepMall = 8, kStepAOnly = 16 };
 
 __device__ __forceinline__ uint32_t rfl(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(512) void k_gemm_step(const uint8_t* __restrict__ s
             const uint4 hi = *reinterpret_cast<const uint4*>(As + row * 128 + (((2 * kg + 1) ^ f) << 4));
             af[ia] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
           }
-          if (i == 0) {
+          if (i == 0 && !(PARTS & kStepAOnly)) {
 #pragma unroll
             for (int jb = 0; jb < 4; ++jb) {
               const int row = (wn * 4 + jb) * 16 + lrow, f = (row & 7) ^ ((row >> 3) & 1);
@@ -264,7 +264,7 @@ int jet_probe_mfma(const int* in, float* out, long long* clocks, int iters, int 
 }
 
 int jet_probe_gemm_step(const void* src, float* out, int steps, int parts, int blocks, void* stream) {
-  if (!src || !out || steps < 1 || blocks < 1 || parts < 0 || parts > 15) return 1;
+  if (!src || !out || steps < 1 || blocks < 1 || parts < 0 || parts > 31) return 1;
   if ((parts & kStepMall) && !(parts & kStepPipe)) return 1;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const uint8_t* s8 = static_cast<const uint8_t*>(src);
@@ -272,7 +272,7 @@ int jet_probe_gemm_step(const void* src, float* out, int steps, int parts, int b
   switch (parts) {
 #define JET_STEP(P) \
   case P: hipLaunchKernelGGL((k_gemm_step<P>), g, b, 0, st, s8, out, steps); break;
-    JET_STEP(0) JET_STEP(1) JET_STEP(3) JET_STEP(4) JET_STEP(7) JET_STEP(11) JET_STEP(15)
+    JET_STEP(0) JET_STEP(1) JET_STEP(17) JET_STEP(3) JET_STEP(4) JET_STEP(7) JET_STEP(11) JET_STEP(15)
 #undef JET_STEP
     default: return 2;
   }

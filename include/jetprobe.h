@@ -38,8 +38,9 @@ int jet_probe_mfma(const int* in, float* out, long long* clocks, int iters, int 
  * up from parts: parts = 0 MFMA only; +1 the step's LDS fragment reads; +2 the
  * pipeline (the next stage's direct global->LDS loads, the wait for them and
  * one barrier per step; needs +1); +4 the per-step FP32 fold; +8 the loads
- * miss L2 (each block cycles a 256 KiB window of its own; needs +2); parts in
- * {0, 1, 3, 4, 7, 11, 15}.  src: device bytes, at least blocks * 262144 (with
+ * miss L2 (each block cycles a 256 KiB window of its own; needs +2); +16 only
+ * the 8 A fragments of the step are read from LDS (with +1); parts in
+ * {0, 1, 17, 3, 4, 7, 11, 15}.  src: device bytes, at least blocks * 262144 (with
  * +8) or 32 * 131072; out: float[blocks * 512]; `steps` K steps per block. */
 int jet_probe_gemm_step(const void* src, float* out, int steps, int parts, int blocks, void* stream);
 
