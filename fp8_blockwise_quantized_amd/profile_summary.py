@@ -219,17 +219,15 @@ def hbm(workload: str, fetch_dir: str, write_dir: str, out: str, cmds):
         for i, (f, w) in enumerate(calls):
             per.setdefault(f"{layers[i % 4]}_{variant}", []).append((f, w))
     elif workload == "kv":
-        # kv_calibrate = clear + amax + scales; then the prefill append, then the decode append
+        # kv_calibrate = clear + amax (whose last workgroup writes the scales);
+        # then the prefill append, then the decode append
         appends, cal = 0, None
         for (n, f), (_, w) in zip(fj, wj):
             k = kind(n)
             if k.startswith("k_kv_clear"):
                 cal = [f, w]
-            elif k.startswith("k_kv_amax") or k.startswith("k_kv_scales"):
-                cal[0] += f
-                cal[1] += w
-                if k.startswith("k_kv_scales"):
-                    per.setdefault("kv_calibrate", []).append(tuple(cal))
+            elif k.startswith("k_kv_amax"):
+                per.setdefault("kv_calibrate", []).append((cal[0] + f, cal[1] + w))
             elif k.startswith("k_kv_append"):
                 per.setdefault("kv_append_prefill" if appends % 2 == 0 else "kv_append_decode", []).append((f, w))
                 appends += 1
