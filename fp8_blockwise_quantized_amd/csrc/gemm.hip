@@ -304,6 +304,24 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
     const int local = slot - e * (nbm * nbn);
     tm = local / nbn;
     tn = local - tm * nbn;
+    // With a multiple of 8 tiles per expert, XCD slot%8 takes one block of a
+    // gy x gx split of the expert's tile grid (the split that minimises the
+    // operand strips the XCDs fetch, as for the dense grid) instead of every
+    // eighth tile of the row-major walk.
+    if ((nbm * nbn) % 8 == 0) {
+      int gy = 0, gx = 0, cost = 0x7fffffff;
+#pragma unroll
+      for (int y = 1; y <= 8; y *= 2) {
+        const int x = 8 / y, c = x * nbm + y * nbn;
+        if (nbm % y == 0 && nbn % x == 0 && c < cost) { cost = c; gy = y; gx = x; }
+      }
+      if (gy > 0) {
+        const int xcd = local % 8, idx = local / 8;
+        const int rows = nbm / gy, cols = nbn / gx;
+        tm = (xcd / gx) * rows + idx % rows;
+        tn = (xcd % gx) * cols + idx / rows;
+      }
+    }
     const SegHit h = seg_find(p.seg, p.E, p.seg_rows, 128, e, true);
     const int first = __builtin_amdgcn_readfirstlane(h.first);
     const int groups = __builtin_amdgcn_readfirstlane((h.hi - h.lo + 127) / 128);
