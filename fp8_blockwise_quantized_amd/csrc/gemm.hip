@@ -83,7 +83,10 @@ struct GemmCfg {
   static constexpr int LOADS = ABLK + BBLK;            // tile DMAs per wave and stage (+1 scale DMA
                                                        // for waves 0 .. RQ+CQ-1)
   static constexpr int EPI_PITCH = BN + 8;             // bf16 per staged output row
-  static constexpr int LDS = (STAGES * STAGE > BM * EPI_PITCH * 2) ? STAGES * STAGE : BM * EPI_PITCH * 2;
+  static constexpr int EPI_PITCH_F32 = BN + 4;         // floats per staged FP32 output row (one wave row)
+  static constexpr int EPI = (BM * EPI_PITCH * 2 > TM * 16 * EPI_PITCH_F32 * 4) ? BM * EPI_PITCH * 2
+                                                                              : TM * 16 * EPI_PITCH_F32 * 4;
+  static constexpr int LDS = (STAGES * STAGE > EPI) ? STAGES * STAGE : EPI;
   static_assert(ABLK * NW * 1024 == ATILE && BBLK * NW * 1024 == BTILE, "DMA split");
   static_assert(ABLK * 8 == OA * 16 && BBLK * 8 == OB * 16, "a wave's DMA rows are whole slabs");
   static_assert(BM % 64 == 0 && BN % 64 == 0 && BN * 4 <= 1024 && NW >= RQ + CQ, "scale DMA shape");
@@ -563,23 +566,44 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
   const int mrow = m0 + wm * TM * 16 + lrow;
   const int ncol = n0 + wn * TN * 16 + 4 * kg;
   if (OUT == kOutF32) {
-    // four adjacent FP32 columns per lane: direct 16-byte stores
+    // Stage the FP32 tile in LDS one wave row (TM*16 rows) at a time and
+    // write it as whole 128-byte lines: each wavefront instruction stores a
+    // contiguous piece of one row.  (Stores of each lane's four columns
+    // straight from the accumulators write partial lines, which the BF16
+    // output measured slower.)
     float* C = static_cast<float*>(p.C);
+    float* t = reinterpret_cast<float*>(lds);
+    constexpr int FP = CFG::EPI_PITCH_F32;                    // floats per staged row
+    constexpr int LPR = BN / 4;                               // lanes per row, 16 bytes each
+    constexpr int RPP = CFG::THREADS / LPR;                   // rows per pass
+    static_assert((TM * 16) % RPP == 0, "whole passes");
+    const int c4 = tid % LPR;
+    const int n = n0 + 4 * c4;
+#pragma unroll 1
+    for (int h = 0; h < CFG::WMW; ++h) {
+      __syncthreads();                                        // the ring, or the previous rows, are free
+      if (wm == h) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int m = mrow + i * 16;
-      if (m >= p.M) continue;
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int n = ncol + j * 16;
-        if (n >= p.N) continue;
-        float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-        float4* dst = reinterpret_cast<float4*>(C + (int64_t)m * p.ldc + n);
-        if (ACCUM) {
-          const float4 o = *dst;
-          v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+          for (int j = 0; j < TN; ++j)
+            *reinterpret_cast<float4*>(t + (i * 16 + lrow) * FP + wn * TN * 16 + j * 16 + 4 * kg) =
+                make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      }
+      __syncthreads();
+#pragma unroll 4
+      for (int pass = 0; pass < TM * 16 / RPP; ++pass) {
+        const int r = tid / LPR + RPP * pass;
+        const int m = m0 + h * TM * 16 + r;
+        float4 v = *reinterpret_cast<const float4*>(t + r * FP + 4 * c4);
+        if (m < p.M && n < p.N) {
+          float4* dst = reinterpret_cast<float4*>(C + (int64_t)m * p.ldc + n);
+          if (ACCUM) {
+            const float4 o = *dst;
+            v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+          }
+          *dst = v;
         }
-        *dst = v;
       }
     }
   } else {
