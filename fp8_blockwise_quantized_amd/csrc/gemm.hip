@@ -768,16 +768,17 @@ hipError_t launch_gemm(const GemmArgs& a, int mode, int out, bool accum, bool fu
 // scale.
 // Wavefront w multiplies W slab w (output columns 16w..16w+15 of the block)
 // with the MT X slabs.
-template <int MT, int NST, int WS>
+template <int MT, int NST, int WS, int KS>
 struct SkinnyCfg {
   static constexpr int BN = 64 * WS;                   // output columns per workgroup
   static constexpr int XT = MT * 16 * 128, WT = BN * 128;
-  static constexpr int STAGE = XT + WT + 1024;
+  static constexpr int SUB = XT + WT + 1024;           // one K step: X tile, W tile, scale slots
+  static constexpr int STAGE = KS * SUB;               // KS consecutive K steps per ring stage
   static constexpr int XBLK = XT / 1024, WBLK = WT / 1024;
-  static constexpr int BPW = (XBLK + WBLK + 3) / 4;    // tile DMAs per wavefront and stage (slots
+  static constexpr int BPW = (XBLK + WBLK + 3) / 4;    // tile DMAs per wavefront and K step (slots
                                                        // past the last block repeat it)
   static constexpr int NSX = (MT + 3) / 4;             // scale slots holding X row scales
-  static constexpr int LOADS = BPW + 1;
+  static constexpr int LOADS = KS * (BPW + 1);         // DMAs per wavefront and stage
   static constexpr int LDS = NST * STAGE;
   static constexpr int TP = BN + 4;                    // FP32 output tile pitch (floats)
   static_assert(NSX >= 1 && NSX < 4, "scale slots");
@@ -786,10 +787,10 @@ struct SkinnyCfg {
   static_assert(LDS <= 160 * 1024, "LDS");
 };
 
-template <int MT, int NST, int WS, int OUT, bool FUSEQ, bool P2 = false>
+template <int MT, int NST, int WS, int KS, int OUT, bool FUSEQ, bool P2 = false>
 __global__ __launch_bounds__(256) void k_gemm_fp8_skinny(GemmArgs p, float* __restrict__ part,
                                                          int splits) {
-  using C = SkinnyCfg<MT, NST, WS>;
+  using C = SkinnyCfg<MT, NST, WS, KS>;
   static_assert(C::BN == 128 || !FUSEQ, "the fused 1x128 output needs whole 128-column groups");
   __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -851,19 +852,33 @@ __global__ __launch_bounds__(256) void k_gemm_fp8_skinny(GemmArgs p, float* __re
   }
   const uint32_t sdst = (uint32_t)(C::XT + C::WT + 256 * wave);
 
+  // Stage `stage` holds K steps kb .. kb+KS-1 of the range (a step past the
+  // range's end loads its last step again and is not computed).  The KS
+  // steps' blocks of the same rows are issued back to back, so each weight
+  // row is requested KS*128 contiguous bytes at a time.
   auto issue = [&](int stage, int kb) __attribute__((always_inline)) {
     const uint32_t sb = lds0 + (uint32_t)(stage * C::STAGE);
 #pragma unroll
     for (int t = 0; t < C::BPW; ++t)
-      dma16(sb + dst[t], (isx[t] ? p.A : p.B) + (int64_t)kb * 128, off[t]);
-    if (wave < C::NSX) dma4(sb + sdst, p.sA + (int64_t)kb * p.sA_ld, soff);
-    else dma4(sb + sdst, p.sB + (int64_t)kb * p.sB_c, soff);
+#pragma unroll
+      for (int u = 0; u < KS; ++u) {
+        const int kk = min(kb + u, kb1 - 1);
+        dma16(sb + (uint32_t)(u * C::SUB) + dst[t], (isx[t] ? p.A : p.B) + (int64_t)kk * 128, off[t]);
+      }
+#pragma unroll
+    for (int u = 0; u < KS; ++u) {
+      const int kk = min(kb + u, kb1 - 1);
+      const uint32_t sd = sb + (uint32_t)(u * C::SUB) + sdst;
+      if (wave < C::NSX) dma4(sd, p.sA + (int64_t)kk * p.sA_ld, soff);
+      else dma4(sd, p.sB + (int64_t)kk * p.sB_c, soff);
+    }
   };
 
   constexpr int D = NST - 1;
+  const int nstages = (nsteps + KS - 1) / KS;
 #pragma unroll
   for (int s = 0; s < D; ++s)
-    if (s < nsteps) issue(s, kb0 + s);
+    if (s < nstages) issue(s, kb0 + s * KS);
 
   v4f acc[WS][MT];
 #pragma unroll
@@ -872,19 +887,22 @@ __global__ __launch_bounds__(256) void k_gemm_fp8_skinny(GemmArgs p, float* __re
     for (int i = 0; i < MT; ++i) acc[j][i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   int st = 0;
-  for (int k = 0; k < nsteps; ++k) {
-    // this wavefront's loads of step k have landed once at most those of the
-    // (up to D-1) later steps already issued are outstanding
-    const int later = min(nsteps - 1 - k, D - 1);
+  for (int k = 0; k < nstages; ++k) {
+    // this wavefront's loads of stage k have landed once at most those of the
+    // (up to D-1) later stages already issued are outstanding
+    const int later = min(nstages - 1 - k, D - 1);
     if (later >= D - 1) wait_vmem<C::LOADS * (D - 1)>();
     else wait_vmem<0>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    const uint8_t* Xs = lds + st * C::STAGE;
+    // the stage stage k-1 used is free: refill it with stage k + D
+    if (k + D < nstages) issue((st + D) % NST, kb0 + (k + D) * KS);
+#pragma unroll
+    for (int u = 0; u < KS; ++u) {
+    if (u > 0 && k * KS + u >= nsteps) break;
+    const uint8_t* Xs = lds + st * C::STAGE + u * C::SUB;
     const uint8_t* Ws = Xs + C::XT;
     const float* Sc = reinterpret_cast<const float*>(Xs + C::XT + C::WT);
-    // the stage step k-1 used is free: refill it with step k + D
-    if (k + D < nsteps) issue((st + D) % NST, kb0 + k + D);
     float sx[MT];
     if constexpr (MT >= 4) {
 #pragma unroll
@@ -913,7 +931,6 @@ __global__ __launch_bounds__(256) void k_gemm_fp8_skinny(GemmArgs p, float* __re
         for (int i = 0; i < MT; ++i)
           acc[j][i] = mfma_fp8_e8m0(bfr, frag32<false>(Xs, i, lane), acc[j][i], eb, ea[i]);
       }
-      st = (st + 1 == NST) ? 0 : st + 1;
       continue;
     }
 #pragma unroll
@@ -928,6 +945,7 @@ __global__ __launch_bounds__(256) void k_gemm_fp8_skinny(GemmArgs p, float* __re
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[j][i][r] = fmaf(pr[i][r], c, acc[j][i][r]);
       }
+    }
     }
     st = (st + 1 == NST) ? 0 : st + 1;
   }
@@ -1067,13 +1085,20 @@ __global__ __launch_bounds__(256) void k_skinny_finish(GemmArgs p, const float* 
 // second, partial wave of workgroups measured slower: Llama-8B decode
 // QKV 6 ranges / 288 workgroups 19.1 us against 5 / 240 at 13.9 us).
 constexpr int kSkWS = 2;        // W slabs per wavefront: 128 output columns per workgroup
-constexpr int kSkNST = 6;       // ring stages of the 16-row groups (one K range, few column blocks)
 // Ring stages of the 64-row workgroups (M <= 64; 4 for M <= 128): with every
 // CU streaming, three stages (two in flight, 48 KB of weights per CU) are
 // enough and deeper rings only lengthen the memory queues (Llama-8B decode
 // step, weights cycled past the MALL: 2 / 3 / 4 / 6 stages 84.5 / 72.1 /
 // 73.5 / 80.8 us).
 constexpr int kSkNST64 = 3;
+// Two K steps per ring stage, i.e. 256 contiguous bytes of each weight row
+// requested at a time, only pay off for the 16-row groups: Llama-8B decode
+// with one K range, down projection 14336 -> 4096 in 64-column blocks,
+// 35.1 -> 33.0 us (3 stages of 2 steps against 6 of 1; 5 of 1: 34.7 us),
+// while for the 64-row gate+up workgroups they cost 32.7 -> 35.0 us.
+constexpr int kSkKS64 = 1;      // K steps per ring stage of the 64-row workgroups
+constexpr int kSkKS16 = 2;      // ... of the 16-row groups
+constexpr int kSkNST = 3;       // ring stages of the 16-row groups (one K range, few column blocks)
 constexpr int kSkFill = 256;    // workgroups of one wave on MI355X (one per CU: the ring fills LDS)
 constexpr int kSkRowSplitBlocks = 64;   // one K range below this many column blocks: 16-row groups
 constexpr int kSkLongK = 64;            // ... of 64 columns from this many K steps on
@@ -1096,13 +1121,13 @@ size_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return S == 1 ? 0 : (size_t)S * (size_t)M * (size_t)N * sizeof(float);
 }
 
-template <int MT, int NST, int WS, int OUT, bool FUSEQ, bool P2 = false>
+template <int MT, int NST, int WS, int KS, int OUT, bool FUSEQ, bool P2 = false>
 static hipError_t launch_skinny_mt(const GemmArgs& a, float* part, int S, hipStream_t st) {
   if (P2 && S != 1) return hipErrorInvalidValue;   // the power-of-two path runs one K range
   // row groups of MT*16 rows (a split launch covers all rows in one group)
   const int R = (a.M + MT * 16 - 1) / (MT * 16);
   if (S > 1 && R != 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_gemm_fp8_skinny<MT, NST, WS, OUT, FUSEQ, P2>),
+  hipLaunchKernelGGL((k_gemm_fp8_skinny<MT, NST, WS, KS, OUT, FUSEQ, P2>),
                      dim3((unsigned)(a.N / (64 * WS)), (unsigned)S, (unsigned)R), dim3(256), 0, st, a,
                      part, S);
   hipError_t e = hipGetLastError();
@@ -1124,21 +1149,21 @@ template <bool P2>
 static hipError_t launch_skinny_rows16_64(const GemmArgs& a, int out, bool fuseq, hipStream_t st) {
   const dim3 g((unsigned)(a.N / 64), 1u, (unsigned)((a.M + 15) / 16));
   if (out == kOutF32) {
-    hipLaunchKernelGGL((k_gemm_fp8_skinny<1, kSkNST, 1, kOutF32, false, P2>), g, dim3(256), 0, st, a, nullptr, 1);
+    hipLaunchKernelGGL((k_gemm_fp8_skinny<1, kSkNST, 1, kSkKS16, kOutF32, false, P2>), g, dim3(256), 0, st, a, nullptr, 1);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((k_gemm_fp8_skinny<1, kSkNST, 1, kOutBf16, false, P2>), g, dim3(256), 0, st, a, nullptr, 1);
+  hipLaunchKernelGGL((k_gemm_fp8_skinny<1, kSkNST, 1, kSkKS16, kOutBf16, false, P2>), g, dim3(256), 0, st, a, nullptr, 1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !fuseq) return e;
   return launch_quant_1x128(static_cast<const uint16_t*>(a.C), a.M, a.N, a.ldc, a.Cq, a.ldc, a.Cs, st, P2);
 }
 
-template <int MT, int NST, bool P2 = false>
+template <int MT, int NST, int KS, bool P2 = false>
 static hipError_t launch_skinny_out(const GemmArgs& a, int out, bool fuseq, float* part, int S,
                                     hipStream_t st) {
-  if (out == kOutF32) return launch_skinny_mt<MT, NST, kSkWS, kOutF32, false, P2>(a, part, S, st);
-  if (fuseq) return launch_skinny_mt<MT, NST, kSkWS, kOutBf16, true, P2>(a, part, S, st);
-  return launch_skinny_mt<MT, NST, kSkWS, kOutBf16, false, P2>(a, part, S, st);
+  if (out == kOutF32) return launch_skinny_mt<MT, NST, kSkWS, KS, kOutF32, false, P2>(a, part, S, st);
+  if (fuseq) return launch_skinny_mt<MT, NST, kSkWS, KS, kOutBf16, true, P2>(a, part, S, st);
+  return launch_skinny_mt<MT, NST, kSkWS, KS, kOutBf16, false, P2>(a, part, S, st);
 }
 
 hipError_t launch_gemm_skinny(const GemmArgs& a, int out, bool fuseq, void* workspace, hipStream_t st,
@@ -1156,9 +1181,9 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, int out, bool fuseq, void* work
   const bool rows16 = a.N / (64 * kSkWS) < kSkRowSplitBlocks;
   if (p2) {   // one K range: the chain of k_gemm_fp8<..., P2> (no workspace)
     if (rows16 && a.Kc / 128 >= kSkLongK) return launch_skinny_rows16_64<true>(a, out, fuseq, st);
-    if (rows16) return launch_skinny_out<1, kSkNST, true>(a, out, fuseq, nullptr, 1, st);
-    if (a.M <= 64) return launch_skinny_out<4, kSkNST64, true>(a, out, fuseq, nullptr, 1, st);
-    return launch_skinny_out<8, 4, true>(a, out, fuseq, nullptr, 1, st);
+    if (rows16) return launch_skinny_out<1, kSkNST, kSkKS16, true>(a, out, fuseq, nullptr, 1, st);
+    if (a.M <= 64) return launch_skinny_out<4, kSkNST64, kSkKS64, true>(a, out, fuseq, nullptr, 1, st);
+    return launch_skinny_out<8, 4, 1, true>(a, out, fuseq, nullptr, 1, st);
   }
   // unsplit: every output element is the same chain of per-step FMAs, in K
   // order, as in k_gemm_fp8 (bit-identical to the large-M forward)
@@ -1166,9 +1191,9 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, int out, bool fuseq, void* work
   if (S > 1 && workspace == nullptr) return hipErrorInvalidValue;
   float* part = static_cast<float*>(workspace);
   if (S == 1 && rows16 && a.Kc / 128 >= kSkLongK) return launch_skinny_rows16_64<false>(a, out, fuseq, st);
-  if (S == 1 && rows16) return launch_skinny_out<1, kSkNST>(a, out, fuseq, part, 1, st);
-  if (a.M <= 64) return launch_skinny_out<4, kSkNST64>(a, out, fuseq, part, S, st);
-  return launch_skinny_out<8, 4>(a, out, fuseq, part, S, st);
+  if (S == 1 && rows16) return launch_skinny_out<1, kSkNST, kSkKS16>(a, out, fuseq, part, 1, st);
+  if (a.M <= 64) return launch_skinny_out<4, kSkNST64, kSkKS64>(a, out, fuseq, part, S, st);
+  return launch_skinny_out<8, 4, 1>(a, out, fuseq, part, S, st);
 }
 
 // Grouped GEMMs use the 256 x 256 tile too: measured on the Qwen3-30B-A3B

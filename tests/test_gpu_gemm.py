@@ -533,6 +533,36 @@ def test_batch_invariant_forward_matches_training_batch(gpu_lib, name):
     print(f"{name}: " + "; ".join(report))
 
 
+@pytest.mark.parametrize("K", [384, 1152, 8320])
+def test_batch_invariant_forward_odd_k_steps(gpu_lib, K):
+    """The 16-row weight-streaming groups load two K steps per ring stage; an
+    odd number of K steps (3, 9, and 65 on the 64-column path for long
+    contractions) leaves a last stage with one step.  Rows of the
+    batch-invariant forward at M = 1, 16 and 37 still equal those of the
+    training-sized batch bit for bit, and the result meets the GEMM
+    tolerance against the oracle."""
+    N, Mb = 256, 512
+    x = inputs.activations_with_outliers(Mb, K, seed=K)
+    w = inputs.normal_bf16((N, K), 0.02, seed=K, tensor_id=inputs.ID_W)
+    xq, xs = gpu_lib.jet_quant_act_1x128(dev_bf16(x))
+    wq, ws, _ = gpu_lib.jet_quant_weight_128x128(dev_bf16(w), transposed=False)
+    yb, yqb, ysb = gpu_lib.jet_fp8_linear_fwd(xq, xs, wq, ws, fuse_quant=True)
+    y32b = gpu_lib.jet_fp8_linear_fwd(xq, xs, wq, ws, out_dtype=torch.float32)
+    for M, r0 in ((1, 3), (16, 40), (37, 300)):
+        rows = slice(r0, r0 + M)
+        xq_s, xs_s = xq[rows].contiguous(), xs[:, rows].contiguous()
+        y, yq, ys = gpu_lib.jet_fp8_linear_fwd_batch_invariant(xq_s, xs_s, wq, ws, fuse_quant=True)
+        y32 = gpu_lib.jet_fp8_linear_fwd_batch_invariant(xq_s, xs_s, wq, ws, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        tag = f"K={K} M={M}"
+        assert torch.equal(y, yb[rows]), f"{tag}: BF16 rows differ from the training batch"
+        assert torch.equal(yq, yqb[rows]) and torch.equal(ys, ysb[:, rows]), f"{tag}: fused codes differ"
+        assert torch.equal(y32, y32b[rows]), f"{tag}: FP32 rows differ from the training batch"
+        a = O.dequant_1x128(host(xq_s), host(xs_s))
+        b = O.dequant_128x128(host(wq), host(ws))
+        check_f32_output(host(y32), a @ b.T, oracle_absprod(a, b), f"invariant fwd f32 {tag}")
+
+
 @pytest.mark.parametrize("pow2", [False, True])
 def test_empty_batch_every_entry_point(gpu_lib, pow2):
     """M = 0 tokens (an empty rollout or micro-batch): every quantizer and GEMM
