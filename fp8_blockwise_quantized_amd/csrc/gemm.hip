@@ -720,24 +720,91 @@ static int cu_count() {
   return cached[dev];
 }
 
+// The output columns [n1, N), or rows [m1, M), of a GEMM as a GEMM of its own.
+static GemmArgs column_part(const GemmArgs& a, int mode, int out, bool fuseq, int n1) {
+  GemmArgs b = a;
+  b.B += (int64_t)n1 * a.ldb;
+  b.sB += (mode == kRowBlock) ? (int64_t)(n1 / 128) * a.sB_o : (int64_t)n1;
+  b.C = static_cast<uint8_t*>(a.C) + (int64_t)n1 * (out == kOutF32 ? 4 : 2);
+  if (fuseq) {
+    b.Cq += n1;
+    b.Cs += (int64_t)(n1 / 128) * a.ldcs;
+  }
+  b.N = a.N - n1;
+  return b;
+}
+
+static GemmArgs row_part(const GemmArgs& a, int out, bool fuseq, int m1) {
+  GemmArgs b = a;
+  b.A += (int64_t)m1 * a.lda;
+  b.sA += m1;
+  b.C = static_cast<uint8_t*>(a.C) + (int64_t)m1 * a.ldc * (out == kOutF32 ? 4 : 2);
+  if (fuseq) {
+    b.Cq += (int64_t)m1 * a.ldc;
+    b.Cs += m1;
+  }
+  b.M = a.M - m1;
+  return b;
+}
+
+template <class CFG>
+static hipError_t dispatch_p2(const GemmArgs& a, int mode, int out, bool accum, bool fuseq, hipStream_t st,
+                              bool p2) {
+  return p2 ? dispatch<CFG, kGrpNone, true>(a, mode, out, accum, fuseq, st)
+            : dispatch<CFG>(a, mode, out, accum, fuseq, st);
+}
+
 hipError_t launch_gemm(const GemmArgs& a, int mode, int out, bool accum, bool fuseq,
                        hipStream_t st, bool p2) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
-  // The big tile keeps the most work per byte staged; use it unless its
-  // grid fills less than 85 % of its waves of workgroups (the small tile
-  // runs at about 85 % of the big tile's rate, so below that the idle CUs of
-  // the big tile's last wave cost more).
-  const int64_t tiles = (int64_t)((a.M + CfgMain::BM - 1) / CfgMain::BM) *
-                        (int64_t)((a.N + CfgMain::BN - 1) / CfgMain::BN);
+  constexpr int BM = CfgMain::BM, BN = CfgMain::BN;
+  const int64_t nbm = (a.M + BM - 1) / BM, nbn = (a.N + BN - 1) / BN;
+  const int64_t tiles = nbm * nbn;
   const int64_t cus = cu_count();
+  // A grid of big tiles that ends in a partial wave: the most whole tile
+  // columns (or rows) whose big tiles fill whole waves, then the rest of the
+  // output in small tiles, when those fit one wave of small workgroups
+  // (CfgSmall::OCC per CU).  Every element is the same chain in either tile,
+  // so the bits do not change.  (Llama-8B at M = 8192: wgrad of the down
+  // projection, 16 x 56 big tiles = 3.5 waves, becomes 16 x 48 big tiles and
+  // one wave of 512 small ones; wgrad of QKV, 24 x 16, becomes 16 x 16 and
+  // 512 small ones instead of 1536 small ones.)
+  if (tiles % cus != 0) {
+    int64_t c1 = 0, r1 = 0;
+    if (a.N % BN == 0)
+      for (int64_t c = nbn - 1; c > 0 && !c1; --c)
+        if ((nbm * c) % cus == 0) c1 = c;
+    if (a.M % BM == 0)
+      for (int64_t r = nbm - 1; r > 0 && !r1; --r)
+        if ((nbn * r) % cus == 0) r1 = r;
+    const auto small_tiles = [](int64_t m, int64_t n) {
+      return ((m + CfgSmall::BM - 1) / CfgSmall::BM) * ((n + CfgSmall::BN - 1) / CfgSmall::BN);
+    };
+    const bool col_ok = c1 > 0 && small_tiles(a.M, a.N - c1 * BN) <= cus * CfgSmall::OCC;
+    const bool row_ok = r1 > 0 && small_tiles(a.M - r1 * BM, a.N) <= cus * CfgSmall::OCC;
+    if (col_ok && (!row_ok || nbm * c1 >= nbn * r1)) {
+      GemmArgs head = a;
+      head.N = (int)(c1 * BN);
+      hipError_t e = dispatch_p2<CfgMain>(head, mode, out, accum, fuseq, st, p2);
+      if (e != hipSuccess) return e;
+      return dispatch_p2<CfgSmall>(column_part(a, mode, out, fuseq, head.N), mode, out, accum, fuseq, st, p2);
+    }
+    if (row_ok) {
+      GemmArgs head = a;
+      head.M = (int)(r1 * BM);
+      hipError_t e = dispatch_p2<CfgMain>(head, mode, out, accum, fuseq, st, p2);
+      if (e != hipSuccess) return e;
+      return dispatch_p2<CfgSmall>(row_part(a, out, fuseq, head.M), mode, out, accum, fuseq, st, p2);
+    }
+  }
+  // Otherwise the big tile, which keeps the most work per byte staged,
+  // unless its grid fills less than 85 % of its waves of workgroups (the
+  // small tile runs at about 85 % of the big tile's rate, so below that the
+  // idle CUs of the big tile's last wave cost more).
   const int64_t slots = (tiles + cus - 1) / cus * cus;
   const bool big = tiles * 100 >= slots * 85;
-  if (p2) {
-    if (big) return dispatch<CfgMain, kGrpNone, true>(a, mode, out, accum, fuseq, st);
-    return dispatch<CfgSmall, kGrpNone, true>(a, mode, out, accum, fuseq, st);
-  }
-  if (big) return dispatch<CfgMain>(a, mode, out, accum, fuseq, st);
-  return dispatch<CfgSmall>(a, mode, out, accum, fuseq, st);
+  if (big) return dispatch_p2<CfgMain>(a, mode, out, accum, fuseq, st, p2);
+  return dispatch_p2<CfgSmall>(a, mode, out, accum, fuseq, st, p2);
 }
 
 // ---------------------------------------------------------------------------

@@ -15,6 +15,7 @@ import pytest
 import torch
 
 from oracle import jet_oracle as O
+from oracle import pow2_scales as P
 from fp8_blockwise_quantized_amd import inputs
 from tests.gpu_helpers import (assert_bits_equal, check_bf16_output, check_f32_output, dev_bf16,
                                host, oracle_absprod)
@@ -430,6 +431,61 @@ def test_training_shapes_sampled(gpu_lib, name):
     a = O.dequant_128x1_T(host(dyqT[nidx]), host(dysT[:, nidx]), M)
     b = O.dequant_128x1_T(host(xqT), host(xsT), M)
     check_f32_output(host(dw[nidx]), a @ b.T, oracle_absprod(a, b), f"wgrad {name}")
+
+
+# --- grids of big tiles that end in a partial wave ----------------------------
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_partial_wave_split_gemms(gpu_lib, pow2):
+    """A 4096-token layer 4096 -> 4352 on 256 CUs: the forward's 16 x 17 grid
+    of 256 x 256 tiles runs as 16 x 16 big tiles plus the last 256 output
+    columns in 128 x 128 tiles; wgrad's 17 x 16 grid as 16 x 16 big tiles
+    plus the last 256 output rows in small ones.  BF16 forward with its fused
+    1x128 output, FP32 forward and FP32 wgrad (also accumulating) against
+    the oracle on sampled rows, half of them in the split-off part."""
+    J = gpu_lib
+    M, N, K = 4096, 4352, 4096
+    x, w, dy = layer_inputs(M, N, K, 3)
+    xd, wd, dyd = dev_bf16(x), dev_bf16(w), dev_bf16(dy)
+    if pow2:
+        xq, xs, xqT, xsT = J.jet_quant_act_1x128_128x1_T_pow2(xd, True)
+        dyq, dys, dyqT, dysT = J.jet_quant_act_1x128_128x1_T_pow2(dyd, False)
+        wq, ws, wqT = J.jet_quant_weight_128x128_pow2(wd)
+        fwd, wgrad = J.jet_fp8_linear_fwd_pow2, J.jet_fp8_linear_wgrad_pow2
+    else:
+        xq, xs, xqT, xsT = J.jet_quant_act_1x128_128x1_T(xd, True)
+        dyq, dys, dyqT, dysT = J.jet_quant_act_1x128_128x1_T(dyd, False)
+        wq, ws, wqT = J.jet_quant_weight_128x128(wd)
+        fwd, wgrad = J.jet_fp8_linear_fwd, J.jet_fp8_linear_wgrad
+    y, yq, ys = fwd(xq, xs, wq, ws, fuse_quant=True)
+    y32 = fwd(xq, xs, wq, ws, out_dtype=torch.float32)
+    dw = wgrad(dyqT, dysT, xqT, xsT, M)
+    dw2 = dw.clone()
+    wgrad(dyqT, dysT, xqT, xsT, M, dw=dw2, accumulate=True)
+    torch.cuda.synchronize()
+    del xd, wd, dyd
+    rng = np.random.default_rng(9)
+    rows = np.sort(rng.choice(M, 32, replace=False))
+    ridx = torch.from_numpy(rows).cuda()
+    bw = O.dequant_128x128(host(wq), host(ws))
+    ax = O.dequant_1x128(host(xq[ridx]), host(xs[:, ridx]))
+    ref, absp = ax @ bw.T, oracle_absprod(ax, bw)
+    tag = "pow2" if pow2 else "fp32 scales"
+    check_bf16_output(host(y[ridx]), ref, absp, f"split fwd bf16 {tag}")
+    check_f32_output(host(y32[ridx]), ref, absp, f"split fwd f32 {tag}")
+    quant = P.quant_1x128_pow2 if pow2 else O.quant_1x128
+    qo, so = quant(host(y[ridx]))
+    assert_bits_equal(host(yq[ridx]), qo, f"split fused codes {tag}")
+    assert_bits_equal(host(ys[:, ridx]), so, f"split fused scales {tag}")
+    del bw
+    nrows = np.sort(np.concatenate([rng.choice(4096, 16, replace=False),
+                                    4096 + rng.choice(N - 4096, 16, replace=False)]))
+    nidx = torch.from_numpy(nrows).cuda()
+    a = O.dequant_128x1_T(host(dyqT[nidx]), host(dysT[:, nidx]), M)
+    b = O.dequant_128x1_T(host(xqT), host(xsT), M)
+    ref, absp = a @ b.T, oracle_absprod(a, b)
+    check_f32_output(host(dw[nidx]), ref, absp, f"split wgrad {tag}")
+    check_f32_output(host(dw2[nidx]), 2 * ref, 2 * absp, f"split wgrad accumulate {tag}")
 
 
 # --- Qwen-14B/32B shapes at M=16384 (sampled) ---------------------------------
