@@ -244,15 +244,6 @@ __device__ __forceinline__ void tile_of_block(int nbm, int nbn, int& tm, int& tn
 
 }  // namespace
 
-// Row-grouped grids are rounded up to a multiple of the 8 XCDs; renumber so
-// each XCD takes a contiguous range of row tiles (equal work per tile, and a
-// segment's rows share an L2).
-__device__ __forceinline__ int xcd_slot() {
-  constexpr int kXcds = 8;
-  const int g = (int)gridDim.x, b = (int)blockIdx.x;
-  return (g % kXcds == 0) ? (b % kXcds) * (g / kXcds) + b / kXcds : b;
-}
-
 template <class CFG, int MODE, int OUT, bool ACCUM, bool FUSEQ, int GRP, bool P2>
 __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa) {
   constexpr int TM = CFG::TM, TN = CFG::TN, BM = CFG::BM, BN = CFG::BN;
@@ -272,9 +263,18 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
   if constexpr (GRP == kGrpNone) {
     tile_of_block((p.M + BM - 1) / BM, (p.N + BN - 1) / BN, tm, tn);
   } else if constexpr (GRP == kGrpRows) {
-    // slot = (row tile of the concatenated segments) x (column tile)
+    // tile = (row tile of the concatenated segments) x (column tile), row
+    // major.  The grid (a multiple of the 8 XCDs) bounds the tiles from the
+    // row count; XCD b%8 takes its contiguous eighth of the tiles that exist
+    // (so the segments' rounding leaves no XCD idle while another has twice
+    // its share), workgroup b/8 of the XCD its (b/8)-th tile.
+    constexpr int kXcds = 8;
     const int nbn = (p.N + BN - 1) / BN;
-    const int slot = xcd_slot();
+    const int total = seg_total(p.seg, p.E, p.seg_rows, BM) * nbn;
+    const int per = (total + kXcds - 1) / kXcds;
+    const int i = (int)blockIdx.x / kXcds;
+    const int slot = ((int)blockIdx.x % kXcds) * per + i;
+    if (i >= per || slot >= total) return;
     const int r = slot / nbn;
     tn = slot - r * nbn;
     tm = 0;

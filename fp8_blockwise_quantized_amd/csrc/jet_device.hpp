@@ -214,6 +214,23 @@ struct SegHit {
   int lo, hi;  // its rows [lo, hi)
 };
 
+// Slots over all segments: the sum of ceil(rows of segment e / unit).
+__device__ __forceinline__ int seg_total(const int32_t* seg, int E, int rows, int unit) {
+  const int lane = threadIdx.x & 63;
+  int sum = 0;
+  for (int c = 0; c < E; c += 64) {
+    const int e = c + lane;
+    if (e < E) {
+      const int lo = min(max(seg[e], 0), rows);
+      const int hi = min(max(seg[e + 1], lo), rows);
+      sum += (hi - lo + unit - 1) / unit;
+    }
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) sum += __shfl_xor(sum, d, 64);
+  return __builtin_amdgcn_readfirstlane(sum);
+}
+
 // by_e = false: the segment owning slot `target`; by_e = true: segment `target`.
 __device__ __forceinline__ SegHit seg_find(const int32_t* seg, int E, int rows, int unit,
                                            int target, bool by_e) {
