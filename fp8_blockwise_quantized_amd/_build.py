@@ -22,6 +22,9 @@ SOURCES = ["abi.hip", "quant.hip", "fused.hip", "kvcache.hip", "gemm.hip"]
 HOSTSAN_LIB = os.path.join(LIBDIR, "libjetfp8_hostsan.so")
 HOSTSAN_FLAGS = ("-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined "
                  "-Xarch_host -fno-sanitize-recover=all -Xarch_host -fno-omit-frame-pointer").split()
+# Diagnostic build: the same library with the GEMM kernel's phase timing
+# compiled in (include/jetphase.h), read by phase_timing.py.
+PHASE_LIB = os.path.join(LIBDIR, "libjetfp8_phase.so")
 # Roofline probes used by the benchmark only (include/jetprobe.h): a library of their own.
 PROBE_LIB = os.path.join(LIBDIR, "libjetprobe.so")
 PROBE_SOURCES = ["probes.hip"]
@@ -49,7 +52,7 @@ def hipcc() -> str:
 def build(verbose: bool = False) -> str:
     os.makedirs(LIBDIR, exist_ok=True)
     # never leave a library built from older sources behind a failed build
-    for lib in (LIB, PROBE_LIB, HOSTSAN_LIB):
+    for lib in (LIB, PROBE_LIB, HOSTSAN_LIB, PHASE_LIB):
         if os.path.exists(lib):
             os.remove(lib)
     objdir = os.path.join(PKG, "_build")
@@ -57,8 +60,11 @@ def build(verbose: bool = False) -> str:
     cc = hipcc()
 
     def compile_one(src: str) -> str:
-        obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        cmd = [cc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        extra = []
+        if src.endswith("#phase"):
+            src, extra = src[:-len("#phase")], ["-DJET_PHASE_TIMING=1"]
+        obj = os.path.join(objdir, src.replace(".hip", "_phase.o" if extra else ".o"))
+        cmd = [cc, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
@@ -66,8 +72,9 @@ def build(verbose: bool = False) -> str:
             raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
         return obj
 
-    with ThreadPoolExecutor(max_workers=len(SOURCES) + len(PROBE_SOURCES)) as ex:
-        objs = list(ex.map(compile_one, SOURCES + PROBE_SOURCES))
+    with ThreadPoolExecutor(max_workers=len(SOURCES) + len(PROBE_SOURCES) + 1) as ex:
+        objs = list(ex.map(compile_one, SOURCES + PROBE_SOURCES + ["gemm.hip#phase"]))
+    phase_obj = objs.pop()
     # the ABI object again with host sanitizers, linked with the same kernel objects
     san_obj = os.path.join(objdir, "abi_hostsan.o")
     flags = [f for f in FLAGS if f != "-O3"] + ["-O1", "-g", *HOSTSAN_FLAGS]
@@ -76,8 +83,9 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on abi.hip (host sanitizers):\n{r.stdout}\n{r.stderr}")
     san_objs = [san_obj if os.path.basename(o) == "abi.o" else o for o in objs[:len(SOURCES)]]
+    phase_objs = [phase_obj if os.path.basename(o) == "gemm.o" else o for o in objs[:len(SOURCES)]]
     for lib, lib_objs in ((LIB, objs[:len(SOURCES)]), (PROBE_LIB, objs[len(SOURCES):]),
-                          (HOSTSAN_LIB, san_objs)):
+                          (HOSTSAN_LIB, san_objs), (PHASE_LIB, phase_objs)):
         tmp = lib + ".tmp"
         cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *lib_objs]
         r = subprocess.run(cmd, capture_output=True, text=True)

@@ -61,8 +61,39 @@
 // and four adjacent columns.
 #include "jet_device.hpp"
 #include "jet_launch.hpp"
+#if JET_PHASE_TIMING
+#include "../../include/jetphase.h"
+#endif
 
 namespace jet {
+
+#if JET_PHASE_TIMING
+// Phase timing, compiled only into the diagnostic build libjetfp8_phase.so
+// (include/jetphase.h): while the flag is non-zero, thread 0 of workgroup b
+// < kPhaseBlocks of k_gemm_fp8 records in record b: the constant-rate wall
+// counter at its entry, before its first DMA, after its K loop and at its
+// exit; its hardware ids; and the shader-clock counter before and after the
+// K loop.
+constexpr int kPhaseBlocks = 16384;
+__device__ unsigned long long g_phase[kPhaseBlocks * 8];
+__device__ int g_phase_on;
+struct PhaseRec {
+  unsigned long long t0, t1 = 0, t2 = 0, c1 = 0, c2 = 0;
+  __device__ PhaseRec() : t0(wall_clock64()) {}
+  __device__ void loop_start() { t1 = wall_clock64(); c1 = clock64(); }
+  __device__ void loop_end() { t2 = wall_clock64(); c2 = clock64(); }
+  __device__ ~PhaseRec() {
+    if (g_phase_on && threadIdx.x == 0 && blockIdx.x < kPhaseBlocks) {
+      unsigned long long* r = g_phase + 8 * blockIdx.x;
+      r[0] = t0; r[1] = t1; r[2] = t2; r[3] = wall_clock64();
+      r[4] = (unsigned long long)__builtin_amdgcn_s_getreg(63492) |     // HW_REG_HW_ID
+             ((unsigned long long)__builtin_amdgcn_s_getreg(63508) << 32);   // HW_REG_XCC_ID
+      r[5] = gridDim.x | ((unsigned long long)blockDim.x << 32);
+      r[6] = c1; r[7] = c2;
+    }
+  }
+};
+#endif
 
 template <int WMW_, int WNW_, int TM_, int TN_, int STAGES_, bool FRAG_, int OCC_ = 1>
 struct GemmCfg {
@@ -250,6 +281,9 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
   constexpr bool FRAG = CFG::FRAG;
   constexpr int64_t kOutBytes = (OUT == kOutF32) ? 4 : 2;
   __shared__ __attribute__((aligned(16))) uint8_t lds[CFG::LDS];
+#if JET_PHASE_TIMING
+  PhaseRec phase;
+#endif
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -457,6 +491,9 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
   constexpr int LAG = 3;
 
   constexpr int D = CFG::STAGES - 1;   // prefetch distance in K steps
+#if JET_PHASE_TIMING
+  phase.loop_start();
+#endif
 #pragma unroll
   for (int s = 0; s < D; ++s)
     if (s < KB) {
@@ -558,6 +595,9 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
   };
   for (; kb < KB - D; ++kb) step(BoolC<true>{});
   for (; kb < KB; ++kb) step(BoolC<false>{});
+#if JET_PHASE_TIMING
+  phase.loop_end();
+#endif
 #undef JET_ISSUE
 
   // ---- epilogue ----
@@ -1284,3 +1324,13 @@ hipError_t launch_gemm_grouped(const GemmArgs& a, int grp, int mode, int out, bo
 }
 
 }  // namespace jet
+
+#if JET_PHASE_TIMING
+extern "C" int jet_phase_buffers(void** records, void** flag, int* capacity) {
+  if (!records || !flag || !capacity) return 1;
+  if (hipGetSymbolAddress(records, HIP_SYMBOL(jet::g_phase)) != hipSuccess) return 2;
+  if (hipGetSymbolAddress(flag, HIP_SYMBOL(jet::g_phase_on)) != hipSuccess) return 2;
+  *capacity = jet::kPhaseBlocks;
+  return 0;
+}
+#endif

@@ -54,6 +54,19 @@ def test_probe_library_exports_its_header():
     assert names <= set(re.findall(r"\bT (jet_probe_\w+)", out))
 
 
+def test_phase_timing_build_exports():
+    """The diagnostic build (include/jetphase.h) exports the whole ABI plus
+    jet_phase_buffers; the ordinary library carries no phase timing."""
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "jetphase.h")).read(), flags=re.S)
+    assert set(re.findall(r"\b(jet_\w+)\s*\(", text)) == {"jet_phase_buffers"}
+    lib_dir = os.path.join(ROOT, "fp8_blockwise_quantized_amd", "lib")
+    nm = lambda name: set(re.findall(r"\bT (jet_\w+)", subprocess.run(
+        ["nm", "-D", "--defined-only", os.path.join(lib_dir, name)], capture_output=True, text=True).stdout))
+    phase, plain = nm("libjetfp8_phase.so"), nm("libjetfp8.so")
+    assert set(declared_functions()) | {"jet_phase_buffers"} <= phase
+    assert "jet_phase_buffers" not in plain
+
+
 def test_binding_covers_header(J):
     assert set(J.SIGNATURES) == set(declared_functions())
 
