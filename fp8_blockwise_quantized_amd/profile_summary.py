@@ -46,9 +46,9 @@ def kind(name: str) -> str:
             k = "dgrad/fwd (bf16)" if out == "0" else "fwd/dgrad (f32)"
         g = {"0": "", "1": "grouped-rows ", "2": "grouped-contraction "}[grp]
         return f"gemm {g}{k} {tile}{' P2' if p2 == 'true' else ''}{' accumulate' if acc == 'true' else ''}"
-    m = re.search(r"k_gemm_fp8_skinny<(\d+), (\d+), (\d+), (\d+), (\w+), (\w+)>", name)
+    m = re.search(r"k_gemm_fp8_skinny<(\d+), (\d+), (\d+), (\d+), (\d+), (\w+), (\w+)>", name)
     if m:
-        mt, nst, ws, out, fq, p2 = m.groups()
+        mt, nst, ws, ks, out, fq, p2 = m.groups()
         return f"gemm small-M forward ({int(mt) * 16}-row groups){' P2' if p2 == 'true' else ''}"
     m = re.search(r"\b(k_\w+)(<[^(]*>)?\(", name)
     if m:
