@@ -327,18 +327,21 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
     p.B += (int64_t)e * p.bE;
     p.sB += (int64_t)e * p.sbE;
   } else {
-    // slot = (expert) x (output tile); expert e contracts over its padded
-    // columns.  Slots keep the hardware's round-robin deal to the XCDs: with
-    // a multiple of 8 tiles per expert every XCD gets an equal share of every
-    // expert, however unequal the segments (a contiguous range of experts
-    // per XCD leaves the XCD with the largest experts doing twice the mean
-    // work under a Zipf load), and the XCDs work on the same experts at the
-    // same time, so their L2 refills of an expert's operands meet in the MALL.
+    // slot = (expert position) x (output tile); an expert contracts over its
+    // padded columns.  Slots keep the hardware's round-robin deal to the
+    // XCDs: with a multiple of 8 tiles per expert every XCD gets an equal
+    // share of every expert, however unequal the segments (a contiguous
+    // range of experts per XCD leaves the XCD with the largest experts doing
+    // twice the mean work under a Zipf load), and the XCDs work on the same
+    // experts at the same time, so their L2 refills of an expert's operands
+    // meet in the MALL.  Experts are taken longest contraction first (up to
+    // 128 experts; beyond that in index order), so the last workgroups to
+    // start are the shortest and the CUs run out of work together.
     const int nbm = (p.M + BM - 1) / BM, nbn = (p.N + BN - 1) / BN;
     const int slot = (int)blockIdx.x;
-    const int e = slot / (nbm * nbn);
-    if (e >= p.E) return;
-    const int local = slot - e * (nbm * nbn);
+    const int q = slot / (nbm * nbn);
+    if (q >= p.E) return;
+    const int local = slot - q * (nbm * nbn);
     tm = local / nbn;
     tn = local - tm * nbn;
     // With a multiple of 8 tiles per expert, XCD slot%8 takes one block of a
@@ -359,7 +362,10 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::OCC) void k_gemm_fp8(GemmArgs pa
         tn = (xcd % gx) * cols + idx / rows;
       }
     }
-    const SegHit h = seg_find(p.seg, p.E, p.seg_rows, 128, e, true);
+    const SegHit h = (p.E <= 128) ? seg_by_size_128(p.seg, p.E, p.seg_rows, 128, q)
+                                  : seg_find(p.seg, p.E, p.seg_rows, 128, q, true);
+    const int e = __builtin_amdgcn_readfirstlane(h.e);
+    if (e < 0) return;
     const int first = __builtin_amdgcn_readfirstlane(h.first);
     const int groups = __builtin_amdgcn_readfirstlane((h.hi - h.lo + 127) / 128);
     const int c0 = min(first * 128, p.kcap);

@@ -231,6 +231,70 @@ __device__ __forceinline__ int seg_total(const int32_t* seg, int E, int rows, in
   return __builtin_amdgcn_readfirstlane(sum);
 }
 
+// At most 128 segments: the segment at position q (0 <= q < E) when they are
+// ordered by slot count, largest first, equal counts by index; `first` is its
+// first slot in index order, as for seg_find.  Lane l holds segments l and
+// l + 64; every offset is loaded in one round.
+__device__ __forceinline__ SegHit seg_by_size_128(const int32_t* seg, int E, int rows, int unit, int q) {
+  const int lane = threadIdx.x & 63;
+  int o[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = lane + 64 * (k >> 1) + (k & 1);
+    o[k] = (i <= E) ? seg[i] : 0;
+  }
+  int lo[2], hi[2], cnt[2], excl[2];
+  bool in[2];
+  int base = 0, top = 0;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    in[h] = lane + 64 * h < E;
+    lo[h] = in[h] ? min(max(o[2 * h], 0), rows) : 0;
+    hi[h] = in[h] ? min(max(o[2 * h + 1], lo[h]), rows) : 0;
+    cnt[h] = (hi[h] - lo[h] + unit - 1) / unit;
+    int incl = cnt[h];
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += v;
+    }
+    excl[h] = base + incl - cnt[h];
+    base += __shfl(incl, 63, 64);
+    top = max(top, cnt[h]);
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) top = max(top, __shfl_xor(top, d, 64));
+  top = __builtin_amdgcn_readfirstlane(top);
+  // segments with at least t slots
+  auto count_ge = [&](int t) {
+    return __popcll(__ballot(in[0] && cnt[0] >= t)) + __popcll(__ballot(in[1] && cnt[1] >= t));
+  };
+  // the largest count T with more than q segments at or above it
+  int T = 0;
+  for (int b = 31 - __clz(max(top, 1)); b >= 0; --b)
+    if (count_ge(T | (1 << b)) > q) T |= 1 << b;
+  // the n-th segment (by index) among those with exactly T slots
+  int n = q - count_ge(T + 1);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const unsigned long long m = __ballot(in[h] && cnt[h] == T);
+    const int c = __popcll(m);
+    if (n < c) {
+      const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+      const unsigned long long w = __ballot(((m >> lane) & 1ull) && below == n);
+      const int l = __ffsll((long long)w) - 1;
+      SegHit s;
+      s.e = 64 * h + l;
+      s.first = __shfl(excl[h], l, 64);
+      s.lo = __shfl(lo[h], l, 64);
+      s.hi = __shfl(hi[h], l, 64);
+      return s;
+    }
+    n -= c;
+  }
+  return SegHit{-1, 0, 0, 0};
+}
+
 // by_e = false: the segment owning slot `target`; by_e = true: segment `target`.
 __device__ __forceinline__ SegHit seg_find(const int32_t* seg, int E, int rows, int unit,
                                            int target, bool by_e) {
