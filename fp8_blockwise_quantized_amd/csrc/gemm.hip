@@ -807,48 +807,61 @@ hipError_t launch_gemm(const GemmArgs& a, int mode, int out, bool accum, bool fu
   const int64_t nbm = (a.M + BM - 1) / BM, nbn = (a.N + BN - 1) / BN;
   const int64_t tiles = nbm * nbn;
   const int64_t cus = cu_count();
-  // A grid of big tiles that ends in a partial wave: the most whole tile
-  // columns (or rows) whose big tiles fill whole waves, then the rest of the
-  // output in small tiles, when those fit one wave of small workgroups
-  // (CfgSmall::OCC per CU).  Every element is the same chain in either tile,
-  // so the bits do not change.  (Llama-8B at M = 8192: wgrad of the down
-  // projection, 16 x 56 big tiles = 3.5 waves, becomes 16 x 48 big tiles and
-  // one wave of 512 small ones; wgrad of QKV, 24 x 16, becomes 16 x 16 and
-  // 512 small ones instead of 1536 small ones.)
-  if (tiles % cus != 0) {
-    int64_t c1 = 0, r1 = 0;
-    if (a.N % BN == 0)
-      for (int64_t c = nbn - 1; c > 0 && !c1; --c)
-        if ((nbm * c) % cus == 0) c1 = c;
-    if (a.M % BM == 0)
-      for (int64_t r = nbm - 1; r > 0 && !r1; --r)
-        if ((nbn * r) % cus == 0) r1 = r;
-    const auto small_tiles = [](int64_t m, int64_t n) {
-      return ((m + CfgSmall::BM - 1) / CfgSmall::BM) * ((n + CfgSmall::BN - 1) / CfgSmall::BN);
-    };
-    const bool col_ok = c1 > 0 && small_tiles(a.M, a.N - c1 * BN) <= cus * CfgSmall::OCC;
-    const bool row_ok = r1 > 0 && small_tiles(a.M - r1 * BM, a.N) <= cus * CfgSmall::OCC;
-    if (col_ok && (!row_ok || nbm * c1 >= nbn * r1)) {
-      GemmArgs head = a;
-      head.N = (int)(c1 * BN);
-      hipError_t e = dispatch_p2<CfgMain>(head, mode, out, accum, fuseq, st, p2);
-      if (e != hipSuccess) return e;
-      return dispatch_p2<CfgSmall>(column_part(a, mode, out, fuseq, head.N), mode, out, accum, fuseq, st, p2);
-    }
-    if (row_ok) {
-      GemmArgs head = a;
-      head.M = (int)(r1 * BM);
-      hipError_t e = dispatch_p2<CfgMain>(head, mode, out, accum, fuseq, st, p2);
-      if (e != hipSuccess) return e;
-      return dispatch_p2<CfgSmall>(row_part(a, out, fuseq, head.M), mode, out, accum, fuseq, st, p2);
-    }
-  }
-  // Otherwise the big tile, which keeps the most work per byte staged,
-  // unless its grid fills less than 85 % of its waves of workgroups (the
-  // small tile runs at about 85 % of the big tile's rate, so below that the
-  // idle CUs of the big tile's last wave cost more).
+  const auto small_tiles = [](int64_t m, int64_t n) {
+    return ((m + CfgSmall::BM - 1) / CfgSmall::BM) * ((n + CfgSmall::BN - 1) / CfgSmall::BN);
+  };
+  // Time of a launch plan in waves of big tiles: whole waves of big tiles
+  // (one per CU), then whole waves of small ones (CfgSmall::OCC per CU); a
+  // wave of small tiles takes about 0.59 of a big one (a quarter of the
+  // work at about 85 % of the big tile's rate, two workgroups sharing a CU).
+  constexpr double kSmallWave = 0.59;
+  const auto plan = [&](int64_t big, int64_t small) {
+    return (double)((big + cus - 1) / cus) +
+           kSmallWave * (double)((small + cus * CfgSmall::OCC - 1) / (cus * CfgSmall::OCC));
+  };
+  // One tile for the whole output: the big tile, which keeps the most work
+  // per byte staged, unless its grid fills less than 85 % of its waves of
+  // workgroups (measured: below that the idle CUs of the big tile's last wave
+  // cost more than the small tile's lower rate).
   const int64_t slots = (tiles + cus - 1) / cus * cus;
   const bool big = tiles * 100 >= slots * 85;
+  double best = big ? plan(tiles, 0) : plan(0, small_tiles(a.M, a.N));
+  // A grid whose big tiles end in a partial wave may instead run its first
+  // c1 tile columns (or r1 tile rows) in big tiles and the rest of the
+  // output in small ones, as two launches, when that plan is shorter.  Every
+  // element is the same chain in either tile, so the bits do not change.
+  // (Llama-8B at M = 8192: wgrad of the down projection, 16 x 56 big tiles =
+  // 3.5 waves, becomes 16 x 48 big tiles and one wave of 512 small ones;
+  // wgrad of QKV, 24 x 16, becomes 16 x 16 and 512 small ones instead of 1536
+  // small ones.)
+  // (Among equal plans the most big tiles: their waves are the fullest.)
+  int64_t c1 = 0, r1 = 0;
+  if (tiles % cus != 0) {
+    if (a.N % BN == 0)
+      for (int64_t c = nbn - 1; c > 0; --c) {
+        const double t = plan(nbm * c, small_tiles(a.M, a.N - c * BN));
+        if (t < best - 1e-9) { best = t; c1 = c; r1 = 0; }
+      }
+    if (a.M % BM == 0)
+      for (int64_t r = nbm - 1; r > 0; --r) {
+        const double t = plan(r * nbn, small_tiles(a.M - r * BM, a.N));
+        if (t < best - 1e-9) { best = t; r1 = r; c1 = 0; }
+      }
+  }
+  if (c1 > 0) {
+    GemmArgs head = a;
+    head.N = (int)(c1 * BN);
+    hipError_t e = dispatch_p2<CfgMain>(head, mode, out, accum, fuseq, st, p2);
+    if (e != hipSuccess) return e;
+    return dispatch_p2<CfgSmall>(column_part(a, mode, out, fuseq, head.N), mode, out, accum, fuseq, st, p2);
+  }
+  if (r1 > 0) {
+    GemmArgs head = a;
+    head.M = (int)(r1 * BM);
+    hipError_t e = dispatch_p2<CfgMain>(head, mode, out, accum, fuseq, st, p2);
+    if (e != hipSuccess) return e;
+    return dispatch_p2<CfgSmall>(row_part(a, out, fuseq, head.M), mode, out, accum, fuseq, st, p2);
+  }
   if (big) return dispatch_p2<CfgMain>(a, mode, out, accum, fuseq, st, p2);
   return dispatch_p2<CfgSmall>(a, mode, out, accum, fuseq, st, p2);
 }
