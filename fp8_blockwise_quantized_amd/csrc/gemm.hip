@@ -873,11 +873,11 @@ hipError_t launch_gemm(const GemmArgs& a, int mode, int out, bool accum, bool fu
 // the K steps into S contiguous ranges and (with one range) the rows into
 // groups of MT*16; a workgroup (4 wavefronts) computes the FP32 sum of one
 // (block, range, row group) through an NST-stage ring of direct
-// global->LDS loads (NST-1 steps of prefetch).  With S = 1 it writes Y (BF16
-// or FP32) and, for BF16, the fused 1x128 quantization of Y itself.  With
-// S > 1 it writes its partial sum to the caller's workspace P[S][M][N] and
-// k_skinny_finish sums the S partials in order s = 0..S-1 (deterministic)
-// and writes the same outputs.  (Finishing inside the split kernel, the last
+// global->LDS loads, KS K steps per stage ((NST-1)*KS steps of prefetch).
+// With S = 1 it writes Y (BF16 or FP32) and, for BF16, the fused 1x128
+// quantization of Y itself.  With S > 1 it writes its partial sum to the
+// caller's workspace P[S][M][N] and k_skinny_finish sums the S partials in
+// order s = 0..S-1 (deterministic) and writes the same outputs.  (Finishing inside the split kernel, the last
 // workgroup of a column block summing the others' partials, measured slower:
 // the partials then have to cross the XCDs' separate L2 caches through memory,
 // three dependent memory round trips at the end of every workgroup, where the
