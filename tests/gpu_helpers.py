@@ -104,10 +104,13 @@ def check_f32_output(got: np.ndarray, ref: np.ndarray, absprod: np.ndarray, what
     return rel
 
 
-def check_bf16_output(got: np.ndarray, ref: np.ndarray, absprod: np.ndarray, what: str) -> float:
+def check_bf16_output(got: np.ndarray, ref: np.ndarray, absprod: np.ndarray, what: str,
+                      fro: bool = True) -> float:
     """BF16 output rule: every element within one BF16 ulp of the float64
     reference plus ACC_ALLOW * sum_k|a_k b_k|, and relative Frobenius distance
-    to bf16_rne(fl32(reference)) <= FRO_BF16."""
+    to bf16_rne(fl32(reference)) <= FRO_BF16 (fro=False: the element rule
+    only, for a piece of an output whose Frobenius distance is checked whole
+    with bf16_frobenius)."""
     got = np.asarray(got, np.float64)
     a = np.abs(ref)
     ulp = np.ldexp(1.0, (np.floor(np.log2(np.maximum(a, 1e-300))) - 7).astype(np.int64))
@@ -118,7 +121,17 @@ def check_bf16_output(got: np.ndarray, ref: np.ndarray, absprod: np.ndarray, wha
         i = tuple(bad[0])
         raise AssertionError(f"{what}: {len(bad)} elements outside tolerance; first {i}: "
                              f"got {got[i]!r} want {ref[i]!r} tol {tol[i]!r}")
-    target = O.bf16_rne(O.fl32(ref)).astype(np.float64)
+    if not fro:
+        return 0.0
+    return bf16_frobenius([got], [ref], what)
+
+
+def bf16_frobenius(gots, refs, what: str) -> float:
+    """Relative Frobenius distance of BF16 outputs (given in pieces) to
+    bf16_rne(fl32(reference)), bounded by FRO_BF16 over the whole output."""
+    got = np.concatenate([np.asarray(g, np.float64).ravel() for g in gots])
+    target = np.concatenate([O.bf16_rne(O.fl32(np.asarray(r, np.float64))).astype(np.float64).ravel()
+                             for r in refs])
     den = np.linalg.norm(target)
     rel = float(np.linalg.norm(got - target) / den) if den > 0 else float(np.linalg.norm(got))
     assert rel <= FRO_BF16, f"{what}: relative Frobenius error {rel:.3e} > {FRO_BF16}"

@@ -13,8 +13,8 @@ import torch
 
 from oracle import jet_oracle as O
 from fp8_blockwise_quantized_amd import inputs
-from tests.gpu_helpers import (assert_bits_equal, check_bf16_output, check_f32_output, dev_bf16,
-                               host, oracle_absprod)
+from tests.gpu_helpers import (assert_bits_equal, bf16_frobenius, check_bf16_output, check_f32_output,
+                               dev_bf16, host, oracle_absprod)
 
 pytestmark = pytest.mark.gpu
 
@@ -141,6 +141,10 @@ def check_grouped(J, lens, N, K, seed, experts=None):
     yqh, ysh = host(yq), host(ys)
     col = O.segment_columns(seg)
     sampled = isinstance(r["wq"], dict)
+    # BF16 outputs: the element rule per expert, the Frobenius bound over all
+    # checked rows together (a one-row segment alone is 256 values, too few
+    # for a norm of the rounding differences to mean anything)
+    fy, ry, fdx, rdx = [], [], [], []
     for e in experts:
         lo, hi = int(seg[e]), int(seg[e + 1])
         tag = f"expert {e} rows {lo}:{hi}"
@@ -163,15 +167,32 @@ def check_grouped(J, lens, N, K, seed, experts=None):
             c0, c1 = int(col[e]), int(col[e + 1])
             dyqT_e, dysT_e = r["dyqT"][:, c0:c1], r["dysT"][c0 // 128:c1 // 128]
             xqT_e, xsT_e = r["xqT"][:, c0:c1], r["xsT"][c0 // 128:c1 // 128]
-        check_bf16_output(y16h[lo:hi], a_x @ b_w.T, oracle_absprod(a_x, b_w), f"grouped fwd {tag}")
-        check_bf16_output(dx16h[lo:hi], a_dy @ b_w, oracle_absprod(a_dy, b_w.T), f"grouped dgrad {tag}")
+        ref_y, ref_dx = a_x @ b_w.T, a_dy @ b_w
+        check_bf16_output(y16h[lo:hi], ref_y, oracle_absprod(a_x, b_w), f"grouped fwd {tag}", fro=False)
+        check_bf16_output(dx16h[lo:hi], ref_dx, oracle_absprod(a_dy, b_w.T), f"grouped dgrad {tag}", fro=False)
+        fy.append(y16h[lo:hi]); ry.append(ref_y); fdx.append(dx16h[lo:hi]); rdx.append(ref_dx)
         a_dyT = O.dequant_128x1_T(dyqT_e, dysT_e, hi - lo)
         a_xT = O.dequant_128x1_T(xqT_e, xsT_e, hi - lo)
         check_f32_output(dw32h[e], a_dyT @ a_xT.T, oracle_absprod(a_dyT, a_xT), f"grouped wgrad {tag}")
+    if fy:
+        bf16_frobenius(fy, ry, "grouped fwd, all checked experts")
+        bf16_frobenius(fdx, rdx, "grouped dgrad, all checked experts")
 
 
 def test_grouped_small_all_steps(gpu_lib):
     check_grouped(gpu_lib, LENS, 256, 384, seed=21)
+
+
+@pytest.mark.parametrize("E", [128, 200])
+def test_grouped_many_experts_all_steps(gpu_lib, E):
+    """128 experts (the wgrad takes them by decreasing contraction, found
+    from the offsets in registers) and 200 (more than one register pass over
+    the offsets: index order in wgrad, looped scans in the row-grouped
+    GEMMs); the lengths repeat (equal contractions), include empty segments
+    and cross 128- and 256-row boundaries.  Every expert checked."""
+    rng = np.random.default_rng(E)
+    lens = [int(v) for v in rng.choice([0, 1, 64, 127, 128, 129, 200, 255, 256, 257, 300], size=E)]
+    check_grouped(gpu_lib, lens, 256, 256, seed=E)
 
 
 def test_grouped_single_expert_equals_dense(gpu_lib):
