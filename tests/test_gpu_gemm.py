@@ -436,15 +436,19 @@ def test_training_shapes_sampled(gpu_lib, name):
 # --- grids of big tiles that end in a partial wave ----------------------------
 
 @pytest.mark.parametrize("pow2", [False, True])
-def test_partial_wave_split_gemms(gpu_lib, pow2):
-    """A 4096-token layer 4096 -> 4352 on 256 CUs: the forward's 16 x 17 grid
-    of 256 x 256 tiles runs as 16 x 16 big tiles plus the last 256 output
-    columns in 128 x 128 tiles; wgrad's 17 x 16 grid as 16 x 16 big tiles
-    plus the last 256 output rows in small ones.  BF16 forward with its fused
-    1x128 output, FP32 forward and FP32 wgrad (also accumulating) against
-    the oracle on sampled rows, half of them in the split-off part."""
+@pytest.mark.parametrize("M,N", [(4096, 4352), (4352, 3968)])
+def test_partial_wave_split_gemms(gpu_lib, pow2, M, N):
+    """Layers whose grids of 256 x 256 tiles end in a partial wave on 256
+    CUs.  4096 tokens, 4096 -> 4352: the forward's 16 x 17 grid runs as 16 x
+    16 big tiles plus the last 256 output columns in 128 x 128 tiles, and
+    wgrad's 17 x 16 grid as 16 x 16 big tiles plus the last 256 output rows
+    in small ones.  4352 tokens, 4096 -> 3968 (N not a multiple of the
+    256-column tile): the forward's 17 x 16 grid as 16 x 16 big tiles plus
+    the last 256 token rows in small ones.  BF16 forward with its fused 1x128 output, FP32
+    forward and FP32 wgrad (also accumulating) against the oracle on sampled
+    rows, half of them in the last 256 rows of each output."""
     J = gpu_lib
-    M, N, K = 4096, 4352, 4096
+    K = 4096
     x, w, dy = layer_inputs(M, N, K, 3)
     xd, wd, dyd = dev_bf16(x), dev_bf16(w), dev_bf16(dy)
     if pow2:
@@ -465,7 +469,9 @@ def test_partial_wave_split_gemms(gpu_lib, pow2):
     torch.cuda.synchronize()
     del xd, wd, dyd
     rng = np.random.default_rng(9)
-    rows = np.sort(rng.choice(M, 32, replace=False))
+    last256 = lambda n: np.sort(np.concatenate([rng.choice(n - 256, 16, replace=False),
+                                                n - 256 + rng.choice(256, 16, replace=False)]))
+    rows = last256(M)
     ridx = torch.from_numpy(rows).cuda()
     bw = O.dequant_128x128(host(wq), host(ws))
     ax = O.dequant_1x128(host(xq[ridx]), host(xs[:, ridx]))
@@ -478,8 +484,7 @@ def test_partial_wave_split_gemms(gpu_lib, pow2):
     assert_bits_equal(host(yq[ridx]), qo, f"split fused codes {tag}")
     assert_bits_equal(host(ys[:, ridx]), so, f"split fused scales {tag}")
     del bw
-    nrows = np.sort(np.concatenate([rng.choice(4096, 16, replace=False),
-                                    4096 + rng.choice(N - 4096, 16, replace=False)]))
+    nrows = last256(N)
     nidx = torch.from_numpy(nrows).cuda()
     a = O.dequant_128x1_T(host(dyqT[nidx]), host(dysT[:, nidx]), M)
     b = O.dequant_128x1_T(host(xqT), host(xsT), M)
